@@ -1,0 +1,314 @@
+"""Benchmark of the NVFP4 hot path on one MI355X.
+
+Headline workload (one "step"): an 8192 x 8192 BF16 activation tensor drawn
+from Student-t(3) is quantized to NVFP4 along rows and along columns
+(transpose re-quantization), each with round-to-nearest-even and with
+stochastic rounding, in separate calls and in the fused row+column call, each
+call computing its own tensor amax; the row and column results are then
+dequantized back to BF16.  `value` is the algorithmic bytes of the step
+(input read once + codes + scales per quantize call; codes + scales + output
+per dequantize call; the amax passes are not credited) divided by the step
+time, in GB/s.  Inputs rotate over 4 device buffers (512 MiB) so that
+consecutive steps do not hit in the 256 MB Infinity Cache.
+
+Also reported, on the same JSON line:
+  roofline     -- the dominant kernel of the step, timed alone with HIP events
+                  on the launch stream, against the 8 TB/s HBM peak;
+  cpu_baseline -- the CPU oracle on a bounded sample of the same step;
+  gemm         -- the block-scaled GEMMs: forward 8192x20480x5120 (BF16 out),
+                  weight-gradient 20480x5120x8192 (FP32 out, Hadamard + column
+                  blocks + SR operands) and the 32-expert MoE forward
+                  (up-projection with SwiGLU, quantize, down-projection), in
+                  TFLOP/s against the FP16 MFMA peak they run on and the FP4
+                  peak.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-gemm] [--no-cpu-baseline]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "NVFP4 quantize GB/s + block-scaled GEMM TFLOP/s, % of MI355X peaks"
+HBM_PEAK_GBS = 8000.0
+FP16_PEAK_TFLOPS = 2500.0
+FP4_PEAK_TFLOPS = 10100.0
+N = 8192
+NBUF = 4
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def bf16_device(bits, torch, np):
+    return torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def time_events(fn, reps, torch):
+    """Average duration (ms) of fn() over reps calls, HIP events on the
+    current stream (the stream the binding launches on)."""
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    fn(0)
+    torch.cuda.synchronize()
+    e0.record(s)
+    for i in range(reps):
+        fn(i)
+    e1.record(s)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("quantize.hip", "nvfp4_device.hpp", "gemm.hip"):
+        with open(os.path.join(ROOT, "bit_block_scaled_quantize_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel_key):
+    """HBM bytes per launch of `kernel_key` from the committed counter
+    summary, or None when absent or taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        t = json.load(fh)
+    if t.get("source_hash") != kernel_source_hash():
+        return None
+    k = t.get("kernels", {}).get(kernel_key)
+    return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-gemm", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernel-reps", type=int, default=20)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the NVFP4 path here has no multi-GPU mode)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import bit_block_scaled_quantize_amd as nv
+    import workloads as W
+
+    torch.cuda.set_device(0)
+    log("generating inputs")
+    xs = [bf16_device(W.f32_to_bf16_bits(W.student_t((N, N), 3.0, seed=1000 + i)), torch, np)
+          for i in range(NBUF)]
+    dev = "cuda"
+    E = N * N
+
+    R, C = nv.NVFP4Tensor.empty(N, N, device=dev), nv.NVFP4Tensor.empty(N, N, device=dev)
+    R2, C2 = nv.NVFP4Tensor.empty(N, N, device=dev), nv.NVFP4Tensor.empty(N, N, device=dev)
+    Q2d = nv.NVFP4Tensor.empty(N, N, nv.NVFP4_SCALE_2D, device=dev)
+    yr = torch.empty((N, N), dtype=torch.bfloat16, device=dev)
+    yc = torch.empty((N, N), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(nv.nvfp4_quantize_workspace_size(N, N) // 4 + 4, dtype=torch.float32, device=dev)
+    amax = [torch.tensor([x.float().abs().max().item()], device=dev) for x in xs]
+
+    ROW, COL, RC = nv.NVFP4_ROW_1D, nv.NVFP4_COL_1D, nv.NVFP4_ROW_COL_1D
+    RNE, SR = nv.NVFP4_RNE, nv.NVFP4_SR
+    q1 = E * 2 + E // 2 + E // 16 + 4                    # one layout: bf16 in, codes, scales
+    q2 = E * 2 + 2 * (E // 2 + E // 16) + 8              # fused row+column
+    dq = E // 2 + E // 16 + 4 + E * 2                    # dequantize to bf16
+    step_ops = [("quant_row_rne", ROW, RNE, q1), ("quant_row_sr", ROW, SR, q1),
+                ("quant_col_rne", COL, RNE, q1), ("quant_col_sr", COL, SR, q1),
+                ("quant_rowcol_rne", RC, RNE, q2), ("quant_rowcol_sr", RC, SR, q2)]
+    step_bytes = sum(op[3] for op in step_ops) + 2 * dq
+
+    def step(i):
+        x = xs[i % NBUF]
+        for _, lay, rnd, _ in step_ops:
+            out = (R2, C2) if lay == RC else (C if lay == COL else R)
+            nv.nvfp4_quantize(x, layout=lay, round=rnd, sr_seed=77 + i, out=out, workspace=ws)
+        nv.nvfp4_dequantize(R, out=yr)
+        nv.nvfp4_dequantize(C, out=yc)
+
+    log("warmup")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log("timed steps")
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / args.steps
+    value = step_bytes / (ms * 1e-3) / 1e9
+
+    # ---- per-kernel durations (amax given, so each call is one kernel)
+    log("per-kernel timing")
+    reps = args.kernel_reps
+    kern = {}
+
+    def qk(lay, rnd, out):
+        return lambda i: nv.nvfp4_quantize(xs[i % NBUF], layout=lay, round=rnd, sr_seed=5,
+                                           amax_in=amax[i % NBUF], out=out)
+
+    for name, lay, rnd, b in step_ops:
+        out = (R2, C2) if lay == RC else (C if lay == COL else R)
+        kern[name] = dict(ms=time_events(qk(lay, rnd, out), reps, torch), bytes=b)
+    kern["quant_2d_rne"] = dict(ms=time_events(qk(nv.NVFP4_BLK_2D, RNE, Q2d), reps, torch), bytes=q1)
+    kern["dequant_row_bf16"] = dict(ms=time_events(lambda i: nv.nvfp4_dequantize(R, out=yr), reps, torch),
+                                    bytes=dq)
+    amax_ms = time_events(lambda i: nv.nvfp4_quantize(xs[i % NBUF], layout=ROW, out=R, workspace=ws),
+                          reps, torch) - kern["quant_row_rne"]["ms"]
+    kern["amax_pass"] = dict(ms=amax_ms, bytes=E * 2)
+    for k, v in kern.items():
+        v["gbs"] = v["bytes"] / (v["ms"] * 1e-3) / 1e9
+        v["frac_hbm"] = v["gbs"] / HBM_PEAK_GBS
+    # time share in the step: each quantize call = amax pass + its kernel
+    share = {k: kern[k]["ms"] for k, *_ in step_ops}
+    share["amax_pass"] = amax_ms * len(step_ops)
+    share["dequant_row_bf16"] = 2 * kern["dequant_row_bf16"]["ms"]
+    dom = max((k for k in share if k != "amax_pass"), key=lambda k: share[k])
+    dk = kern[dom]
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": round(dk["gbs"], 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(dk["frac_hbm"], 4), "traffic": traffic_for(dom),
+                "avg_launch_ms": round(dk["ms"], 5), "algorithmic_bytes_per_launch": dk["bytes"]}
+
+    result = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "quantize_8192x8192_bf16_student_t3", "rows": N, "cols": N,
+                   "input": "bf16", "step": [k for k, *_ in step_ops] + ["dequant_row_bf16",
+                                                                       "dequant_col_bf16"],
+                   "amax": "computed per quantize call (current scaling)",
+                   "bytes_per_step": step_bytes, "input_buffers": NBUF},
+        "roofline": roofline,
+        "kernels": {k: {"ms": round(v["ms"], 5), "GB/s": round(v["gbs"], 1),
+                        "frac_hbm": round(v["frac_hbm"], 4)} for k, v in kern.items()},
+    }
+
+    del xs
+    torch.cuda.empty_cache()
+    if not args.no_gemm:
+        result["gemm"] = bench_gemm(nv, W, np, torch, reps=max(3, reps // 4))
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(np, W)
+    print(json.dumps(result), flush=True)
+
+
+def bench_gemm(nv, W, np, torch, reps):
+    """Block-scaled GEMM throughput at the forward, weight-gradient and MoE
+    shapes; operands are quantized on the GPU from seeded inputs."""
+    out = {}
+
+    def gen(shape, seed, kind):
+        if kind == "t3":
+            x = W.student_t(shape, 3.0, seed=seed)
+        elif kind == "w":
+            x = W.normal(shape, 0.02, seed=seed)
+        else:
+            x = W.with_spikes(W.normal(shape, 1.0, seed=seed), 1e-4, 100.0, seed=seed + 1)
+        return bf16_device(W.f32_to_bf16_bits(x), torch, np)
+
+    def entry(name, flop, ms):
+        tf = flop / (ms * 1e-3) / 1e12
+        out[name] = {"ms": round(ms, 4), "TFLOP/s": round(tf, 1),
+                     "frac_fp16_mfma_peak": round(tf / FP16_PEAK_TFLOPS, 4),
+                     "frac_fp4_mfma_peak": round(tf / FP4_PEAK_TFLOPS, 4)}
+
+    log("gemm: forward")
+    X = nv.nvfp4_quantize(gen((8192, 5120), 4000, "t3"))
+    Wt = nv.nvfp4_quantize(gen((20480, 5120), 4001, "w"), layout=nv.NVFP4_BLK_2D)
+    Y = torch.empty((8192, 20480), dtype=torch.bfloat16, device="cuda")
+    entry("forward_8192x20480x5120_bf16", 2 * 8192 * 20480 * 5120,
+          time_events(lambda i: nv.nvfp4_gemm(X, Wt, out=Y), reps, torch))
+    del X, Wt, Y
+    log("gemm: wgrad")
+    kw = dict(layout=nv.NVFP4_COL_1D, round=nv.NVFP4_SR, hadamard=True, hadamard_seed=5200)
+    dYq = nv.nvfp4_quantize(gen((8192, 20480), 5000, "spiky"), sr_seed=5100, **kw)
+    Xq = nv.nvfp4_quantize(gen((8192, 5120), 5002, "spiky"), sr_seed=5101, **kw)
+    dW = torch.empty((20480, 5120), dtype=torch.float32, device="cuda")
+    entry("wgrad_20480x5120x8192_f32", 2 * 20480 * 5120 * 8192,
+          time_events(lambda i: nv.nvfp4_gemm(dYq, Xq, out=dW), reps, torch))
+    del dYq, Xq, dW
+    torch.cuda.empty_cache()
+
+    log("gemm: moe")
+    E, Hd, F, T = 32, 7168, 2048, 16384
+    counts = W.zipf_expert_counts(E, T, 4, 1.1)
+    offs, token = W.moe_routing(counts, T)
+    Xq = nv.nvfp4_quantize(gen((T, Hd), 6000, "t3"))
+    idx = torch.from_numpy(token).cuda()
+    A = nv.NVFP4Tensor(Xq.codes.index_select(0, idx), Xq.scales.index_select(0, idx),
+                       Xq.tensor_scale, int(offs[-1]), Hd)
+
+    def stacked(rows, cols, seed):
+        Wq = nv.NVFP4Tensor.empty(E * rows, cols, nv.NVFP4_SCALE_2D, n_scales=E)
+        for e in range(E):
+            q = nv.nvfp4_quantize(gen((rows, cols), seed + e, "w"), layout=nv.NVFP4_BLK_2D)
+            Wq.codes[e * rows:(e + 1) * rows].copy_(q.codes)
+            Wq.scales[e * rows // 16:(e + 1) * rows // 16].copy_(q.scales)
+            Wq.tensor_scale[e:e + 1].copy_(q.tensor_scale)
+        return Wq
+
+    W1 = stacked(2 * F, Hd, 6100)
+    W2 = stacked(Hd, F, 6200)
+    offs_d = torch.from_numpy(offs).cuda()
+    H = torch.empty((int(offs[-1]), F), dtype=torch.bfloat16, device="cuda")
+    Y = torch.empty((int(offs[-1]), Hd), dtype=torch.bfloat16, device="cuda")
+    amax = torch.zeros(1, dtype=torch.float32, device="cuda")
+    Hq = nv.NVFP4Tensor.empty(int(offs[-1]), F)
+    rows = int(offs[-1])
+    up_flop = 2 * rows * 2 * F * Hd
+    down_flop = 2 * rows * Hd * F
+    up_ms = time_events(lambda i: nv.nvfp4_grouped_gemm(A, offs_d, W1, E, epilogue=nv.NVFP4_EPI_SWIGLU,
+                                                        out=H, amax_out=amax), reps, torch)
+    q_ms = time_events(lambda i: nv.nvfp4_quantize(H, amax_in=amax, out=Hq), reps, torch)
+    down_ms = time_events(lambda i: nv.nvfp4_grouped_gemm(Hq, offs_d, W2, E, out=Y), reps, torch)
+    entry("moe_up_swiglu_65536x4096x7168", up_flop, up_ms)
+    entry("moe_down_65536x7168x2048", down_flop, down_ms)
+    entry("moe_expert_forward_total", up_flop + down_flop, up_ms + q_ms + down_ms)
+    out["moe_expert_forward_total"]["quantize_h_ms"] = round(q_ms, 4)
+    return out
+
+
+def cpu_baseline(np, W):
+    """The oracle on rows 0..2047 of the step's input (a quarter of the
+    tensor): the same quantize calls and dequantizations, single thread."""
+    import oracle as O
+    rows = 2048
+    x = W.f32_to_bf16_bits(W.student_t((N, N), 3.0, seed=1000))[:rows].copy()
+    E = rows * N
+    t0 = time.perf_counter()
+    for lay in (O.ROW_1D, O.COL_1D):
+        for rnd in (O.RNE, O.SR):
+            O.quantize(x, O.BF16, lay, rnd, sr_seed=77)
+    for rnd in (O.RNE, O.SR):
+        qr, qc = O.quantize(x, O.BF16, O.ROW_COL_1D, rnd, sr_seed=77)
+    O.dequantize(qr, O.BF16)
+    O.dequantize(qc, O.BF16)
+    dt = time.perf_counter() - t0
+    q1 = E * 2 + E // 2 + E // 16 + 4
+    q2 = E * 2 + 2 * (E // 2 + E // 16) + 8
+    dq = E // 2 + E // 16 + 4 + E * 2
+    b = 4 * q1 + 2 * q2 + 2 * dq
+    return {"value": round(b / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"rows 0..{rows - 1} of the 8192x8192 step input; the full step's quantize and "
+                      f"dequantize calls; {dt:.1f} s single-threaded"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,52 @@
+// Internal host interface between the C-ABI layer (nvfp4_api.hip) and the
+// kernel translation units.  Arguments are already validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+namespace nvfp4 {
+
+enum { kLayoutRow = 0, kLayoutCol = 1, kLayoutRowCol = 2, kLayout2D = 3 };
+
+// Upper bound on the per-workgroup partial maxima of one amax pass; the
+// quantize workspace holds 4 floats (the final amax, padded) + kMaxPartials.
+constexpr int64_t kMaxPartials = 2048;
+constexpr size_t kQuantWorkspaceBytes = (size_t)(4 + kMaxPartials) * sizeof(float);
+
+struct QOut {
+    uint8_t* codes;
+    uint8_t* scales;
+    float* ts;
+};
+
+hipError_t launch_quantize(const void* x, bool bf16, int64_t rows, int64_t cols, int64_t ld,
+                           int layout, bool sr, uint64_t seed, bool rht, uint64_t hseed,
+                           const float* amax_in, const QOut* out, float* ws, hipStream_t s);
+
+hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, const float* ts,
+                             int64_t rows, int64_t cols, bool scale_2d, void* y, bool bf16,
+                             int64_t ld, hipStream_t s);
+
+// One GEMM operand as the kernels see it.
+struct Operand {
+    const uint8_t* codes;   // rows x K/2
+    const uint8_t* scales;  // 1D: rows x K/16; 2D: rows/16 x K/16
+    const float* ts;        // tensor scale(s)
+    int scale_2d;
+};
+
+// C (M x N, ldc) = A * B^T; c_bf16 selects the output type.
+hipError_t launch_gemm(const Operand& A, const Operand& B, int64_t M, int64_t N, int64_t K,
+                       void* C, bool c_bf16, int64_t ldc, hipStream_t s);
+
+// Grouped GEMM over G groups (see nvfp4_grouped_gemm).  n_per_group = rows of
+// one group's weight matrix; swiglu halves the output width.
+hipError_t launch_grouped_gemm(int G, const Operand& A, const int64_t* offsets, int64_t total_rows,
+                               const Operand& B, int64_t n_per_group, int64_t K, void* C,
+                               bool c_bf16, int64_t ldc, bool swiglu, float* amax_out,
+                               hipStream_t s);
+
+}  // namespace nvfp4

@@ -1,0 +1,203 @@
+// C ABI of the NVFP4 library (declared in include/nvfp4.h): host-side argument
+// validation, then dispatch to the kernel launchers.  No entry point allocates
+// memory or keeps state; every error is reported before anything is enqueued.
+#include "nvfp4.h"
+
+#include <hip/hip_runtime.h>
+
+#include "launch.hpp"
+
+using namespace nvfp4;
+
+namespace {
+
+constexpr int64_t kMaxGridY = 65535;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t dtype_size(int dt) { return dt == NVFP4_BF16 ? 2 : 4; }
+
+bool valid_dtype(int dt) { return dt == NVFP4_F32 || dt == NVFP4_BF16; }
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// The output tensor a layout implies for an input of rows x cols.
+nvfp4_status check_out(const nvfp4_tensor* t, int64_t r, int64_t c, int mode) {
+    if (!t->tensor_scale) return NVFP4_ERR_NULL;
+    if (r > 0 && c > 0 && (!t->codes || !t->scales)) return NVFP4_ERR_NULL;
+    if (t->rows != r || t->cols != c || t->scale_mode != mode) return NVFP4_ERR_SHAPE;
+    if (!aligned(t->codes, 16)) return NVFP4_ERR_ALIGN;
+    return NVFP4_OK;
+}
+
+// A GEMM operand: shape, scale layout, pointers, alignment.
+nvfp4_status check_operand(const nvfp4_tensor* t) {
+    if (!t) return NVFP4_ERR_NULL;
+    if (t->rows < 0 || t->cols < 0) return NVFP4_ERR_SHAPE;
+    if (t->scale_mode != NVFP4_SCALE_1D && t->scale_mode != NVFP4_SCALE_2D) return NVFP4_ERR_ENUM;
+    if (t->cols % 16) return NVFP4_ERR_SHAPE;
+    if (t->scale_mode == NVFP4_SCALE_2D && t->rows % 16) return NVFP4_ERR_SHAPE;
+    if (t->rows > 0 && t->cols > 0 && (!t->codes || !t->scales)) return NVFP4_ERR_NULL;
+    if (!t->tensor_scale) return NVFP4_ERR_NULL;
+    if (!aligned(t->codes, 16)) return NVFP4_ERR_ALIGN;
+    return NVFP4_OK;
+}
+
+Operand as_operand(const nvfp4_tensor* t) {
+    return Operand{t->codes, t->scales, t->tensor_scale, t->scale_mode == NVFP4_SCALE_2D ? 1 : 0};
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t nvfp4_quantize_workspace_size(int64_t rows, int64_t cols, const nvfp4_quant_opts* opts) {
+    (void)rows;
+    (void)cols;
+    if (opts && opts->amax_in) return 0;
+    return kQuantWorkspaceBytes;
+}
+
+nvfp4_status nvfp4_quantize(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols, int64_t ld,
+                            const nvfp4_quant_opts* opts, nvfp4_tensor* out, void* ws,
+                            size_t ws_bytes, void* stream) {
+    if (!opts || !out) return NVFP4_ERR_NULL;
+    if (!valid_dtype(dt)) return NVFP4_ERR_ENUM;
+    const int layout = opts->layout;
+    if (layout < NVFP4_ROW_1D || layout > NVFP4_BLK_2D) return NVFP4_ERR_ENUM;
+    if (opts->round != NVFP4_RNE && opts->round != NVFP4_SR) return NVFP4_ERR_ENUM;
+    if (rows < 0 || cols < 0 || ld < cols) return NVFP4_ERR_SHAPE;
+    const bool row_blocks = layout == NVFP4_ROW_1D || layout == NVFP4_ROW_COL_1D || layout == NVFP4_BLK_2D;
+    const bool col_blocks = layout == NVFP4_COL_1D || layout == NVFP4_ROW_COL_1D || layout == NVFP4_BLK_2D;
+    if (row_blocks && cols % 16) return NVFP4_ERR_SHAPE;
+    if (col_blocks && rows % 16) return NVFP4_ERR_SHAPE;
+    if (opts->hadamard && (layout == NVFP4_BLK_2D || layout == NVFP4_ROW_COL_1D))
+        return NVFP4_ERR_UNSUPPORTED;
+    const bool empty = rows == 0 || cols == 0;
+    if (!empty && !x) return NVFP4_ERR_NULL;
+    if (!aligned(x, 16) || (ld * (int64_t)dtype_size(dt)) % 16) return NVFP4_ERR_ALIGN;
+
+    nvfp4_status st;
+    switch (layout) {
+        case NVFP4_ROW_1D: st = check_out(&out[0], rows, cols, NVFP4_SCALE_1D); break;
+        case NVFP4_COL_1D: st = check_out(&out[0], cols, rows, NVFP4_SCALE_1D); break;
+        case NVFP4_BLK_2D: st = check_out(&out[0], rows, cols, NVFP4_SCALE_2D); break;
+        default:
+            st = check_out(&out[0], rows, cols, NVFP4_SCALE_1D);
+            if (st == NVFP4_OK) st = check_out(&out[1], cols, rows, NVFP4_SCALE_1D);
+    }
+    if (st != NVFP4_OK) return st;
+
+    // grid-size limits of the launches (y dimensions)
+    if (cdiv(cols, 1024) > kMaxGridY || cdiv(cols, 64) > kMaxGridY) return NVFP4_ERR_UNSUPPORTED;
+    if (cdiv(rows, 16) > 0x7FFFFFFF) return NVFP4_ERR_UNSUPPORTED;
+
+    if (!empty && !opts->amax_in) {
+        if (!ws) return NVFP4_ERR_WORKSPACE;
+        if (ws_bytes < kQuantWorkspaceBytes) return NVFP4_ERR_WORKSPACE;
+        if (!aligned(ws, 16)) return NVFP4_ERR_ALIGN;
+    }
+
+    QOut o[2];
+    o[0] = QOut{out[0].codes, out[0].scales, out[0].tensor_scale};
+    if (layout == NVFP4_ROW_COL_1D) o[1] = QOut{out[1].codes, out[1].scales, out[1].tensor_scale};
+    else o[1] = QOut{nullptr, nullptr, nullptr};
+    hipError_t e = launch_quantize(x, dt == NVFP4_BF16, rows, cols, ld, layout, opts->round == NVFP4_SR,
+                                   opts->sr_seed, opts->hadamard != 0, opts->hadamard_seed,
+                                   opts->amax_in, o, static_cast<float*>(ws),
+                                   static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
+}
+
+nvfp4_status nvfp4_dequantize(const nvfp4_tensor* q, void* y, nvfp4_dtype dt, int64_t ld,
+                              void* stream) {
+    if (!q) return NVFP4_ERR_NULL;
+    if (!valid_dtype(dt)) return NVFP4_ERR_ENUM;
+    nvfp4_status st = check_operand(q);
+    if (st != NVFP4_OK) return st;
+    if (ld < q->cols) return NVFP4_ERR_SHAPE;
+    const bool empty = q->rows == 0 || q->cols == 0;
+    if (!empty && !y) return NVFP4_ERR_NULL;
+    if (!aligned(y, 16) || (ld * (int64_t)dtype_size(dt)) % 16) return NVFP4_ERR_ALIGN;
+    if (cdiv(q->cols / 16, 64) > kMaxGridY) return NVFP4_ERR_UNSUPPORTED;
+    hipError_t e = launch_dequantize(q->codes, q->scales, q->tensor_scale, q->rows, q->cols,
+                                     q->scale_mode == NVFP4_SCALE_2D, y, dt == NVFP4_BF16, ld,
+                                     static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
+}
+
+nvfp4_status nvfp4_gemm(const nvfp4_tensor* A, const nvfp4_tensor* B, void* C, nvfp4_dtype c_dt,
+                        int64_t ldc, nvfp4_epilogue ep, void* stream) {
+    if (!A || !B) return NVFP4_ERR_NULL;
+    if (!valid_dtype(c_dt)) return NVFP4_ERR_ENUM;
+    if (ep != NVFP4_EPI_NONE && ep != NVFP4_EPI_SWIGLU) return NVFP4_ERR_ENUM;
+    if (ep != NVFP4_EPI_NONE) return NVFP4_ERR_UNSUPPORTED;
+    nvfp4_status st = check_operand(A);
+    if (st != NVFP4_OK) return st;
+    st = check_operand(B);
+    if (st != NVFP4_OK) return st;
+    if (A->cols != B->cols) return NVFP4_ERR_SHAPE;
+    const int64_t M = A->rows, N = B->rows, K = A->cols;
+    if (ldc < N) return NVFP4_ERR_SHAPE;
+    if (M > 0 && N > 0 && !C) return NVFP4_ERR_NULL;
+    if (!aligned(C, dtype_size(c_dt))) return NVFP4_ERR_ALIGN;
+    if (cdiv(M, 128) > kMaxGridY) return NVFP4_ERR_UNSUPPORTED;
+    hipError_t e = launch_gemm(as_operand(A), as_operand(B), M, N, K, C, c_dt == NVFP4_BF16, ldc,
+                               static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
+}
+
+nvfp4_status nvfp4_grouped_gemm(int32_t G, const nvfp4_tensor* A, const int64_t* offsets,
+                                const nvfp4_tensor* B, void* C, nvfp4_dtype c_dt, int64_t ldc,
+                                nvfp4_epilogue ep, float* amax_out, void* ws, size_t ws_bytes,
+                                void* stream) {
+    (void)ws;
+    (void)ws_bytes;
+    if (!A || !B || !offsets) return NVFP4_ERR_NULL;
+    if (!valid_dtype(c_dt)) return NVFP4_ERR_ENUM;
+    if (ep != NVFP4_EPI_NONE && ep != NVFP4_EPI_SWIGLU) return NVFP4_ERR_ENUM;
+    if (G < 1) return NVFP4_ERR_SHAPE;
+    nvfp4_status st = check_operand(A);
+    if (st != NVFP4_OK) return st;
+    st = check_operand(B);
+    if (st != NVFP4_OK) return st;
+    if (A->scale_mode != NVFP4_SCALE_1D) return NVFP4_ERR_UNSUPPORTED;
+    if (A->cols != B->cols) return NVFP4_ERR_SHAPE;
+    if (B->rows % G) return NVFP4_ERR_SHAPE;
+    const int64_t Ng = B->rows / G, K = A->cols, total = A->rows;
+    if (B->scale_mode == NVFP4_SCALE_2D && Ng % 16) return NVFP4_ERR_SHAPE;
+    const bool swiglu = ep == NVFP4_EPI_SWIGLU;
+    if (swiglu) {
+        if (Ng % 2 || (Ng / 2) % 16) return NVFP4_ERR_SHAPE;
+        if (c_dt != NVFP4_BF16) return NVFP4_ERR_UNSUPPORTED;
+    } else if (amax_out) {
+        return NVFP4_ERR_UNSUPPORTED;
+    }
+    const int64_t ncols = swiglu ? Ng / 2 : Ng;
+    if (ldc < ncols) return NVFP4_ERR_SHAPE;
+    if (total > 0 && ncols > 0 && !C) return NVFP4_ERR_NULL;
+    if (!aligned(C, dtype_size(c_dt))) return NVFP4_ERR_ALIGN;
+    if (cdiv(total, 128) + G > kMaxGridY) return NVFP4_ERR_UNSUPPORTED;
+    hipError_t e = launch_grouped_gemm(G, as_operand(A), offsets, total, as_operand(B), Ng, K, C,
+                                       c_dt == NVFP4_BF16, ldc, swiglu, amax_out,
+                                       static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
+}
+
+const char* nvfp4_status_string(nvfp4_status s) {
+    switch (s) {
+        case NVFP4_OK: return "ok";
+        case NVFP4_ERR_NULL: return "a required pointer is NULL";
+        case NVFP4_ERR_ENUM: return "an enum argument is out of range";
+        case NVFP4_ERR_SHAPE: return "invalid or inconsistent shape";
+        case NVFP4_ERR_ALIGN: return "pointer or leading dimension misaligned";
+        case NVFP4_ERR_UNSUPPORTED: return "unsupported combination";
+        case NVFP4_ERR_WORKSPACE: return "workspace missing or too small";
+        case NVFP4_ERR_HIP: return "HIP launch error";
+    }
+    return "unknown status";
+}
+
+int32_t nvfp4_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,133 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+declared in include/nvfp4.h, and rejects invalid arguments on the host
+before anything is launched (those paths make no HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4.h")
+
+
+@pytest.fixture(scope="module")
+def nv():
+    import bit_block_scaled_quantize_amd.nvfp4 as nv
+    return nv
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(nvfp4_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_four_operations():
+    fns = declared_functions()
+    for f in ["nvfp4_quantize", "nvfp4_dequantize", "nvfp4_gemm", "nvfp4_grouped_gemm"]:
+        assert f in fns
+
+
+def test_library_exports_every_declared_symbol(nv):
+    lib = ctypes.CDLL(nv.LIB_PATH)
+    for f in declared_functions():
+        assert hasattr(lib, f), f
+    assert sorted(nv.EXPORTED) == declared_functions()
+
+
+def test_status_strings_and_version(nv):
+    for s in range(8):
+        assert nv.lib.nvfp4_status_string(s)
+    assert nv.lib.nvfp4_version() >= 100
+
+
+def test_workspace_size(nv):
+    assert nv.nvfp4_quantize_workspace_size(8192, 8192) > 0
+    o = nv.CQuantOpts(0, 0, 0, 0, 0, 1234)
+    assert nv.lib.nvfp4_quantize_workspace_size(8192, 8192, ctypes.byref(o)) == 0
+
+
+def _t(rows, cols, mode=0, codes=4096, scales=8192, ts=16384):
+    import bit_block_scaled_quantize_amd.nvfp4 as nv
+    return nv.CTensor(codes, scales, ts, rows, cols, mode)
+
+
+def _quant(nv, x=65536, dt=1, rows=32, cols=32, ld=32, layout=0, rnd=0, had=0, outs=None,
+           ws=1 << 20, ws_bytes=1 << 20, amax=None):
+    o = nv.CQuantOpts(layout, rnd, 1, had, 2, amax)
+    arr = (nv.CTensor * 2)()
+    if outs is None:
+        outs = [_t(rows, cols)]
+    for i, t in enumerate(outs):
+        arr[i] = t
+    return nv.lib.nvfp4_quantize(x, dt, rows, cols, ld, ctypes.byref(o), arr, ws, ws_bytes, None)
+
+
+def test_quantize_rejects_bad_arguments(nv):
+    E = dict(NULL=1, ENUM=2, SHAPE=3, ALIGN=4, UNSUP=5, WS=6)
+    assert _quant(nv, x=None) == E["NULL"]
+    assert _quant(nv, dt=7) == E["ENUM"]
+    assert _quant(nv, layout=9) == E["ENUM"]
+    assert _quant(nv, rnd=5) == E["ENUM"]
+    assert _quant(nv, cols=24, ld=32, outs=[_t(32, 24)]) == E["SHAPE"]        # cols % 16
+    assert _quant(nv, rows=24, layout=1, outs=[_t(32, 24)]) == E["SHAPE"]     # rows % 16 (COL)
+    assert _quant(nv, ld=16) == E["SHAPE"]                                     # ld < cols
+    assert _quant(nv, ld=36) == E["ALIGN"]                                     # 72 bytes
+    assert _quant(nv, x=65536 + 2) == E["ALIGN"]
+    assert _quant(nv, layout=3, had=1, outs=[_t(32, 32, 1)]) == E["UNSUP"]
+    assert _quant(nv, layout=2, had=1, outs=[_t(32, 32), _t(32, 32)]) == E["UNSUP"]
+    assert _quant(nv, outs=[_t(32, 32, 1)]) == E["SHAPE"]                     # wrong scale mode
+    assert _quant(nv, layout=1, outs=[_t(32, 64)]) == E["SHAPE"]              # COL output shape
+    assert _quant(nv, outs=[_t(32, 32, codes=None)]) == E["NULL"]
+    assert _quant(nv, outs=[_t(32, 32, codes=4100)]) == E["ALIGN"]
+    assert _quant(nv, ws=None) == E["WS"]
+    assert _quant(nv, ws_bytes=16) == E["WS"]
+
+
+def test_dequantize_rejects_bad_arguments(nv):
+    q = _t(32, 32)
+    assert nv.lib.nvfp4_dequantize(None, 65536, 0, 32, None) == 1
+    assert nv.lib.nvfp4_dequantize(ctypes.byref(q), None, 0, 32, None) == 1
+    assert nv.lib.nvfp4_dequantize(ctypes.byref(q), 65536, 3, 32, None) == 2
+    assert nv.lib.nvfp4_dequantize(ctypes.byref(q), 65536, 0, 16, None) == 3
+    assert nv.lib.nvfp4_dequantize(ctypes.byref(q), 65540, 0, 32, None) == 4
+    bad = _t(32, 24)
+    assert nv.lib.nvfp4_dequantize(ctypes.byref(bad), 65536, 0, 32, None) == 3
+    bad2 = _t(24, 32, 1)
+    assert nv.lib.nvfp4_dequantize(ctypes.byref(bad2), 65536, 0, 32, None) == 3
+
+
+def test_gemm_rejects_bad_arguments(nv):
+    a, b = _t(64, 64), _t(32, 64)
+    g = nv.lib.nvfp4_gemm
+    assert g(None, ctypes.byref(b), 65536, 0, 32, 0, None) == 1
+    assert g(ctypes.byref(a), ctypes.byref(b), 65536, 9, 32, 0, None) == 2
+    assert g(ctypes.byref(a), ctypes.byref(b), 65536, 0, 32, 1, None) == 5     # SwiGLU is grouped-only
+    b2 = _t(32, 48)
+    assert g(ctypes.byref(a), ctypes.byref(b2), 65536, 0, 32, 0, None) == 3    # K mismatch
+    assert g(ctypes.byref(a), ctypes.byref(b), 65536, 0, 16, 0, None) == 3     # ldc < N
+    assert g(ctypes.byref(a), ctypes.byref(b), None, 0, 32, 0, None) == 1
+    a3 = _t(64, 40)
+    b3 = _t(32, 40)
+    assert g(ctypes.byref(a3), ctypes.byref(b3), 65536, 0, 32, 0, None) == 3   # K % 16
+
+
+def test_grouped_gemm_rejects_bad_arguments(nv):
+    a, b = _t(100, 64), _t(4 * 32, 64, 1)
+    g = nv.lib.nvfp4_grouped_gemm
+    args = lambda **k: dict(dict(G=4, A=ctypes.byref(a), off=65536, B=ctypes.byref(b), C=65536,
+                                 dt=1, ldc=32, ep=0, amax=None), **k)
+
+    def call(d):
+        return g(d["G"], d["A"], d["off"], d["B"], d["C"], d["dt"], d["ldc"], d["ep"], d["amax"],
+                 None, 0, None)
+
+    assert call(args(off=None)) == 1
+    assert call(args(G=0)) == 3
+    assert call(args(G=3)) == 3                      # B rows not divisible by G
+    assert call(args(ep=1, dt=0, ldc=16)) == 5       # SwiGLU needs bf16 output
+    assert call(args(ep=1, ldc=8)) == 3              # ldc < F
+    assert call(args(amax=65536)) == 5               # amax only with SwiGLU
+    a2 = _t(100, 64, 1)
+    assert call(args(A=ctypes.byref(a2))) == 3 or call(args(A=ctypes.byref(a2))) == 5

@@ -1,0 +1,261 @@
+"""GPU parity of the block-scaled GEMM and grouped GEMM against the oracle's
+float64 dequantize-then-matmul: |gpu - oracle| <= 1e-5 * sum_k |a_k b_k| per
+element (plus half a bf16 ulp for bf16 outputs)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+from parity_utils import bf16_tensor_to_bits, gemm_tol, q_to_device, q_to_host, require_gpu, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def nv():
+    return require_gpu()
+
+
+def out_to_f64(t):
+    torch.cuda.synchronize()
+    if t.dtype == torch.bfloat16:
+        return W.bf16_bits_to_f32(bf16_tensor_to_bits(t)).astype(np.float64)
+    return t.cpu().numpy().astype(np.float64)
+
+
+def check(got, Cref, Wref, bf16_out, what):
+    tol = gemm_tol(Cref, Wref, bf16_out)
+    err = np.abs(got - Cref)
+    bad = err > tol
+    if bad.any():
+        i = np.argwhere(bad)[0]
+        raise AssertionError(f"{what}: {bad.sum()} entries out of tolerance, first {i.tolist()}: "
+                             f"gpu={got[tuple(i)]!r} ref={Cref[tuple(i)]!r} tol={tol[tuple(i)]!r}")
+
+
+def quant_host(x, layout, rnd=O.RNE, seed=0):
+    return O.quantize(x, O.F32, layout, rnd, sr_seed=seed)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 16), (32, 32, 64), (100, 70, 80), (130, 260, 1040),
+                                   (300, 128, 4112), (257, 129, 48)])
+@pytest.mark.parametrize("bmode", [O.ROW_1D, O.BLK_2D])
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_gemm_small(nv, M, N, K, bmode, out):
+    if bmode == O.BLK_2D and N % 16:
+        N = (N + 15) // 16 * 16
+    a = W.with_spikes(W.student_t((M, K), 3.0, seed=M + K), 1e-3, 50.0, seed=1)
+    b = W.normal((N, K), 0.02, seed=N + 3 * K)
+    A, B = quant_host(a, O.ROW_1D), quant_host(b, bmode)
+    C = nv.nvfp4_gemm(q_to_device(A, nv), q_to_device(B, nv),
+                      out_dtype=torch.float32 if out == "f32" else torch.bfloat16)
+    Cref, Wref = O.gemm(A, B)
+    check(out_to_f64(C), Cref, Wref, out == "bf16", f"gemm {M}x{N}x{K}")
+
+
+def test_gemm_exact_unit_scales(nv):
+    """Every block multiplier 1 and tensor scale 1: products are multiples of
+    1/4 and sums stay below 2^24, so the FP32 result must be exact."""
+    M, N, K = 160, 96, 512
+    r = W.rng(5)
+    grid = np.array([0, .5, 1, 1.5, 2, 3, 4, 6], dtype=np.float32)
+
+    def make(rows):
+        x = grid[r.integers(0, 8, size=(rows, K))] * np.where(r.random((rows, K)) < 0.5, -1, 1)
+        x = x.astype(np.float32)
+        x[:, ::16] = 6.0
+        return x
+
+    A = O.quantize(make(M), O.F32, O.ROW_1D, amax_in=2688.0)
+    B = O.quantize(make(N), O.F32, O.ROW_1D, amax_in=2688.0)
+    C = nv.nvfp4_gemm(q_to_device(A, nv), q_to_device(B, nv))
+    Cref, _ = O.gemm(A, B)
+    assert np.array_equal(out_to_f64(C), Cref)
+
+
+def test_gemm_256_config(nv):
+    """M = N = K = 256, A and B FP32 N(0,1) with 0.1% x50 outliers; A
+    quantized along rows, B (K x N) along K (column blocks), RNE; FP32 out."""
+    n = 256
+    a = W.with_spikes(W.normal((n, n), 1.0, seed=1), 1e-3, 50.0, seed=2)
+    b = W.with_spikes(W.normal((n, n), 1.0, seed=3), 1e-3, 50.0, seed=4)
+    Ad = nv.nvfp4_quantize(to_device(a), layout=nv.NVFP4_ROW_1D)
+    Bd = nv.nvfp4_quantize(to_device(b), layout=nv.NVFP4_COL_1D)   # B^T, N x K
+    C = nv.nvfp4_gemm(Ad, Bd)
+    A, B = q_to_host(Ad), q_to_host(Bd)
+    Aref, Bref = O.quantize(a, O.F32, O.ROW_1D), O.quantize(b, O.F32, O.COL_1D)
+    assert np.array_equal(A.codes, Aref.codes) and np.array_equal(B.codes, Bref.codes)
+    Cref, Wref = O.gemm(A, B)
+    check(out_to_f64(C), Cref, Wref, False, "gemm 256")
+
+
+def _sample_entries(M, N, n, seed):
+    r = W.rng(seed)
+    mi = np.concatenate([r.integers(0, M, n), np.arange(8), M - 1 - np.arange(8)])
+    ni = np.concatenate([r.integers(0, N, n), np.arange(8), N - 1 - np.arange(8)])
+    return mi, ni
+
+
+def test_forward_8192x20480x5120_sampled(nv):
+    """Y = X W^T: X 8192 x 5120 Student-t(3) row blocks, W 20480 x 5120
+    N(0, 0.02) 16x16 blocks, BF16 output; sampled entries."""
+    x = W.f32_to_bf16_bits(W.student_t((8192, 5120), 3.0, seed=4000))
+    w = W.f32_to_bf16_bits(W.normal((20480, 5120), 0.02, seed=4001))
+    Xq = nv.nvfp4_quantize(to_device(x), layout=nv.NVFP4_ROW_1D)
+    Wq = nv.nvfp4_quantize(to_device(w), layout=nv.NVFP4_BLK_2D)
+    Y = nv.nvfp4_gemm(Xq, Wq, out_dtype=torch.bfloat16)
+    mi, ni = _sample_entries(8192, 20480, 1024, 4002)
+    Cref, Wref = O.gemm(q_to_host(Xq), q_to_host(Wq), entries=(mi, ni))
+    got = out_to_f64(Y)[mi, ni]
+    check(got, Cref, Wref, True, "forward sampled")
+
+
+def test_wgrad_20480x5120x8192_sampled(nv):
+    """dW = dY^T X with K = 8192 tokens: both operands Hadamard-transformed
+    along tokens with one shared sign seed, column blocks, SR; FP32 out."""
+    dy = W.f32_to_bf16_bits(W.with_spikes(W.normal((8192, 20480), 1.0, seed=5000), 1e-4, 100.0, seed=5001))
+    x = W.f32_to_bf16_bits(W.with_spikes(W.normal((8192, 5120), 1.0, seed=5002), 1e-4, 100.0, seed=5003))
+    kw = dict(layout=nv.NVFP4_COL_1D, round=nv.NVFP4_SR, hadamard=True, hadamard_seed=5200)
+    dYq = nv.nvfp4_quantize(to_device(dy), sr_seed=5100, **kw)
+    Xq = nv.nvfp4_quantize(to_device(x), sr_seed=5101, **kw)
+    dW = nv.nvfp4_gemm(dYq, Xq, out_dtype=torch.float32)
+    mi, ni = _sample_entries(20480, 5120, 1024, 5003)
+    Cref, Wref = O.gemm(q_to_host(dYq), q_to_host(Xq), entries=(mi, ni))
+    check(out_to_f64(dW)[mi, ni], Cref, Wref, False, "wgrad sampled")
+
+
+# ---------------------------------------------------------------- grouped
+def _grouped_inputs(counts, N, K, seed, bmode=O.BLK_2D):
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    a = W.student_t((int(offs[-1]), K), 3.0, seed=seed)
+    A = quant_host(a, O.ROW_1D)
+    Bs = [quant_host(W.normal((N, K), 0.02, seed=seed + 1 + g), bmode) for g in range(len(counts))]
+    return offs, A, Bs
+
+
+def _stack_device(Bs, nv):
+    codes = np.concatenate([b.codes for b in Bs])
+    scales = np.concatenate([b.scales for b in Bs])
+    ts = torch.tensor([b.ts for b in Bs], dtype=torch.float32, device="cuda")
+    return nv.NVFP4Tensor(torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda(), ts,
+                          sum(b.rows for b in Bs), Bs[0].cols, Bs[0].scale_mode)
+
+
+@pytest.mark.parametrize("counts", [[5, 0, 130, 64], [1], [0, 0, 300], [128, 128, 1, 255, 17]])
+@pytest.mark.parametrize("bmode", [O.ROW_1D, O.BLK_2D])
+def test_grouped_gemm_small(nv, counts, bmode):
+    N, K = 96, 208
+    offs, A, Bs = _grouped_inputs(counts, N, K, seed=sum(counts) + 7, bmode=bmode)
+    C = nv.nvfp4_grouped_gemm(q_to_device(A, nv), torch.from_numpy(offs).cuda(), _stack_device(Bs, nv),
+                              len(counts), out_dtype=torch.float32)
+    Cref, Wref = O.grouped_gemm(A, offs, Bs)
+    check(out_to_f64(C), Cref, Wref, False, f"grouped {counts}")
+
+
+def _swiglu_tol(G_, U_, Wg, Wu):
+    from scipy.special import expit
+    s = expit(G_)
+    dh_dg = np.abs(s * (1.0 + G_ * (1.0 - s)) * U_)
+    dh_du = np.abs(G_ * s)
+    h = np.abs(G_ * s * U_)
+    e = np.floor(np.log2(np.where(h > 0, h, 1.0)))
+    ulp = np.where(h > 0, 2.0 ** (e - 7), 2.0 ** -133)
+    return dh_dg * 1e-5 * Wg + dh_du * 1e-5 * Wu + 1e-6 * h + ulp
+
+
+def check_swiglu(nv, counts, F, K, seed):
+    offs, A, Bs = _grouped_inputs(counts, 2 * F, K, seed)
+    amax = torch.zeros(1, dtype=torch.float32, device="cuda")
+    H = nv.nvfp4_grouped_gemm(q_to_device(A, nv), torch.from_numpy(offs).cuda(), _stack_device(Bs, nv),
+                              len(counts), epilogue=nv.NVFP4_EPI_SWIGLU, amax_out=amax)
+    got = out_to_f64(H)
+    Cref, Wref = O.grouped_gemm(A, offs, Bs)
+    G_, U_ = Cref[:, :F], Cref[:, F:]
+    href = O.swiglu(G_, U_)
+    tol = _swiglu_tol(G_, U_, Wref[:, :F], Wref[:, F:])
+    err = np.abs(got - href)
+    assert (err <= tol).all(), f"swiglu: {np.sum(err > tol)} entries out of tolerance"
+    assert amax.item() == np.abs(got).max()
+    return H, amax
+
+
+def test_grouped_swiglu_small(nv):
+    check_swiglu(nv, [70, 0, 129, 33], F=80, K=160, seed=21)
+
+
+def test_swiglu_then_quantize_is_oracle_exact(nv):
+    """The quantize step after the SwiGLU epilogue, fed the GPU's BF16 H and
+    the amax the epilogue produced, matches the oracle on that same H."""
+    H, amax = check_swiglu(nv, [64, 100], F=64, K=128, seed=31)
+    q = nv.nvfp4_quantize(H, layout=nv.NVFP4_ROW_1D, amax_in=amax)
+    hb = bf16_tensor_to_bits(H)
+    ref = O.quantize(hb, O.BF16, O.ROW_1D)
+    g = q_to_host(q)
+    assert g.ts == ref.ts and np.array_equal(g.codes, ref.codes) and np.array_equal(g.scales, ref.scales)
+
+
+def test_moe_expert_forward_sampled(nv):
+    """32 experts, hidden 7168, FFN 2048, 16384 tokens top-4 with Zipf(1.1)
+    counts: up-projection with SwiGLU, quantize, down-projection; sampled
+    rows of every stage against the oracle."""
+    E, Hd, F, T = 32, 7168, 2048, 16384
+    counts = W.zipf_expert_counts(E, T, 4, 1.1)
+    offs, token = W.moe_routing(counts, T)
+    x = W.f32_to_bf16_bits(W.student_t((T, Hd), 3.0, seed=6000))
+    Xq = nv.nvfp4_quantize(to_device(x), layout=nv.NVFP4_ROW_1D)
+    idx = torch.from_numpy(token).cuda()
+    Aperm = nv.NVFP4Tensor(Xq.codes.index_select(0, idx), Xq.scales.index_select(0, idx),
+                           Xq.tensor_scale, int(offs[-1]), Hd, nv.NVFP4_SCALE_1D)
+    w1 = [W.f32_to_bf16_bits(W.normal((2 * F, Hd), 0.02, seed=6100 + e)) for e in range(E)]
+    W1 = nv.NVFP4Tensor.empty(E * 2 * F, Hd, nv.NVFP4_SCALE_2D, n_scales=E)
+    for e in range(E):
+        q = nv.nvfp4_quantize(to_device(w1[e]), layout=nv.NVFP4_BLK_2D)
+        W1.codes[e * 2 * F:(e + 1) * 2 * F].copy_(q.codes)
+        W1.scales[e * 2 * F // 16:(e + 1) * 2 * F // 16].copy_(q.scales)
+        W1.tensor_scale[e:e + 1].copy_(q.tensor_scale)
+    offs_d = torch.from_numpy(offs).cuda()
+    amax = torch.zeros(1, dtype=torch.float32, device="cuda")
+    H = nv.nvfp4_grouped_gemm(Aperm, offs_d, W1, E, epilogue=nv.NVFP4_EPI_SWIGLU, amax_out=amax)
+    # sampled rows: first/last rows of a big, a middle and the smallest group
+    A_h = q_to_host(Aperm)
+    W1h = O.QTensor(W1.codes.cpu().numpy(), W1.scales.cpu().numpy(), 1.0, W1.rows, W1.cols, O.SCALE_2D)
+    ts1 = W1.tensor_scale.cpu().numpy()
+    Hh = out_to_f64(H)
+    for g_ in (0, 15, 31):
+        r0, r1 = int(offs[g_]), int(offs[g_ + 1])
+        rows = np.array([r0, r0 + 1, (r0 + r1) // 2, r1 - 1])
+        Bg = O.row_slice(W1h, g_ * 2 * F, (g_ + 1) * 2 * F)
+        Bg.ts = float(ts1[g_])
+        cols = np.arange(0, F, 37)
+        mi = np.repeat(rows, cols.size)
+        gi = np.tile(cols, rows.size)
+        Cg, Wg = O.gemm(A_h, Bg, entries=(mi, gi))
+        Cu, Wu = O.gemm(A_h, Bg, entries=(mi, gi + F))
+        href = O.swiglu(Cg, Cu)
+        tol = _swiglu_tol(Cg, Cu, Wg, Wu)
+        assert (np.abs(Hh[mi, gi] - href) <= tol).all(), f"group {g_}"
+    # down projection on the GPU's quantized H
+    Hq = nv.nvfp4_quantize(H, layout=nv.NVFP4_ROW_1D, amax_in=amax)
+    W2 = nv.NVFP4Tensor.empty(E * Hd, F, nv.NVFP4_SCALE_2D, n_scales=E)
+    for e in range(E):
+        w2 = W.f32_to_bf16_bits(W.normal((Hd, F), 0.02, seed=6200 + e))
+        q = nv.nvfp4_quantize(to_device(w2), layout=nv.NVFP4_BLK_2D)
+        W2.codes[e * Hd:(e + 1) * Hd].copy_(q.codes)
+        W2.scales[e * Hd // 16:(e + 1) * Hd // 16].copy_(q.scales)
+        W2.tensor_scale[e:e + 1].copy_(q.tensor_scale)
+    Y = nv.nvfp4_grouped_gemm(Hq, offs_d, W2, E, out_dtype=torch.bfloat16)
+    Hqh = q_to_host(Hq)
+    W2h = O.QTensor(W2.codes.cpu().numpy(), W2.scales.cpu().numpy(), 1.0, W2.rows, W2.cols, O.SCALE_2D)
+    ts2 = W2.tensor_scale.cpu().numpy()
+    Yh = out_to_f64(Y)
+    for g_ in (0, 7, 31):
+        r0, r1 = int(offs[g_]), int(offs[g_ + 1])
+        rows = np.array([r0, (r0 + r1) // 2, r1 - 1])
+        Bg = O.row_slice(W2h, g_ * Hd, (g_ + 1) * Hd)
+        Bg.ts = float(ts2[g_])
+        cols = np.arange(3, Hd, 101)
+        mi = np.repeat(rows, cols.size)
+        ni = np.tile(cols, rows.size)
+        Cref, Wref = O.gemm(Hqh, Bg, entries=(mi, ni))
+        check(Yh[mi, ni], Cref, Wref, True, f"down group {g_}")

@@ -1,0 +1,220 @@
+"""GPU parity of quantize / dequantize against the CPU oracle: codes, scale
+bytes, tensor scales and stochastic-rounding outputs must match bit for bit;
+dequantized values must equal the oracle's bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+from parity_utils import assert_q_equal, bf16_tensor_to_bits, q_to_device, q_to_host, require_gpu, to_device
+
+pytestmark = pytest.mark.gpu
+
+LAYOUT_NAMES = {0: "row", 1: "col", 2: "rowcol", 3: "2d"}
+
+
+@pytest.fixture(scope="module")
+def nv():
+    return require_gpu()
+
+
+def make_input(rows, cols, dtype, seed, kind="t3"):
+    if kind == "t3":
+        x = W.student_t((rows, cols), 3.0, seed=seed)
+    elif kind == "spiky":
+        x = W.with_spikes(W.normal((rows, cols), 1.0, seed=seed), 1e-3, 100.0, seed=seed + 1)
+    elif kind == "w":
+        x = W.normal((rows, cols), 0.02, seed=seed)
+    else:
+        raise ValueError(kind)
+    if dtype == O.BF16:
+        return W.f32_to_bf16_bits(x)
+    return x
+
+
+def run_both(nv, x, dtype, layout, rnd, seed=7, had=False, hseed=0, amax_in=None, pad=None):
+    xd = to_device(x, pad)
+    amax_d = None if amax_in is None else torch.tensor([amax_in], dtype=torch.float32, device="cuda")
+    got = nv.nvfp4_quantize(xd, layout=layout, round=rnd, sr_seed=seed, hadamard=had,
+                            hadamard_seed=hseed, amax_in=amax_d)
+    ref = O.quantize(x, dtype, layout, rnd, sr_seed=seed, hadamard=had, hadamard_seed=hseed,
+                     amax_in=amax_in)
+    if layout == O.ROW_COL_1D:
+        return [q_to_host(g) for g in got], list(ref)
+    return [q_to_host(got)], [ref]
+
+
+SHAPES_ROW = [(1, 16), (7, 48), (64, 64), (100, 1040), (333, 2064)]
+SHAPES_COL = [(16, 1), (48, 7), (64, 64), (96, 37), (208, 1031), (1040, 100)]
+SHAPES_BOTH = [(16, 16), (48, 80), (64, 64), (208, 1040), (1024, 96)]
+
+
+@pytest.mark.parametrize("dtype", [O.BF16, O.F32])
+@pytest.mark.parametrize("rnd", [O.RNE, O.SR])
+@pytest.mark.parametrize("had", [False, True])
+@pytest.mark.parametrize("shape", SHAPES_ROW)
+def test_row(nv, dtype, rnd, had, shape):
+    x = make_input(*shape, dtype, seed=shape[0] * 7 + shape[1])
+    got, ref = run_both(nv, x, dtype, O.ROW_1D, rnd, seed=99, had=had, hseed=1234)
+    assert_q_equal(got[0], ref[0], f"row {shape}")
+
+
+@pytest.mark.parametrize("dtype", [O.BF16, O.F32])
+@pytest.mark.parametrize("rnd", [O.RNE, O.SR])
+@pytest.mark.parametrize("had", [False, True])
+@pytest.mark.parametrize("shape", SHAPES_COL)
+def test_col(nv, dtype, rnd, had, shape):
+    x = make_input(*shape, dtype, seed=shape[0] * 5 + shape[1], kind="spiky")
+    pad = (shape[1] + 7) // 8 * 8 if dtype == O.BF16 else (shape[1] + 3) // 4 * 4
+    got, ref = run_both(nv, x, dtype, O.COL_1D, rnd, seed=5, had=had, hseed=77, pad=pad)
+    assert_q_equal(got[0], ref[0], f"col {shape}")
+
+
+@pytest.mark.parametrize("dtype", [O.BF16, O.F32])
+@pytest.mark.parametrize("rnd", [O.RNE, O.SR])
+@pytest.mark.parametrize("shape", SHAPES_BOTH)
+def test_rowcol_and_2d(nv, dtype, rnd, shape):
+    x = make_input(*shape, dtype, seed=shape[0] + shape[1] * 3)
+    got, ref = run_both(nv, x, dtype, O.ROW_COL_1D, rnd, seed=11)
+    assert_q_equal(got[0], ref[0], f"rowcol/row {shape}")
+    assert_q_equal(got[1], ref[1], f"rowcol/col {shape}")
+    got, ref = run_both(nv, x, dtype, O.BLK_2D, rnd, seed=12)
+    assert_q_equal(got[0], ref[0], f"2d {shape}")
+
+
+def test_fused_rowcol_equals_separate_calls(nv):
+    x = make_input(128, 192, O.BF16, seed=3)
+    xd = to_device(x)
+    r, c = nv.nvfp4_quantize(xd, layout=nv.NVFP4_ROW_COL_1D, round=nv.NVFP4_SR, sr_seed=4)
+    r1 = nv.nvfp4_quantize(xd, layout=nv.NVFP4_ROW_1D, round=nv.NVFP4_SR, sr_seed=4)
+    c1 = nv.nvfp4_quantize(xd, layout=nv.NVFP4_COL_1D, round=nv.NVFP4_SR, sr_seed=4)
+    assert_q_equal(q_to_host(r), q_to_host(r1), "fused row")
+    assert_q_equal(q_to_host(c), q_to_host(c1), "fused col")
+
+
+@pytest.mark.parametrize("layout", [O.ROW_1D, O.COL_1D, O.BLK_2D])
+def test_edge_values(nv, layout):
+    """Zeros, signed zeros, one huge outlier, tiny (subnormal-scale) blocks,
+    exact ties of the E2M1 grid, and a given amax."""
+    x = W.student_t((64, 64), 3.0, seed=1)
+    x[0:16, 0:16] = 0.0
+    x[3, 5] = -0.0
+    x[20, 20] = 3.0e5
+    x[32:48, 16:32] *= 1e-7
+    x[48, 0:16] = np.array([6, 5, 3.5, 2.5, 1.75, 1.25, .75, .25, -6, -5, -3.5, -2.5, -1.75, -1.25,
+                            -.75, -.25], dtype=np.float32)
+    for rnd in (O.RNE, O.SR):
+        for dt in (O.F32, O.BF16):
+            xx = x if dt == O.F32 else W.f32_to_bf16_bits(x)
+            got, ref = run_both(nv, xx, dt, layout, rnd, seed=21)
+            assert_q_equal(got[0], ref[0], f"edge {layout} {rnd} {dt}")
+            got, ref = run_both(nv, xx, dt, layout, rnd, seed=21, amax_in=2688.0)
+            assert_q_equal(got[0], ref[0], f"edge amax_in {layout} {rnd} {dt}")
+
+
+def test_zero_and_empty_tensors(nv):
+    x = np.zeros((32, 32), dtype=np.float32)
+    got, ref = run_both(nv, x, O.F32, O.ROW_1D, O.SR)
+    assert_q_equal(got[0], ref[0], "zeros")
+    e = torch.zeros((0, 32), dtype=torch.bfloat16, device="cuda")
+    q = nv.nvfp4_quantize(e)
+    torch.cuda.synchronize()
+    assert q.tensor_scale.item() == 1.0
+
+
+@pytest.mark.parametrize("layout", [O.ROW_1D, O.COL_1D, O.BLK_2D])
+@pytest.mark.parametrize("out_dt", [O.F32, O.BF16])
+def test_dequantize(nv, layout, out_dt):
+    x = make_input(96, 160, O.BF16, seed=8, kind="spiky")
+    ref_q = O.quantize(x, O.BF16, layout)
+    qd = q_to_device(ref_q, nv)
+    y = nv.nvfp4_dequantize(qd, dtype=torch.bfloat16 if out_dt == O.BF16 else torch.float32)
+    ref = O.dequantize(ref_q, out_dt)
+    got = bf16_tensor_to_bits(y) if out_dt == O.BF16 else y.cpu().numpy()
+    assert np.array_equal(got.view(np.uint32 if out_dt == O.F32 else np.uint16),
+                          ref.view(np.uint32 if out_dt == O.F32 else np.uint16))
+
+
+def test_gpu_idempotence(nv):
+    x = make_input(128, 256, O.F32, seed=31)
+    xd = to_device(x)
+    q = nv.nvfp4_quantize(xd)
+    y = nv.nvfp4_dequantize(q, dtype=torch.float32)
+    amax = torch.tensor([float(np.abs(x).max())], device="cuda")
+    q2 = nv.nvfp4_quantize(y, amax_in=amax)
+    assert_q_equal(q_to_host(q2), q_to_host(q), "idempotence")
+
+
+# ---------------------------------------------------------- full-size samples
+def _band_ref(x, layout, rnd, seed, amax, b0, width, had=False, hseed=0):
+    """Oracle output rows b0 .. b0+width of the full tensor's quantization:
+    the matching input band with the full tensor's amax and the band's
+    position as the base of its random-draw indices."""
+    rows, cols = x.shape
+    if layout == O.COL_1D:
+        sub = np.ascontiguousarray(x[:, b0:b0 + width])
+        base = b0 * rows
+    else:
+        sub = np.ascontiguousarray(x[b0:b0 + width])
+        base = b0 * cols
+    return O.quantize(sub, O.BF16, layout, rnd, sr_seed=seed, hadamard=had, hadamard_seed=hseed,
+                      amax_in=amax, index_base=base)
+
+
+def _check_bands(g, x, layout, rnd, seed, amax, bands, width=64, had=False, hseed=0):
+    for b0 in bands:
+        ref = _band_ref(x, layout, rnd, seed, amax, b0, width, had, hseed)
+        assert np.array_equal(g.codes[b0:b0 + width], ref.codes), f"codes band {b0}"
+        sc = g.scales[b0 // 16:(b0 + width) // 16] if layout == O.BLK_2D else g.scales[b0:b0 + width]
+        assert np.array_equal(sc, ref.scales), f"scales band {b0}"
+
+
+@pytest.mark.parametrize("layout,rnd", [(O.ROW_1D, O.RNE), (O.ROW_1D, O.SR), (O.COL_1D, O.RNE),
+                                        (O.COL_1D, O.SR), (O.BLK_2D, O.RNE), (O.BLK_2D, O.SR)])
+def test_activation_8192_sampled(nv, layout, rnd):
+    """8192 x 8192 BF16 Student-t(3), the launch configuration the benchmark
+    times: the tensor scale against the oracle's amax of the whole tensor,
+    and bands of the output against the oracle."""
+    n = 8192
+    x = make_input(n, n, O.BF16, seed=1000 + layout)
+    q = nv.nvfp4_quantize(to_device(x), layout=layout, round=rnd, sr_seed=1100)
+    g = q_to_host(q)
+    amax = O.amax(x, O.BF16, layout)
+    assert g.ts == O.tensor_scale(amax)
+    _check_bands(g, x, layout, rnd, 1100, amax, (0, 4096 + 48, n - 64))
+
+
+def test_activation_8192_rowcol_sampled(nv):
+    n = 8192
+    x = make_input(n, n, O.BF16, seed=1010)
+    r, c = nv.nvfp4_quantize(to_device(x), layout=nv.NVFP4_ROW_COL_1D, round=nv.NVFP4_SR,
+                             sr_seed=1200)
+    gr, gc = q_to_host(r), q_to_host(c)
+    amax = O.amax(x, O.BF16, O.ROW_1D)
+    assert gr.ts == gc.ts == O.tensor_scale(amax)
+    _check_bands(gr, x, O.ROW_1D, O.SR, 1200, amax, (0, n - 64))
+    _check_bands(gc, x, O.COL_1D, O.SR, 1200, amax, (0, 2000, n - 64))
+
+
+def test_weight_2d_20480x5120_sampled(nv):
+    """Weight 20480 x 5120 BF16 N(0, 0.02), 16 x 16 blocks, RNE."""
+    x = make_input(20480, 5120, O.BF16, seed=2000, kind="w")
+    g = q_to_host(nv.nvfp4_quantize(to_device(x), layout=nv.NVFP4_BLK_2D))
+    amax = O.amax(x, O.BF16, O.BLK_2D)
+    assert g.ts == O.tensor_scale(amax)
+    _check_bands(g, x, O.BLK_2D, O.RNE, 0, amax, (0, 10240, 20480 - 64))
+
+
+@pytest.mark.parametrize("rows,cols,seed", [(8192, 20480, 3000), (8192, 5120, 3010)])
+def test_wgrad_hadamard_col_sr_sampled(nv, rows, cols, seed):
+    """dY 8192 x 20480 and X 8192 x 5120, N(0,1) with 0.01% x100 spikes:
+    Hadamard along tokens, column blocks, stochastic rounding."""
+    x = W.f32_to_bf16_bits(W.with_spikes(W.normal((rows, cols), 1.0, seed=seed), 1e-4, 100.0,
+                                         seed=seed + 1))
+    q = q_to_host(nv.nvfp4_quantize(to_device(x), layout=nv.NVFP4_COL_1D, round=nv.NVFP4_SR,
+                                    sr_seed=seed + 100, hadamard=True, hadamard_seed=seed + 200))
+    amax = O.amax(x, O.BF16, O.COL_1D, hadamard=True, hadamard_seed=seed + 200)
+    assert q.ts == O.tensor_scale(amax)
+    _check_bands(q, x, O.COL_1D, O.SR, seed + 100, amax, (0, cols // 2 + 16, cols - 64), had=True,
+                 hseed=seed + 200)
