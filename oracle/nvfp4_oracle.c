@@ -226,8 +226,8 @@ static void put_code(uint8_t* codes, int64_t cols, int64_t r, int64_t c, uint32_
 /* 1D quantization of the oriented tensor t [R x C] (fp32, dense): blocks of
  * 16 consecutive elements along each row [P3 "Детали"]. */
 static void quantize_rows(const float* t, int64_t R, int64_t C, float amax_t, int round,
-                          uint64_t seed, uint32_t stream, uint8_t* codes, uint8_t* scales,
-                          float* ts) {
+                          uint64_t seed, uint32_t stream, uint64_t index_base, uint8_t* codes,
+                          uint8_t* scales, float* ts) {
     float st = orc_tensor_scale(amax_t);
     *ts = st;
     for (int64_t r = 0; r < R; ++r) {
@@ -239,7 +239,7 @@ static void quantize_rows(const float* t, int64_t R, int64_t C, float amax_t, in
             for (int64_t c = c0; c < c0 + 16; ++c)
                 put_code(codes, C, r, c,
                          encode_elem(t[r * C + c], b, round, seed, stream,
-                                     (uint64_t)(r * C + c)));
+                                     index_base + (uint64_t)(r * C + c)));
         }
     }
 }
@@ -248,7 +248,8 @@ static void quantize_rows(const float* t, int64_t R, int64_t C, float amax_t, in
  * с FP8": 2D weight scaling; P3 "Как это работает": one multiplier per 16x16
  * square, unchanged by the transpose]. */
 static void quantize_2d(const float* t, int64_t R, int64_t C, float amax_t, int round,
-                        uint64_t seed, uint8_t* codes, uint8_t* scales, float* ts) {
+                        uint64_t seed, uint64_t index_base, uint8_t* codes, uint8_t* scales,
+                        float* ts) {
     float st = orc_tensor_scale(amax_t);
     *ts = st;
     for (int64_t r0 = 0; r0 < R; r0 += 16) {
@@ -262,7 +263,7 @@ static void quantize_2d(const float* t, int64_t R, int64_t C, float amax_t, int 
                 for (int64_t c = c0; c < c0 + 16; ++c)
                     put_code(codes, C, r, c,
                              encode_elem(t[r * C + c], b, round, seed, ORC_STREAM_2D,
-                                         (uint64_t)(r * C + c)));
+                                         index_base + (uint64_t)(r * C + c)));
         }
     }
 }
@@ -297,7 +298,7 @@ static float* oriented(const void* x, int dtype, int64_t rows, int64_t cols, int
 
 int orc_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld,
                  int layout, int round, uint64_t sr_seed, int hadamard,
-                 uint64_t hadamard_seed, const float* amax_in,
+                 uint64_t hadamard_seed, const float* amax_in, uint64_t index_base,
                  uint8_t* codes, uint8_t* scales, float* ts,
                  uint8_t* codes2, uint8_t* scales2, float* ts2) {
     if (rows < 0 || cols < 0 || ld < cols) return 1;
@@ -313,7 +314,7 @@ int orc_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64_t l
         int64_t R = tr ? cols : rows, C = tr ? rows : cols;
         float a = amax_in ? *amax_in : amax_of(t, R * C);
         quantize_rows(t, R, C, a, round, sr_seed, tr ? ORC_STREAM_COL : ORC_STREAM_ROW,
-                      codes, scales, ts);
+                      index_base, codes, scales, ts);
         free(t);
         return 0;
     }
@@ -322,8 +323,10 @@ int orc_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64_t l
         float* tt = oriented(x, dtype, rows, cols, ld, 1, 0, 0);
         if ((!t || !tt) && rows > 0 && cols > 0) { free(t); free(tt); return 4; }
         float a = amax_in ? *amax_in : amax_of(t, rows * cols);
-        quantize_rows(t, rows, cols, a, round, sr_seed, ORC_STREAM_ROW, codes, scales, ts);
-        quantize_rows(tt, cols, rows, a, round, sr_seed, ORC_STREAM_COL, codes2, scales2, ts2);
+        quantize_rows(t, rows, cols, a, round, sr_seed, ORC_STREAM_ROW, index_base, codes, scales,
+                      ts);
+        quantize_rows(tt, cols, rows, a, round, sr_seed, ORC_STREAM_COL, index_base, codes2,
+                      scales2, ts2);
         free(t);
         free(tt);
         return 0;
@@ -332,11 +335,21 @@ int orc_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64_t l
         float* t = oriented(x, dtype, rows, cols, ld, 0, 0, 0);
         if (!t && rows > 0 && cols > 0) return 4;
         float a = amax_in ? *amax_in : amax_of(t, rows * cols);
-        quantize_2d(t, rows, cols, a, round, sr_seed, codes, scales, ts);
+        quantize_2d(t, rows, cols, a, round, sr_seed, index_base, codes, scales, ts);
         free(t);
         return 0;
     }
     return 5;
+}
+
+float orc_amax(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld, int layout,
+               int hadamard, uint64_t hadamard_seed) {
+    int tr = (layout == ORC_COL_1D);
+    float* t = oriented(x, dtype, rows, cols, ld, tr, hadamard, hadamard_seed);
+    if (!t) return 0.0f;
+    float a = amax_of(t, rows * cols);
+    free(t);
+    return a;
 }
 
 /* ========================================================================

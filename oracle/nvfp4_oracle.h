@@ -79,12 +79,20 @@ void orc_rht16(const float in[16], uint32_t sign_mask, float out[16]);
  * or rows/16 x cols/16 (2D).  COL_1D outputs describe the transpose:
  * codes cols x rows/2, scales cols x rows/16.  ROW_COL_1D writes the row
  * output to (codes, scales, ts) and the column output to (codes2, ...).
+ * index_base is added to every element's linear output index before its
+ * random draw, so that a band of a larger tensor can be recomputed alone
+ * (0 for a whole tensor).
  * Returns 0 on success, nonzero for an unsupported request. */
 int orc_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld,
                  int layout, int round, uint64_t sr_seed, int hadamard,
-                 uint64_t hadamard_seed, const float* amax_in,
+                 uint64_t hadamard_seed, const float* amax_in, uint64_t index_base,
                  uint8_t* codes, uint8_t* scales, float* ts,
                  uint8_t* codes2, uint8_t* scales2, float* ts2);
+
+/* A_t: the largest magnitude of the tensor that `layout` quantizes (after
+ * the Hadamard transform along the block dimension when requested). */
+float orc_amax(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld, int layout,
+               int hadamard, uint64_t hadamard_seed);
 
 /* out: rows x cols (stored orientation), dtype ORC_F32 or ORC_BF16 (bits). */
 void orc_dequantize(const uint8_t* codes, const uint8_t* scales, float ts,

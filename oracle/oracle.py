@@ -59,9 +59,12 @@ def lib():
         L.orc_rht16.restype = None
         L.orc_quantize.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
                                    ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_uint64,
-                                   ctypes.c_int, ctypes.c_uint64, f32p,
+                                   ctypes.c_int, ctypes.c_uint64, f32p, ctypes.c_uint64,
                                    u8p, u8p, f32p, u8p, u8p, f32p]
         L.orc_quantize.restype = ctypes.c_int
+        L.orc_amax.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+                               ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_uint64]
+        L.orc_amax.restype = ctypes.c_float
         L.orc_dequantize.argtypes = [u8p, u8p, ctypes.c_float, ctypes.c_int64, ctypes.c_int64,
                                      ctypes.c_int, ctypes.c_void_p, ctypes.c_int]
         L.orc_dequantize.restype = None
@@ -142,10 +145,11 @@ class QTensor:
 
 
 def quantize(x, dtype, layout, rnd=RNE, sr_seed=0, hadamard=False, hadamard_seed=0,
-             amax_in=None, ld=None):
+             amax_in=None, ld=None, index_base=0):
     """x: numpy float32 [rows x cols] (dtype F32) or uint16 bf16 bits (BF16).
 
-    Returns one QTensor, or (row, col) for ROW_COL_1D."""
+    index_base offsets every element's random-draw index (a band of a larger
+    tensor).  Returns one QTensor, or (row, col) for ROW_COL_1D."""
     x = np.ascontiguousarray(x)
     rows, cols = x.shape
     if ld is None:
@@ -182,7 +186,7 @@ def quantize(x, dtype, layout, rnd=RNE, sr_seed=0, hadamard=False, hadamard_seed
         x.ctypes.data_as(ctypes.c_void_p), dtype, rows, cols, ld, layout, rnd,
         ctypes.c_uint64(sr_seed), int(bool(hadamard)), ctypes.c_uint64(hadamard_seed),
         _p(amax_arr, ctypes.c_float) if amax_arr is not None else nulf,
-        _p(codes, ctypes.c_uint8), _p(scales, ctypes.c_uint8), _p(ts, ctypes.c_float),
+        ctypes.c_uint64(index_base), _p(codes, ctypes.c_uint8), _p(scales, ctypes.c_uint8), _p(ts, ctypes.c_float),
         _p(codes2, ctypes.c_uint8) if codes2 is not None else nul8,
         _p(scales2, ctypes.c_uint8) if scales2 is not None else nul8,
         _p(ts2, ctypes.c_float) if ts2 is not None else nulf)
@@ -192,6 +196,14 @@ def quantize(x, dtype, layout, rnd=RNE, sr_seed=0, hadamard=False, hadamard_seed
     if layout == ROW_COL_1D:
         return q, QTensor(codes2, scales2, float(ts2[0]), cols, rows, SCALE_1D)
     return q
+
+
+def amax(x, dtype, layout, hadamard=False, hadamard_seed=0):
+    """A_t of the tensor `layout` quantizes (after the optional transform)."""
+    x = np.ascontiguousarray(x)
+    rows, cols = x.shape
+    return float(lib().orc_amax(x.ctypes.data_as(ctypes.c_void_p), dtype, rows, cols, cols, layout,
+                                int(bool(hadamard)), ctypes.c_uint64(hadamard_seed)))
 
 
 def dequantize(q, out_dtype=F32):
