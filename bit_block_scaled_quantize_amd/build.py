@@ -38,6 +38,9 @@ def flags():
     return ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
             "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
             "-fno-gpu-flush-denormals-to-zero",
+            # loops marked for full unrolling stay unrolled even when the body
+            # is large (a rolled loop would index register arrays dynamically)
+            "-mllvm", "-pragma-unroll-threshold=262144",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             "-Wall", "-Wno-unused-function",
             "-I", CSRC, "-I", INCLUDE]

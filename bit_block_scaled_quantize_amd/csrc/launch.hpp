@@ -12,9 +12,10 @@ namespace nvfp4 {
 enum { kLayoutRow = 0, kLayoutCol = 1, kLayoutRowCol = 2, kLayout2D = 3 };
 
 // Upper bound on the per-workgroup partial maxima of one amax pass; the
-// quantize workspace holds 4 floats (the final amax, padded) + kMaxPartials.
-constexpr int64_t kMaxPartials = 2048;
-constexpr size_t kQuantWorkspaceBytes = (size_t)(4 + kMaxPartials) * sizeof(float);
+// quantize workspace holds exactly these floats, and every quantize
+// workgroup reduces them in its prologue.
+constexpr int64_t kMaxPartials = 512;
+constexpr size_t kQuantWorkspaceBytes = (size_t)kMaxPartials * sizeof(float);
 
 struct QOut {
     uint8_t* codes;
@@ -24,7 +25,8 @@ struct QOut {
 
 hipError_t launch_quantize(const void* x, bool bf16, int64_t rows, int64_t cols, int64_t ld,
                            int layout, bool sr, uint64_t seed, bool rht, uint64_t hseed,
-                           const float* amax_in, const QOut* out, float* ws, hipStream_t s);
+                           const float* amax_in, float* amax_out, const QOut* out, float* ws,
+                           hipStream_t s);
 
 hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, const float* ts,
                              int64_t rows, int64_t cols, bool scale_2d, void* y, bool bf16,

@@ -88,9 +88,11 @@ nvfp4_status nvfp4_quantize(const void* x, nvfp4_dtype dt, int64_t rows, int64_t
     }
     if (st != NVFP4_OK) return st;
 
-    // grid-size limits of the launches (y dimensions)
-    if (cdiv(cols, 1024) > kMaxGridY || cdiv(cols, 64) > kMaxGridY) return NVFP4_ERR_UNSUPPORTED;
-    if (cdiv(rows, 16) > 0x7FFFFFFF) return NVFP4_ERR_UNSUPPORTED;
+    // grid-size limits of the launches (y counts row tiles / row bands)
+    if (cdiv(cols, 128) > 0x7FFFFFFF) return NVFP4_ERR_UNSUPPORTED;
+    if ((layout == NVFP4_COL_1D || layout == NVFP4_ROW_COL_1D) && cdiv(rows, 256) > kMaxGridY)
+        return NVFP4_ERR_UNSUPPORTED;
+    if (layout == NVFP4_BLK_2D && cdiv(rows, 64) > kMaxGridY) return NVFP4_ERR_UNSUPPORTED;
 
     if (!empty && !opts->amax_in) {
         if (!ws) return NVFP4_ERR_WORKSPACE;
@@ -104,7 +106,7 @@ nvfp4_status nvfp4_quantize(const void* x, nvfp4_dtype dt, int64_t rows, int64_t
     else o[1] = QOut{nullptr, nullptr, nullptr};
     hipError_t e = launch_quantize(x, dt == NVFP4_BF16, rows, cols, ld, layout, opts->round == NVFP4_SR,
                                    opts->sr_seed, opts->hadamard != 0, opts->hadamard_seed,
-                                   opts->amax_in, o, static_cast<float*>(ws),
+                                   opts->amax_in, opts->amax_out, o, static_cast<float*>(ws),
                                    static_cast<hipStream_t>(stream));
     return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
@@ -119,7 +121,6 @@ nvfp4_status nvfp4_dequantize(const nvfp4_tensor* q, void* y, nvfp4_dtype dt, in
     const bool empty = q->rows == 0 || q->cols == 0;
     if (!empty && !y) return NVFP4_ERR_NULL;
     if (!aligned(y, 16) || (ld * (int64_t)dtype_size(dt)) % 16) return NVFP4_ERR_ALIGN;
-    if (cdiv(q->cols / 16, 64) > kMaxGridY) return NVFP4_ERR_UNSUPPORTED;
     hipError_t e = launch_dequantize(q->codes, q->scales, q->tensor_scale, q->rows, q->cols,
                                      q->scale_mode == NVFP4_SCALE_2D, y, dt == NVFP4_BF16, ld,
                                      static_cast<hipStream_t>(stream));

@@ -66,55 +66,85 @@ __host__ __device__ inline uint32_t hadamard_sign_mask(uint64_t seed) {
            0xFFFFu;
 }
 
-// Sixteen 16-bit draws for output elements base .. base+15 (base % 16 == 0):
-// two Philox calls with counters base/8 and base/8 + 1.  d[j] is the draw of
-// element base + j (16 bits of word (j % 8) / 2, low half for even j).
-__device__ __forceinline__ void draws16(uint64_t seed, uint32_t stream, uint64_t base,
-                                        uint32_t d[16]) {
-    uint64_t q = base >> 3;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        uint64_t qq = q + h;
-        Words4 w = philox4x32_10((uint32_t)qq, (uint32_t)(qq >> 32), stream, 0u, (uint32_t)seed,
-                                 (uint32_t)(seed >> 32));
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            d[8 * h + 2 * j] = w.w[j] & 0xFFFFu;
-            d[8 * h + 2 * j + 1] = w.w[j] >> 16;
-        }
+// Device-side Philox rounds kept as a rolled loop (compact code, so that the
+// callers' loops over blocks can be fully unrolled), advancing two counters
+// that share a key in lockstep: two independent multiply chains per round.
+__device__ __forceinline__ void philox4x32_10_pair(uint32_t a[4], uint32_t b[4], uint32_t k0,
+                                                   uint32_t k1) {
+#pragma unroll 1
+    for (int i = 0; i < 10; ++i) {
+        const uint64_t pa0 = (uint64_t)0xD2511F53u * a[0], pa1 = (uint64_t)0xCD9E8D57u * a[2];
+        const uint64_t pb0 = (uint64_t)0xD2511F53u * b[0], pb1 = (uint64_t)0xCD9E8D57u * b[2];
+        const uint32_t na0 = (uint32_t)(pa1 >> 32) ^ a[1] ^ k0, na2 = (uint32_t)(pa0 >> 32) ^ a[3] ^ k1;
+        const uint32_t nb0 = (uint32_t)(pb1 >> 32) ^ b[1] ^ k0, nb2 = (uint32_t)(pb0 >> 32) ^ b[3] ^ k1;
+        a[1] = (uint32_t)pa1;
+        a[3] = (uint32_t)pa0;
+        a[0] = na0;
+        a[2] = na2;
+        b[1] = (uint32_t)pb1;
+        b[3] = (uint32_t)pb0;
+        b[0] = nb0;
+        b[2] = nb2;
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
     }
 }
 
-// Eight draws for elements base .. base+7 (base % 8 == 0): one Philox call.
-__device__ __forceinline__ void draws8(uint64_t seed, uint32_t stream, uint64_t base,
-                                       uint32_t d[8]) {
-    uint64_t q = base >> 3;
-    Words4 w = philox4x32_10((uint32_t)q, (uint32_t)(q >> 32), stream, 0u, (uint32_t)seed,
-                             (uint32_t)(seed >> 32));
+// Sixteen 16-bit draws for output elements base .. base+15 (base % 16 == 0):
+// Philox with counters base/8 and base/8 + 1.  d[j] is the draw of element
+// base + j (16 bits of word (j % 8) / 2, low half for even j).
+__device__ __forceinline__ void draws16(uint64_t seed, uint32_t stream, uint64_t base,
+                                        uint32_t d[16]) {
+    const uint64_t q = base >> 3, q1 = q + 1;
+    uint32_t a[4] = {(uint32_t)q, (uint32_t)(q >> 32), stream, 0u};
+    uint32_t b[4] = {(uint32_t)q1, (uint32_t)(q1 >> 32), stream, 0u};
+    philox4x32_10_pair(a, b, (uint32_t)seed, (uint32_t)(seed >> 32));
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        d[2 * j] = w.w[j] & 0xFFFFu;
-        d[2 * j + 1] = w.w[j] >> 16;
+        d[2 * j] = a[j] & 0xFFFFu;
+        d[2 * j + 1] = a[j] >> 16;
+        d[8 + 2 * j] = b[j] & 0xFFFFu;
+        d[8 + 2 * j + 1] = b[j] >> 16;
     }
+}
+
+// Eight draws for each of two element groups (bases a_base and b_base, both
+// multiples of 8): one paired Philox run.
+__device__ __forceinline__ void draws8x2(uint64_t seed, uint32_t stream, uint64_t a_base,
+                                         uint64_t b_base, uint32_t da[8], uint32_t db[8]) {
+    const uint64_t qa = a_base >> 3, qb = b_base >> 3;
+    uint32_t a[4] = {(uint32_t)qa, (uint32_t)(qa >> 32), stream, 0u};
+    uint32_t b[4] = {(uint32_t)qb, (uint32_t)(qb >> 32), stream, 0u};
+    philox4x32_10_pair(a, b, (uint32_t)seed, (uint32_t)(seed >> 32));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        da[2 * j] = a[j] & 0xFFFFu;
+        da[2 * j + 1] = a[j] >> 16;
+        db[2 * j] = b[j] & 0xFFFFu;
+        db[2 * j + 1] = b[j] >> 16;
+    }
+}
+
+// Eight draws for elements base .. base+7 (base % 8 == 0).
+__device__ __forceinline__ void draws8(uint64_t seed, uint32_t stream, uint64_t base,
+                                       uint32_t d[8]) {
+    uint32_t unused[8];
+    draws8x2(seed, stream, base, base + 8, d, unused);
 }
 
 // ---------------------------------------------------------------- formats
-// binary32 value of an E4M3 byte (bias 7; exponent field 0 = multiples of 2^-9).
+// binary32 value of an E4M3 byte (bias 7; exponent field 0 = multiples of 2^-9)
+// (the gfx950 FP8 -> binary32 convert is exact for every finite E4M3 byte)
 __device__ __forceinline__ float e4m3_value(uint32_t s) {
-    uint32_t e = s >> 3, m = s & 7u;
-    return e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
+    return __builtin_amdgcn_cvt_f32_fp8((int)s, 0);
 }
 
 // Nearest E4M3 byte to u >= 0, ties to the even code, clamped to 448 (0x7E).
+// The gfx950 FP8 convert rounds to nearest-even onto E4M3 (subnormals
+// included) but does not saturate above 464; clamping to 448 first makes it
+// the required clamp-then-round.
 __device__ __forceinline__ uint32_t e4m3_encode(float u) {
-    if (!(u > 0.0f)) return 0u;
-    if (u >= 448.0f) return 0x7Eu;
-    if (u < 0.015625f) return (uint32_t)__builtin_rintf(u * 512.0f);  // subnormal grid, 0..8
-    uint32_t b = __float_as_uint(u);
-    uint32_t code = (((b >> 23) - 120u) << 3) | ((b >> 20) & 7u);
-    uint32_t rem = b & 0xFFFFFu;
-    uint32_t up = (rem > 0x80000u) | ((rem == 0x80000u) & (code & 1u));
-    return code + up;  // a carry out of the 3 mantissa bits bumps the exponent
+    return __builtin_amdgcn_cvt_pk_fp8_f32(fminf(u, 448.0f), 0.0f, 0, false) & 0xFFu;
 }
 
 // E2M1 magnitude code (0..7) of y >= 0, round to nearest, ties to even,
@@ -172,6 +202,11 @@ __device__ __forceinline__ BlockScale block_scale(float amax_b, float six_st, fl
 // 4-bit codes of N values (N = 8 or 16; sign copied) packed into N/8 32-bit
 // words, the even element in the low nibble.  d holds the 16-bit draws when
 // SR is used.
+//   RNE: the values are scaled first (y = t * R keeps the sign; its magnitude
+//   is fl(|t| * R)), then the gfx950 FP4 pack instruction with scale operand
+//   1.0 rounds two of them to nearest-even E2M1 with saturation at 6 and writes
+//   their codes into one byte of the word.
+//   SR: e2m1_sr on the magnitude, sign bit copied, nibbles packed in VALU.
 template <bool SR, int N>
 __device__ __forceinline__ void encode(const float* v, BlockScale bs, const uint32_t* d,
                                        uint32_t* out) {
@@ -191,16 +226,45 @@ __device__ __forceinline__ void encode(const float* v, BlockScale bs, const uint
 #pragma unroll
     for (int k = 0; k < N / 8; ++k) {
         uint32_t w = 0u;
+        if (!SR) {
+            const float* p = v + 8 * k;
+            w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, p[0] * bs.R, p[1] * bs.R, 1.0f, 0);
+            w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, p[2] * bs.R, p[3] * bs.R, 1.0f, 1);
+            w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, p[4] * bs.R, p[5] * bs.R, 1.0f, 2);
+            w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, p[6] * bs.R, p[7] * bs.R, 1.0f, 3);
+        } else {
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-            const int j = 8 * k + jj;
-            uint32_t bits = __float_as_uint(v[j]);
-            float y = __uint_as_float(bits & 0x7FFFFFFFu) * bs.R;
-            uint32_t mag = SR ? e2m1_sr(y, d[j]) : e2m1_rne(y);
-            w |= (((bits >> 28) & 8u) | mag) << (4 * jj);
+            for (int jj = 0; jj < 8; ++jj) {
+                const int j = 8 * k + jj;
+                uint32_t bits = __float_as_uint(v[j]);
+                float y = __uint_as_float(bits & 0x7FFFFFFFu) * bs.R;
+                uint32_t mag = e2m1_sr(y, d[j]);
+                w |= (((bits >> 28) & 8u) | mag) << (4 * jj);
+            }
         }
         out[k] = w;
     }
+}
+
+// Two E2M1 codes (byte `sel` of w; low nibble first) as exact binary32 values,
+// by the gfx950 FP4 unpack instruction with scale operand 1.0.
+__device__ __forceinline__ float2 e2m1x2_unpack(uint32_t w, int sel) {
+    typedef float f2_t __attribute__((ext_vector_type(2)));
+    f2_t r;
+    switch (sel) {
+        case 0: r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0); break;
+        case 1: r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1); break;
+        case 2: r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2); break;
+        default: r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3); break;
+    }
+    return make_float2(r[0], r[1]);
+}
+
+// Two binary32 values -> packed bf16 pair (nearest-even), the first in the
+// low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)a) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)b) << 16);
 }
 
 // E2M1 magnitude value (no sign) as binary32.

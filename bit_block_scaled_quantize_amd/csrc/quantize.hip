@@ -9,59 +9,107 @@
 // работает"), with an optional 16-point random Hadamard transform (asector.ru
 // page, "Эксперименты и сравнение с FP8").
 //
-// All of these are HBM-bound streaming kernels.  Shared structure:
-//   - 256-thread workgroups (four wave64s), 16-byte vector loads whose lanes
-//     cover contiguous addresses, and stores that are contiguous across lanes;
-//   - the tensor amax is a separate pass (per-workgroup partial maxima, then one
-//     small reduction) unless the caller supplies it, because the block
-//     multiplier of every block depends on it;
-//   - the column layout stages a 64 x 64 tile in LDS so that both the loads
-//     (along input rows) and the stores (along output rows, i.e. input columns)
-//     stay contiguous.
+// All of these are HBM-bound streaming kernels whose second limit is VALU
+// issue.  Shared structure:
+//   - 256-thread workgroups (four wave64s); grid dimension x runs over column
+//     groups, so workgroups dispatched together sweep contiguous stretches of
+//     each row (this alone is worth ~25% of HBM throughput against a
+//     row-group-first order); dimension y runs over row groups with a
+//     grid-stride loop;
+//   - 16-byte loads whose lanes cover contiguous spans, and every 128-byte
+//     output line written by one workgroup (or by workgroups dispatched
+//     together);
+//   - the tensor amax is a separate streaming pass writing at most
+//     kMaxPartials per-workgroup maxima, which every consumer workgroup
+//     reduces in its prologue, unless the caller supplies the amax;
+//   - column blocks come from a register tile: a thread holds 16 rows of a
+//     patch, so a column block is 16 values the thread already has (no LDS);
+//   - a 16-element row block lives in a lane pair (quad for fp32 input); the
+//     lanes join their maxima with lane exchanges and split the block-scale
+//     arithmetic between rows;
+//   - nearest-even encoding uses the gfx950 FP4 pack instruction on the
+//     already-scaled values (scale operand 1.0), two codes per instruction.
 #include "launch.hpp"
 #include "nvfp4_device.hpp"
 
 namespace nvfp4 {
 
 // ============================================================ amax
-// Per-workgroup partial maxima of |x| over a rows x cols tensor (no transform),
-// visiting 16-byte chunks along rows.  partial[blockIdx] is always written.
+// A_t for the calling workgroup (all 256 threads must call): n == 0 means
+// src[0] is A_t itself, otherwise the maximum of the n partials src[0..n).
+__device__ __forceinline__ float workgroup_tensor_amax(const float* __restrict__ src, int n) {
+    __shared__ float red[4];
+    if (n == 0) return src[0];
+    float a = 0.0f;
+    for (int i = threadIdx.x; i < n; i += 256) a = fmaxf(a, src[i]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) a = fmaxf(a, __shfl_xor(a, o, 64));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = a;
+    __syncthreads();
+    return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+__device__ __forceinline__ void store_partial(float a, float* __restrict__ partial) {
+    __shared__ float red[4];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) a = fmaxf(a, __shfl_xor(a, o, 64));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = a;
+    __syncthreads();
+    if (threadIdx.x == 0)
+        partial[blockIdx.y * gridDim.x + blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+// 16-byte chunk j of row `row` as binary32 (8 bf16 or 4 fp32 values).
+template <typename T>
+__device__ __forceinline__ void load_chunk(const T* __restrict__ row, int64_t j, float v[8]) {
+    if constexpr (sizeof(T) == 2) {
+        load8(reinterpret_cast<const uint16_t*>(row) + j * 8, v);
+    } else {
+        float4 q = *reinterpret_cast<const float4*>(row + j * 4);
+        v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+    }
+}
+
+// Partial maxima of |x| (no transform).  Rows by, by + gy, ...; in each row
+// the 16-byte chunks bx*256 + tid + 256*(gx*k + u), four per thread per
+// iteration.  A contiguous tensor is passed as one long row.
 template <typename T>
 __global__ void __launch_bounds__(256) k_amax_plain(const T* __restrict__ x, int64_t rows,
                                                     int64_t cols, int64_t ld,
                                                     float* __restrict__ partial) {
-    constexpr int CH = 16 / sizeof(T);  // elements per 16-byte chunk
+    constexpr int CH = 16 / sizeof(T);
+    constexpr int U = 4;
     const int64_t nch = (cols + CH - 1) / CH;
+    const int64_t step = (int64_t)gridDim.x * 256 * U;
     float a = 0.0f;
     for (int64_t r = blockIdx.y; r < rows; r += gridDim.y) {
         const T* row = x + r * ld;
-        for (int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x; j < nch; j += (int64_t)gridDim.x * 256) {
-            float v[8];
-            if constexpr (sizeof(T) == 2) {
-                load8(reinterpret_cast<const uint16_t*>(row) + j * CH, v);
-            } else {
-                float4 q = *reinterpret_cast<const float4*>(row + j * CH);
-                v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
-            }
-            int64_t valid = cols - j * CH;
+        for (int64_t j0 = (int64_t)blockIdx.x * 256 * U + threadIdx.x; j0 < nch; j0 += step) {
+            float v[U][8];
 #pragma unroll
-            for (int e = 0; e < CH; ++e)
-                if (e < valid) a = fmaxf(a, fabsf(v[e]));
+            for (int u = 0; u < U; ++u) {
+                const int64_t j = j0 + 256 * u;
+                if (j < nch) {
+                    load_chunk(row, j, v[u]);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) v[u][e] = 0.0f;
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t valid = cols - (j0 + 256 * u) * CH;
+#pragma unroll
+                for (int e = 0; e < CH; ++e)
+                    if (e < valid) a = fmaxf(a, fabsf(v[u][e]));
+            }
         }
     }
-    // wave reduction then workgroup reduction
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) a = fmaxf(a, __shfl_xor(a, o, 64));
-    __shared__ float red[4];
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = a;
-    __syncthreads();
-    if (threadIdx.x == 0)
-        partial[blockIdx.y * gridDim.x + blockIdx.x] =
-            fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    store_partial(a, partial);
 }
 
-// Partial maxima of |H16 D x| with the transform applied along rows (groups
-// of 16 consecutive columns; cols % 16 == 0).
+// Partial maxima of |H16 D x| with the transform along rows (16 consecutive
+// columns; cols % 16 == 0): two 16-element groups per thread per row.
 template <typename T>
 __global__ void __launch_bounds__(256) k_amax_hadamard_rows(const T* __restrict__ x, int64_t rows,
                                                             int64_t cols, int64_t ld,
@@ -70,27 +118,31 @@ __global__ void __launch_bounds__(256) k_amax_hadamard_rows(const T* __restrict_
     const int64_t nb = cols / 16;
     float a = 0.0f;
     for (int64_t r = blockIdx.y; r < rows; r += gridDim.y) {
-        const T* row = x + r * ld;
-        for (int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x; j < nb; j += (int64_t)gridDim.x * 256) {
-            float v[16];
-            load8(row + j * 16, v);
-            load8(row + j * 16 + 8, v + 8);
-            hadamard16(v, sign_mask);
-            a = fmaxf(a, absmax16(v));
+        for (int64_t b0 = (int64_t)blockIdx.x * 512 + threadIdx.x; b0 < nb; b0 += (int64_t)gridDim.x * 512) {
+            float v[2][16];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int64_t b = b0 + 256 * u;
+                if (b < nb) {
+                    load8(x + r * ld + b * 16, v[u]);
+                    load8(x + r * ld + b * 16 + 8, v[u] + 8);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) v[u][e] = 0.0f;
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                hadamard16(v[u], sign_mask);
+                a = fmaxf(a, absmax16(v[u]));
+            }
         }
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) a = fmaxf(a, __shfl_xor(a, o, 64));
-    __shared__ float red[4];
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = a;
-    __syncthreads();
-    if (threadIdx.x == 0)
-        partial[blockIdx.y * gridDim.x + blockIdx.x] =
-            fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    store_partial(a, partial);
 }
 
-// Partial maxima with the transform applied down columns (groups of 16
-// consecutive rows; rows % 16 == 0).  A thread owns a 16-row x 16-byte patch.
+// Partial maxima with the transform down columns (16 consecutive rows;
+// rows % 16 == 0).  A thread owns a 16-row x 16-byte patch.
 template <typename T>
 __global__ void __launch_bounds__(256) k_amax_hadamard_cols(const T* __restrict__ x, int64_t rows,
                                                             int64_t cols, int64_t ld,
@@ -105,18 +157,12 @@ __global__ void __launch_bounds__(256) k_amax_hadamard_cols(const T* __restrict_
             float col[CH][16];
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const T* p = x + (rb * 16 + i) * ld + j * CH;
                 float v[8];
-                if constexpr (sizeof(T) == 2) {
-                    load8(reinterpret_cast<const uint16_t*>(p), v);
-                } else {
-                    float4 q = *reinterpret_cast<const float4*>(p);
-                    v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
-                }
+                load_chunk(x + (rb * 16 + i) * ld, j, v);
 #pragma unroll
                 for (int e = 0; e < CH; ++e) col[e][i] = v[e];
             }
-            int64_t valid = cols - j * CH;
+            const int64_t valid = cols - j * CH;
 #pragma unroll
             for (int e = 0; e < CH; ++e) {
                 hadamard16(col[e], sign_mask);
@@ -124,255 +170,338 @@ __global__ void __launch_bounds__(256) k_amax_hadamard_cols(const T* __restrict_
             }
         }
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) a = fmaxf(a, __shfl_xor(a, o, 64));
-    __shared__ float red[4];
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = a;
-    __syncthreads();
-    if (threadIdx.x == 0)
-        partial[blockIdx.y * gridDim.x + blockIdx.x] =
-            fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    store_partial(a, partial);
 }
 
-// One workgroup: out[0] = max(partial[0 .. n)).
-__global__ void __launch_bounds__(256) k_amax_final(const float* __restrict__ partial, int n,
-                                                    float* __restrict__ out) {
-    float a = 0.0f;
-    for (int i = threadIdx.x; i < n; i += 256) a = fmaxf(a, partial[i]);
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) a = fmaxf(a, __shfl_xor(a, o, 64));
-    __shared__ float red[4];
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = a;
-    __syncthreads();
-    if (threadIdx.x == 0) out[0] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-}
-
-// tensor_scale outputs of an empty tensor (no element kernel runs).
-__global__ void k_write_tensor_scale(const float* amax_in, float* ts0, float* ts1) {
-    float st = tensor_scale_of(amax_in ? amax_in[0] : 0.0f);
+// tensor_scale (and amax_out) of an empty tensor: no element kernel runs.
+__global__ void k_write_tensor_scale(const float* amax_in, float* ts0, float* ts1, float* amax_out) {
+    float a = amax_in ? amax_in[0] : 0.0f;
+    float st = tensor_scale_of(a);
     if (ts0) ts0[0] = st;
     if (ts1) ts1[0] = st;
+    if (amax_out) amax_out[0] = a;
+}
+
+// Shared prologue: reduce A_t, derive s_t, and let workgroup 0 publish s_t
+// and A_t.
+struct TensorScale {
+    float st, six_st;
+};
+
+__device__ __forceinline__ TensorScale prologue(const float* amax_src, int n_partials, float* ts0,
+                                                float* ts1, float* amax_out) {
+    const float a = workgroup_tensor_amax(amax_src, n_partials);
+    TensorScale t;
+    t.st = tensor_scale_of(a);
+    t.six_st = 6.0f * t.st;
+    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
+        if (ts0) ts0[0] = t.st;
+        if (ts1) ts1[0] = t.st;
+        if (amax_out) amax_out[0] = a;
+    }
+    return t;
+}
+
+// ============================================================ shared pieces
+// The Hadamard transform of a block split over a lane pair: stages 1, 2, 4 run
+// in each lane; the distance-8 stage pairs element j of the even lane with
+// element j of the odd lane, computed as (even + odd) on the even lane and
+// (even - odd) on the odd lane -- the same operations on the same operands as
+// the sequential butterfly.
+__device__ __forceinline__ void hadamard8_pair(float v[8], uint32_t sign_mask, bool odd) {
+    const uint32_t m = odd ? (sign_mask >> 8) : sign_mask;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        if ((m >> j) & 1u) v[j] = -v[j];
+#pragma unroll
+    for (int hh = 1; hh < 8; hh <<= 1) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (j & hh) continue;
+            float a = v[j], b = v[j + hh];
+            v[j] = a + b;
+            v[j + hh] = a - b;
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const float p = __shfl_xor(v[j], 1, 64);
+        v[j] = odd ? (p - v[j]) : (v[j] + p);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = 0.25f * v[j];
+}
+
+// Lane-pair block scales for two rows (r, r+1) whose 16-element blocks are
+// split 8 + 8 between lanes 2k (even) and 2k+1 (odd): both lanes join both
+// rows' maxima, the even lane derives row r's multiplier and the odd lane row
+// r+1's, and one exchange hands each lane both.
+__device__ __forceinline__ void pair_block_scales(float a0, float a1, bool odd, const TensorScale& ts,
+                                                  BlockScale& b0, BlockScale& b1) {
+    a0 = fmaxf(a0, __shfl_xor(a0, 1, 64));
+    a1 = fmaxf(a1, __shfl_xor(a1, 1, 64));
+    const BlockScale mine = block_scale(odd ? a1 : a0, ts.six_st, ts.st);
+    BlockScale other;
+    other.R = __shfl_xor(mine.R, 1, 64);
+    other.byte = (uint32_t)__shfl_xor((int)mine.byte, 1, 64);
+    b0 = odd ? other : mine;
+    b1 = odd ? mine : other;
 }
 
 // ============================================================ ROW_1D
-// Workgroup = 4 waves x 4 rows (rows 16*blockIdx.x ..); lane l of a wave owns
-// block (blockIdx.y * 64 + l) of each of its rows: 32 bytes of bf16 (or 64 of
-// fp32) in, 8 code bytes and one scale byte out.  The lanes of a wave cover
-// 2 (4) KiB of one row.
+// Every lane holds 8 consecutive elements of a row (one 16-byte load for bf16,
+// two for fp32); lanes 2k and 2k+1 hold the two halves of one 16-element block.
+// Wave w owns rows 8 * rg + 2w, +1 of row group rg and 512 columns from
+// 512 * blockIdx.x; a wave-wide load reads 1 KiB (bf16) of one row.
 template <typename T, bool SR, bool RHT>
 __global__ void __launch_bounds__(256) k_quant_row(const T* __restrict__ x, int64_t rows,
                                                    int64_t cols, int64_t ld,
-                                                   const float* __restrict__ amax_ptr,
+                                                   const float* __restrict__ amax_src, int n_part,
                                                    uint64_t seed, uint32_t sign_mask,
                                                    uint8_t* __restrict__ codes,
                                                    uint8_t* __restrict__ scales,
-                                                   float* __restrict__ ts_out) {
-    const float st = tensor_scale_of(amax_ptr[0]);
-    const float six_st = 6.0f * st;
-    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) ts_out[0] = st;
-    const int64_t nb = cols / 16;
-    const int64_t b = (int64_t)blockIdx.y * 64 + (threadIdx.x & 63);
-    if (b >= nb) return;
-    const int64_t r0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 4;
+                                                   float* __restrict__ ts_out, float* amax_out) {
+    const TensorScale ts = prologue(amax_src, n_part, ts_out, nullptr, amax_out);
+    const int lane = threadIdx.x & 63;
+    const bool odd = lane & 1;
+    const int64_t c = (int64_t)blockIdx.x * 512 + 8 * lane;
+    const bool col_ok = c < cols;  // cols % 16 == 0: both lanes of a pair agree
+    const int64_t nrg = (rows + 7) / 8;
+    for (int64_t rg = blockIdx.y; rg < nrg; rg += gridDim.y) {
+        const int64_t r = rg * 8 + 2 * (threadIdx.x >> 6);
+        float v[2][8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int64_t r = r0 + i;
-        if (r >= rows) break;
-        const T* p = x + r * ld + b * 16;
-        float v[16];
-        load8(p, v);
-        load8(p + 8, v + 8);
-        if (RHT) hadamard16(v, sign_mask);
-        BlockScale bs = block_scale(absmax16(v), six_st, st);
-        uint32_t d[16];
-        if (SR) draws16(seed, kStreamRow, (uint64_t)(r * cols + b * 16), d);
-        uint32_t w[2];
-        encode<SR, 16>(v, bs, d, w);
-        const int64_t blk = r * nb + b;
-        *reinterpret_cast<uint2*>(codes + blk * 8) = make_uint2(w[0], w[1]);
-        scales[blk] = (uint8_t)bs.byte;
-    }
-}
-
-// ============================================================ tiles through LDS
-// A 64 x 64 tile of x (rows r0.., cols c0..) as binary32 in LDS, row stride 65
-// floats (the odd stride spreads column walks over the banks).
-constexpr int kTile = 64;
-constexpr int kTileStride = 65;
-
-template <typename T>
-__device__ __forceinline__ void load_tile(const T* __restrict__ x, int64_t rows, int64_t cols,
-                                          int64_t ld, int64_t r0, int64_t c0, float* tile) {
-    constexpr int CH = 16 / sizeof(T);           // elements per 16-byte chunk
-    constexpr int NCH = kTile / CH;              // chunks per tile row
-    constexpr int PER = kTile * NCH / 256;       // chunks per thread
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-        const int idx = threadIdx.x + 256 * k;
-        const int tr = idx / NCH, tc = (idx % NCH) * CH;
-        const int64_t r = r0 + tr, c = c0 + tc;
-        float v[8];
-        if (r < rows && c < cols) {
-            const T* p = x + r * ld + c;
-            if constexpr (sizeof(T) == 2) {
-                load8(reinterpret_cast<const uint16_t*>(p), v);
+        for (int k = 0; k < 2; ++k) {
+            if (col_ok && r + k < rows) {
+                load8(x + (r + k) * ld + c, v[k]);
             } else {
-                float4 q = *reinterpret_cast<const float4*>(p);
-                v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[k][e] = 0.0f;
             }
-        } else {
-#pragma unroll
-            for (int e = 0; e < CH; ++e) v[e] = 0.0f;
         }
+        if (RHT) {
+            hadamard8_pair(v[0], sign_mask, odd);
+            hadamard8_pair(v[1], sign_mask, odd);
+        }
+        float a[2] = {0.0f, 0.0f};
 #pragma unroll
-        for (int e = 0; e < CH; ++e) tile[tr * kTileStride + tc + e] = v[e];
+        for (int k = 0; k < 2; ++k)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) a[k] = fmaxf(a[k], fabsf(v[k][e]));
+        BlockScale bs[2];
+        pair_block_scales(a[0], a[1], odd, ts, bs[0], bs[1]);
+        if (!col_ok) continue;
+        uint32_t d[2][8];
+        if (SR) draws8x2(seed, kStreamRow, (uint64_t)(r * cols + c), (uint64_t)((r + 1) * cols + c), d[0], d[1]);
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            if (r + k >= rows) break;
+            uint32_t w[1];
+            encode<SR, 8>(v[k], bs[k], d[k], w);
+            *reinterpret_cast<uint32_t*>(codes + (r + k) * (cols / 2) + c / 2) = w[0];
+            if (odd == (k == 1)) scales[(r + k) * (cols / 16) + c / 16] = (uint8_t)bs[k].byte;
+        }
     }
 }
 
-// Column blocks of the tile: thread t quantizes column c0 + t/4, rows
-// r0 + 16*(t%4) .. +15, into row (c0 + t/4) of the transposed output.
-template <bool SR, bool RHT>
-__device__ __forceinline__ void quant_tile_cols(const float* tile, int64_t rows, int64_t cols,
-                                                int64_t r0, int64_t c0, float st, float six_st,
-                                                uint64_t seed, uint32_t sign_mask,
-                                                uint8_t* __restrict__ codes,
-                                                uint8_t* __restrict__ scales) {
-    const int tc = threadIdx.x >> 2, rb = threadIdx.x & 3;
-    const int64_t c = c0 + tc, r = r0 + 16 * rb;
-    if (c >= cols || r >= rows) return;
-    float v[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) v[i] = tile[(16 * rb + i) * kTileStride + tc];
-    if (RHT) hadamard16(v, sign_mask);
-    BlockScale bs = block_scale(absmax16(v), six_st, st);
-    uint32_t d[16];
-    if (SR) draws16(seed, kStreamCol, (uint64_t)(c * rows + r), d);
-    uint32_t w[2];
-    encode<SR, 16>(v, bs, d, w);
-    *reinterpret_cast<uint2*>(codes + c * (rows / 2) + r / 2) = make_uint2(w[0], w[1]);
-    scales[c * (rows / 16) + r / 16] = (uint8_t)bs.byte;
-}
+// ============================================================ register tile
+// COL_1D and ROW_COL_1D.  Workgroup (x, y) owns the tile of 256 rows from
+// 256 * y and 32*CH columns from 32*CH * x (CH = 8 bf16 or 4 fp32 elements per
+// 16-byte chunk).  Thread (pc, pr) =
+// (lane % 16, lane / 16 + 4 * wave) holds rows 16 pr .. 16 pr + 15 of two
+// chunks: columns CH * pc .. and CH * (pc + 16) .. of the tile, so every
+// wave-wide load reads 4 rows x 256 contiguous bytes.
+//   column blocks: the 16 values of one column in the thread -> 8 code bytes
+//     of output row c; the tile's 16 row bands complete each 128-byte line;
+//   row blocks (ROW_COL): a 16-element row block spans LPB = 16 / CH lanes
+//     (a pair for bf16, a quad for fp32); the lanes join their maxima, split
+//     the block-scale arithmetic over LPB rows, and exchange the results.
+template <typename T>
+struct Patch {
+    static constexpr int CH = 16 / sizeof(T);  // elements per 16-byte chunk
+    static constexpr int LPB = 16 / CH;        // lanes per 16-element row block
+    static constexpr int TW = 32 * CH;         // tile width (columns)
+};
 
-// Row blocks of the tile: thread t quantizes row r0 + t/4, columns
-// c0 + 16*(t%4) .. +15.
-template <bool SR>
-__device__ __forceinline__ void quant_tile_rows(const float* tile, int64_t rows, int64_t cols,
-                                                int64_t r0, int64_t c0, float st, float six_st,
-                                                uint64_t seed, uint8_t* __restrict__ codes,
-                                                uint8_t* __restrict__ scales) {
-    const int tr = threadIdx.x >> 2, cb = threadIdx.x & 3;
-    const int64_t r = r0 + tr, c = c0 + 16 * cb;
-    if (r >= rows || c >= cols) return;
-    float v[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) v[i] = tile[tr * kTileStride + 16 * cb + i];
-    BlockScale bs = block_scale(absmax16(v), six_st, st);
-    uint32_t d[16];
-    if (SR) draws16(seed, kStreamRow, (uint64_t)(r * cols + c), d);
-    uint32_t w[2];
-    encode<SR, 16>(v, bs, d, w);
-    *reinterpret_cast<uint2*>(codes + r * (cols / 2) + c / 2) = make_uint2(w[0], w[1]);
-    scales[r * (cols / 16) + c / 16] = (uint8_t)bs.byte;
-}
-
-// COL_1D: grid (rows/64 tiles, cols/64 tiles); consecutive workgroups walk down
-// the rows so that their output segments of one transposed row are adjacent.
-template <typename T, bool SR, bool RHT>
-__global__ void __launch_bounds__(256) k_quant_col(const T* __restrict__ x, int64_t rows,
-                                                   int64_t cols, int64_t ld,
-                                                   const float* __restrict__ amax_ptr,
-                                                   uint64_t seed, uint32_t sign_mask,
-                                                   uint8_t* __restrict__ codes,
-                                                   uint8_t* __restrict__ scales,
-                                                   float* __restrict__ ts_out) {
-    __shared__ float tile[kTile * kTileStride];
-    const float st = tensor_scale_of(amax_ptr[0]);
-    const float six_st = 6.0f * st;
-    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) ts_out[0] = st;
-    const int64_t r0 = (int64_t)blockIdx.x * kTile, c0 = (int64_t)blockIdx.y * kTile;
-    load_tile(x, rows, cols, ld, r0, c0, tile);
-    __syncthreads();
-    quant_tile_cols<SR, RHT>(tile, rows, cols, r0, c0, st, six_st, seed, sign_mask, codes, scales);
-}
-
-// ROW_COL_1D: one read of each tile, both outputs.
-template <typename T, bool SR>
-__global__ void __launch_bounds__(256) k_quant_rowcol(const T* __restrict__ x, int64_t rows,
-                                                      int64_t cols, int64_t ld,
-                                                      const float* __restrict__ amax_ptr,
-                                                      uint64_t seed, uint8_t* __restrict__ rcodes,
-                                                      uint8_t* __restrict__ rscales,
-                                                      float* __restrict__ rts,
-                                                      uint8_t* __restrict__ ccodes,
-                                                      uint8_t* __restrict__ cscales,
-                                                      float* __restrict__ cts) {
-    __shared__ float tile[kTile * kTileStride];
-    const float st = tensor_scale_of(amax_ptr[0]);
-    const float six_st = 6.0f * st;
-    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
-        rts[0] = st;
-        cts[0] = st;
+// Element e of a raw 16-byte chunk (bf16 pairs or fp32).
+template <typename T>
+__device__ __forceinline__ float chunk_elem(const uint4& q, int e) {
+    if constexpr (sizeof(T) == 2) {
+        const uint32_t w = (e >> 1) == 0 ? q.x : (e >> 1) == 1 ? q.y : (e >> 1) == 2 ? q.z : q.w;
+        return (e & 1) ? __uint_as_float(w & 0xFFFF0000u) : __uint_as_float(w << 16);
+    } else {
+        return __uint_as_float(e == 0 ? q.x : e == 1 ? q.y : e == 2 ? q.z : q.w);
     }
-    const int64_t r0 = (int64_t)blockIdx.x * kTile, c0 = (int64_t)blockIdx.y * kTile;
-    load_tile(x, rows, cols, ld, r0, c0, tile);
-    __syncthreads();
-    quant_tile_rows<SR>(tile, rows, cols, r0, c0, st, six_st, seed, rcodes, rscales);
-    quant_tile_cols<SR, false>(tile, rows, cols, r0, c0, st, six_st, seed, 0u, ccodes, cscales);
+}
+
+template <typename T, bool DO_ROW, bool DO_COL, bool SR, bool RHT>
+__global__ void __launch_bounds__(256) k_quant_tile(const T* __restrict__ x, int64_t rows,
+                                                    int64_t cols, int64_t ld,
+                                                    const float* __restrict__ amax_src, int n_part,
+                                                    uint64_t seed, uint32_t sign_mask,
+                                                    uint8_t* __restrict__ rcodes,
+                                                    uint8_t* __restrict__ rscales,
+                                                    float* __restrict__ rts,
+                                                    uint8_t* __restrict__ ccodes,
+                                                    uint8_t* __restrict__ cscales,
+                                                    float* __restrict__ cts, float* amax_out) {
+    constexpr int CH = Patch<T>::CH, LPB = Patch<T>::LPB, TW = Patch<T>::TW;
+    const TensorScale ts = prologue(amax_src, n_part, DO_ROW ? rts : nullptr, DO_COL ? cts : nullptr,
+                                    amax_out);
+    const int lane = threadIdx.x & 63;
+    const int pc = lane & 15, pr = (lane >> 4) + 4 * (threadIdx.x >> 6);
+    const int q = pc % LPB;  // this lane's quarter / half of a row block
+    int64_t cb[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) cb[h] = (int64_t)blockIdx.x * TW + CH * (pc + 16 * h);
+    {
+        const int64_t r0 = (int64_t)blockIdx.y * 256 + 16 * pr;
+        const bool rows_ok = r0 < rows;  // rows % 16 == 0: a patch is wholly inside or outside
+
+        uint4 raw[16][2];
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                raw[i][h] = make_uint4(0u, 0u, 0u, 0u);
+                if (rows_ok && cb[h] < cols) raw[i][h] = *reinterpret_cast<const uint4*>(x + (r0 + i) * ld + cb[h]);
+            }
+
+        if (DO_COL && rows_ok) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int e = 0; e < CH; ++e) {
+                    const int64_t c = cb[h] + e;
+                    if (c >= cols) continue;  // (not break: the loop must unroll fully)
+                    float col[16];
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) col[i] = chunk_elem<T>(raw[i][h], e);
+                    if (RHT) hadamard16(col, sign_mask);
+                    BlockScale bs = block_scale(absmax16(col), ts.six_st, ts.st);
+                    uint32_t d[16];
+                    if (SR) draws16(seed, kStreamCol, (uint64_t)(c * rows + r0), d);
+                    uint32_t w[2];
+                    encode<SR, 16>(col, bs, d, w);
+                    *reinterpret_cast<uint2*>(ccodes + c * (rows / 2) + r0 / 2) = make_uint2(w[0], w[1]);
+                    cscales[c * (rows / 16) + r0 / 16] = (uint8_t)bs.byte;
+                }
+        }
+
+        if (DO_ROW) {
+            // cols % 16 == 0 and rows % 16 == 0 here: the LPB lanes of a block agree
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const bool ok = rows_ok && cb[h] < cols;
+#pragma unroll
+                for (int i0 = 0; i0 < 16; i0 += LPB) {
+                    // maxima of this lane's part of rows i0 .. i0+LPB-1, joined over the block's lanes
+                    float a[LPB];
+#pragma unroll
+                    for (int k = 0; k < LPB; ++k) {
+                        float m = 0.0f;
+#pragma unroll
+                        for (int e = 0; e < CH; ++e) m = fmaxf(m, fabsf(chunk_elem<T>(raw[i0 + k][h], e)));
+#pragma unroll
+                        for (int o = 1; o < LPB; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+                        a[k] = m;
+                    }
+                    // lane q of the block derives row i0+q's multiplier; gather all LPB
+                    float mine_a = a[0];
+#pragma unroll
+                    for (int k = 1; k < LPB; ++k) mine_a = (q == k) ? a[k] : mine_a;
+                    const BlockScale mine = block_scale(mine_a, ts.six_st, ts.st);
+                    BlockScale bs[LPB];
+                    const int base = lane - q;
+#pragma unroll
+                    for (int k = 0; k < LPB; ++k) {
+                        bs[k].R = __shfl(mine.R, base + k, 64);
+                        bs[k].byte = (uint32_t)__shfl((int)mine.byte, base + k, 64);
+                    }
+                    if (!ok) continue;
+#pragma unroll
+                    for (int k = 0; k < LPB; ++k) {
+                        const int64_t r = r0 + i0 + k;
+                        float v[8];
+#pragma unroll
+                        for (int e = 0; e < CH; ++e) v[e] = chunk_elem<T>(raw[i0 + k][h], e);
+#pragma unroll
+                        for (int e = CH; e < 8; ++e) v[e] = 0.0f;
+                        uint32_t d[8];
+                        if (SR) draws8(seed, kStreamRow, (uint64_t)((r * cols + cb[h]) & ~(int64_t)7), d);
+                        if (SR && CH == 4 && (cb[h] & 4)) {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) d[e] = d[e + 4];
+                        }
+                        uint32_t w[1];
+                        encode<SR, 8>(v, bs[k], d, w);
+                        uint8_t* dst = rcodes + r * (cols / 2) + cb[h] / 2;
+                        if (CH == 8) *reinterpret_cast<uint32_t*>(dst) = w[0];
+                        else *reinterpret_cast<uint16_t*>(dst) = (uint16_t)w[0];
+                        if (q == k) rscales[r * (cols / 16) + cb[h] / 16] = (uint8_t)bs[k].byte;
+                    }
+                }
+            }
+        }
+    }
 }
 
 // ============================================================ BLK_2D
 // A thread owns a 16-row x 8-column patch; lanes 2k and 2k+1 together hold one
-// 16 x 16 square and combine their maxima with one lane exchange.  Wave w of
-// the workgroup takes row band 4*blockIdx.x + w; the 64 lanes cover 512
-// columns (from 512*blockIdx.y), so every 16-byte load of a wave reads 1 KiB
-// of one row.
+// 16 x 16 square and combine their maxima with one lane exchange.  Wave w takes
+// row band 4 * blockIdx.y + w; the 64 lanes cover 512 columns from
+// 512 * blockIdx.x, so every 16-byte load of a wave reads 1 KiB of one
+// row and every code store writes 256 contiguous bytes.
 template <typename T, bool SR>
 __global__ void __launch_bounds__(256) k_quant_2d(const T* __restrict__ x, int64_t rows,
                                                   int64_t cols, int64_t ld,
-                                                  const float* __restrict__ amax_ptr,
+                                                  const float* __restrict__ amax_src, int n_part,
                                                   uint64_t seed, uint8_t* __restrict__ codes,
                                                   uint8_t* __restrict__ scales,
-                                                  float* __restrict__ ts_out) {
-    const float st = tensor_scale_of(amax_ptr[0]);
-    const float six_st = 6.0f * st;
-    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) ts_out[0] = st;
+                                                  float* __restrict__ ts_out, float* amax_out) {
+    const TensorScale ts = prologue(amax_src, n_part, ts_out, nullptr, amax_out);
     const int lane = threadIdx.x & 63;
-    const int64_t rband = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int64_t c = (int64_t)blockIdx.y * 512 + lane * 8;
-    const int64_t r0 = rband * 16;
-    const bool active = (r0 < rows) && (c < cols);
-    float v[16][8];
-    float a = 0.0f;
-    if (active) {
+    const int64_t c = (int64_t)blockIdx.x * 512 + lane * 8;
+    {
+        const int64_t rband = (int64_t)blockIdx.y * 4 + (threadIdx.x >> 6);
+        const int64_t r0 = rband * 16;
+        const bool active = (r0 < rows) && (c < cols);
+        float v[16][8];
+        float a = 0.0f;
+        if (active) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) load8(x + (r0 + i) * ld + c, v[i]);
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(v[i][e]));
+        }
+        // the partner lane holds the other 8 columns of the square (both are
+        // active or both inactive, since cols % 16 == 0)
+        a = fmaxf(a, __shfl_xor(a, 1, 64));
+        if (!active) return;
+        BlockScale bs = block_scale(a, ts.six_st, ts.st);
+        if ((lane & 1) == 0) scales[rband * (cols / 16) + c / 16] = (uint8_t)bs.byte;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            load8(x + (r0 + i) * ld + c, v[i]);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(v[i][e]));
+            const int64_t r = r0 + i;
+            uint32_t d[8];
+            if (SR) draws8(seed, kStream2D, (uint64_t)(r * cols + c), d);
+            uint32_t w[1];
+            encode<SR, 8>(v[i], bs, d, w);
+            *reinterpret_cast<uint32_t*>(codes + r * (cols / 2) + c / 2) = w[0];
         }
-    }
-    // partner lane holds the other 8 columns of the square (both are active or
-    // both inactive, since cols % 16 == 0)
-    a = fmaxf(a, __shfl_xor(a, 1, 64));
-    if (!active) return;
-    BlockScale bs = block_scale(a, six_st, st);
-    const int64_t ncb = cols / 16;
-    if ((lane & 1) == 0) scales[rband * ncb + c / 16] = (uint8_t)bs.byte;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int64_t r = r0 + i;
-        uint32_t d[8];
-        if (SR) draws8(seed, kStream2D, (uint64_t)(r * cols + c), d);
-        uint32_t w[1];
-        encode<SR, 8>(v[i], bs, d, w);
-        *reinterpret_cast<uint32_t*>(codes + r * (cols / 2) + c / 2) = w[0];
     }
 }
 
 // ============================================================ dequantize
-// Same geometry as the row quantizer (rows on grid x, 64-block column groups on
-// grid y): a lane expands one 16-element block of each of 4 rows; 8 code bytes and a scale byte in, 32 (bf16) or 64 (fp32)
-// bytes out.
+// A lane expands one 16-element block of each of 4 rows (row group rg = 16
+// rows per workgroup); the 64 lanes of a wave cover 1024 columns from
+// 1024 * blockIdx.x: 8 code bytes and a scale byte in, 32 (bf16) or 64 (fp32)
+// bytes out per row.  Codes are expanded two at a time by the gfx950 FP4
+// unpack instruction (scale operand 1.0, so the values are exact), then
+// multiplied by the block multiplier (exact: at most 6 significant bits) and
+// by s_t (one rounding).
 template <typename TOut>
 __global__ void __launch_bounds__(256) k_dequant(const uint8_t* __restrict__ codes,
                                                  const uint8_t* __restrict__ scales,
@@ -381,40 +510,48 @@ __global__ void __launch_bounds__(256) k_dequant(const uint8_t* __restrict__ cod
                                                  int64_t ld) {
     const float st = ts[0];
     const int64_t nb = cols / 16;
-    const int64_t b = (int64_t)blockIdx.y * 64 + (threadIdx.x & 63);
+    const int64_t b = (int64_t)blockIdx.x * 64 + (threadIdx.x & 63);
     if (b >= nb) return;
-    const int64_t r0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 4;
+    const int64_t nrg = (rows + 15) / 16;
+    for (int64_t rg = blockIdx.y; rg < nrg; rg += gridDim.y) {
+        const int64_t r0 = rg * 16 + 4 * (threadIdx.x >> 6);
+        uint2 cw[4];
+        uint32_t sb[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int64_t r = r0 + i;
-        if (r >= rows) break;
-        const uint2 cw = *reinterpret_cast<const uint2*>(codes + (r * nb + b) * 8);
-        const uint32_t sb = scale_2d ? scales[(r / 16) * nb + b] : scales[r * nb + b];
-        const float sv = e4m3_value(sb);
-        float o[16];
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            uint32_t code = ((j < 8 ? cw.x : cw.y) >> (4 * (j & 7))) & 15u;
-            float p = e2m1_value(code) * sv;  // exact: at most 6 significant bits
-            o[j] = p * st;
-        }
-        TOut* q = y + r * ld + b * 16;
-        if constexpr (sizeof(TOut) == 2) {
-            uint32_t pk[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                uint32_t lo = __float_as_uint(o[2 * j]), hi = __float_as_uint(o[2 * j + 1]);
-                lo = (lo + 0x7FFFu + ((lo >> 16) & 1u)) >> 16;   // nearest-even to bf16
-                hi = (hi + 0x7FFFu + ((hi >> 16) & 1u)) >> 16;
-                pk[j] = lo | (hi << 16);
+        for (int i = 0; i < 4; ++i) {
+            const int64_t r = r0 + i;
+            cw[i] = make_uint2(0u, 0u);
+            sb[i] = 0u;
+            if (r < rows) {
+                cw[i] = *reinterpret_cast<const uint2*>(codes + (r * nb + b) * 8);
+                sb[i] = scale_2d ? scales[(r / 16) * nb + b] : scales[r * nb + b];
             }
-            uint4* qq = reinterpret_cast<uint4*>(q);
-            qq[0] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-            qq[1] = make_uint4(pk[4], pk[5], pk[6], pk[7]);
-        } else {
-            float4* qq = reinterpret_cast<float4*>(q);
+        }
 #pragma unroll
-            for (int j = 0; j < 4; ++j) qq[j] = make_float4(o[4 * j], o[4 * j + 1], o[4 * j + 2], o[4 * j + 3]);
+        for (int i = 0; i < 4; ++i) {
+            const int64_t r = r0 + i;
+            if (r >= rows) break;
+            const float sv = e4m3_value(sb[i]);
+            float o[16];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                float2 p = e2m1x2_unpack(k < 4 ? cw[i].x : cw[i].y, k & 3);
+                o[2 * k] = (p.x * sv) * st;
+                o[2 * k + 1] = (p.y * sv) * st;
+            }
+            TOut* qp = y + r * ld + b * 16;
+            if constexpr (sizeof(TOut) == 2) {
+                uint32_t pk[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) pk[j] = pack_bf16x2(o[2 * j], o[2 * j + 1]);
+                uint4* qq = reinterpret_cast<uint4*>(qp);
+                qq[0] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+                qq[1] = make_uint4(pk[4], pk[5], pk[6], pk[7]);
+            } else {
+                float4* qq = reinterpret_cast<float4*>(qp);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) qq[j] = make_float4(o[4 * j], o[4 * j + 1], o[4 * j + 2], o[4 * j + 3]);
+            }
         }
     }
 }
@@ -424,112 +561,102 @@ namespace {
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// grid of an amax pass: x covers `units_x` per-thread units (256 per
-// workgroup), y covers `units_y` rows (or row bands); at most kMaxPartials
-// workgroups in total, both loops grid-stride.
-dim3 amax_grid(int64_t units_x, int64_t units_y) {
-    int64_t gx = std::min<int64_t>(std::max<int64_t>(cdiv(units_x, 256), 1), kMaxPartials);
-    int64_t gy = std::min<int64_t>(std::max<int64_t>(units_y, 1), kMaxPartials / gx);
-    return dim3((unsigned)gx, (unsigned)gy, 1);
-}
+// grid y covers `units` row groups, capped (the kernels loop over the rest)
+inline unsigned grid_y(int64_t units) { return (unsigned)std::max<int64_t>(1, std::min<int64_t>(units, 65535)); }
 
+// Launch the amax pass; returns the number of partials written to ws
+// (at most kMaxPartials).
 template <typename T>
-hipError_t amax_typed(const T* x, int64_t rows, int64_t cols, int64_t ld, int hadamard_dim,
-                      uint32_t sign_mask, float* ws, hipStream_t s) {
-    float* out = ws;
-    float* partial = ws + 4;
-    dim3 g;
+int amax_partials(const T* x, int64_t rows, int64_t cols, int64_t ld, int hadamard_dim,
+                  uint32_t sign_mask, float* ws, hipStream_t s) {
+    constexpr int CH = 16 / sizeof(T);
+    int64_t gx, gy;
     if (hadamard_dim == 1) {          // along rows
-        g = amax_grid(cols / 16, rows);
-        hipLaunchKernelGGL(k_amax_hadamard_rows<T>, g, dim3(256), 0, s, x, rows, cols, ld, sign_mask, partial);
+        gx = std::min<int64_t>(std::max<int64_t>(cdiv(cols / 16, 512), 1), kMaxPartials);
+        gy = std::min<int64_t>(std::max<int64_t>(rows, 1), kMaxPartials / gx);
+        hipLaunchKernelGGL(k_amax_hadamard_rows<T>, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, s, x,
+                           rows, cols, ld, sign_mask, ws);
     } else if (hadamard_dim == 2) {   // down columns
-        constexpr int CH = 16 / sizeof(T);
-        g = amax_grid(cdiv(cols, CH), rows / 16);
-        hipLaunchKernelGGL(k_amax_hadamard_cols<T>, g, dim3(256), 0, s, x, rows, cols, ld, sign_mask, partial);
+        gx = std::min<int64_t>(std::max<int64_t>(cdiv(cdiv(cols, CH), 256), 1), kMaxPartials);
+        gy = std::min<int64_t>(std::max<int64_t>(rows / 16, 1), kMaxPartials / gx);
+        hipLaunchKernelGGL(k_amax_hadamard_cols<T>, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, s, x,
+                           rows, cols, ld, sign_mask, ws);
     } else {
-        constexpr int CH = 16 / sizeof(T);
-        g = amax_grid(cdiv(cols, CH), rows);
-        hipLaunchKernelGGL(k_amax_plain<T>, g, dim3(256), 0, s, x, rows, cols, ld, partial);
+        // a contiguous tensor streams as one long row
+        const bool flat = (ld == cols) || rows == 1;
+        const int64_t r = flat ? 1 : rows, c = flat ? rows * cols : cols;
+        gx = std::min<int64_t>(std::max<int64_t>(cdiv(cdiv(c, CH), 1024), 1), kMaxPartials);
+        gy = std::min<int64_t>(r, kMaxPartials / gx);
+        hipLaunchKernelGGL(k_amax_plain<T>, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, s, x, r, c,
+                           flat ? c : ld, ws);
     }
-    hipLaunchKernelGGL(k_amax_final, dim3(1), dim3(256), 0, s, partial, (int)(g.x * g.y), out);
-    return hipGetLastError();
-}
-
-template <typename T, bool SR>
-void launch_row(const T* x, int64_t rows, int64_t cols, int64_t ld, const float* amax, uint64_t seed,
-                bool rht, uint32_t mask, const QOut& o, hipStream_t s) {
-    dim3 g((unsigned)cdiv(rows, 16), (unsigned)cdiv(cols / 16, 64));
-    if (rht)
-        hipLaunchKernelGGL((k_quant_row<T, SR, true>), g, dim3(256), 0, s, x, rows, cols, ld, amax,
-                           seed, mask, o.codes, o.scales, o.ts);
-    else
-        hipLaunchKernelGGL((k_quant_row<T, SR, false>), g, dim3(256), 0, s, x, rows, cols, ld, amax,
-                           seed, mask, o.codes, o.scales, o.ts);
-}
-
-template <typename T, bool SR>
-void launch_col(const T* x, int64_t rows, int64_t cols, int64_t ld, const float* amax, uint64_t seed,
-                bool rht, uint32_t mask, const QOut& o, hipStream_t s) {
-    dim3 g((unsigned)cdiv(rows, kTile), (unsigned)cdiv(cols, kTile));
-    if (rht)
-        hipLaunchKernelGGL((k_quant_col<T, SR, true>), g, dim3(256), 0, s, x, rows, cols, ld, amax,
-                           seed, mask, o.codes, o.scales, o.ts);
-    else
-        hipLaunchKernelGGL((k_quant_col<T, SR, false>), g, dim3(256), 0, s, x, rows, cols, ld, amax,
-                           seed, mask, o.codes, o.scales, o.ts);
-}
-
-template <typename T, bool SR>
-void launch_rowcol(const T* x, int64_t rows, int64_t cols, int64_t ld, const float* amax,
-                   uint64_t seed, const QOut& r, const QOut& c, hipStream_t s) {
-    dim3 g((unsigned)cdiv(rows, kTile), (unsigned)cdiv(cols, kTile));
-    hipLaunchKernelGGL((k_quant_rowcol<T, SR>), g, dim3(256), 0, s, x, rows, cols, ld, amax, seed,
-                       r.codes, r.scales, r.ts, c.codes, c.scales, c.ts);
-}
-
-template <typename T, bool SR>
-void launch_2d(const T* x, int64_t rows, int64_t cols, int64_t ld, const float* amax, uint64_t seed,
-               const QOut& o, hipStream_t s) {
-    dim3 g((unsigned)cdiv(rows / 16, 4), (unsigned)cdiv(cols, 512));
-    hipLaunchKernelGGL((k_quant_2d<T, SR>), g, dim3(256), 0, s, x, rows, cols, ld, amax, seed,
-                       o.codes, o.scales, o.ts);
+    return (int)(gx * gy);
 }
 
 template <typename T>
 hipError_t quantize_typed(const T* x, int64_t rows, int64_t cols, int64_t ld, int layout, bool sr,
                           uint64_t seed, bool rht, uint64_t hseed, const float* amax_in,
-                          const QOut* out, float* ws, hipStream_t s) {
+                          float* amax_out, const QOut* out, float* ws, hipStream_t s) {
     const uint32_t mask = rht ? hadamard_sign_mask(hseed) : 0u;
     if (rows == 0 || cols == 0) {
         hipLaunchKernelGGL(k_write_tensor_scale, dim3(1), dim3(1), 0, s, amax_in, out[0].ts,
-                           layout == kLayoutRowCol ? out[1].ts : nullptr);
+                           layout == kLayoutRowCol ? out[1].ts : nullptr, amax_out);
         return hipGetLastError();
     }
     const float* amax = amax_in;
+    int np = 0;
     if (!amax) {
-        int hdim = 0;
-        if (rht) hdim = (layout == kLayoutCol) ? 2 : 1;
-        hipError_t e = amax_typed(x, rows, cols, ld, hdim, mask, ws, s);
-        if (e != hipSuccess) return e;
+        const int hdim = rht ? ((layout == kLayoutCol) ? 2 : 1) : 0;
+        np = amax_partials(x, rows, cols, ld, hdim, mask, ws, s);
         amax = ws;
     }
+    const QOut& o = out[0];
+    constexpr int TW = Patch<T>::TW;
     switch (layout) {
-        case kLayoutRow:
-            sr ? launch_row<T, true>(x, rows, cols, ld, amax, seed, rht, mask, out[0], s)
-               : launch_row<T, false>(x, rows, cols, ld, amax, seed, rht, mask, out[0], s);
+        case kLayoutRow: {
+            dim3 g((unsigned)cdiv(cols, 512), grid_y(cdiv(rows, 8)));
+#define NVFP4_ROW(SRV, RHTV)                                                                         \
+    hipLaunchKernelGGL((k_quant_row<T, SRV, RHTV>), g, dim3(256), 0, s, x, rows, cols, ld, amax, np, \
+                       seed, mask, o.codes, o.scales, o.ts, amax_out)
+            if (sr) {
+                if (rht) NVFP4_ROW(true, true); else NVFP4_ROW(true, false);
+            } else {
+                if (rht) NVFP4_ROW(false, true); else NVFP4_ROW(false, false);
+            }
+#undef NVFP4_ROW
             break;
+        }
         case kLayoutCol:
-            sr ? launch_col<T, true>(x, rows, cols, ld, amax, seed, rht, mask, out[0], s)
-               : launch_col<T, false>(x, rows, cols, ld, amax, seed, rht, mask, out[0], s);
+        case kLayoutRowCol: {
+            dim3 g((unsigned)cdiv(cols, TW), (unsigned)cdiv(rows, 256));
+            const QOut& r = out[0];
+            const QOut& c = layout == kLayoutCol ? out[0] : out[1];
+#define NVFP4_TILE(ROWV, SRV, RHTV)                                                                  \
+    hipLaunchKernelGGL((k_quant_tile<T, ROWV, true, SRV, RHTV>), g, dim3(256), 0, s, x, rows, cols, \
+                       ld, amax, np, seed, mask, r.codes, r.scales, r.ts, c.codes, c.scales, c.ts,  \
+                       amax_out)
+            if (layout == kLayoutCol) {
+                if (sr) {
+                    if (rht) NVFP4_TILE(false, true, true); else NVFP4_TILE(false, true, false);
+                } else {
+                    if (rht) NVFP4_TILE(false, false, true); else NVFP4_TILE(false, false, false);
+                }
+            } else {
+                if (sr) NVFP4_TILE(true, true, false); else NVFP4_TILE(true, false, false);
+            }
+#undef NVFP4_TILE
             break;
-        case kLayoutRowCol:
-            sr ? launch_rowcol<T, true>(x, rows, cols, ld, amax, seed, out[0], out[1], s)
-               : launch_rowcol<T, false>(x, rows, cols, ld, amax, seed, out[0], out[1], s);
+        }
+        case kLayout2D: {
+            dim3 g((unsigned)cdiv(cols, 512), (unsigned)cdiv(rows / 16, 4));
+            if (sr)
+                hipLaunchKernelGGL((k_quant_2d<T, true>), g, dim3(256), 0, s, x, rows, cols, ld, amax,
+                                   np, seed, o.codes, o.scales, o.ts, amax_out);
+            else
+                hipLaunchKernelGGL((k_quant_2d<T, false>), g, dim3(256), 0, s, x, rows, cols, ld, amax,
+                                   np, seed, o.codes, o.scales, o.ts, amax_out);
             break;
-        case kLayout2D:
-            sr ? launch_2d<T, true>(x, rows, cols, ld, amax, seed, out[0], s)
-               : launch_2d<T, false>(x, rows, cols, ld, amax, seed, out[0], s);
-            break;
+        }
         default:
             return hipErrorInvalidValue;
     }
@@ -540,19 +667,20 @@ hipError_t quantize_typed(const T* x, int64_t rows, int64_t cols, int64_t ld, in
 
 hipError_t launch_quantize(const void* x, bool bf16, int64_t rows, int64_t cols, int64_t ld,
                            int layout, bool sr, uint64_t seed, bool rht, uint64_t hseed,
-                           const float* amax_in, const QOut* out, float* ws, hipStream_t s) {
+                           const float* amax_in, float* amax_out, const QOut* out, float* ws,
+                           hipStream_t s) {
     if (bf16)
         return quantize_typed(static_cast<const uint16_t*>(x), rows, cols, ld, layout, sr, seed, rht,
-                              hseed, amax_in, out, ws, s);
+                              hseed, amax_in, amax_out, out, ws, s);
     return quantize_typed(static_cast<const float*>(x), rows, cols, ld, layout, sr, seed, rht, hseed,
-                          amax_in, out, ws, s);
+                          amax_in, amax_out, out, ws, s);
 }
 
 hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, const float* ts,
                              int64_t rows, int64_t cols, bool scale_2d, void* y, bool bf16,
                              int64_t ld, hipStream_t s) {
     if (rows == 0 || cols == 0) return hipSuccess;
-    dim3 g((unsigned)cdiv(rows, 16), (unsigned)cdiv(cols / 16, 64));
+    dim3 g((unsigned)cdiv(cols / 16, 64), grid_y(cdiv(rows, 16)));
     if (bf16)
         hipLaunchKernelGGL(k_dequant<uint16_t>, g, dim3(256), 0, s, codes, scales, ts, rows, cols,
                            (int)scale_2d, static_cast<uint16_t*>(y), ld);

@@ -35,7 +35,7 @@ class CTensor(ctypes.Structure):
 class CQuantOpts(ctypes.Structure):
     _fields_ = [("layout", ctypes.c_int32), ("round", ctypes.c_int32), ("sr_seed", ctypes.c_uint64),
                 ("hadamard", ctypes.c_int32), ("hadamard_seed", ctypes.c_uint64),
-                ("amax_in", ctypes.c_void_p)]
+                ("amax_in", ctypes.c_void_p), ("amax_out", ctypes.c_void_p)]
 
 
 def _load():
@@ -123,16 +123,18 @@ class NVFP4Tensor:
 
 
 def nvfp4_quantize_workspace_size(rows, cols, amax_in=None):
-    o = CQuantOpts(0, 0, 0, 0, 0, None if amax_in is None else amax_in.data_ptr())
+    o = CQuantOpts(0, 0, 0, 0, 0, None if amax_in is None else amax_in.data_ptr(), None)
     return int(lib.nvfp4_quantize_workspace_size(rows, cols, ctypes.byref(o)))
 
 
 def nvfp4_quantize(x, layout=NVFP4_ROW_1D, round=NVFP4_RNE, sr_seed=0, hadamard=False,
-                   hadamard_seed=0, amax_in=None, out=None, workspace=None, stream=None):
+                   hadamard_seed=0, amax_in=None, out=None, workspace=None, amax_out=None,
+                   stream=None):
     """Quantize a 2-D device tensor (float32 or bfloat16, unit column stride).
 
     Returns an NVFP4Tensor, or (row, col) for NVFP4_ROW_COL_1D.  `out` may
-    pass preallocated outputs (one NVFP4Tensor, or a pair for ROW_COL)."""
+    pass preallocated outputs (one NVFP4Tensor, or a pair for ROW_COL);
+    `amax_out` (float32 device tensor) receives the tensor amax used."""
     assert x.dim() == 2 and x.stride(1) == 1
     rows, cols = x.shape
     ld = x.stride(0) if rows > 1 else max(cols, x.stride(0))
@@ -153,7 +155,8 @@ def nvfp4_quantize(x, layout=NVFP4_ROW_1D, round=NVFP4_RNE, sr_seed=0, hadamard=
     for i, t in enumerate(outs):
         arr[i] = t.c()
     opts = CQuantOpts(layout, round, sr_seed, int(bool(hadamard)), hadamard_seed,
-                      None if amax_in is None else amax_in.data_ptr())
+                      None if amax_in is None else amax_in.data_ptr(),
+                      None if amax_out is None else amax_out.data_ptr())
     need = int(lib.nvfp4_quantize_workspace_size(rows, cols, ctypes.byref(opts)))
     if workspace is None and need:
         workspace = torch.empty((need + 15) // 16 * 4, dtype=torch.float32, device=dev)

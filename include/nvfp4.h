@@ -119,6 +119,9 @@ typedef struct {
     const float* amax_in;    /* nullable DEVICE pointer: use *amax_in as A_t instead of
                                 computing it (the caller vouches that it is the largest
                                 magnitude of the tensor being quantized) */
+    float* amax_out;         /* nullable DEVICE pointer: receives the A_t used (computed or
+                                given), so later calls on the same tensor can pass it as
+                                amax_in and skip the amax pass */
 } nvfp4_quant_opts;
 
 /* Bytes of workspace nvfp4_quantize needs for this request (0 when amax_in is

@@ -44,7 +44,7 @@ def test_status_strings_and_version(nv):
 
 def test_workspace_size(nv):
     assert nv.nvfp4_quantize_workspace_size(8192, 8192) > 0
-    o = nv.CQuantOpts(0, 0, 0, 0, 0, 1234)
+    o = nv.CQuantOpts(0, 0, 0, 0, 0, 1234, None)
     assert nv.lib.nvfp4_quantize_workspace_size(8192, 8192, ctypes.byref(o)) == 0
 
 
@@ -55,7 +55,7 @@ def _t(rows, cols, mode=0, codes=4096, scales=8192, ts=16384):
 
 def _quant(nv, x=65536, dt=1, rows=32, cols=32, ld=32, layout=0, rnd=0, had=0, outs=None,
            ws=1 << 20, ws_bytes=1 << 20, amax=None):
-    o = nv.CQuantOpts(layout, rnd, 1, had, 2, amax)
+    o = nv.CQuantOpts(layout, rnd, 1, had, 2, amax, None)
     arr = (nv.CTensor * 2)()
     if outs is None:
         outs = [_t(rows, cols)]

@@ -136,6 +136,28 @@ def test_dequantize(nv, layout, out_dt):
                           ref.view(np.uint32 if out_dt == O.F32 else np.uint16))
 
 
+@pytest.mark.parametrize("had", [False, True])
+def test_amax_out_chaining(nv, had):
+    """amax_out publishes the A_t a call used; passing it as amax_in to the
+    next call on the same tensor gives the same result as computing it."""
+    x = make_input(256, 320, O.BF16, seed=41, kind="spiky")
+    xd = to_device(x)
+    lay = nv.NVFP4_COL_1D if had else nv.NVFP4_ROW_1D
+    a = torch.zeros(1, dtype=torch.float32, device="cuda")
+    q1 = nv.nvfp4_quantize(xd, layout=lay, round=nv.NVFP4_SR, sr_seed=3, hadamard=had,
+                           hadamard_seed=9, amax_out=a)
+    torch.cuda.synchronize()
+    assert a.item() == O.amax(x, O.BF16, lay, hadamard=had, hadamard_seed=9)
+    q2 = nv.nvfp4_quantize(xd, layout=lay, round=nv.NVFP4_SR, sr_seed=3, hadamard=had,
+                           hadamard_seed=9, amax_in=a)
+    assert_q_equal(q_to_host(q2), q_to_host(q1), "chained")
+    if not had:
+        r, c = nv.nvfp4_quantize(xd, layout=nv.NVFP4_ROW_COL_1D, amax_in=a)
+        ref_r, ref_c = O.quantize(x, O.BF16, O.ROW_COL_1D)
+        assert_q_equal(q_to_host(r), ref_r, "chained rowcol row")
+        assert_q_equal(q_to_host(c), ref_c, "chained rowcol col")
+
+
 def test_gpu_idempotence(nv):
     x = make_input(128, 256, O.F32, seed=31)
     xd = to_device(x)
