@@ -90,46 +90,41 @@ __device__ __forceinline__ void philox4x32_10_pair(uint32_t a[4], uint32_t b[4],
     }
 }
 
-// Sixteen 16-bit draws for output elements base .. base+15 (base % 16 == 0):
-// Philox with counters base/8 and base/8 + 1.  d[j] is the draw of element
-// base + j (16 bits of word (j % 8) / 2, low half for even j).
-__device__ __forceinline__ void draws16(uint64_t seed, uint32_t stream, uint64_t base,
-                                        uint32_t d[16]) {
-    const uint64_t q = base >> 3, q1 = q + 1;
-    uint32_t a[4] = {(uint32_t)q, (uint32_t)(q >> 32), stream, 0u};
-    uint32_t b[4] = {(uint32_t)q1, (uint32_t)(q1 >> 32), stream, 0u};
-    philox4x32_10_pair(a, b, (uint32_t)seed, (uint32_t)(seed >> 32));
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        d[2 * j] = a[j] & 0xFFFFu;
-        d[2 * j + 1] = a[j] >> 16;
-        d[8 + 2 * j] = b[j] & 0xFFFFu;
-        d[8 + 2 * j + 1] = b[j] >> 16;
-    }
-}
-
-// Eight draws for each of two element groups (bases a_base and b_base, both
-// multiples of 8): one paired Philox run.
-__device__ __forceinline__ void draws8x2(uint64_t seed, uint32_t stream, uint64_t a_base,
-                                         uint64_t b_base, uint32_t da[8], uint32_t db[8]) {
+// Philox words of the 8-element groups that start at output indices a_base and
+// b_base (multiples of 8): counters a_base/8 and b_base/8, one paired run.
+// Word j of a group holds the 16-bit draws of elements 2j (low half) and
+// 2j + 1 (high half).
+__device__ __forceinline__ void philox_words2(uint64_t seed, uint32_t stream, uint64_t a_base,
+                                              uint64_t b_base, uint32_t wa[4], uint32_t wb[4]) {
     const uint64_t qa = a_base >> 3, qb = b_base >> 3;
-    uint32_t a[4] = {(uint32_t)qa, (uint32_t)(qa >> 32), stream, 0u};
-    uint32_t b[4] = {(uint32_t)qb, (uint32_t)(qb >> 32), stream, 0u};
-    philox4x32_10_pair(a, b, (uint32_t)seed, (uint32_t)(seed >> 32));
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        da[2 * j] = a[j] & 0xFFFFu;
-        da[2 * j + 1] = a[j] >> 16;
-        db[2 * j] = b[j] & 0xFFFFu;
-        db[2 * j + 1] = b[j] >> 16;
-    }
+    wa[0] = (uint32_t)qa;
+    wa[1] = (uint32_t)(qa >> 32);
+    wa[2] = stream;
+    wa[3] = 0u;
+    wb[0] = (uint32_t)qb;
+    wb[1] = (uint32_t)(qb >> 32);
+    wb[2] = stream;
+    wb[3] = 0u;
+    philox4x32_10_pair(wa, wb, (uint32_t)seed, (uint32_t)(seed >> 32));
 }
 
-// Eight draws for elements base .. base+7 (base % 8 == 0).
-__device__ __forceinline__ void draws8(uint64_t seed, uint32_t stream, uint64_t base,
-                                       uint32_t d[8]) {
-    uint32_t unused[8];
-    draws8x2(seed, stream, base, base + 8, d, unused);
+// Words of the 16 elements base .. base+15 (base % 16 == 0): w[0..3] for the
+// first 8, w[4..7] for the second 8.
+__device__ __forceinline__ void philox_words16(uint64_t seed, uint32_t stream, uint64_t base,
+                                               uint32_t w[8]) {
+    philox_words2(seed, stream, base, base + 8, w, w + 4);
+}
+
+// Words of the 8 elements base .. base+7 (base % 8 == 0).
+__device__ __forceinline__ void philox_words8(uint64_t seed, uint32_t stream, uint64_t base,
+                                              uint32_t w[4]) {
+    uint32_t unused[4];
+    philox_words2(seed, stream, base, base + 8, w, unused);
+}
+
+// 16-bit draw of element j of a group (word j / 2, low half for even j).
+__device__ __forceinline__ uint32_t draw16(const uint32_t* w, int j) {
+    return (j & 1) ? (w[j >> 1] >> 16) : (w[j >> 1] & 0xFFFFu);
 }
 
 // ---------------------------------------------------------------- formats
@@ -199,50 +194,93 @@ __device__ __forceinline__ BlockScale block_scale(float amax_b, float six_st, fl
     return bs;
 }
 
+// Seed operand of the gfx950 stochastic-rounding FP4 convert for a 16-bit
+// draw r16.  That instruction adds the top 22 bits of its seed to the 22
+// binary32 significand bits below the kept E2M1 bit and truncates.  With seed
+// = ~(r16 << 16) those 22 bits are (65535 - r16) * 64 + 63, so the carry
+// happens exactly when F > 64 r16, F the 22 fraction bits: round up iff
+// r16 < f * 2^16 whenever the whole fraction f fits in those 22 bits.  For
+// inputs below 1 the instruction first shifts the significand right and drops
+// the bits shifted out; feeding it the value rounded up to a multiple of
+// 2^-23 makes the dropped bits zero, and since r16 * 64 is an integer,
+// "64 r16 < ceil(f 2^22)" is the same decision as "64 r16 < f 2^22".  (This
+// pairing of seed and pre-rounding was checked against the integer rule of
+// e2m1_sr over 3.6e8 value/draw pairs spanning every E2M1 interval, binary32
+// subnormals and both signs, for the instruction's first slot; its second
+// slot does not follow this rule, so every call here converts one value, in
+// the first slot.)
+__device__ __forceinline__ uint32_t sr_seed(uint32_t word, int high_half) {
+    const uint32_t nw = ~word;
+    return high_half ? (nw | 0xFFFFu) : ((nw << 16) | 0xFFFFu);
+}
+
 // 4-bit codes of N values (N = 8 or 16; sign copied) packed into N/8 32-bit
-// words, the even element in the low nibble.  d holds the 16-bit draws when
-// SR is used.
+// words, the even element in the low nibble.  w holds the Philox words of the
+// N elements (draws of elements 2j, 2j+1 in word j) when SR is used; amax_b
+// is the block's largest magnitude.
 //   RNE: the values are scaled first (y = t * R keeps the sign; its magnitude
 //   is fl(|t| * R)), then the gfx950 FP4 pack instruction with scale operand
 //   1.0 rounds two of them to nearest-even E2M1 with saturation at 6 and writes
 //   their codes into one byte of the word.
-//   SR: e2m1_sr on the magnitude, sign bit copied, nibbles packed in VALU.
+//   SR: y = fl(|t| * R), z = ceil(y * 2^23) carries t's sign, and the SR
+//   convert with scale operand 2^23 (so it sees z * 2^-23, y rounded up to the
+//   2^-23 grid) and seed sr_seed(draw) produces the code.  Each call converts
+//   one value in the instruction's first slot into byte 0 of a fresh register
+//   (the second slot converts +0, so the byte's high nibble is 0; the
+//   compiler does not carry the builtin's `old` operand through, so nothing
+//   else of that register is used); byte permutes then gather the codes of
+//   even and odd elements into the low and high nibbles of the output word.
+//   Blocks with R = inf (S below 2^-128), or whose scaled values could
+//   overflow (amax_b * R >= 2^100, possible only with a caller-supplied A_t
+//   below the true one), take the plain VALU path of e2m1_rne / e2m1_sr.
 template <bool SR, int N>
-__device__ __forceinline__ void encode(const float* v, BlockScale bs, const uint32_t* d,
+__device__ __forceinline__ void encode(const float* v, BlockScale bs, float amax_b, const uint32_t* w,
                                        uint32_t* out) {
-    if (__builtin_expect(__builtin_isinf(bs.R), 0)) {
-        // Reciprocal overflow (S below 2^-128): every nonzero element maps past
-        // 6 and saturates; zeros stay zero.
+    typedef float f2_t __attribute__((ext_vector_type(2)));
+    const bool slow = SR ? !(amax_b * bs.R < 0x1p100f) : __builtin_isinf(bs.R);
+    if (__builtin_expect(slow, 0)) {
 #pragma unroll
         for (int k = 0; k < N / 8; ++k) out[k] = 0u;
 #pragma unroll
         for (int j = 0; j < N; ++j) {
-            uint32_t c = (__float_as_uint(v[j]) >> 28) & 8u;
-            c |= (v[j] != 0.0f) ? 7u : 0u;
-            out[j >> 3] |= c << (4 * (j & 7));
+            const uint32_t bits = __float_as_uint(v[j]);
+            const float a = __uint_as_float(bits & 0x7FFFFFFFu);
+            const float y = a == 0.0f ? 0.0f : a * bs.R;  // (0 * inf would be NaN)
+            const uint32_t mag = SR ? e2m1_sr(y, draw16(w, j)) : e2m1_rne(y);
+            out[j >> 3] |= (((bits >> 28) & 8u) | mag) << (4 * (j & 7));
         }
         return;
     }
 #pragma unroll
     for (int k = 0; k < N / 8; ++k) {
-        uint32_t w = 0u;
+        const float* p = v + 8 * k;
         if (!SR) {
-            const float* p = v + 8 * k;
-            w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, p[0] * bs.R, p[1] * bs.R, 1.0f, 0);
-            w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, p[2] * bs.R, p[3] * bs.R, 1.0f, 1);
-            w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, p[4] * bs.R, p[5] * bs.R, 1.0f, 2);
-            w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, p[6] * bs.R, p[7] * bs.R, 1.0f, 3);
+            uint32_t c = 0u;
+            c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, p[0] * bs.R, p[1] * bs.R, 1.0f, 0);
+            c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, p[2] * bs.R, p[3] * bs.R, 1.0f, 1);
+            c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, p[4] * bs.R, p[5] * bs.R, 1.0f, 2);
+            c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, p[6] * bs.R, p[7] * bs.R, 1.0f, 3);
+            out[k] = c;
         } else {
+            uint32_t ce[4], co[4];
+            const uint32_t* wk = w + 4 * k;
 #pragma unroll
-            for (int jj = 0; jj < 8; ++jj) {
-                const int j = 8 * k + jj;
-                uint32_t bits = __float_as_uint(v[j]);
-                float y = __uint_as_float(bits & 0x7FFFFFFFu) * bs.R;
-                uint32_t mag = e2m1_sr(y, d[j]);
-                w |= (((bits >> 28) & 8u) | mag) << (4 * jj);
+            for (int J = 0; J < 4; ++J) {
+                const float z0 = __builtin_ceilf((fabsf(p[2 * J]) * bs.R) * 0x1p23f);
+                const float z1 = __builtin_ceilf((fabsf(p[2 * J + 1]) * bs.R) * 0x1p23f);
+                const f2_t e = {__uint_as_float(__float_as_uint(z0) | (__float_as_uint(p[2 * J]) & 0x80000000u)), 0.0f};
+                const f2_t o = {__uint_as_float(__float_as_uint(z1) | (__float_as_uint(p[2 * J + 1]) & 0x80000000u)), 0.0f};
+                ce[J] = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, e, sr_seed(wk[J], 0), 0x1p23f, 0);
+                co[J] = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, o, sr_seed(wk[J], 1), 0x1p23f, 0);
             }
+            // perm(b, a, lo2): byte 0 of a -> byte 0, byte 0 of b -> byte 1, bytes 2 and 3 zero
+            const uint32_t lo2 = 0x0C0C0400u;
+            const uint32_t ev = (__builtin_amdgcn_perm(ce[1], ce[0], lo2) |
+                                 (__builtin_amdgcn_perm(ce[3], ce[2], lo2) << 16)) & 0x0F0F0F0Fu;
+            const uint32_t od = (__builtin_amdgcn_perm(co[1], co[0], lo2) |
+                                 (__builtin_amdgcn_perm(co[3], co[2], lo2) << 16)) & 0x0F0F0F0Fu;
+            out[k] = ev | (od << 4);
         }
-        out[k] = w;
     }
 }
 

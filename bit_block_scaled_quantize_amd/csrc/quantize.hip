@@ -10,25 +10,31 @@
 // page, "Эксперименты и сравнение с FP8").
 //
 // All of these are HBM-bound streaming kernels whose second limit is VALU
-// issue.  Shared structure:
+// issue (Philox dominates under stochastic rounding).  Shared structure:
 //   - 256-thread workgroups (four wave64s); grid dimension x runs over column
 //     groups, so workgroups dispatched together sweep contiguous stretches of
 //     each row (this alone is worth ~25% of HBM throughput against a
-//     row-group-first order); dimension y runs over row groups with a
-//     grid-stride loop;
+//     row-group-first order); dimension y runs over row groups (the row and
+//     dequantize kernels loop over row groups beyond 65535);
 //   - 16-byte loads whose lanes cover contiguous spans, and every 128-byte
 //     output line written by one workgroup (or by workgroups dispatched
 //     together);
 //   - the tensor amax is a separate streaming pass writing at most
 //     kMaxPartials per-workgroup maxima, which every consumer workgroup
 //     reduces in its prologue, unless the caller supplies the amax;
-//   - column blocks come from a register tile: a thread holds 16 rows of a
-//     patch, so a column block is 16 values the thread already has (no LDS);
+//   - column blocks go through an LDS transpose: a 256-row x 128-byte tile is
+//     loaded with full-row 16-byte loads, written to LDS with a per-row-band
+//     XOR swizzle, and read back as 16-row x 8-byte column strips, so every
+//     thread ends up with whole column blocks and each 128-byte line of the
+//     transposed output comes from 16 lanes of one wave;
 //   - a 16-element row block lives in a lane pair (quad for fp32 input); the
 //     lanes join their maxima with lane exchanges and split the block-scale
 //     arithmetic between rows;
 //   - nearest-even encoding uses the gfx950 FP4 pack instruction on the
-//     already-scaled values (scale operand 1.0), two codes per instruction.
+//     already-scaled values (scale operand 1.0), two codes per instruction;
+//     stochastic rounding uses the gfx950 SR convert, one code per
+//     instruction, with the value pre-rounded so that the instruction's
+//     decision is exactly "draw < fraction" (see encode()).
 #include "launch.hpp"
 #include "nvfp4_device.hpp"
 
@@ -71,14 +77,16 @@ __device__ __forceinline__ void load_chunk(const T* __restrict__ row, int64_t j,
 }
 
 // Partial maxima of |x| (no transform).  Rows by, by + gy, ...; in each row
-// the 16-byte chunks bx*256 + tid + 256*(gx*k + u), four per thread per
-// iteration.  A contiguous tensor is passed as one long row.
+// the 16-byte chunks bx*256*U + tid + 256*u + k*(gx*256*U), U = 8 per thread
+// per iteration (128 bytes in flight per thread keeps enough requests
+// outstanding with only kMaxPartials workgroups).  A contiguous tensor is
+// passed as one long row.
 template <typename T>
 __global__ void __launch_bounds__(256) k_amax_plain(const T* __restrict__ x, int64_t rows,
                                                     int64_t cols, int64_t ld,
                                                     float* __restrict__ partial) {
     constexpr int CH = 16 / sizeof(T);
-    constexpr int U = 4;
+    constexpr int U = 8;
     const int64_t nch = (cols + CH - 1) / CH;
     const int64_t step = (int64_t)gridDim.x * 256 * U;
     float a = 0.0f;
@@ -235,8 +243,9 @@ __device__ __forceinline__ void hadamard8_pair(float v[8], uint32_t sign_mask, b
 // Lane-pair block scales for two rows (r, r+1) whose 16-element blocks are
 // split 8 + 8 between lanes 2k (even) and 2k+1 (odd): both lanes join both
 // rows' maxima, the even lane derives row r's multiplier and the odd lane row
-// r+1's, and one exchange hands each lane both.
-__device__ __forceinline__ void pair_block_scales(float a0, float a1, bool odd, const TensorScale& ts,
+// r+1's, and one exchange hands each lane both.  a0, a1 return the joined
+// block maxima.
+__device__ __forceinline__ void pair_block_scales(float& a0, float& a1, bool odd, const TensorScale& ts,
                                                   BlockScale& b0, BlockScale& b1) {
     a0 = fmaxf(a0, __shfl_xor(a0, 1, 64));
     a1 = fmaxf(a1, __shfl_xor(a1, 1, 64));
@@ -291,36 +300,41 @@ __global__ void __launch_bounds__(256) k_quant_row(const T* __restrict__ x, int6
         BlockScale bs[2];
         pair_block_scales(a[0], a[1], odd, ts, bs[0], bs[1]);
         if (!col_ok) continue;
-        uint32_t d[2][8];
-        if (SR) draws8x2(seed, kStreamRow, (uint64_t)(r * cols + c), (uint64_t)((r + 1) * cols + c), d[0], d[1]);
+        uint32_t wd[2][4];
+        if (SR) philox_words2(seed, kStreamRow, (uint64_t)(r * cols + c), (uint64_t)((r + 1) * cols + c), wd[0], wd[1]);
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
             if (r + k >= rows) break;
             uint32_t w[1];
-            encode<SR, 8>(v[k], bs[k], d[k], w);
+            encode<SR, 8>(v[k], bs[k], a[k], wd[k], w);
             *reinterpret_cast<uint32_t*>(codes + (r + k) * (cols / 2) + c / 2) = w[0];
             if (odd == (k == 1)) scales[(r + k) * (cols / 16) + c / 16] = (uint8_t)bs[k].byte;
         }
     }
 }
 
-// ============================================================ register tile
+// ============================================================ LDS transpose tile
 // COL_1D and ROW_COL_1D.  Workgroup (x, y) owns the tile of 256 rows from
-// 256 * y and 32*CH columns from 32*CH * x (CH = 8 bf16 or 4 fp32 elements per
-// 16-byte chunk).  Thread (pc, pr) =
-// (lane % 16, lane / 16 + 4 * wave) holds rows 16 pr .. 16 pr + 15 of two
-// chunks: columns CH * pc .. and CH * (pc + 16) .. of the tile, so every
-// wave-wide load reads 4 rows x 256 contiguous bytes.
-//   column blocks: the 16 values of one column in the thread -> 8 code bytes
-//     of output row c; the tile's 16 row bands complete each 128-byte line;
-//   row blocks (ROW_COL): a 16-element row block spans LPB = 16 / CH lanes
-//     (a pair for bf16, a quad for fp32); the lanes join their maxima, split
-//     the block-scale arithmetic over LPB rows, and exchange the results.
+// 256 * y and 128 bytes of each row (TWC = 64 bf16 or 32 fp32 columns) from
+// column TWC * x.
+//   load: thread t reads 16-byte chunk t % 8 of tile rows t / 8 + 32 k
+//     (k = 0..7): each wave-wide load covers 8 rows x 128 bytes.  The chunk's
+//     two 8-byte units land in LDS at unit (2 ch + h) ^ (band % 16) of the row
+//     (band = row / 16; rows padded to 136 bytes), so the column reads below
+//     spread over the banks;
+//   row blocks (ROW_COL): straight from the loaded chunks, a 16-element block
+//     spanning LPB = 2 (bf16) or 4 (fp32) lanes, as in the row kernel;
+//   column blocks: thread t takes row band t % 16 and 8-byte unit t / 16: 16
+//     LDS reads give it 16 rows x UE columns (UE = 4 bf16 or 2 fp32), i.e. UE
+//     complete column blocks.  The 16 lanes that share a unit write the 16
+//     consecutive 8-byte code groups (one 128-byte line) of each column.
 template <typename T>
-struct Patch {
-    static constexpr int CH = 16 / sizeof(T);  // elements per 16-byte chunk
-    static constexpr int LPB = 16 / CH;        // lanes per 16-element row block
-    static constexpr int TW = 32 * CH;         // tile width (columns)
+struct ColTile {
+    static constexpr int CH = 16 / sizeof(T);    // elements per 16-byte chunk
+    static constexpr int TWC = 128 / sizeof(T);  // tile width in columns
+    static constexpr int UE = 8 / sizeof(T);     // elements per 8-byte unit
+    static constexpr int LPB = 16 / CH;          // lanes per 16-element row block
+    static constexpr int STRIDE = 136;           // LDS bytes per tile row
 };
 
 // Element e of a raw 16-byte chunk (bf16 pairs or fp32).
@@ -334,8 +348,92 @@ __device__ __forceinline__ float chunk_elem(const uint4& q, int e) {
     }
 }
 
-template <typename T, bool DO_ROW, bool DO_COL, bool SR, bool RHT>
-__global__ void __launch_bounds__(256) k_quant_tile(const T* __restrict__ x, int64_t rows,
+// Element e of a raw 8-byte unit.
+template <typename T>
+__device__ __forceinline__ float unit_elem(const uint2& q, int e) {
+    if constexpr (sizeof(T) == 2) {
+        const uint32_t w = (e >> 1) == 0 ? q.x : q.y;
+        return (e & 1) ? __uint_as_float(w & 0xFFFF0000u) : __uint_as_float(w << 16);
+    } else {
+        return __uint_as_float(e == 0 ? q.x : q.y);
+    }
+}
+
+// Row blocks of the 8 loaded chunks (ROW_COL): rows R0 + t/8 + 32 k, columns
+// gc .. gc + CH - 1.  cols % 16 == 0 and rows % 16 == 0, so the LPB lanes of a
+// block agree on validity.
+template <typename T, bool SR>
+__device__ __forceinline__ void tile_row_blocks(const uint4 (&raw)[8], int64_t R0, int lr0, int64_t gc,
+                                                int64_t rows, int64_t cols, const TensorScale& ts,
+                                                uint64_t seed, uint8_t* __restrict__ rcodes,
+                                                uint8_t* __restrict__ rscales) {
+    constexpr int CH = ColTile<T>::CH, LPB = ColTile<T>::LPB;
+    const int lane = threadIdx.x & 63;
+    const int q = lane % LPB;
+    const bool col_ok = gc < cols;
+    float a[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        float m = 0.0f;
+#pragma unroll
+        for (int e = 0; e < CH; ++e) m = fmaxf(m, fabsf(chunk_elem<T>(raw[k], e)));
+#pragma unroll
+        for (int o = 1; o < LPB; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+        a[k] = m;
+    }
+    // lane q of a block derives the multipliers of rows k = q, q + LPB, ...;
+    // the lanes then exchange them
+    BlockScale bs[8];
+#pragma unroll
+    for (int i0 = 0; i0 < 8; i0 += LPB) {
+        float mine_a = a[i0];
+#pragma unroll
+        for (int k = 1; k < LPB; ++k) mine_a = (q == k) ? a[i0 + k] : mine_a;
+        const BlockScale mine = block_scale(mine_a, ts.six_st, ts.st);
+        const int base = lane - q;
+#pragma unroll
+        for (int k = 0; k < LPB; ++k) {
+            bs[i0 + k].R = __shfl(mine.R, base + k, 64);
+            bs[i0 + k].byte = (uint32_t)__shfl((int)mine.byte, base + k, 64);
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < 8; k += 2) {
+        const int64_t r = R0 + lr0 + 32 * k;  // rows r and r + 32
+        if (!col_ok || r >= rows) continue;
+        uint32_t wd[2][4];
+        if (SR) {
+            philox_words2(seed, kStreamRow, (uint64_t)((r * cols + gc) & ~(int64_t)7),
+                          (uint64_t)(((r + 32) * cols + gc) & ~(int64_t)7), wd[0], wd[1]);
+            if (CH == 4 && (gc & 4)) {
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    wd[h][0] = wd[h][2];
+                    wd[h][1] = wd[h][3];
+                }
+            }
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int64_t rr = r + 32 * h;
+            if (rr >= rows) continue;
+            float v[8];
+#pragma unroll
+            for (int e = 0; e < CH; ++e) v[e] = chunk_elem<T>(raw[k + h], e);
+#pragma unroll
+            for (int e = CH; e < 8; ++e) v[e] = 0.0f;
+            uint32_t w[1];
+            encode<SR, 8>(v, bs[k + h], a[k + h], wd[h], w);
+            uint8_t* dst = rcodes + rr * (cols / 2) + gc / 2;
+            if (CH == 8) *reinterpret_cast<uint32_t*>(dst) = w[0];
+            else *reinterpret_cast<uint16_t*>(dst) = (uint16_t)w[0];
+            if (q == (k + h) % LPB) rscales[rr * (cols / 16) + gc / 16] = (uint8_t)bs[k + h].byte;
+        }
+    }
+}
+
+template <typename T, bool DO_ROW, bool SR, bool RHT>
+__global__ void __launch_bounds__(256) k_quant_colt(const T* __restrict__ x, int64_t rows,
                                                     int64_t cols, int64_t ld,
                                                     const float* __restrict__ amax_src, int n_part,
                                                     uint64_t seed, uint32_t sign_mask,
@@ -345,104 +443,58 @@ __global__ void __launch_bounds__(256) k_quant_tile(const T* __restrict__ x, int
                                                     uint8_t* __restrict__ ccodes,
                                                     uint8_t* __restrict__ cscales,
                                                     float* __restrict__ cts, float* amax_out) {
-    constexpr int CH = Patch<T>::CH, LPB = Patch<T>::LPB, TW = Patch<T>::TW;
-    const TensorScale ts = prologue(amax_src, n_part, DO_ROW ? rts : nullptr, DO_COL ? cts : nullptr,
-                                    amax_out);
-    const int lane = threadIdx.x & 63;
-    const int pc = lane & 15, pr = (lane >> 4) + 4 * (threadIdx.x >> 6);
-    const int q = pc % LPB;  // this lane's quarter / half of a row block
-    int64_t cb[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) cb[h] = (int64_t)blockIdx.x * TW + CH * (pc + 16 * h);
-    {
-        const int64_t r0 = (int64_t)blockIdx.y * 256 + 16 * pr;
-        const bool rows_ok = r0 < rows;  // rows % 16 == 0: a patch is wholly inside or outside
+    constexpr int CH = ColTile<T>::CH, TWC = ColTile<T>::TWC, UE = ColTile<T>::UE,
+                  STRIDE = ColTile<T>::STRIDE;
+    __shared__ __attribute__((aligned(16))) uint8_t tile[256 * STRIDE];
+    const TensorScale ts = prologue(amax_src, n_part, DO_ROW ? rts : nullptr, cts, amax_out);
+    const int t = threadIdx.x;
+    const int64_t R0 = (int64_t)blockIdx.y * 256, C0 = (int64_t)blockIdx.x * TWC;
 
-        uint4 raw[16][2];
+    // ---- load 256 rows x 128 bytes; stage into LDS
+    const int ch = t & 7, lr0 = t >> 3;
+    const int64_t gc = C0 + CH * ch;
+    uint4 raw[8];
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
+    for (int k = 0; k < 8; ++k) {
+        const int64_t gr = R0 + lr0 + 32 * k;
+        raw[k] = make_uint4(0u, 0u, 0u, 0u);
+        if (gr < rows && gc < cols) raw[k] = *reinterpret_cast<const uint4*>(x + gr * ld + gc);
+    }
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                raw[i][h] = make_uint4(0u, 0u, 0u, 0u);
-                if (rows_ok && cb[h] < cols) raw[i][h] = *reinterpret_cast<const uint4*>(x + (r0 + i) * ld + cb[h]);
-            }
+    for (int k = 0; k < 8; ++k) {
+        const int lr = lr0 + 32 * k;
+        const int sw = (lr >> 4) & 15;
+        uint8_t* rowp = tile + lr * STRIDE;
+        *reinterpret_cast<uint2*>(rowp + 8 * ((2 * ch) ^ sw)) = make_uint2(raw[k].x, raw[k].y);
+        *reinterpret_cast<uint2*>(rowp + 8 * ((2 * ch + 1) ^ sw)) = make_uint2(raw[k].z, raw[k].w);
+    }
+    if (DO_ROW) tile_row_blocks<T, SR>(raw, R0, lr0, gc, rows, cols, ts, seed, rcodes, rscales);
+    __syncthreads();
 
-        if (DO_COL && rows_ok) {
+    // ---- column blocks: row band rb, unit u
+    const int rb = t & 15, u = t >> 4;
+    const int64_t r0 = R0 + 16 * rb;
+    if (r0 >= rows) return;  // rows % 16 == 0: a band is wholly inside or outside
+    uint2 q[16];
 #pragma unroll
-            for (int h = 0; h < 2; ++h)
+    for (int i = 0; i < 16; ++i)
+        q[i] = *reinterpret_cast<const uint2*>(tile + (16 * rb + i) * STRIDE + 8 * (u ^ rb));
 #pragma unroll
-                for (int e = 0; e < CH; ++e) {
-                    const int64_t c = cb[h] + e;
-                    if (c >= cols) continue;  // (not break: the loop must unroll fully)
-                    float col[16];
+    for (int e = 0; e < UE; ++e) {
+        const int64_t c = C0 + UE * u + e;
+        if (c >= cols) continue;  // (not break: the loop must unroll fully)
+        float col[16];
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) col[i] = chunk_elem<T>(raw[i][h], e);
-                    if (RHT) hadamard16(col, sign_mask);
-                    BlockScale bs = block_scale(absmax16(col), ts.six_st, ts.st);
-                    uint32_t d[16];
-                    if (SR) draws16(seed, kStreamCol, (uint64_t)(c * rows + r0), d);
-                    uint32_t w[2];
-                    encode<SR, 16>(col, bs, d, w);
-                    *reinterpret_cast<uint2*>(ccodes + c * (rows / 2) + r0 / 2) = make_uint2(w[0], w[1]);
-                    cscales[c * (rows / 16) + r0 / 16] = (uint8_t)bs.byte;
-                }
-        }
-
-        if (DO_ROW) {
-            // cols % 16 == 0 and rows % 16 == 0 here: the LPB lanes of a block agree
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const bool ok = rows_ok && cb[h] < cols;
-#pragma unroll
-                for (int i0 = 0; i0 < 16; i0 += LPB) {
-                    // maxima of this lane's part of rows i0 .. i0+LPB-1, joined over the block's lanes
-                    float a[LPB];
-#pragma unroll
-                    for (int k = 0; k < LPB; ++k) {
-                        float m = 0.0f;
-#pragma unroll
-                        for (int e = 0; e < CH; ++e) m = fmaxf(m, fabsf(chunk_elem<T>(raw[i0 + k][h], e)));
-#pragma unroll
-                        for (int o = 1; o < LPB; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-                        a[k] = m;
-                    }
-                    // lane q of the block derives row i0+q's multiplier; gather all LPB
-                    float mine_a = a[0];
-#pragma unroll
-                    for (int k = 1; k < LPB; ++k) mine_a = (q == k) ? a[k] : mine_a;
-                    const BlockScale mine = block_scale(mine_a, ts.six_st, ts.st);
-                    BlockScale bs[LPB];
-                    const int base = lane - q;
-#pragma unroll
-                    for (int k = 0; k < LPB; ++k) {
-                        bs[k].R = __shfl(mine.R, base + k, 64);
-                        bs[k].byte = (uint32_t)__shfl((int)mine.byte, base + k, 64);
-                    }
-                    if (!ok) continue;
-#pragma unroll
-                    for (int k = 0; k < LPB; ++k) {
-                        const int64_t r = r0 + i0 + k;
-                        float v[8];
-#pragma unroll
-                        for (int e = 0; e < CH; ++e) v[e] = chunk_elem<T>(raw[i0 + k][h], e);
-#pragma unroll
-                        for (int e = CH; e < 8; ++e) v[e] = 0.0f;
-                        uint32_t d[8];
-                        if (SR) draws8(seed, kStreamRow, (uint64_t)((r * cols + cb[h]) & ~(int64_t)7), d);
-                        if (SR && CH == 4 && (cb[h] & 4)) {
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) d[e] = d[e + 4];
-                        }
-                        uint32_t w[1];
-                        encode<SR, 8>(v, bs[k], d, w);
-                        uint8_t* dst = rcodes + r * (cols / 2) + cb[h] / 2;
-                        if (CH == 8) *reinterpret_cast<uint32_t*>(dst) = w[0];
-                        else *reinterpret_cast<uint16_t*>(dst) = (uint16_t)w[0];
-                        if (q == k) rscales[r * (cols / 16) + cb[h] / 16] = (uint8_t)bs[k].byte;
-                    }
-                }
-            }
-        }
+        for (int i = 0; i < 16; ++i) col[i] = unit_elem<T>(q[i], e);
+        if (RHT) hadamard16(col, sign_mask);
+        const float ab = absmax16(col);
+        const BlockScale bs = block_scale(ab, ts.six_st, ts.st);
+        uint32_t wd[8];
+        if (SR) philox_words16(seed, kStreamCol, (uint64_t)(c * rows + r0), wd);
+        uint32_t w[2];
+        encode<SR, 16>(col, bs, ab, wd, w);
+        *reinterpret_cast<uint2*>(ccodes + c * (rows / 2) + r0 / 2) = make_uint2(w[0], w[1]);
+        cscales[c * (rows / 16) + r0 / 16] = (uint8_t)bs.byte;
     }
 }
 
@@ -483,13 +535,16 @@ __global__ void __launch_bounds__(256) k_quant_2d(const T* __restrict__ x, int64
         BlockScale bs = block_scale(a, ts.six_st, ts.st);
         if ((lane & 1) == 0) scales[rband * (cols / 16) + c / 16] = (uint8_t)bs.byte;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
+        for (int i = 0; i < 16; i += 2) {
             const int64_t r = r0 + i;
-            uint32_t d[8];
-            if (SR) draws8(seed, kStream2D, (uint64_t)(r * cols + c), d);
-            uint32_t w[1];
-            encode<SR, 8>(v[i], bs, d, w);
-            *reinterpret_cast<uint32_t*>(codes + r * (cols / 2) + c / 2) = w[0];
+            uint32_t wd[2][4];
+            if (SR) philox_words2(seed, kStream2D, (uint64_t)(r * cols + c), (uint64_t)((r + 1) * cols + c), wd[0], wd[1]);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                uint32_t w[1];
+                encode<SR, 8>(v[i + h], bs, a, wd[h], w);
+                *reinterpret_cast<uint32_t*>(codes + (r + h) * (cols / 2) + c / 2) = w[0];
+            }
         }
     }
 }
@@ -585,7 +640,7 @@ int amax_partials(const T* x, int64_t rows, int64_t cols, int64_t ld, int hadama
         // a contiguous tensor streams as one long row
         const bool flat = (ld == cols) || rows == 1;
         const int64_t r = flat ? 1 : rows, c = flat ? rows * cols : cols;
-        gx = std::min<int64_t>(std::max<int64_t>(cdiv(cdiv(c, CH), 1024), 1), kMaxPartials);
+        gx = std::min<int64_t>(std::max<int64_t>(cdiv(cdiv(c, CH), 2048), 1), kMaxPartials);
         gy = std::min<int64_t>(r, kMaxPartials / gx);
         hipLaunchKernelGGL(k_amax_plain<T>, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, s, x, r, c,
                            flat ? c : ld, ws);
@@ -611,7 +666,6 @@ hipError_t quantize_typed(const T* x, int64_t rows, int64_t cols, int64_t ld, in
         amax = ws;
     }
     const QOut& o = out[0];
-    constexpr int TW = Patch<T>::TW;
     switch (layout) {
         case kLayoutRow: {
             dim3 g((unsigned)cdiv(cols, 512), grid_y(cdiv(rows, 8)));
@@ -628,12 +682,12 @@ hipError_t quantize_typed(const T* x, int64_t rows, int64_t cols, int64_t ld, in
         }
         case kLayoutCol:
         case kLayoutRowCol: {
-            dim3 g((unsigned)cdiv(cols, TW), (unsigned)cdiv(rows, 256));
+            dim3 g((unsigned)cdiv(cols, ColTile<T>::TWC), (unsigned)cdiv(rows, 256));
             const QOut& r = out[0];
             const QOut& c = layout == kLayoutCol ? out[0] : out[1];
 #define NVFP4_TILE(ROWV, SRV, RHTV)                                                                  \
-    hipLaunchKernelGGL((k_quant_tile<T, ROWV, true, SRV, RHTV>), g, dim3(256), 0, s, x, rows, cols, \
-                       ld, amax, np, seed, mask, r.codes, r.scales, r.ts, c.codes, c.scales, c.ts,  \
+    hipLaunchKernelGGL((k_quant_colt<T, ROWV, SRV, RHTV>), g, dim3(256), 0, s, x, rows, cols, ld,   \
+                       amax, np, seed, mask, r.codes, r.scales, r.ts, c.codes, c.scales, c.ts,      \
                        amax_out)
             if (layout == kLayoutCol) {
                 if (sr) {

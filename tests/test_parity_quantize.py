@@ -113,6 +113,23 @@ def test_edge_values(nv, layout):
             assert_q_equal(got[0], ref[0], f"edge amax_in {layout} {rnd} {dt}")
 
 
+@pytest.mark.parametrize("layout", [O.ROW_1D, O.COL_1D, O.ROW_COL_1D, O.BLK_2D])
+def test_understated_amax(nv, layout):
+    """A caller-supplied A_t below the true amax: block multipliers clamp at
+    448, scaled magnitudes run past 6 (to ~1e33 for A_t = 1e-30) and R
+    overflows to inf once s_t is subnormal (A_t = 1e-39); every such element
+    saturates, on both sides, under both roundings."""
+    x = W.student_t((96, 80), 3.0, seed=5)
+    true_amax = float(np.abs(x).max())
+    for amax_in in (0.5 * true_amax, 1e-2 * true_amax, 1e-30, 1e-39):
+        for rnd in (O.RNE, O.SR):
+            for dt in (O.F32, O.BF16):
+                xx = x if dt == O.F32 else W.f32_to_bf16_bits(x)
+                got, ref = run_both(nv, xx, dt, layout, rnd, seed=31, amax_in=amax_in)
+                for i in range(len(ref)):
+                    assert_q_equal(got[i], ref[i], f"amax_in={amax_in} {layout}/{i} {rnd} {dt}")
+
+
 def test_zero_and_empty_tensors(nv):
     x = np.zeros((32, 32), dtype=np.float32)
     got, ref = run_both(nv, x, O.F32, O.ROW_1D, O.SR)
