@@ -20,8 +20,9 @@
 //     output line written by one workgroup (or by workgroups dispatched
 //     together);
 //   - the tensor amax is a separate streaming pass writing at most
-//     kMaxPartials per-workgroup maxima, which every consumer workgroup
-//     reduces in its prologue, unless the caller supplies the amax;
+//     kMaxPartials per-workgroup maxima, which every consumer wave reduces
+//     in its prologue (issued after the wave's first loads, no barrier),
+//     unless the caller supplies the amax;
 //   - column blocks go through an LDS transpose: a 256-row x 128-byte tile is
 //     loaded with full-row 16-byte loads, written to LDS with a per-row-band
 //     XOR swizzle, and read back as 16-row x 8-byte column strips, so every
@@ -41,18 +42,24 @@
 namespace nvfp4 {
 
 // ============================================================ amax
-// A_t for the calling workgroup (all 256 threads must call): n == 0 means
-// src[0] is A_t itself, otherwise the maximum of the n partials src[0..n).
-__device__ __forceinline__ float workgroup_tensor_amax(const float* __restrict__ src, int n) {
-    __shared__ float red[4];
+// A_t for the calling wave: n == 0 means src[0] is A_t itself, otherwise the
+// maximum of the n partials src[0..n) (n <= kMaxPartials).  Every wave reduces
+// the partials on its own (eight L2-resident loads per lane, issued together
+// from clamped indices, then lane exchanges), so no barrier is needed and the
+// caller's own loads can be in flight meanwhile.
+__device__ __forceinline__ float tensor_amax_of(const float* __restrict__ src, int n) {
     if (n == 0) return src[0];
+    constexpr int PER_LANE = (int)(kMaxPartials / 64);
+    const int lane = threadIdx.x & 63;
+    float p[PER_LANE];
+#pragma unroll
+    for (int k = 0; k < PER_LANE; ++k) p[k] = src[min(lane + 64 * k, n - 1)];
     float a = 0.0f;
-    for (int i = threadIdx.x; i < n; i += 256) a = fmaxf(a, src[i]);
+#pragma unroll
+    for (int k = 0; k < PER_LANE; ++k) a = fmaxf(a, p[k]);
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) a = fmaxf(a, __shfl_xor(a, o, 64));
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = a;
-    __syncthreads();
-    return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    return a;
 }
 
 __device__ __forceinline__ void store_partial(float a, float* __restrict__ partial) {
@@ -87,29 +94,35 @@ __global__ void __launch_bounds__(256) k_amax_plain(const T* __restrict__ x, int
                                                     float* __restrict__ partial) {
     constexpr int CH = 16 / sizeof(T);
     constexpr int U = 8;
+    const int64_t nfull = cols / CH;  // chunks wholly inside a row
     const int64_t nch = (cols + CH - 1) / CH;
     const int64_t step = (int64_t)gridDim.x * 256 * U;
     float a = 0.0f;
     for (int64_t r = blockIdx.y; r < rows; r += gridDim.y) {
         const T* row = x + r * ld;
-        for (int64_t j0 = (int64_t)blockIdx.x * 256 * U + threadIdx.x; j0 < nch; j0 += step) {
+        int64_t j0 = (int64_t)blockIdx.x * 256 * U + threadIdx.x;
+        // all U chunks in range: unconditional loads, issued back to back
+        for (; j0 + 256 * (U - 1) < nfull; j0 += step) {
             float v[U][8];
+#pragma unroll
+            for (int u = 0; u < U; ++u) load_chunk(row, j0 + 256 * u, v[u]);
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int e = 0; e < CH; ++e) a = fmaxf(a, fabsf(v[u][e]));
+        }
+        // the rest, chunk by chunk
+        for (; j0 < nch; j0 += step) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int64_t j = j0 + 256 * u;
-                if (j < nch) {
-                    load_chunk(row, j, v[u]);
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) v[u][e] = 0.0f;
-                }
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int64_t valid = cols - (j0 + 256 * u) * CH;
+                if (j >= nch) continue;
+                float v[8];
+                load_chunk(row, j, v);
+                const int64_t valid = cols - j * CH;
 #pragma unroll
                 for (int e = 0; e < CH; ++e)
-                    if (e < valid) a = fmaxf(a, fabsf(v[u][e]));
+                    if (e < valid) a = fmaxf(a, fabsf(v[e]));
             }
         }
     }
@@ -198,7 +211,7 @@ struct TensorScale {
 
 __device__ __forceinline__ TensorScale prologue(const float* amax_src, int n_partials, float* ts0,
                                                 float* ts1, float* amax_out) {
-    const float a = workgroup_tensor_amax(amax_src, n_partials);
+    const float a = tensor_amax_of(amax_src, n_partials);
     TensorScale t;
     t.st = tensor_scale_of(a);
     t.six_st = 6.0f * t.st;
@@ -270,24 +283,26 @@ __global__ void __launch_bounds__(256) k_quant_row(const T* __restrict__ x, int6
                                                    uint8_t* __restrict__ codes,
                                                    uint8_t* __restrict__ scales,
                                                    float* __restrict__ ts_out, float* amax_out) {
-    const TensorScale ts = prologue(amax_src, n_part, ts_out, nullptr, amax_out);
     const int lane = threadIdx.x & 63;
     const bool odd = lane & 1;
     const int64_t c = (int64_t)blockIdx.x * 512 + 8 * lane;
     const bool col_ok = c < cols;  // cols % 16 == 0: both lanes of a pair agree
+    // Lanes past the last column and rows past the last row read a clamped
+    // in-range chunk whose results are never stored, so the loads carry no
+    // branch and issue together.
+    const int64_t cl = col_ok ? c : cols - 8;
     const int64_t nrg = (rows + 7) / 8;
-    for (int64_t rg = blockIdx.y; rg < nrg; rg += gridDim.y) {
+    float v[2][8];
+    auto load_group = [&](int64_t rg) {
         const int64_t r = rg * 8 + 2 * (threadIdx.x >> 6);
-        float v[2][8];
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            if (col_ok && r + k < rows) {
-                load8(x + (r + k) * ld + c, v[k]);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) v[k][e] = 0.0f;
-            }
-        }
+        for (int k = 0; k < 2; ++k) load8(x + (r + k < rows ? r + k : rows - 1) * ld + cl, v[k]);
+    };
+    int64_t rg = blockIdx.y;  // < nrg: grid y is at most the row-group count
+    load_group(rg);
+    const TensorScale ts = prologue(amax_src, n_part, ts_out, nullptr, amax_out);
+    for (;;) {
+        const int64_t r = rg * 8 + 2 * (threadIdx.x >> 6);
         if (RHT) {
             hadamard8_pair(v[0], sign_mask, odd);
             hadamard8_pair(v[1], sign_mask, odd);
@@ -299,17 +314,21 @@ __global__ void __launch_bounds__(256) k_quant_row(const T* __restrict__ x, int6
             for (int e = 0; e < 8; ++e) a[k] = fmaxf(a[k], fabsf(v[k][e]));
         BlockScale bs[2];
         pair_block_scales(a[0], a[1], odd, ts, bs[0], bs[1]);
-        if (!col_ok) continue;
-        uint32_t wd[2][4];
-        if (SR) philox_words2(seed, kStreamRow, (uint64_t)(r * cols + c), (uint64_t)((r + 1) * cols + c), wd[0], wd[1]);
+        if (col_ok) {
+            uint32_t wd[2][4];
+            if (SR) philox_words2(seed, kStreamRow, (uint64_t)(r * cols + c), (uint64_t)((r + 1) * cols + c), wd[0], wd[1]);
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            if (r + k >= rows) break;
-            uint32_t w[1];
-            encode<SR, 8>(v[k], bs[k], a[k], wd[k], w);
-            *reinterpret_cast<uint32_t*>(codes + (r + k) * (cols / 2) + c / 2) = w[0];
-            if (odd == (k == 1)) scales[(r + k) * (cols / 16) + c / 16] = (uint8_t)bs[k].byte;
+            for (int k = 0; k < 2; ++k) {
+                if (r + k >= rows) break;
+                uint32_t w[1];
+                encode<SR, 8>(v[k], bs[k], a[k], wd[k], w);
+                *reinterpret_cast<uint32_t*>(codes + (r + k) * (cols / 2) + c / 2) = w[0];
+                if (odd == (k == 1)) scales[(r + k) * (cols / 16) + c / 16] = (uint8_t)bs[k].byte;
+            }
         }
+        rg += gridDim.y;
+        if (rg >= nrg) break;
+        load_group(rg);
     }
 }
 
@@ -432,6 +451,32 @@ __device__ __forceinline__ void tile_row_blocks(const uint4 (&raw)[8], int64_t R
     }
 }
 
+// Tile of the calling workgroup.  Workgroups are handed to the eight XCDs
+// round robin in dispatch order, and each XCD has its own L2.  With
+// xcd_group = G (> 1; G divides the grid width), each run of G consecutive
+// tiles along a tile row is served by workgroups of one XCD: within every
+// block of 8 G dispatched workgroups, workgroup L takes tile
+// G * (L % 8) + (L / 8) % G of the block.  Output lines that those G tiles
+// write in parts (row codes and scales of the fused layout) are then
+// completed in one L2.  A last partial block keeps the identity order.
+struct TileXY {
+    int64_t x, y;
+};
+
+__device__ __forceinline__ TileXY xcd_tile(int xcd_group) {
+    const int64_t gx = gridDim.x;
+    int64_t L = (int64_t)blockIdx.y * gx + blockIdx.x;
+    if (xcd_group > 1) {
+        const int64_t blk = 8 * (int64_t)xcd_group;
+        if (L < ((int64_t)gridDim.y * gx) / blk * blk)
+            L = L / blk * blk + xcd_group * (L % 8) + (L / 8) % xcd_group;
+    }
+    TileXY r;
+    r.x = L % gx;
+    r.y = L / gx;
+    return r;
+}
+
 template <typename T, bool DO_ROW, bool SR, bool RHT>
 __global__ void __launch_bounds__(256) k_quant_colt(const T* __restrict__ x, int64_t rows,
                                                     int64_t cols, int64_t ld,
@@ -442,13 +487,14 @@ __global__ void __launch_bounds__(256) k_quant_colt(const T* __restrict__ x, int
                                                     float* __restrict__ rts,
                                                     uint8_t* __restrict__ ccodes,
                                                     uint8_t* __restrict__ cscales,
-                                                    float* __restrict__ cts, float* amax_out) {
+                                                    float* __restrict__ cts, float* amax_out,
+                                                    int xcd_group) {
     constexpr int CH = ColTile<T>::CH, TWC = ColTile<T>::TWC, UE = ColTile<T>::UE,
                   STRIDE = ColTile<T>::STRIDE;
     __shared__ __attribute__((aligned(16))) uint8_t tile[256 * STRIDE];
-    const TensorScale ts = prologue(amax_src, n_part, DO_ROW ? rts : nullptr, cts, amax_out);
     const int t = threadIdx.x;
-    const int64_t R0 = (int64_t)blockIdx.y * 256, C0 = (int64_t)blockIdx.x * TWC;
+    const TileXY tl = xcd_tile(xcd_group);
+    const int64_t R0 = tl.y * 256, C0 = tl.x * TWC;
 
     // ---- load 256 rows x 128 bytes; stage into LDS
     const int ch = t & 7, lr0 = t >> 3;
@@ -460,6 +506,7 @@ __global__ void __launch_bounds__(256) k_quant_colt(const T* __restrict__ x, int
         raw[k] = make_uint4(0u, 0u, 0u, 0u);
         if (gr < rows && gc < cols) raw[k] = *reinterpret_cast<const uint4*>(x + gr * ld + gc);
     }
+    const TensorScale ts = prologue(amax_src, n_part, DO_ROW ? rts : nullptr, cts, amax_out);
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
         const int lr = lr0 + 32 * k;
@@ -511,23 +558,24 @@ __global__ void __launch_bounds__(256) k_quant_2d(const T* __restrict__ x, int64
                                                   uint64_t seed, uint8_t* __restrict__ codes,
                                                   uint8_t* __restrict__ scales,
                                                   float* __restrict__ ts_out, float* amax_out) {
-    const TensorScale ts = prologue(amax_src, n_part, ts_out, nullptr, amax_out);
     const int lane = threadIdx.x & 63;
     const int64_t c = (int64_t)blockIdx.x * 512 + lane * 8;
     {
         const int64_t rband = (int64_t)blockIdx.y * 4 + (threadIdx.x >> 6);
         const int64_t r0 = rband * 16;
         const bool active = (r0 < rows) && (c < cols);
+        // inactive lanes read a clamped in-range patch (never stored), so the
+        // 16 loads carry no branch and issue together
+        const int64_t rl = r0 < rows ? r0 : rows - 16, cl = c < cols ? c : cols - 8;
         float v[16][8];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) load8(x + (rl + i) * ld + cl, v[i]);
+        const TensorScale ts = prologue(amax_src, n_part, ts_out, nullptr, amax_out);
         float a = 0.0f;
-        if (active) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) load8(x + (r0 + i) * ld + c, v[i]);
+        for (int i = 0; i < 16; ++i)
 #pragma unroll
-            for (int i = 0; i < 16; ++i)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(v[i][e]));
-        }
+            for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(v[i][e]));
         // the partner lane holds the other 8 columns of the square (both are
         // active or both inactive, since cols % 16 == 0)
         a = fmaxf(a, __shfl_xor(a, 1, 64));
@@ -683,12 +731,17 @@ hipError_t quantize_typed(const T* x, int64_t rows, int64_t cols, int64_t ld, in
         case kLayoutCol:
         case kLayoutRowCol: {
             dim3 g((unsigned)cdiv(cols, ColTile<T>::TWC), (unsigned)cdiv(rows, 256));
+            // fused layout: a 128-byte line of row codes spans 4 (bf16) or 8
+            // (fp32) tiles, a line of row scales 32 or 64
+            const int xg = layout != kLayoutRowCol ? 1
+                           : (g.x % (16 * sizeof(T)) == 0) ? (int)(16 * sizeof(T))
+                           : (g.x % (2 * sizeof(T)) == 0) ? (int)(2 * sizeof(T)) : 1;
             const QOut& r = out[0];
             const QOut& c = layout == kLayoutCol ? out[0] : out[1];
 #define NVFP4_TILE(ROWV, SRV, RHTV)                                                                  \
     hipLaunchKernelGGL((k_quant_colt<T, ROWV, SRV, RHTV>), g, dim3(256), 0, s, x, rows, cols, ld,   \
                        amax, np, seed, mask, r.codes, r.scales, r.ts, c.codes, c.scales, c.ts,      \
-                       amax_out)
+                       amax_out, xg)
             if (layout == kLayoutCol) {
                 if (sr) {
                     if (rht) NVFP4_TILE(false, true, true); else NVFP4_TILE(false, true, false);
