@@ -17,17 +17,22 @@
 //
 // Geometry: a 256-thread workgroup owns a 256 x 256 output tile; its four
 // waves form a 2 x 2 grid of 128 x 128 wave tiles (4 x 4 MFMA tiles of 32 x 32,
-// 256 FP32 accumulators per lane).  Each 64-wide K step:
-//   1. every thread loads one A row and one B row of the step (32 code bytes +
-//      4 scale bytes each) for the NEXT step into registers;
-//   2. the waves run the 64 MFMAs of the current step from LDS;
-//   3. every thread dequantizes its two prefetched rows to FP16 (FP4 unpack
-//      instruction, round-toward-zero pack -- exact here -- and one packed
-//      FP16 multiply by the block multiplier) into the other LDS stage;
-//   4. one barrier.
-// Each operand element is thus expanded once per workgroup instead of once
-// per wave that uses it.  LDS: 2 stages x (A, B) x 256 rows x 144 bytes
-// (64 FP16 + 16 bytes of padding that spreads the row starts over the banks).
+// 256 FP32 accumulators per lane).  Every thread stages one A row and one B
+// row: it loads the rows' 32 code bytes and 4 scale bytes per 64-wide K step
+// into registers, at least two steps before use, and dequantizes the step
+// after the current one into the other LDS stage (FP4 unpack instruction,
+// round-toward-zero pack -- exact here -- and one packed FP16 multiply by the
+// block multiplier).  The current step runs as four 16-wide K substeps of 16
+// MFMAs per wave, and the dequantization is cut into 16 two-element pieces
+// per substep that issue between those MFMAs (one wave per SIMD: the same
+// wave has to keep the matrix core and the VALU busy, and without the
+// interleave the two ran one after the other); sched_barrier pins that order.
+// One workgroup barrier per step.  Loads and dequantization are branch-free
+// in the loop: steps past the end are clamped re-reads, and the blocks of a
+// partial last step read an in-range block with its multiplier forced to 0.
+// Each operand element is expanded once per workgroup.  LDS: 2 stages x (A, B)
+// x 256 rows x 144 bytes (64 FP16 + 16 bytes of padding that spreads the row
+// starts over the banks).
 #include "launch.hpp"
 #include "nvfp4_device.hpp"
 
@@ -58,32 +63,51 @@ struct GemmArgs {
 // One row's share of a K step: 64 codes and their four block multipliers.
 struct RowStep {
     uint4 c0, c1;  // code bytes 0..15 and 16..31
-    uint32_t sc;   // scale bytes of the four 16-element blocks
+    uint32_t sc;   // scale bytes of the four 16-element blocks (byte q = block q)
 };
 
-// Load row `row` of operand `op` for K step kc (zeros past K; K % 16 == 0).
-__device__ __forceinline__ RowStep load_row_step(const Operand& op, int64_t row, int64_t K,
-                                                 int64_t kc, bool full, bool scales_aligned) {
+// The staged row of one operand: its code row and its scale row.
+struct RowSrc {
+    const uint8_t* codes;   // row start (K/2 bytes)
+    const uint8_t* scales;  // first scale byte of the row (1D) or of its 16-row band (2D)
+};
+
+__device__ __forceinline__ RowSrc row_src(const Operand& op, int64_t row, int64_t K) {
+    RowSrc r;
+    r.codes = op.codes + row * (K / 2);
+    r.scales = op.scales + (op.scale_2d ? (row / 16) : row) * (K / 16);
+    return r;
+}
+
+// K step kc (0 <= kc < number of steps) of a staged row.  FAST: K % 64 == 0
+// and the scale rows are 4-byte aligned, so a step is two 16-byte code loads
+// and one 4-byte scale load.  Otherwise each 16-element block is loaded on its
+// own; blocks past K re-read the last valid block with multiplier byte 0, so
+// they dequantize to zeros.
+template <bool FAST>
+__device__ __forceinline__ RowStep load_row_step(const RowSrc& src, int64_t K, int64_t kc) {
     RowStep r;
-    const uint8_t* cp = op.codes + row * (K / 2) + kc * (kBK / 2);
-    const int64_t kb = kc * (kBK / 16);
-    const uint8_t* sp = op.scale_2d ? op.scales + (row / 16) * (K / 16) + kb
-                                    : op.scales + row * (K / 16) + kb;
-    if (full) {
+    if (FAST) {
+        const uint8_t* cp = src.codes + kc * (kBK / 2);
         r.c0 = *reinterpret_cast<const uint4*>(cp);
         r.c1 = *reinterpret_cast<const uint4*>(cp + 16);
-        r.sc = scales_aligned ? *reinterpret_cast<const uint32_t*>(sp)
-                              : (uint32_t)sp[0] | ((uint32_t)sp[1] << 8) | ((uint32_t)sp[2] << 16) |
-                                    ((uint32_t)sp[3] << 24);
+        r.sc = *reinterpret_cast<const uint32_t*>(src.scales + kc * (kBK / 16));
     } else {
-        const int64_t nblk = (K - kc * kBK) / 16;  // 1..3 valid 16-element blocks
-        r.c0 = make_uint4(0u, 0u, 0u, 0u);
-        r.c1 = make_uint4(0u, 0u, 0u, 0u);
+        const int64_t nkb = K / 16, kb0 = kc * (kBK / 16);
+        uint32_t w[8];
         r.sc = 0u;
-        const uint2* c2 = reinterpret_cast<const uint2*>(cp);
-        if (nblk > 0) { uint2 t = c2[0]; r.c0.x = t.x; r.c0.y = t.y; r.sc = sp[0]; }
-        if (nblk > 1) { uint2 t = c2[1]; r.c0.z = t.x; r.c0.w = t.y; r.sc |= (uint32_t)sp[1] << 8; }
-        if (nblk > 2) { uint2 t = c2[2]; r.c1.x = t.x; r.c1.y = t.y; r.sc |= (uint32_t)sp[2] << 16; }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int64_t kb = kb0 + q;
+            const int64_t kbl = kb < nkb ? kb : nkb - 1;
+            const uint2 t = *reinterpret_cast<const uint2*>(src.codes + 8 * kbl);
+            w[2 * q] = t.x;
+            w[2 * q + 1] = t.y;
+            const uint32_t sb = src.scales[kbl];
+            r.sc |= (kb < nkb ? sb : 0u) << (8 * q);
+        }
+        r.c0 = make_uint4(w[0], w[1], w[2], w[3]);
+        r.c1 = make_uint4(w[4], w[5], w[6], w[7]);
     }
     return r;
 }
@@ -109,127 +133,83 @@ __device__ __forceinline__ half2_t scale_pair(uint32_t sb) {
     return r;
 }
 
-// Dequantize one RowStep into LDS row `dst` (64 FP16, natural K order).
-__device__ __forceinline__ void store_row_step(const RowStep& r, _Float16* dst) {
-    const uint32_t w[8] = {r.c0.x, r.c0.y, r.c0.z, r.c0.w, r.c1.x, r.c1.y, r.c1.z, r.c1.w};
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const half2_t sc = scale_pair((r.sc >> (8 * q)) & 0xFFu);
-        *reinterpret_cast<uint4*>(dst + 16 * q) = dequant8_f16(w[2 * q], sc);
-        *reinterpret_cast<uint4*>(dst + 16 * q + 8) = dequant8_f16(w[2 * q + 1], sc);
-    }
+// Dequantize 16-element block q of a RowStep into LDS row `dst` (64 FP16,
+// natural K order).
+__device__ __forceinline__ void store_block(const RowStep& r, int q, _Float16* dst) {
+    const uint32_t wa = q == 0 ? r.c0.x : q == 1 ? r.c0.z : q == 2 ? r.c1.x : r.c1.z;
+    const uint32_t wb = q == 0 ? r.c0.y : q == 1 ? r.c0.w : q == 2 ? r.c1.y : r.c1.w;
+    const half2_t sc = scale_pair((r.sc >> (8 * q)) & 0xFFu);
+    *reinterpret_cast<uint4*>(dst + 16 * q) = dequant8_f16(wa, sc);
+    *reinterpret_cast<uint4*>(dst + 16 * q + 8) = dequant8_f16(wb, sc);
 }
 
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
     return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
-template <bool GROUPED, bool SWIGLU, bool OUT_BF16>
-__global__ void __launch_bounds__(256, 1) k_gemm(GemmArgs p) {
-    __shared__ __attribute__((aligned(16))) _Float16 smem[2][2][kBM][kLdsK];
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, w = tid >> 6;
-    const int wm = w >> 1, wn = w & 1;
-    const int h = lane >> 5, l32 = lane & 31;
+// Rows of A (and the group) of the workgroup's output tile.  Grouped: tiles
+// are numbered group by group, each group's rows split into 256-row tiles
+// (its last one partial); tiles past the last group have ok = false.
+struct TileRows {
+    int64_t m0, m_end;
+    int g;
+    bool ok;
+};
 
-    // ---- tile -> (rows of A, group) ----
-    int64_t m_end = p.M, m0 = 0;
-    int g = 0;
+template <bool GROUPED>
+__device__ __forceinline__ TileRows tile_rows(const GemmArgs& p) {
+    TileRows t{0, p.M, 0, true};
     if (GROUPED) {
-        int64_t t = blockIdx.y;
-        g = -1;
+        int64_t r = blockIdx.y;
+        t.ok = false;
         for (int gg = 0; gg < p.G; ++gg) {
             const int64_t lo = min(max(p.offsets[gg], (int64_t)0), p.M);
             const int64_t hi = min(max(p.offsets[gg + 1], lo), p.M);
             const int64_t tiles = (hi - lo + kBM - 1) / kBM;
-            if (t < tiles) {
-                g = gg;
-                m_end = hi;
-                m0 = lo + t * kBM;
+            if (r < tiles) {
+                t.g = gg;
+                t.m_end = hi;
+                t.m0 = lo + r * kBM;
+                t.ok = true;
                 break;
             }
-            t -= tiles;
+            r -= tiles;
         }
-        if (g < 0) return;  // uniform across the workgroup
     } else {
-        m0 = (int64_t)blockIdx.y * kBM;
+        t.m0 = (int64_t)blockIdx.y * kBM;
     }
-    const int64_t K = p.K, Ng = p.N;
-    const int64_t bbase = GROUPED ? (int64_t)g * Ng : 0;
+    return t;
+}
 
-    // ---- the A row and B row this thread stages ----
-    const int64_t arow = min(m0 + tid, m_end - 1);
-    int64_t brow;
+// Row of B staged as tile row r (0..255), clamped into range.  SwiGLU: tile
+// rows 0..127 are gate rows j0 + r and 128..255 the matching up rows F + j0 + r
+// of the group's 2F weight rows.
+template <bool SWIGLU>
+__device__ __forceinline__ int64_t b_row(const GemmArgs& p, int64_t bbase, int r) {
+    const int64_t Ng = p.N;
     if (SWIGLU) {
         const int64_t F = Ng / 2, j0 = (int64_t)blockIdx.x * (kBN / 2);
-        const int64_t c = min(j0 + (tid & 127), F - 1);
-        brow = bbase + (tid < 128 ? c : F + c);
-    } else {
-        brow = bbase + min((int64_t)blockIdx.x * kBN + tid, Ng - 1);
+        const int64_t c = min(j0 + (r & 127), F - 1);
+        return bbase + (r < 128 ? c : F + c);
     }
+    return bbase + min((int64_t)blockIdx.x * kBN + r, Ng - 1);
+}
 
-    float16_t acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+// LDS tile row of B that MFMA column tile j of wave column wn reads.
+template <bool SWIGLU>
+__device__ __forceinline__ int b_tile_row(int wn, int j) {
+    return SWIGLU ? ((j < 2 ? 0 : 128) + 64 * wn + 32 * (j & 1)) : 128 * wn + 32 * j;
+}
 
-    const int64_t nsteps = (K + kBK - 1) / kBK;
-    const int64_t nfull = K / kBK;
-    // 4-byte scale loads when every step's four scale bytes are 4-byte aligned
-    const bool sal_a = (K % kBK) == 0 && (reinterpret_cast<uintptr_t>(p.A.scales) & 3) == 0;
-    const bool sal_b = (K % kBK) == 0 && (reinterpret_cast<uintptr_t>(p.B.scales) & 3) == 0;
-
-    // LDS rows read by this wave's MFMA tiles (A: 4 tiles of 32 rows; B likewise)
-    int brow_lds[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-        brow_lds[j] = SWIGLU ? ((j < 2 ? 0 : 128) + 64 * wn + 32 * (j & 1)) : 128 * wn + 32 * j;
-
-    if (nsteps > 0) {
-        RowStep ra = load_row_step(p.A, arow, K, 0, nfull > 0, sal_a);
-        RowStep rb = load_row_step(p.B, brow, K, 0, nfull > 0, sal_b);
-        store_row_step(ra, &smem[0][0][tid][0]);
-        store_row_step(rb, &smem[0][1][tid][0]);
-    }
-    __syncthreads();
-
-    for (int64_t kc = 0; kc < nsteps; ++kc) {
-        const int st = (int)(kc & 1);
-        const bool more = kc + 1 < nsteps;
-        RowStep na, nb;
-        if (more) {
-            const bool full = kc + 1 < nfull;
-            na = load_row_step(p.A, arow, K, kc + 1, full, sal_a);
-            nb = load_row_step(p.B, brow, K, kc + 1, full, sal_b);
-        }
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            half8_t bo[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                bo[j] = *reinterpret_cast<const half8_t*>(&smem[st][1][brow_lds[j] + l32][16 * s + 8 * h]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const half8_t ao =
-                    *reinterpret_cast<const half8_t*>(&smem[st][0][128 * wm + 32 * i + l32][16 * s + 8 * h]);
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ao, bo[j], acc[i][j], 0, 0, 0);
-            }
-        }
-        if (more) {
-            store_row_step(na, &smem[st ^ 1][0][tid][0]);
-            store_row_step(nb, &smem[st ^ 1][1][tid][0]);
-        }
-        __syncthreads();
-    }
-
-    // ---- epilogue ----
+// Scale by the two tensor scales and write the wave's 128 x 128 tile (or, for
+// SwiGLU, its 128 x 64 gate/up pairs) of C.  Accumulator r of MFMA tile
+// (i, j) holds row 32i + 8(r/4) + 4h + r%4, column 32j + l32 of the wave tile.
+template <bool GROUPED, bool SWIGLU, bool OUT_BF16>
+__device__ __forceinline__ void epilogue(const GemmArgs& p, float16_t (&acc)[4][4], int64_t m0,
+                                         int64_t m_end, int g, int wm, int wn, int h, int l32,
+                                         int lane) {
+    const int64_t Ng = p.N;
     const float alpha = p.A.ts[0] * p.B.ts[GROUPED ? g : 0];
-    // accumulator r of MFMA tile (i, j): row 32i + 8(r/4) + 4h + r%4, col 32j + l32
     const int64_t mw = m0 + 128 * wm;
     if (SWIGLU) {
         uint16_t* C = static_cast<uint16_t*>(p.C);
@@ -281,12 +261,389 @@ __global__ void __launch_bounds__(256, 1) k_gemm(GemmArgs p) {
         }
 }
 
+template <bool GROUPED, bool SWIGLU, bool OUT_BF16, bool FAST>
+__global__ void __launch_bounds__(256, 1) k_gemm(GemmArgs p) {
+    __shared__ __attribute__((aligned(16))) _Float16 smem[2][2][kBM][kLdsK];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, w = tid >> 6;
+    const int wm = w >> 1, wn = w & 1;
+    const int h = lane >> 5, l32 = lane & 31;
+
+    const TileRows tr = tile_rows<GROUPED>(p);
+    if (!tr.ok) return;  // uniform across the workgroup
+    const int64_t m0 = tr.m0, m_end = tr.m_end;
+    const int g = tr.g;
+    const int64_t K = p.K;
+    const int64_t bbase = GROUPED ? (int64_t)g * p.N : 0;
+
+    // ---- the A row and B row this thread stages ----
+    const int64_t arow = min(m0 + tid, m_end - 1);
+    const int64_t brow = b_row<SWIGLU>(p, bbase, tid);
+
+    float16_t acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    const int64_t nsteps = (K + kBK - 1) / kBK;
+    const RowSrc sa = row_src(p.A, arow, K), sb = row_src(p.B, brow, K);
+
+    // LDS rows read by this wave's MFMA tiles (A: 4 tiles of 32 rows; B likewise)
+    int brow_lds[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) brow_lds[j] = b_tile_row<SWIGLU>(wn, j);
+
+    if (nsteps > 0) {  // K == 0: the accumulators stay zero
+        // The loop runs K steps four at a time.  Staged rows live in two
+        // register sets of two steps each: while one set's steps are being
+        // dequantized (one step ahead of the MFMAs), the other set's loads are
+        // in flight, issued at least two steps before their first use.  The
+        // sets swap roles every two steps, so the unrolled body has static
+        // register names and no copies.  A step count that is not a multiple
+        // of 4 gets leading all-zero steps (scale bytes forced to 0: they
+        // dequantize to zeros and add nothing).  Step j covers K step j - pad.
+        const int64_t pad = (4 - nsteps % 4) % 4, nj = nsteps + pad, last = nsteps - 1;
+        auto load_j = [&](const RowSrc& src, int64_t j) {
+            const int64_t kc = j - pad;
+            RowStep r = load_row_step<FAST>(src, K, kc < 0 ? 0 : (kc > last ? last : kc));
+            if (kc < 0) r.sc = 0u;
+            return r;
+        };
+        struct TwoSteps {
+            RowStep a0, b0, a1, b1;  // A row and B row of the first and second step
+        };
+        auto load2 = [&](TwoSteps& t, int64_t j) {
+            t.a0 = load_j(sa, j);
+            t.b0 = load_j(sb, j);
+            t.a1 = load_j(sa, j + 1);
+            t.b1 = load_j(sb, j + 1);
+        };
+        {
+            const RowStep ra = load_j(sa, 0), rb = load_j(sb, 0);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                store_block(ra, q, &smem[0][0][tid][0]);
+                store_block(rb, q, &smem[0][1][tid][0]);
+            }
+        }
+        TwoSteps P, Q;
+        load2(P, 1);
+        load2(Q, 3);
+        __syncthreads();
+
+        // One step: MFMAs from LDS stage j & 1 while da/db (step j + 1) are
+        // dequantized into the other stage.  Per 16-wide substep the
+        // wave's 16 MFMAs alternate with the 16 two-element dequantization
+        // pieces of block s of both staged rows (3 VALU each), the next
+        // substep's 8 fragment reads go out after the third MFMA, and each
+        // completed 8-element group is written to LDS; sched_barrier(0) keeps
+        // that order.
+        auto step = [&](int64_t j, const RowStep& da, const RowStep& db) {
+            const int st = (int)(j & 1);
+            half8_t fr[2][8];  // [set][A0..A3, B0..B3]
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                fr[0][i] = *reinterpret_cast<const half8_t*>(&smem[st][0][128 * wm + 32 * i + l32][8 * h]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                fr[0][4 + j] = *reinterpret_cast<const half8_t*>(&smem[st][1][brow_lds[j] + l32][8 * h]);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const int cur = s & 1, nxt = cur ^ 1;
+                const uint32_t wsrc[4] = {
+                    s == 0 ? da.c0.x : s == 1 ? da.c0.z : s == 2 ? da.c1.x : da.c1.z,
+                    s == 0 ? da.c0.y : s == 1 ? da.c0.w : s == 2 ? da.c1.y : da.c1.w,
+                    s == 0 ? db.c0.x : s == 1 ? db.c0.z : s == 2 ? db.c1.x : db.c1.z,
+                    s == 0 ? db.c0.y : s == 1 ? db.c0.w : s == 2 ? db.c1.y : db.c1.w};
+                const half2_t sca = scale_pair((da.sc >> (8 * s)) & 0xFFu);
+                const half2_t scb = scale_pair((db.sc >> (8 * s)) & 0xFFu);
+                uint32_t outw[4][4];
+#pragma unroll
+                for (int m = 0; m < 16; ++m) {
+                    const int i = m >> 2, j = m & 3;
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fr[cur][i], fr[cur][4 + j], acc[i][j], 0, 0, 0);
+                    if (m == 2 && s < 3) {
+#pragma unroll
+                        for (int ii = 0; ii < 4; ++ii)
+                            fr[nxt][ii] = *reinterpret_cast<const half8_t*>(
+                                &smem[st][0][128 * wm + 32 * ii + l32][16 * (s + 1) + 8 * h]);
+#pragma unroll
+                        for (int jj = 0; jj < 4; ++jj)
+                            fr[nxt][4 + jj] = *reinterpret_cast<const half8_t*>(
+                                &smem[st][1][brow_lds[jj] + l32][16 * (s + 1) + 8 * h]);
+                    }
+                    // dequantization piece m: word m / 4, code pair m % 4
+                    const int wq = m >> 2, pq = m & 3;
+                    const float2 f = e2m1x2_unpack(wsrc[wq], pq);
+                    const half2_t hv = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_pkrtz(f.x, f.y));
+                    outw[wq][pq] = __builtin_bit_cast(uint32_t, hv * (wq < 2 ? sca : scb));
+                    if (pq == 3)
+                        *reinterpret_cast<uint4*>(&smem[st ^ 1][wq >> 1][tid][16 * s + 8 * (wq & 1)]) =
+                            make_uint4(outw[wq][0], outw[wq][1], outw[wq][2], outw[wq][3]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            __syncthreads();
+        };
+
+        // (loads past the last step are clamped re-reads, unused)
+        for (int64_t j = 0; j < nj; j += 4) {
+            step(j, P.a0, P.b0);
+            step(j + 1, P.a1, P.b1);
+            load2(P, j + 5);
+            step(j + 2, Q.a0, Q.b0);
+            step(j + 3, Q.a1, Q.b1);
+            load2(Q, j + 7);
+        }
+    }
+
+    epilogue<GROUPED, SWIGLU, OUT_BF16>(p, acc, m0, m_end, g, wm, wn, h, l32, lane);
+}
+
+// ============================================================ ring kernel
+// The kernel for whole 64-wide K steps and 4-byte-aligned scale rows (every
+// shape of the benchmarked workloads).  Raw operands go straight from global
+// memory into LDS: a ring of kRing slots, each holding one K step of both
+// operands' codes (256 rows x 32 bytes) and scale bytes (256 rows x 4 bytes),
+// loaded by global_load_lds (no register staging; lane i of a load lands at
+// the slot base + i x size), kRing - 1 steps ahead of use.  Each wave then
+// converts its own MFMA fragments straight into registers: FP4 pair -> FP16
+// pair with the gfx950 convert (exact), times the block multiplier (FP8 pair
+// -> FP16 pair convert, exact; the product has at most 6 significant bits).
+// LDS carries 4.5 bits per element instead of 16, and no FP16 tile is written.
+//
+// K order inside a step: lane (l32, h) of substep s supplies elements
+// K = 32 h + 8 s .. + 7 of the step (the same map on A and B, so every product
+// pairs equal K; over the four substeps and both lane halves it covers the 64
+// elements once).  A lane's codes for the whole step are then one 16-byte LDS
+// read per fragment row, and the 64 lanes of a read cover 1 KiB contiguously.
+//
+// Per step, per wave: 4 substeps of 16 MFMAs; between the MFMAs of substep s
+// the fragments of substep s + 1 are converted (32 two-element pieces, 2 VALU
+// each).  In substep 2 the wave waits for its own loads of the next step,
+// joins the workgroup barrier, reads the next step's raw fragments and issues
+// the loads of the step kRing steps ahead into the slot just consumed.
+constexpr int kRing = 4;
+constexpr int kSlotCodes = kBM * (kBK / 2);   // 8192 bytes per operand
+constexpr int kSlotScales = kBM * (kBK / 16); // 1024 bytes per operand
+
+struct RingSlot {
+    uint8_t a_codes[kSlotCodes];
+    uint8_t b_codes[kSlotCodes];
+    uint8_t a_sc[kSlotScales];
+    uint8_t b_sc[kSlotScales];
+};
+
+typedef __attribute__((address_space(1))) void gmem_t;
+typedef __attribute__((address_space(3))) void lmem_t;
+
+// Per-thread global sources of the ring loads: code rows for tile rows
+// 64 w + L/2 and 64 w + 32 + L/2 (16-byte chunk L % 2), scale rows for tile
+// row 64 w + L (L = lane, w = wave).
+struct RingSrc {
+    const uint8_t *a0, *a1, *b0, *b1, *as, *bs;
+};
+
+__device__ __forceinline__ void ring_load(const RingSrc& rs, int64_t kc, RingSlot& slot, int w) {
+    const int64_t co = kc * (kBK / 2), so = kc * (kBK / 16);
+    __builtin_amdgcn_global_load_lds((gmem_t*)(rs.a0 + co), (lmem_t*)&slot.a_codes[64 * w * 32], 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((gmem_t*)(rs.a1 + co), (lmem_t*)&slot.a_codes[(64 * w + 32) * 32], 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((gmem_t*)(rs.b0 + co), (lmem_t*)&slot.b_codes[64 * w * 32], 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((gmem_t*)(rs.b1 + co), (lmem_t*)&slot.b_codes[(64 * w + 32) * 32], 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((gmem_t*)(rs.as + so), (lmem_t*)&slot.a_sc[64 * w * 4], 4, 0, 0);
+    __builtin_amdgcn_global_load_lds((gmem_t*)(rs.bs + so), (lmem_t*)&slot.b_sc[64 * w * 4], 4, 0, 0);
+}
+constexpr int kRingLoadsPerStep = 6;
+
+// s_waitcnt immediate (gfx9 encoding) that waits until at most n vector
+// memory operations of this wave are outstanding, leaving the other counters.
+constexpr unsigned vmcnt_at_most(unsigned n) {
+    return (n & 15u) | ((n >> 4) << 14) | (7u << 4) | (15u << 8);
+}
+
+// A wave's raw fragments of one step: codes of its 4 A and 4 B fragment rows
+// (32 codes each), their two scale bytes, and (after scale_frags) the two
+// block multipliers as an FP16 pair.
+struct RawFrags {
+    uint4 c[8];       // A0..A3, B0..B3
+    uint32_t sb[8];   // scale bytes of blocks 2h, 2h + 1
+    half2_t sc[8];
+    bool zero;        // a leading padding step: multipliers forced to 0
+};
+
+__device__ __forceinline__ void read_frags(const RingSlot& slot, int arow0, const int (&brow)[4], int l32,
+                                           int h, bool zero, RawFrags& f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = arow0 + 32 * i + l32;
+        f.c[i] = *reinterpret_cast<const uint4*>(&slot.a_codes[r * 32 + 16 * h]);
+        f.sb[i] = *reinterpret_cast<const uint16_t*>(&slot.a_sc[r * 4 + 2 * h]);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int r = brow[j] + l32;
+        f.c[4 + j] = *reinterpret_cast<const uint4*>(&slot.b_codes[r * 32 + 16 * h]);
+        f.sb[4 + j] = *reinterpret_cast<const uint16_t*>(&slot.b_sc[r * 4 + 2 * h]);
+    }
+    f.zero = zero;
+}
+
+// Block multipliers of the fragments: FP8 pair -> FP16 pair (exact).
+__device__ __forceinline__ void scale_frags(RawFrags& f) {
+#pragma unroll
+    for (int o = 0; o < 8; ++o)
+        f.sc[o] = __builtin_bit_cast(half2_t,
+                                     __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(f.zero ? 0u : f.sb[o], 1.0f, false));
+}
+
+// Piece p (0..3) of fragment o for substep s: codes 2p, 2p+1 of the substep's
+// 8 -> one FP16 pair times the block multiplier.
+__device__ __forceinline__ uint32_t frag_piece(const RawFrags& f, int o, int s, int p) {
+    const uint4& c = f.c[o];
+    const uint32_t w = s == 0 ? c.x : s == 1 ? c.y : s == 2 ? c.z : c.w;
+    half2_t v;
+    switch (p) {
+        case 0: v = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0)); break;
+        case 1: v = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1)); break;
+        case 2: v = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2)); break;
+        default: v = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3)); break;
+    }
+    const _Float16 m = s < 2 ? f.sc[o].x : f.sc[o].y;  // block 2h (s = 0, 1) or 2h + 1
+    return __builtin_bit_cast(uint32_t, v * m);
+}
+
+template <bool GROUPED, bool SWIGLU, bool OUT_BF16>
+__global__ void __launch_bounds__(256, 1) k_gemm_ring(GemmArgs p) {
+    __shared__ __attribute__((aligned(16))) RingSlot ring0, ring1, ring2, ring3;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, w = tid >> 6;
+    const int wm = w >> 1, wn = w & 1;
+    const int h = lane >> 5, l32 = lane & 31;
+
+    const TileRows tr = tile_rows<GROUPED>(p);
+    if (!tr.ok) return;  // uniform across the workgroup
+    const int64_t m0 = tr.m0, m_end = tr.m_end;
+    const int g = tr.g;
+    const int64_t K = p.K;
+    const int64_t bbase = GROUPED ? (int64_t)g * p.N : 0;
+
+    RingSrc rs;
+    {
+        const int r0 = 64 * w + (lane >> 1), r1 = r0 + 32, rsc = 64 * w + lane;
+        const int64_t chunk = 16 * (lane & 1);
+        const RowSrc a0 = row_src(p.A, min(m0 + r0, m_end - 1), K);
+        const RowSrc a1 = row_src(p.A, min(m0 + r1, m_end - 1), K);
+        const RowSrc b0 = row_src(p.B, b_row<SWIGLU>(p, bbase, r0), K);
+        const RowSrc b1 = row_src(p.B, b_row<SWIGLU>(p, bbase, r1), K);
+        rs.a0 = a0.codes + chunk;
+        rs.a1 = a1.codes + chunk;
+        rs.b0 = b0.codes + chunk;
+        rs.b1 = b1.codes + chunk;
+        rs.as = row_src(p.A, min(m0 + rsc, m_end - 1), K).scales;
+        rs.bs = row_src(p.B, b_row<SWIGLU>(p, bbase, rsc), K).scales;
+    }
+    const int arow0 = 128 * wm;
+    int brow[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) brow[j] = b_tile_row<SWIGLU>(wn, j);
+
+    float16_t acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    const int64_t nsteps = K / kBK;
+    if (nsteps > 0) {  // K == 0: the accumulators stay zero
+        // Steps run four at a time (ring slots and fragment buffers then have
+        // static names); a step count that is not a multiple of 4 gets leading
+        // steps whose multipliers are forced to 0.  Step j covers K step j - pad.
+        const int64_t pad = (4 - nsteps % 4) % 4, nj = nsteps + pad, last = nsteps - 1;
+        auto kc_of = [&](int64_t j) {
+            const int64_t kc = j - pad;
+            return kc < 0 ? (int64_t)0 : (kc > last ? last : kc);
+        };
+        ring_load(rs, kc_of(0), ring0, w);
+        ring_load(rs, kc_of(1), ring1, w);
+        ring_load(rs, kc_of(2), ring2, w);
+        ring_load(rs, kc_of(3), ring3, w);
+        // step 0 landed (three later steps may be outstanding), then the barrier
+        __builtin_amdgcn_s_waitcnt(vmcnt_at_most(3 * kRingLoadsPerStep));
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+
+        RawFrags fx, fy;            // raw fragments of the current / next step (alternating)
+        uint32_t op[2][8][4];       // converted fragments, double-buffered by substep
+        read_frags(ring0, arow0, brow, l32, h, pad > 0, fx);
+        scale_frags(fx);
+#pragma unroll
+        for (int o = 0; o < 8; ++o)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) op[0][o][q] = frag_piece(fx, o, 0, q);
+
+        auto step = [&](int64_t j, RingSlot& cur, RingSlot& nxt, RawFrags& fc, RawFrags& fn) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const int ob = s & 1;
+                if (s == 2) {
+                    // own loads of step j + 1 done (steps j + 2, j + 3 may be
+                    // in flight), workgroup barrier: every wave's part of step
+                    // j + 1 is in LDS and every wave is done reading `cur`
+                    __builtin_amdgcn_s_waitcnt(vmcnt_at_most(2 * kRingLoadsPerStep));
+                    asm volatile("" ::: "memory");
+                    __builtin_amdgcn_s_barrier();
+                    asm volatile("" ::: "memory");
+                    read_frags(nxt, arow0, brow, l32, h, j + 1 < pad, fn);
+                    ring_load(rs, kc_of(j + 4), cur, w);
+                }
+                if (s == 3) scale_frags(fn);  // first use of the next step's fragments
+#pragma unroll
+                for (int m = 0; m < 16; ++m) {
+                    const int i = m >> 2, jj = m & 3;
+                    acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                        __builtin_bit_cast(half8_t, op[ob][i]), __builtin_bit_cast(half8_t, op[ob][4 + jj]),
+                        acc[i][jj], 0, 0, 0);
+                    // two conversion pieces for the next substep (or step)
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) {
+                        const int piece = 2 * m + u, o = piece >> 2, q = piece & 3;
+                        op[ob ^ 1][o][q] = s < 3 ? frag_piece(fc, o, s + 1, q) : frag_piece(fn, o, 0, q);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+        };
+        for (int64_t j = 0; j < nj; j += 4) {
+            step(j, ring0, ring1, fx, fy);
+            step(j + 1, ring1, ring2, fy, fx);
+            step(j + 2, ring2, ring3, fx, fy);
+            step(j + 3, ring3, ring0, fy, fx);
+        }
+        // the last steps' look-ahead loads (clamped re-reads into slots nobody
+        // reads again) must land before the workgroup's LDS is released
+        __builtin_amdgcn_s_waitcnt(vmcnt_at_most(0));
+    }
+    epilogue<GROUPED, SWIGLU, OUT_BF16>(p, acc, m0, m_end, g, wm, wn, h, l32, lane);
+}
+
 __global__ void k_zero_float(float* p) {
     if (threadIdx.x == 0) p[0] = 0.0f;
 }
 
 namespace {
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Whole 64-wide steps and 4-byte-aligned scale rows: the two-load step reader.
+inline bool fast_path(const Operand& A, const Operand& B, int64_t K) {
+    return K % kBK == 0 && (reinterpret_cast<uintptr_t>(A.scales) & 3) == 0 &&
+           (reinterpret_cast<uintptr_t>(B.scales) & 3) == 0;
+}
 }  // namespace
 
 hipError_t launch_gemm(const Operand& A, const Operand& B, int64_t M, int64_t N, int64_t K,
@@ -294,10 +651,17 @@ hipError_t launch_gemm(const Operand& A, const Operand& B, int64_t M, int64_t N,
     if (M == 0 || N == 0) return hipSuccess;
     GemmArgs p{A, B, M, N, K, C, ldc, nullptr, 1, nullptr};
     dim3 grid((unsigned)cdiv(N, kBN), (unsigned)cdiv(M, kBM));
-    if (c_bf16)
-        hipLaunchKernelGGL((k_gemm<false, false, true>), grid, dim3(256), 0, s, p);
-    else
-        hipLaunchKernelGGL((k_gemm<false, false, false>), grid, dim3(256), 0, s, p);
+    if (fast_path(A, B, K)) {
+        if (c_bf16)
+            hipLaunchKernelGGL((k_gemm_ring<false, false, true>), grid, dim3(256), 0, s, p);
+        else
+            hipLaunchKernelGGL((k_gemm_ring<false, false, false>), grid, dim3(256), 0, s, p);
+    } else {
+        if (c_bf16)
+            hipLaunchKernelGGL((k_gemm<false, false, true, false>), grid, dim3(256), 0, s, p);
+        else
+            hipLaunchKernelGGL((k_gemm<false, false, false, false>), grid, dim3(256), 0, s, p);
+    }
     return hipGetLastError();
 }
 
@@ -310,16 +674,23 @@ hipError_t launch_grouped_gemm(int G, const Operand& A, const int64_t* offsets, 
     GemmArgs p{A, B, total_rows, n_per_group, K, C, ldc, offsets, G, amax_out};
     // every group wastes at most one partial tile
     const int64_t mtiles = cdiv(total_rows, kBM) + G;
+    const bool fast = fast_path(A, B, K);
+#define NVFP4_GROUPED(SW, BF)                                                                   \
+    do {                                                                                        \
+        if (fast)                                                                               \
+            hipLaunchKernelGGL((k_gemm_ring<true, SW, BF>), grid, dim3(256), 0, s, p);         \
+        else                                                                                    \
+            hipLaunchKernelGGL((k_gemm<true, SW, BF, false>), grid, dim3(256), 0, s, p);       \
+    } while (0)
     if (swiglu) {
         dim3 grid((unsigned)cdiv(n_per_group / 2, kBN / 2), (unsigned)mtiles);
-        hipLaunchKernelGGL((k_gemm<true, true, true>), grid, dim3(256), 0, s, p);
+        NVFP4_GROUPED(true, true);
     } else {
         dim3 grid((unsigned)cdiv(n_per_group, kBN), (unsigned)mtiles);
-        if (c_bf16)
-            hipLaunchKernelGGL((k_gemm<true, false, true>), grid, dim3(256), 0, s, p);
-        else
-            hipLaunchKernelGGL((k_gemm<true, false, false>), grid, dim3(256), 0, s, p);
+        if (c_bf16) NVFP4_GROUPED(false, true);
+        else NVFP4_GROUPED(false, false);
     }
+#undef NVFP4_GROUPED
     return hipGetLastError();
 }
 

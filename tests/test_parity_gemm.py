@@ -39,7 +39,8 @@ def quant_host(x, layout, rnd=O.RNE, seed=0):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 16), (32, 32, 64), (100, 70, 80), (130, 260, 1040),
-                                   (300, 128, 4112), (257, 129, 48)])
+                                   (300, 128, 4112), (257, 129, 48), (64, 256, 192), (96, 160, 320),
+                                   (260, 300, 1024)])
 @pytest.mark.parametrize("bmode", [O.ROW_1D, O.BLK_2D])
 @pytest.mark.parametrize("out", ["f32", "bf16"])
 def test_gemm_small(nv, M, N, K, bmode, out):
