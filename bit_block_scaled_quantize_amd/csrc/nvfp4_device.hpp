@@ -66,17 +66,28 @@ __host__ __device__ inline uint32_t hadamard_sign_mask(uint64_t seed) {
            0xFFFFu;
 }
 
-// Device-side Philox rounds kept as a rolled loop (compact code, so that the
-// callers' loops over blocks can be fully unrolled), advancing two counters
-// that share a key in lockstep: two independent multiply chains per round.
+// Three-input XOR in one VALU instruction (gfx950 v_bitop3_b32, truth table
+// 0x96); c is wave-uniform (a Philox round key).
+__device__ __forceinline__ uint32_t xor3_vvs(uint32_t a, uint32_t b, uint32_t c) {
+    uint32_t r;
+    asm("v_bitop3_b32 %0, %1, %2, %3 bitop3:0x96" : "=v"(r) : "v"(a), "v"(b), "s"(c));
+    return r;
+}
+
+// Device-side Philox: two counters that share a key advanced in lockstep
+// (two independent multiply chains per round), fully unrolled, each round's
+// two XORs fused into one instruction.  About 9.3 VALU instructions per round
+// and counter.
 __device__ __forceinline__ void philox4x32_10_pair(uint32_t a[4], uint32_t b[4], uint32_t k0,
                                                    uint32_t k1) {
-#pragma unroll 1
+#pragma unroll
     for (int i = 0; i < 10; ++i) {
         const uint64_t pa0 = (uint64_t)0xD2511F53u * a[0], pa1 = (uint64_t)0xCD9E8D57u * a[2];
         const uint64_t pb0 = (uint64_t)0xD2511F53u * b[0], pb1 = (uint64_t)0xCD9E8D57u * b[2];
-        const uint32_t na0 = (uint32_t)(pa1 >> 32) ^ a[1] ^ k0, na2 = (uint32_t)(pa0 >> 32) ^ a[3] ^ k1;
-        const uint32_t nb0 = (uint32_t)(pb1 >> 32) ^ b[1] ^ k0, nb2 = (uint32_t)(pb0 >> 32) ^ b[3] ^ k1;
+        const uint32_t na0 = xor3_vvs((uint32_t)(pa1 >> 32), a[1], k0);
+        const uint32_t na2 = xor3_vvs((uint32_t)(pa0 >> 32), a[3], k1);
+        const uint32_t nb0 = xor3_vvs((uint32_t)(pb1 >> 32), b[1], k0);
+        const uint32_t nb2 = xor3_vvs((uint32_t)(pb0 >> 32), b[3], k1);
         a[1] = (uint32_t)pa1;
         a[3] = (uint32_t)pa0;
         a[0] = na0;
@@ -225,10 +236,10 @@ __device__ __forceinline__ uint32_t sr_seed(uint32_t word, int high_half) {
 //   SR: y = fl(|t| * R), z = ceil(y * 2^23) carries t's sign, and the SR
 //   convert with scale operand 2^23 (so it sees z * 2^-23, y rounded up to the
 //   2^-23 grid) and seed sr_seed(draw) produces the code.  Each call converts
-//   one value in the instruction's first slot into byte 0 of a fresh register
-//   (the second slot converts +0, so the byte's high nibble is 0; the
-//   compiler does not carry the builtin's `old` operand through, so nothing
-//   else of that register is used); byte permutes then gather the codes of
+//   one value in the instruction's first slot into the low nibble of byte 0
+//   of a fresh register (the second slot's input is left unspecified and the
+//   rest of the register is masked off; the compiler does not carry the
+//   builtin's `old` operand through); byte permutes then gather the codes of
 //   even and odd elements into the low and high nibbles of the output word.
 //   Blocks with R = inf (S below 2^-128), or whose scaled values could
 //   overflow (amax_b * R >= 2^100, possible only with a caller-supplied A_t
@@ -268,8 +279,10 @@ __device__ __forceinline__ void encode(const float* v, BlockScale bs, float amax
             for (int J = 0; J < 4; ++J) {
                 const float z0 = __builtin_ceilf((fabsf(p[2 * J]) * bs.R) * 0x1p23f);
                 const float z1 = __builtin_ceilf((fabsf(p[2 * J + 1]) * bs.R) * 0x1p23f);
-                const f2_t e = {__uint_as_float(__float_as_uint(z0) | (__float_as_uint(p[2 * J]) & 0x80000000u)), 0.0f};
-                const f2_t o = {__uint_as_float(__float_as_uint(z1) | (__float_as_uint(p[2 * J + 1]) & 0x80000000u)), 0.0f};
+                // the second slot's value is left unspecified: its nibble is masked off
+                const float any = __builtin_nondeterministic_value(z0);
+                const f2_t e = {__uint_as_float(__float_as_uint(z0) | (__float_as_uint(p[2 * J]) & 0x80000000u)), any};
+                const f2_t o = {__uint_as_float(__float_as_uint(z1) | (__float_as_uint(p[2 * J + 1]) & 0x80000000u)), any};
                 ce[J] = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, e, sr_seed(wk[J], 0), 0x1p23f, 0);
                 co[J] = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, o, sr_seed(wk[J], 1), 0x1p23f, 0);
             }
