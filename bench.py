@@ -98,7 +98,8 @@ def main():
     ap.add_argument("--kernel-reps", type=int, default=20)
     ap.add_argument("--pmc-driver", action="store_true",
                     help="for rocprofv3 --pmc runs: a 256 MiB device copy (calibration), then each "
-                         "step kernel alone, 3 launches each, and exit")
+                         "step kernel alone, 3 launches each, then (unless --no-gemm) the forward "
+                         "GEMM twice, and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -130,6 +131,11 @@ def main():
     RNE, SR = nv.NVFP4_RNE, nv.NVFP4_SR
     if args.pmc_driver:
         pmc_driver(nv, torch, xs, amax, R, C, R2, C2, Q2d, yr)
+        if not args.no_gemm:
+            del xs
+            torch.cuda.empty_cache()
+            pmc_driver_gemm(nv, W, np, torch)
+        print("pmc driver done", flush=True)
         return
     q1 = E * 2 + E // 2 + E // 16 + 4                    # one layout: bf16 in, codes, scales
     q2 = E * 2 + 2 * (E // 2 + E // 16) + 8              # fused row+column
@@ -178,7 +184,8 @@ def main():
     for name, lay, rnd, b in step_ops:
         out = (R2, C2) if lay == RC else (C if lay == COL else R)
         kern[name] = dict(ms=time_events(qk(lay, rnd, out), reps, torch), bytes=b)
-    kern["quant_2d_rne"] = dict(ms=time_events(qk(nv.NVFP4_BLK_2D, RNE, Q2d), reps, torch), bytes=q1)
+    q2d = E * 2 + E // 2 + E // 256 + 4                  # 2D: one scale byte per 16 x 16 tile
+    kern["quant_2d_rne"] = dict(ms=time_events(qk(nv.NVFP4_BLK_2D, RNE, Q2d), reps, torch), bytes=q2d)
     kern["dequant_row_bf16"] = dict(ms=time_events(lambda i: nv.nvfp4_dequantize(R, out=yr), reps, torch),
                                     bytes=dq)
     amax_ms = time_events(lambda i: nv.nvfp4_quantize(xs[i % NBUF], layout=ROW, out=R, workspace=ws),
@@ -224,15 +231,19 @@ def main():
 
 def pmc_driver(nv, torch, xs, amax, R, C, R2, C2, Q2d, yr):
     """Kernel sequence for hardware-counter runs: the calibration copy first
-    (256 MiB read + 256 MiB written by torch's copy kernel), then every step
-    kernel alone (amax given), three launches each, on distinct inputs."""
-    src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+    (1 GiB read + 1 GiB written by torch's copy kernel, its source evicted
+    from the caches by a 1 GiB fill of another buffer before each copy), then
+    every step kernel alone (amax given), three launches each, on distinct
+    inputs."""
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
+    flush = torch.empty_like(src)
     src.fill_(1)
-    torch.cuda.synchronize()
     for _ in range(3):
+        flush.fill_(2)
         dst.copy_(src)
     torch.cuda.synchronize()
+    del src, dst, flush
     ROW, COL, RC, B2 = nv.NVFP4_ROW_1D, nv.NVFP4_COL_1D, nv.NVFP4_ROW_COL_1D, nv.NVFP4_BLK_2D
     for lay, rnd, out in [(ROW, 0, R), (ROW, 1, R), (COL, 0, C), (COL, 1, C), (RC, 0, (R2, C2)),
                           (RC, 1, (R2, C2)), (B2, 0, Q2d)]:
@@ -242,7 +253,19 @@ def pmc_driver(nv, torch, xs, amax, R, C, R2, C2, Q2d, yr):
     for i in range(3):
         nv.nvfp4_dequantize(R, out=yr)
     torch.cuda.synchronize()
-    print("pmc driver done", flush=True)
+
+
+def pmc_driver_gemm(nv, W, np, torch):
+    """Counter runs of the block-scaled GEMM: the forward shape (8192 x 20480
+    x 5120, BF16 out, 2D-scaled weights), two launches."""
+    X = nv.nvfp4_quantize(bf16_device(W.f32_to_bf16_bits(W.student_t((8192, 5120), 3.0, seed=4000)), torch, np))
+    Wt = nv.nvfp4_quantize(bf16_device(W.f32_to_bf16_bits(W.normal((20480, 5120), 0.02, seed=4001)), torch, np),
+                           layout=nv.NVFP4_BLK_2D)
+    Y = torch.empty((8192, 20480), dtype=torch.bfloat16, device="cuda")
+    torch.cuda.synchronize()
+    for _ in range(2):
+        nv.nvfp4_gemm(X, Wt, out=Y)
+    torch.cuda.synchronize()
 
 
 def bench_gemm(nv, W, np, torch, reps):
