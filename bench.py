@@ -188,6 +188,20 @@ def main():
     kern["quant_2d_rne"] = dict(ms=time_events(qk(nv.NVFP4_BLK_2D, RNE, Q2d), reps, torch), bytes=q2d)
     kern["dequant_row_bf16"] = dict(ms=time_events(lambda i: nv.nvfp4_dequantize(R, out=yr), reps, torch),
                                     bytes=dq)
+    # re-quantization of the row-quantized tensor along columns (not part of the step):
+    # codes + scales in, codes + scales out, 1.125 B/element
+    rq = 2 * (E // 2 + E // 16 + 4)
+    Rq = nv.nvfp4_quantize(xs[0], layout=ROW, round=SR, sr_seed=3)
+    Cq = nv.NVFP4Tensor.empty(N, N, device=dev)
+    ramax = torch.zeros(1, dtype=torch.float32, device=dev)
+    nv.nvfp4_requantize(Rq, out=Cq, amax_out=ramax, workspace=ws)
+    ramax_h = torch.zeros(1, dtype=torch.float32, device=dev)
+    nv.nvfp4_requantize(Rq, out=Cq, hadamard=True, hadamard_seed=4, amax_out=ramax_h, workspace=ws)
+    kern["requant_col_sr"] = dict(ms=time_events(
+        lambda i: nv.nvfp4_requantize(Rq, round=SR, sr_seed=6 + i, amax_in=ramax, out=Cq), reps, torch), bytes=rq)
+    kern["requant_col_sr_hadamard"] = dict(ms=time_events(
+        lambda i: nv.nvfp4_requantize(Rq, round=SR, sr_seed=6 + i, hadamard=True, hadamard_seed=4,
+                                      amax_in=ramax_h, out=Cq), reps, torch), bytes=rq)
     amax_ms = time_events(lambda i: nv.nvfp4_quantize(xs[i % NBUF], layout=ROW, out=R, workspace=ws),
                           reps, torch) - kern["quant_row_rne"]["ms"]
     kern["amax_pass"] = dict(ms=amax_ms, bytes=E * 2)

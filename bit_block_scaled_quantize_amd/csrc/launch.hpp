@@ -28,6 +28,13 @@ hipError_t launch_quantize(const void* x, bool bf16, int64_t rows, int64_t cols,
                            const float* amax_in, float* amax_out, const QOut* out, float* ws,
                            hipStream_t s);
 
+// COL_1D re-quantization of a row-blocked NVFP4 tensor (rows x cols, both
+// multiples of 16); out is cols x rows.
+hipError_t launch_requantize(const uint8_t* icodes, const uint8_t* iscales, const float* its,
+                             int64_t rows, int64_t cols, bool sr, uint64_t seed, bool rht,
+                             uint64_t hseed, const float* amax_in, float* amax_out, const QOut* out,
+                             float* ws, hipStream_t s);
+
 hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, const float* ts,
                              int64_t rows, int64_t cols, bool scale_2d, void* y, bool bf16,
                              int64_t ld, hipStream_t s);

@@ -111,6 +111,34 @@ nvfp4_status nvfp4_quantize(const void* x, nvfp4_dtype dt, int64_t rows, int64_t
     return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
 
+nvfp4_status nvfp4_requantize(const nvfp4_tensor* in, const nvfp4_quant_opts* opts, nvfp4_tensor* out,
+                              void* ws, size_t ws_bytes, void* stream) {
+    if (!in || !opts || !out) return NVFP4_ERR_NULL;
+    if (opts->layout < NVFP4_ROW_1D || opts->layout > NVFP4_BLK_2D) return NVFP4_ERR_ENUM;
+    if (opts->round != NVFP4_RNE && opts->round != NVFP4_SR) return NVFP4_ERR_ENUM;
+    nvfp4_status st = check_operand(in);
+    if (st != NVFP4_OK) return st;
+    if (in->scale_mode != NVFP4_SCALE_1D) return NVFP4_ERR_UNSUPPORTED;
+    if (opts->layout != NVFP4_COL_1D) return NVFP4_ERR_UNSUPPORTED;
+    const int64_t rows = in->rows, cols = in->cols;
+    if (rows % 16) return NVFP4_ERR_SHAPE;
+    st = check_out(out, cols, rows, NVFP4_SCALE_1D);
+    if (st != NVFP4_OK) return st;
+    if (cdiv(rows, 256) > kMaxGridY) return NVFP4_ERR_UNSUPPORTED;
+    const bool empty = rows == 0 || cols == 0;
+    if (!empty && !opts->amax_in) {
+        if (!ws) return NVFP4_ERR_WORKSPACE;
+        if (ws_bytes < kQuantWorkspaceBytes) return NVFP4_ERR_WORKSPACE;
+        if (!aligned(ws, 16)) return NVFP4_ERR_ALIGN;
+    }
+    const QOut o{out->codes, out->scales, out->tensor_scale};
+    hipError_t e = launch_requantize(in->codes, in->scales, in->tensor_scale, rows, cols,
+                                     opts->round == NVFP4_SR, opts->sr_seed, opts->hadamard != 0,
+                                     opts->hadamard_seed, opts->amax_in, opts->amax_out, &o,
+                                     static_cast<float*>(ws), static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
+}
+
 nvfp4_status nvfp4_dequantize(const nvfp4_tensor* q, void* y, nvfp4_dtype dt, int64_t ld,
                               void* stream) {
     if (!q) return NVFP4_ERR_NULL;

@@ -477,6 +477,42 @@ __device__ __forceinline__ TileXY xcd_tile(int xcd_group) {
     return r;
 }
 
+// Column blocks of a staged tile (after the barrier): thread t takes row band
+// t % 16 and 8-byte unit t / 16 (16 rows x UE columns), i.e. UE whole column
+// blocks of the transposed output.
+template <typename T, bool SR, bool RHT>
+__device__ __forceinline__ void tile_col_blocks(const uint8_t* tile, int64_t R0, int64_t C0, int64_t rows,
+                                                int64_t cols, const TensorScale& ts, uint64_t seed,
+                                                uint32_t sign_mask, uint8_t* __restrict__ ccodes,
+                                                uint8_t* __restrict__ cscales) {
+    constexpr int UE = ColTile<T>::UE, STRIDE = ColTile<T>::STRIDE;
+    const int t = threadIdx.x;
+    const int rb = t & 15, u = t >> 4;
+    const int64_t r0 = R0 + 16 * rb;
+    if (r0 >= rows) return;  // rows % 16 == 0: a band is wholly inside or outside (no barrier follows)
+    uint2 q[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+        q[i] = *reinterpret_cast<const uint2*>(tile + (16 * rb + i) * STRIDE + 8 * (u ^ rb));
+#pragma unroll
+    for (int e = 0; e < UE; ++e) {
+        const int64_t c = C0 + UE * u + e;
+        if (c >= cols) continue;  // (not break: the loop must unroll fully)
+        float col[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) col[i] = unit_elem<T>(q[i], e);
+        if (RHT) hadamard16(col, sign_mask);
+        const float ab = absmax16(col);
+        const BlockScale bs = block_scale(ab, ts.six_st, ts.st);
+        uint32_t wd[8];
+        if (SR) philox_words16(seed, kStreamCol, (uint64_t)(c * rows + r0), wd);
+        uint32_t w[2];
+        encode<SR, 16>(col, bs, ab, wd, w);
+        *reinterpret_cast<uint2*>(ccodes + c * (rows / 2) + r0 / 2) = make_uint2(w[0], w[1]);
+        cscales[c * (rows / 16) + r0 / 16] = (uint8_t)bs.byte;
+    }
+}
+
 template <typename T, bool DO_ROW, bool SR, bool RHT>
 __global__ void __launch_bounds__(256) k_quant_colt(const T* __restrict__ x, int64_t rows,
                                                     int64_t cols, int64_t ld,
@@ -518,31 +554,7 @@ __global__ void __launch_bounds__(256) k_quant_colt(const T* __restrict__ x, int
     if (DO_ROW) tile_row_blocks<T, SR>(raw, R0, lr0, gc, rows, cols, ts, seed, rcodes, rscales);
     __syncthreads();
 
-    // ---- column blocks: row band rb, unit u
-    const int rb = t & 15, u = t >> 4;
-    const int64_t r0 = R0 + 16 * rb;
-    if (r0 >= rows) return;  // rows % 16 == 0: a band is wholly inside or outside
-    uint2 q[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-        q[i] = *reinterpret_cast<const uint2*>(tile + (16 * rb + i) * STRIDE + 8 * (u ^ rb));
-#pragma unroll
-    for (int e = 0; e < UE; ++e) {
-        const int64_t c = C0 + UE * u + e;
-        if (c >= cols) continue;  // (not break: the loop must unroll fully)
-        float col[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) col[i] = unit_elem<T>(q[i], e);
-        if (RHT) hadamard16(col, sign_mask);
-        const float ab = absmax16(col);
-        const BlockScale bs = block_scale(ab, ts.six_st, ts.st);
-        uint32_t wd[8];
-        if (SR) philox_words16(seed, kStreamCol, (uint64_t)(c * rows + r0), wd);
-        uint32_t w[2];
-        encode<SR, 16>(col, bs, ab, wd, w);
-        *reinterpret_cast<uint2*>(ccodes + c * (rows / 2) + r0 / 2) = make_uint2(w[0], w[1]);
-        cscales[c * (rows / 16) + r0 / 16] = (uint8_t)bs.byte;
-    }
+    tile_col_blocks<T, SR, RHT>(tile, R0, C0, rows, cols, ts, seed, sign_mask, ccodes, cscales);
 }
 
 // ============================================================ BLK_2D
@@ -656,6 +668,132 @@ __global__ void __launch_bounds__(256) k_dequant(const uint8_t* __restrict__ cod
                 for (int j = 0; j < 4; ++j) qq[j] = make_float4(o[4 * j], o[4 * j + 1], o[4 * j + 2], o[4 * j + 3]);
             }
         }
+    }
+}
+
+// ============================================================ re-quantize
+// Re-quantization of a row-blocked NVFP4 tensor along columns (the backward
+// pass's transposed operand formed from the stored forward tensor, "Thinking
+// Machines ускорила обучение Inkling 2 Small 4-битными числами", iitak.ru,
+// section "Как это работает"): the result equals COL_1D quantization of the
+// binary32 dequantization x = fl(fl(v * e4m3(sb)) * s_t).  The input is read
+// as codes and scale bytes only (0.5625 bytes per element).
+
+// Dequantized values of 8 consecutive elements of one row (one code word, one
+// multiplier), exactly as k_dequant forms them.
+__device__ __forceinline__ void dequant8(uint32_t w, float sv, float st, float v[8]) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const float2 p = e2m1x2_unpack(w, k);
+        v[2 * k] = (p.x * sv) * st;
+        v[2 * k + 1] = (p.y * sv) * st;
+    }
+}
+
+// Partial maxima of |x| (RHT: of the transform of x down columns) over the
+// dequantized tensor.  A thread takes a 16-row band x 8-column group (16 code
+// words and 16 multipliers), groups along a band first.
+template <bool RHT>
+__global__ void __launch_bounds__(256) k_amax_req(const uint8_t* __restrict__ icodes,
+                                                  const uint8_t* __restrict__ iscales,
+                                                  const float* __restrict__ its, int64_t rows,
+                                                  int64_t cols, uint32_t sign_mask,
+                                                  float* __restrict__ partial) {
+    const float st = its[0];
+    const int64_t ng = cols / 8, nunits = (rows / 16) * ng;
+    float a = 0.0f;
+    for (int64_t un = (int64_t)(blockIdx.y * gridDim.x + blockIdx.x) * 256 + threadIdx.x; un < nunits;
+         un += (int64_t)gridDim.x * gridDim.y * 256) {
+        const int64_t band = un / ng, g = un % ng;
+        float v[16][8];
+        uint32_t w[16], sb[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int64_t r = band * 16 + i;
+            w[i] = *reinterpret_cast<const uint32_t*>(icodes + r * (cols / 2) + g * 4);
+            sb[i] = iscales[r * (cols / 16) + g / 2];
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) dequant8(w[i], e4m3_value(sb[i]), st, v[i]);
+        if (RHT) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float col[16];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) col[i] = v[i][e];
+                hadamard16(col, sign_mask);
+                a = fmaxf(a, absmax16(col));
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(v[i][e]));
+        }
+    }
+    store_partial(a, partial);
+}
+
+// Workgroup (x, y) takes rows 256 y .. + 255 and kReqTiles consecutive tiles of
+// 32 columns from 32 kReqTiles x.  Thread t loads row t's codes and
+// multipliers of all its tiles up front, then per tile dequantizes its 32
+// values into binary32 in the LDS layout of the FP32 column tile, and the
+// column phase runs exactly as for FP32 input.
+constexpr int kReqTiles = 4;
+
+template <bool SR, bool RHT>
+__global__ void __launch_bounds__(256) k_requant_col(const uint8_t* __restrict__ icodes,
+                                                     const uint8_t* __restrict__ iscales,
+                                                     const float* __restrict__ its, int64_t rows,
+                                                     int64_t cols, const float* __restrict__ amax_src,
+                                                     int n_part, uint64_t seed, uint32_t sign_mask,
+                                                     uint8_t* __restrict__ ccodes,
+                                                     uint8_t* __restrict__ cscales,
+                                                     float* __restrict__ cts, float* amax_out) {
+    constexpr int STRIDE = ColTile<float>::STRIDE;  // 32 binary32 columns + padding
+    __shared__ __attribute__((aligned(16))) uint8_t tile[256 * STRIDE];
+    const int t = threadIdx.x;
+    const int64_t R0 = (int64_t)blockIdx.y * 256, Cb = (int64_t)blockIdx.x * (32 * kReqTiles);
+    // Rows past the end read a clamped in-range row (their band is never
+    // encoded); a tile with 16 valid columns (cols % 32 == 16) reads its valid
+    // half twice, and tiles past the last column read the last 16 columns
+    // (those copies are never encoded either).
+    const int64_t gr = min(R0 + t, rows - 1);
+    uint2 lo[kReqTiles], hi[kReqTiles];
+    uint32_t s0[kReqTiles], s1[kReqTiles];
+#pragma unroll
+    for (int k = 0; k < kReqTiles; ++k) {
+        const int64_t C0 = Cb + 32 * k;
+        const int64_t cl = C0 < cols ? C0 : cols - 16;
+        const bool two = cl + 32 <= cols;
+        const uint8_t* cp = icodes + gr * (cols / 2) + cl / 2;
+        const uint8_t* sp = iscales + gr * (cols / 16) + cl / 16;
+        lo[k] = *reinterpret_cast<const uint2*>(cp);
+        hi[k] = *reinterpret_cast<const uint2*>(cp + (two ? 8 : 0));
+        s0[k] = sp[0];
+        s1[k] = sp[two ? 1 : 0];
+    }
+    const float st_in = its[0];
+    const TensorScale ts = prologue(amax_src, n_part, cts, nullptr, amax_out);
+    const int sw = (t >> 4) & 15;
+    uint8_t* rowp = tile + t * STRIDE;
+#pragma unroll
+    for (int k = 0; k < kReqTiles; ++k) {
+        const int64_t C0 = Cb + 32 * k;
+        if (C0 >= cols) break;  // uniform across the workgroup
+        if (k > 0) __syncthreads();  // the previous tile's column reads are done
+        float v[32];
+        dequant8(lo[k].x, e4m3_value(s0[k]), st_in, v);
+        dequant8(lo[k].y, e4m3_value(s0[k]), st_in, v + 8);
+        dequant8(hi[k].x, e4m3_value(s1[k]), st_in, v + 16);
+        dequant8(hi[k].y, e4m3_value(s1[k]), st_in, v + 24);
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+            *reinterpret_cast<uint2*>(rowp + 8 * (j ^ sw)) =
+                make_uint2(__float_as_uint(v[2 * j]), __float_as_uint(v[2 * j + 1]));
+        __syncthreads();
+        if (R0 + 16 * (t & 15) < rows)  // (a band past the end: no column work, but stay for the barriers)
+            tile_col_blocks<float, SR, RHT>(tile, R0, C0, rows, cols, ts, seed, sign_mask, ccodes, cscales);
     }
 }
 
@@ -781,6 +919,43 @@ hipError_t launch_quantize(const void* x, bool bf16, int64_t rows, int64_t cols,
                               hseed, amax_in, amax_out, out, ws, s);
     return quantize_typed(static_cast<const float*>(x), rows, cols, ld, layout, sr, seed, rht, hseed,
                           amax_in, amax_out, out, ws, s);
+}
+
+hipError_t launch_requantize(const uint8_t* icodes, const uint8_t* iscales, const float* its,
+                             int64_t rows, int64_t cols, bool sr, uint64_t seed, bool rht,
+                             uint64_t hseed, const float* amax_in, float* amax_out, const QOut* out,
+                             float* ws, hipStream_t s) {
+    const uint32_t mask = rht ? hadamard_sign_mask(hseed) : 0u;
+    if (rows == 0 || cols == 0) {
+        hipLaunchKernelGGL(k_write_tensor_scale, dim3(1), dim3(1), 0, s, amax_in, out->ts, nullptr,
+                           amax_out);
+        return hipGetLastError();
+    }
+    const float* amax = amax_in;
+    int np = 0;
+    if (!amax) {
+        const int64_t units = (rows / 16) * (cols / 8);
+        const unsigned gx = (unsigned)std::max<int64_t>(1, std::min<int64_t>(cdiv(units, 256 * 4), kMaxPartials));
+        if (rht)
+            hipLaunchKernelGGL(k_amax_req<true>, dim3(gx), dim3(256), 0, s, icodes, iscales, its, rows,
+                               cols, mask, ws);
+        else
+            hipLaunchKernelGGL(k_amax_req<false>, dim3(gx), dim3(256), 0, s, icodes, iscales, its, rows,
+                               cols, mask, ws);
+        amax = ws;
+        np = (int)gx;
+    }
+    dim3 g((unsigned)cdiv(cols, 32 * kReqTiles), (unsigned)cdiv(rows, 256));
+#define NVFP4_REQ(SRV, RHTV)                                                                       \
+    hipLaunchKernelGGL((k_requant_col<SRV, RHTV>), g, dim3(256), 0, s, icodes, iscales, its, rows, \
+                       cols, amax, np, seed, mask, out->codes, out->scales, out->ts, amax_out)
+    if (sr) {
+        if (rht) NVFP4_REQ(true, true); else NVFP4_REQ(true, false);
+    } else {
+        if (rht) NVFP4_REQ(false, true); else NVFP4_REQ(false, false);
+    }
+#undef NVFP4_REQ
+    return hipGetLastError();
 }
 
 hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, const float* ts,

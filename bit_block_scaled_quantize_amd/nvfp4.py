@@ -22,8 +22,8 @@ NVFP4_RNE, NVFP4_SR = 0, 1
 NVFP4_EPI_NONE, NVFP4_EPI_SWIGLU = 0, 1
 NVFP4_SCALE_1D, NVFP4_SCALE_2D = 0, 1
 
-EXPORTED = ["nvfp4_quantize_workspace_size", "nvfp4_quantize", "nvfp4_dequantize", "nvfp4_gemm",
-            "nvfp4_grouped_gemm", "nvfp4_status_string", "nvfp4_version"]
+EXPORTED = ["nvfp4_quantize_workspace_size", "nvfp4_quantize", "nvfp4_requantize", "nvfp4_dequantize",
+            "nvfp4_gemm", "nvfp4_grouped_gemm", "nvfp4_status_string", "nvfp4_version"]
 
 
 class CTensor(ctypes.Structure):
@@ -51,6 +51,9 @@ def _load():
     L.nvfp4_quantize.restype = i32
     L.nvfp4_dequantize.argtypes = [ctypes.POINTER(CTensor), vp, i32, i64, vp]
     L.nvfp4_dequantize.restype = i32
+    L.nvfp4_requantize.argtypes = [ctypes.POINTER(CTensor), ctypes.POINTER(CQuantOpts),
+                                   ctypes.POINTER(CTensor), vp, sz, vp]
+    L.nvfp4_requantize.restype = i32
     L.nvfp4_gemm.argtypes = [ctypes.POINTER(CTensor), ctypes.POINTER(CTensor), vp, i32, i64, i32, vp]
     L.nvfp4_gemm.restype = i32
     L.nvfp4_grouped_gemm.argtypes = [i32, ctypes.POINTER(CTensor), vp, ctypes.POINTER(CTensor), vp,
@@ -165,6 +168,28 @@ def nvfp4_quantize(x, layout=NVFP4_ROW_1D, round=NVFP4_RNE, sr_seed=0, hadamard=
                             ctypes.byref(opts), arr, _ptr(workspace), ws_bytes, _stream(stream))
     _check("nvfp4_quantize", st)
     return tuple(outs) if layout == NVFP4_ROW_COL_1D else outs[0]
+
+
+def nvfp4_requantize(q, round=NVFP4_RNE, sr_seed=0, hadamard=False, hadamard_seed=0, amax_in=None,
+                     out=None, workspace=None, amax_out=None, stream=None):
+    """COL_1D re-quantization of a row-blocked NVFP4Tensor q (rows x cols):
+    returns the cols x rows NVFP4Tensor that quantizing q's binary32
+    dequantization along columns gives."""
+    dev = q.codes.device
+    if out is None:
+        out = NVFP4Tensor.empty(q.cols, q.rows, NVFP4_SCALE_1D, dev)
+    opts = CQuantOpts(NVFP4_COL_1D, round, sr_seed, int(bool(hadamard)), hadamard_seed,
+                      None if amax_in is None else amax_in.data_ptr(),
+                      None if amax_out is None else amax_out.data_ptr())
+    need = int(lib.nvfp4_quantize_workspace_size(q.rows, q.cols, ctypes.byref(opts)))
+    if workspace is None and need:
+        workspace = torch.empty((need + 15) // 16 * 4, dtype=torch.float32, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    ci, co = q.c(), out.c()
+    st = lib.nvfp4_requantize(ctypes.byref(ci), ctypes.byref(opts), ctypes.byref(co), _ptr(workspace),
+                              ws_bytes, _stream(stream))
+    _check("nvfp4_requantize", st)
+    return out
 
 
 def nvfp4_dequantize(q, dtype=torch.float32, out=None, stream=None):

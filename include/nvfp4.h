@@ -161,6 +161,23 @@ nvfp4_status nvfp4_quantize(const void* x, nvfp4_dtype dt, int64_t rows, int64_t
 nvfp4_status nvfp4_dequantize(const nvfp4_tensor* q, void* y, nvfp4_dtype dt, int64_t ld,
                               void* stream);
 
+/* Re-quantize a row-blocked NVFP4 tensor `in` (rows x cols, SCALE_1D) along
+ * columns: out (cols x rows, SCALE_1D) receives exactly what nvfp4_quantize
+ * with layout COL_1D would produce from the binary32 dequantization of `in`
+ * (the values nvfp4_dequantize writes for dtype F32), reading only the codes
+ * and scale bytes.  opts: layout must be NVFP4_COL_1D (others return
+ * UNSUPPORTED); round, sr_seed, hadamard (along columns), hadamard_seed,
+ * amax_in and amax_out as for nvfp4_quantize, where the amax is that of the
+ * dequantized tensor (after the transform when hadamard is set).
+ * Requirements: rows % 16 == 0, cols % 16 == 0, in->codes and out->codes
+ * 16-byte aligned; ws as for nvfp4_quantize (nvfp4_quantize_workspace_size).
+ * rows == 0 or cols == 0 only writes out->tensor_scale.  Errors as for
+ * nvfp4_quantize.
+ * Source: iitak.ru page, "Как это работает" (row blocks of the forward
+ * tensor re-formed along columns for the backward pass). */
+nvfp4_status nvfp4_requantize(const nvfp4_tensor* in, const nvfp4_quant_opts* opts, nvfp4_tensor* out,
+                              void* ws, size_t ws_bytes, void* stream);
+
 /* C = A * B^T for A (M x K) and B (N x K) NVFP4 tensors, accumulated in
  * binary32 over exactly dequantized products; C (M x N, row stride ldc
  * elements, dtype c_dt) = (s_A * s_B) * sum_k (v_A sb_A)(v_B sb_B).

@@ -214,6 +214,19 @@ def dequantize(q, out_dtype=F32):
     return out
 
 
+def requantize(q, rnd=RNE, sr_seed=0, hadamard=False, hadamard_seed=0, amax_in=None, index_base=0):
+    """Re-quantization of a row-blocked QTensor along columns: the backward
+    pass forms column blocks from the stored forward tensor ("Thinking
+    Machines ускорила обучение Inkling 2 Small 4-битными числами", iitak.ru,
+    section "Как это работает").  It is the COL_1D quantization of the
+    binary32 dequantization, written as exactly that composition (no
+    arithmetic of its own)."""
+    assert q.scale_mode == SCALE_1D
+    x = dequantize(q, F32)
+    return quantize(x, F32, COL_1D, rnd, sr_seed=sr_seed, hadamard=hadamard,
+                    hadamard_seed=hadamard_seed, amax_in=amax_in, index_base=index_base)
+
+
 def dequantize_f64(q):
     out = np.zeros((q.rows, q.cols), dtype=np.float64)
     lib().orc_dequantize_f64(_p(q.codes, ctypes.c_uint8), _p(q.scales, ctypes.c_uint8),

@@ -98,6 +98,28 @@ def test_dequantize_rejects_bad_arguments(nv):
     assert nv.lib.nvfp4_dequantize(ctypes.byref(bad2), 65536, 0, 32, None) == 3
 
 
+def test_requantize_rejects_bad_arguments(nv):
+    def call(q, layout=1, rnd=0, out=None, ws=1 << 20, ws_bytes=1 << 20, amax=None):
+        o = nv.CQuantOpts(layout, rnd, 1, 0, 2, amax, None)
+        out = _t(q.cols, q.rows) if out is None else out
+        return nv.lib.nvfp4_requantize(ctypes.byref(q), ctypes.byref(o), ctypes.byref(out), ws, ws_bytes,
+                                       None)
+
+    q = _t(64, 32)
+    o = nv.CQuantOpts(1, 0, 1, 0, 2, None, None)
+    assert nv.lib.nvfp4_requantize(None, ctypes.byref(o), ctypes.byref(_t(32, 64)), 1 << 20, 1 << 20,
+                                   None) == 1
+    assert call(q, layout=7) == 2
+    assert call(q, rnd=5) == 2
+    assert call(q, layout=0) == 5                     # only COL_1D re-quantization
+    assert call(_t(64, 32, 1)) == 5                   # input must carry row-block scales
+    assert call(_t(40, 32)) == 3                      # rows % 16
+    assert call(q, out=_t(64, 32)) == 3               # output is cols x rows
+    assert call(q, out=_t(32, 64, codes=4100)) == 4
+    assert call(q, ws=None) == 6
+    assert call(q, ws_bytes=16) == 6
+
+
 def test_gemm_rejects_bad_arguments(nv):
     a, b = _t(64, 64), _t(32, 64)
     g = nv.lib.nvfp4_gemm

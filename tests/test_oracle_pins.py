@@ -492,3 +492,37 @@ def test_swiglu_closed_forms():
     ref = g * expit(g) * u
     assert np.allclose(O.swiglu(g, u), ref, rtol=1e-14, atol=0)
     assert O.swiglu(0.0, 7.0) == 0.0
+
+
+@pytest.mark.parametrize("rnd", [O.RNE, O.SR])
+def test_requantize_of_grid_exact_tensor_is_the_transpose(rnd):
+    """Re-quantization along columns (iitak.ru page, "Как это работает"):
+    for a tensor whose values lie on the E2M1 grid and in which every
+    16-element row block and column block holds a +-6, with A_t = 2688 the
+    multipliers are all 1 (byte 0x38) and every value is exact, so the row
+    quantization stores x exactly, its dequantization gives x back, and the
+    column re-quantization must store x transposed: its code nibbles are the
+    transpose of the row codes' nibbles.  Stochastic rounding has fraction 0
+    everywhere and must agree."""
+    rng = np.random.default_rng(7)
+    grid = np.array([0, .5, 1, 1.5, 2, 3, 4, 6], dtype=np.float32)
+    rows, cols = 48, 64
+    x = grid[rng.integers(0, 8, size=(rows, cols))] * np.where(rng.random((rows, cols)) < 0.5, -1, 1)
+    x = x.astype(np.float32)
+    for i in range(rows):                      # a +-6 in every row block and every column block
+        for b in range(cols // 16):
+            x[i, 16 * b + (i + 5 * b) % 16] = 6.0 if (i + b) % 2 else -6.0
+    q = O.quantize(x, O.F32, O.ROW_1D, O.RNE, amax_in=2688.0)
+    assert np.all(q.scales == 0x38)
+    assert np.array_equal(O.dequantize(q, O.F32), x)
+    r = O.requantize(q, rnd, sr_seed=3, amax_in=2688.0)
+    assert (r.rows, r.cols) == (cols, rows)
+    assert np.all(r.scales == 0x38)
+
+    def nibbles(c):
+        n = np.empty((c.shape[0], 2 * c.shape[1]), dtype=np.uint8)
+        n[:, 0::2], n[:, 1::2] = c & 15, c >> 4
+        return n
+
+    assert np.array_equal(nibbles(r.codes), nibbles(q.codes).T)
+
