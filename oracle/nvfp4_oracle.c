@@ -448,3 +448,143 @@ void orc_gemm(const uint8_t* a_codes, const uint8_t* a_scales, double a_ts, int 
 double orc_swiglu(double g, double u) {
     return g / (1.0 + exp(-g)) * u;
 }
+
+/* ========================================================================
+ * MX formats (OCP Microscaling).
+ *
+ * The pages name MXFP8 (the backward pass at Thinking Machines runs in it:
+ * P3 "Как это работает"; Blackwell tensor cores support MXFP8/MXFP6/MXFP4:
+ * P2 "NVFP4 и Blackwell"), MXFP4 (the Open Compute Project's 4-bit format
+ * NVFP4 is compared with: P1; P2 "Эксперименты и сравнение с FP8") and an
+ * 8.25-bit transit format for expert outputs (P3 "Но"), but define none of
+ * them.  The reading here is the OCP Microscaling definition: blocks of 32
+ * consecutive elements along the block dimension share one E8M0 scale
+ * X = 2^s, s = floor(log2(max |V|)) - emax (emax = 8 for E4M3 elements,
+ * 2 for E2M1), clamped to [-127, 127] (s = -127 for an all-zero block);
+ * element P = round(V / X) onto the element format with saturation at its
+ * largest finite value (448 or 6).  As for NVFP4 every step is binary32 with
+ * one rounding: y = fl(|V| * 2^-s) (a multiply by an exact power of two),
+ * then y is rounded to nearest-even or stochastically with a 16-bit Philox
+ * draw (round up iff r16 < f * 2^16, f the position of y between its grid
+ * neighbours), the sign copied.  The 8-bit element and 8-bit scale per 32
+ * give 8 + 8/32 = 8.25 bits per number (P3 "Но").
+ * ====================================================================== */
+
+/* floor(log2(a)) - emax clamped to [-127, 127]; -127 when a == 0. */
+int orc_mx_scale_exp(float amax, int elem) {
+    if (!(amax > 0.0f)) return -127;
+    int e;
+    frexpf(amax, &e);                      /* amax = f * 2^e, f in [0.5, 1) */
+    int s = (e - 1) - (elem == ORC_MX_FP8 ? 8 : 2);
+    if (s < -127) s = -127;
+    if (s > 127) s = 127;
+    return s;
+}
+
+/* E4M3 stochastic rounding of y >= 0 (y >= 448 saturates to 0x7E): lo = the
+ * largest finite E4M3 value <= y (found by a plain search over the codes),
+ * hi the next one, round up iff r16 < f * 2^16.  Exact in binary64. */
+uint32_t orc_e4m3_sr(float yf, uint32_t r16) {
+    double y = (double)yf;
+    if (y >= 448.0) return 0x7Eu;
+    uint32_t lo = 0;
+    for (uint32_t b = 1; b <= 0x7Eu; ++b)
+        if (orc_e4m3_value(b) <= y) lo = b;
+    double vlo = orc_e4m3_value(lo), vhi = orc_e4m3_value(lo + 1);
+    double f = (y - vlo) / (vhi - vlo);
+    return ((double)r16 < f * 65536.0) ? lo + 1 : lo;
+}
+
+/* Value of an MX element code: E4M3 byte (sign in bit 7) or E2M1 nibble. */
+double orc_mx_elem_value(uint32_t code, int elem) {
+    if (elem == ORC_MX_FP8) {
+        double v = orc_e4m3_value(code & 0x7Fu);
+        return (code & 0x80u) ? -v : v;
+    }
+    return (double)orc_e2m1_value(code & 15u);
+}
+
+static uint32_t mx_encode(float v, float p2, int elem, int round, uint64_t seed, uint32_t stream,
+                          uint64_t index) {
+    float y = fabsf(v) * p2;
+    uint32_t r16 = round == ORC_SR ? orc_draw16(seed, stream, index) : 0u;
+    if (elem == ORC_MX_FP8) {
+        uint32_t sign = signbit(v) ? 0x80u : 0u;
+        uint32_t mag = round == ORC_SR ? orc_e4m3_sr(y, r16) : orc_e4m3_encode(y);
+        return sign | mag;
+    }
+    uint32_t sign = signbit(v) ? 8u : 0u;
+    return sign | (round == ORC_SR ? orc_e2m1_sr(y, r16) : orc_e2m1_rne(y));
+}
+
+int orc_mx_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld, int layout,
+                    int elem, int round, uint64_t seed, uint64_t index_base, uint8_t* codes,
+                    uint8_t* scales) {
+    if (layout != ORC_ROW_1D && layout != ORC_COL_1D) return 1;
+    if (elem != ORC_MX_FP8 && elem != ORC_MX_FP4) return 2;
+    const int transpose = layout == ORC_COL_1D;
+    const int64_t R = transpose ? cols : rows, C = transpose ? rows : cols;
+    if (C % 32) return 3;
+    float* t = oriented(x, dtype, rows, cols, ld, transpose, 0, 0);
+    if (!t) return 4;
+    const uint32_t stream = transpose ? ORC_STREAM_MX_COL : ORC_STREAM_MX_ROW;
+    for (int64_t r = 0; r < R; ++r) {
+        for (int64_t c0 = 0; c0 < C; c0 += 32) {
+            float ab = 0.0f;
+            for (int64_t c = c0; c < c0 + 32; ++c) ab = fmaxf(ab, fabsf(t[r * C + c]));
+            int s = orc_mx_scale_exp(ab, elem);
+            scales[r * (C / 32) + c0 / 32] = (uint8_t)(s + 127);
+            float p2 = ldexpf(1.0f, -s);   /* exact: 2^-127 .. 2^127 */
+            for (int64_t c = c0; c < c0 + 32; ++c) {
+                uint32_t code = mx_encode(t[r * C + c], p2, elem, round, seed, stream,
+                                          index_base + (uint64_t)(r * C + c));
+                if (elem == ORC_MX_FP8) codes[r * C + c] = (uint8_t)code;
+                else put_code(codes, C, r, c, code);
+            }
+        }
+    }
+    free(t);
+    return 0;
+}
+
+static double mx_deq(const uint8_t* codes, const uint8_t* scales, int elem, int64_t cols, int64_t r,
+                     int64_t c) {
+    uint32_t code = elem == ORC_MX_FP8 ? codes[r * cols + c] : get_code(codes, cols, r, c);
+    int s = (int)scales[r * (cols / 32) + c / 32] - 127;
+    return ldexp(orc_mx_elem_value(code, elem), s);   /* exact */
+}
+
+/* out: rows x cols, ORC_F32 (the exact value, which binary32 holds), ORC_BF16
+ * (nearest-even of that value) or float64 when out_dtype == 2. */
+void orc_mx_dequantize(const uint8_t* codes, const uint8_t* scales, int elem, int64_t rows,
+                       int64_t cols, void* out, int out_dtype) {
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < cols; ++c) {
+            double v = mx_deq(codes, scales, elem, cols, r, c);
+            if (out_dtype == 2) ((double*)out)[r * cols + c] = v;
+            else if (out_dtype == ORC_BF16) ((uint16_t*)out)[r * cols + c] = f32_to_bf16_rne((float)v);
+            else ((float*)out)[r * cols + c] = (float)v;
+        }
+}
+
+/* C[m,n] = sum_k A[m,k] B[n,k] over exactly dequantized MX operands (the
+ * block-scaled MMA the pages describe for Blackwell, P2 "NVFP4 и
+ * Blackwell"), float64, natural k order; W = sum |a b|; entries as orc_gemm. */
+void orc_mx_gemm(const uint8_t* a_codes, const uint8_t* a_scales, int a_elem, const uint8_t* b_codes,
+                 const uint8_t* b_scales, int b_elem, int64_t M, int64_t N, int64_t K,
+                 const int64_t* entries_m, const int64_t* entries_n, int64_t n_entries, double* C,
+                 double* W) {
+    int64_t count = n_entries >= 0 ? n_entries : M * N;
+    for (int64_t i = 0; i < count; ++i) {
+        int64_t m = n_entries >= 0 ? entries_m[i] : i / N;
+        int64_t n = n_entries >= 0 ? entries_n[i] : i % N;
+        double acc = 0.0, wacc = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            double p = mx_deq(a_codes, a_scales, a_elem, K, m, k) * mx_deq(b_codes, b_scales, b_elem, K, n, k);
+            acc += p;
+            wacc += fabs(p);
+        }
+        C[i] = acc;
+        W[i] = wacc;
+    }
+}

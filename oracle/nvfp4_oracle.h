@@ -37,6 +37,10 @@
  *   - the Hadamard transform is the 16-point Sylvester matrix scaled by 1/4,
  *     applied after a per-tensor vector of 16 seeded random signs.
  *
+ * The MX formats (MXFP8 / MXFP4, and the 8.25-bit transit format) that the
+ * pages name without defining follow the OCP Microscaling definition; see the
+ * MX section of nvfp4_oracle.c.
+ *
  * Parity status of each function is recorded next to it.
  */
 #ifndef NVFP4_ORACLE_H
@@ -114,6 +118,27 @@ void orc_gemm(const uint8_t* a_codes, const uint8_t* a_scales, double a_ts, int 
 
 /* SwiGLU on float64: h = g * sigmoid(g) * u. */
 double orc_swiglu(double g, double u);
+
+/* ---- MX formats (OCP Microscaling; the reading for MXFP8 / MXFP4 and the
+ * 8.25-bit transit format): 32-element blocks, E8M0 scale 2^s per block,
+ * E4M3 or E2M1 elements; see nvfp4_oracle.c. ------------------------------ */
+enum { ORC_MX_FP8 = 0, ORC_MX_FP4 = 1 };
+enum { ORC_STREAM_MX_ROW = 4, ORC_STREAM_MX_COL = 5 };
+int orc_mx_scale_exp(float amax, int elem);
+uint32_t orc_e4m3_sr(float y, uint32_t r16);       /* y >= 0 -> E4M3 byte 0..0x7E */
+double orc_mx_elem_value(uint32_t code, int elem);
+/* ROW_1D: codes rows x cols (FP8, one byte each) or rows x cols/2 (FP4),
+ * scales rows x cols/32; COL_1D describes the transpose.  Returns 0 on
+ * success. */
+int orc_mx_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld, int layout,
+                    int elem, int round, uint64_t seed, uint64_t index_base, uint8_t* codes,
+                    uint8_t* scales);
+void orc_mx_dequantize(const uint8_t* codes, const uint8_t* scales, int elem, int64_t rows,
+                       int64_t cols, void* out, int out_dtype);
+void orc_mx_gemm(const uint8_t* a_codes, const uint8_t* a_scales, int a_elem, const uint8_t* b_codes,
+                 const uint8_t* b_scales, int b_elem, int64_t M, int64_t N, int64_t K,
+                 const int64_t* entries_m, const int64_t* entries_n, int64_t n_entries, double* C,
+                 double* W);
 
 #ifdef __cplusplus
 }

@@ -21,6 +21,8 @@ ROW_1D, COL_1D, ROW_COL_1D, BLK_2D = 0, 1, 2, 3
 RNE, SR = 0, 1
 SCALE_1D, SCALE_2D = 0, 1
 STREAM_ROW, STREAM_COL, STREAM_2D, STREAM_RHT = 0, 1, 2, 3
+MX_FP8, MX_FP4 = 0, 1
+STREAM_MX_ROW, STREAM_MX_COL = 4, 5
 
 _lib = None
 
@@ -78,6 +80,23 @@ def lib():
         L.orc_gemm.restype = None
         L.orc_swiglu.argtypes = [ctypes.c_double, ctypes.c_double]
         L.orc_swiglu.restype = ctypes.c_double
+        L.orc_mx_scale_exp.argtypes = [ctypes.c_float, ctypes.c_int]
+        L.orc_mx_scale_exp.restype = ctypes.c_int
+        L.orc_e4m3_sr.argtypes = [ctypes.c_float, ctypes.c_uint32]
+        L.orc_e4m3_sr.restype = ctypes.c_uint32
+        L.orc_mx_elem_value.argtypes = [ctypes.c_uint32, ctypes.c_int]
+        L.orc_mx_elem_value.restype = ctypes.c_double
+        L.orc_mx_quantize.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+                                      ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_uint64, ctypes.c_uint64, u8p, u8p]
+        L.orc_mx_quantize.restype = ctypes.c_int
+        L.orc_mx_dequantize.argtypes = [u8p, u8p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+                                        ctypes.c_void_p, ctypes.c_int]
+        L.orc_mx_dequantize.restype = None
+        L.orc_mx_gemm.argtypes = [u8p, u8p, ctypes.c_int, u8p, u8p, ctypes.c_int,
+                                  ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                  i64p, i64p, ctypes.c_int64, f64p, f64p]
+        L.orc_mx_gemm.restype = None
         _lib = L
     return _lib
 
@@ -309,3 +328,63 @@ def swiglu(g, u):
     for i, (a, b) in enumerate(zip(g.ravel(), u.ravel())):
         out.flat[i] = f(float(a), float(b))
     return out
+
+
+# ---------------------------------------------------------------- MX formats
+class MXTensor:
+    """MX tensor: codes (FP8: rows x cols bytes; FP4: rows x cols/2), E8M0
+    scales rows x cols/32, element format elem (MX_FP8 or MX_FP4)."""
+
+    def __init__(self, codes, scales, rows, cols, elem):
+        self.codes, self.scales = codes, scales
+        self.rows, self.cols, self.elem = rows, cols, elem
+
+
+def mx_quantize(x, dtype, layout, elem, rnd=RNE, seed=0, index_base=0):
+    """OCP-MX quantization (E8M0 scale per 32 along the block dimension) of
+    x (numpy float32, or uint16 bf16 bits); layout ROW_1D or COL_1D (the
+    result describes the transpose)."""
+    x = np.ascontiguousarray(x)
+    rows, cols = x.shape
+    assert x.dtype == (np.uint16 if dtype == BF16 else np.float32)
+    r, c = (cols, rows) if layout == COL_1D else (rows, cols)
+    codes = np.zeros((r, c if elem == MX_FP8 else c // 2), dtype=np.uint8)
+    scales = np.zeros((r, c // 32), dtype=np.uint8)
+    rc = lib().orc_mx_quantize(x.ctypes.data_as(ctypes.c_void_p), dtype, rows, cols, cols, layout,
+                               elem, rnd, ctypes.c_uint64(seed), ctypes.c_uint64(index_base),
+                               _p(codes, ctypes.c_uint8), _p(scales, ctypes.c_uint8))
+    if rc != 0:
+        raise ValueError(f"oracle mx_quantize rejected the request (code {rc})")
+    return MXTensor(codes, scales, r, c, elem)
+
+
+def mx_dequantize(q, out_dtype=F32):
+    """out_dtype F32, BF16 (uint16 bits) or 2 (float64, exact)."""
+    dt = {F32: np.float32, BF16: np.uint16, 2: np.float64}[out_dtype]
+    out = np.zeros((q.rows, q.cols), dtype=dt)
+    lib().orc_mx_dequantize(_p(q.codes, ctypes.c_uint8), _p(q.scales, ctypes.c_uint8), q.elem,
+                            q.rows, q.cols, out.ctypes.data_as(ctypes.c_void_p), out_dtype)
+    return out
+
+
+def mx_gemm(A, B, entries=None):
+    """C = A B^T over exactly dequantized MX operands in float64; (C, W) as gemm."""
+    assert A.cols == B.cols
+    M, N, K = A.rows, B.rows, A.cols
+    if entries is None:
+        C = np.zeros((M, N), dtype=np.float64)
+        W = np.zeros((M, N), dtype=np.float64)
+        em = en = ctypes.POINTER(ctypes.c_int64)()
+        ne = -1
+    else:
+        mi = np.ascontiguousarray(entries[0], dtype=np.int64)
+        ni = np.ascontiguousarray(entries[1], dtype=np.int64)
+        ne = mi.size
+        C = np.zeros(ne, dtype=np.float64)
+        W = np.zeros(ne, dtype=np.float64)
+        em, en = _p(mi, ctypes.c_int64), _p(ni, ctypes.c_int64)
+    lib().orc_mx_gemm(_p(A.codes, ctypes.c_uint8), _p(A.scales, ctypes.c_uint8), A.elem,
+                      _p(B.codes, ctypes.c_uint8), _p(B.scales, ctypes.c_uint8), B.elem,
+                      M, N, K, em, en, ne, _p(C, ctypes.c_double), _p(W, ctypes.c_double))
+    return C, W
+
