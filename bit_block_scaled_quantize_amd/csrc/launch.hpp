@@ -11,6 +11,9 @@ namespace nvfp4 {
 
 enum { kLayoutRow = 0, kLayoutCol = 1, kLayoutRowCol = 2, kLayout2D = 3 };
 
+// MX element formats (nvfp4_mx_elem).
+enum { kMxE4M3 = 0, kMxE2M1 = 1 };
+
 // Upper bound on the per-workgroup partial maxima of one amax pass; the
 // quantize workspace holds exactly these floats, and every quantize
 // workgroup reduces them in its prologue.
@@ -57,5 +60,14 @@ hipError_t launch_grouped_gemm(int G, const Operand& A, const int64_t* offsets, 
                                const Operand& B, int64_t n_per_group, int64_t K, void* C,
                                bool c_bf16, int64_t ldc, bool swiglu, float* amax_out,
                                hipStream_t s);
+
+// MX quantization (layout kLayoutRow or kLayoutCol; the block dimension is a
+// multiple of 32) into codes / E8M0 scales of the output orientation.
+hipError_t launch_mx_quantize(const void* x, bool bf16, int64_t rows, int64_t cols, int64_t ld, int layout,
+                              int elem, bool sr, uint64_t seed, uint8_t* codes, uint8_t* scales,
+                              hipStream_t s);
+
+hipError_t launch_mx_dequantize(const uint8_t* codes, const uint8_t* scales, int elem, int64_t rows,
+                                int64_t cols, void* y, bool bf16, int64_t ld, hipStream_t s);
 
 }  // namespace nvfp4

@@ -213,6 +213,49 @@ nvfp4_status nvfp4_grouped_gemm(int32_t G, const nvfp4_tensor* A, const int64_t*
     return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
 
+// ---------------------------------------------------------------- MX formats
+nvfp4_status nvfp4_mx_quantize(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols, int64_t ld,
+                               nvfp4_layout layout, nvfp4_round round, uint64_t sr_seed,
+                               nvfp4_mx_tensor* out, void* stream) {
+    if (!out) return NVFP4_ERR_NULL;
+    if (!valid_dtype(dt)) return NVFP4_ERR_ENUM;
+    if (layout < NVFP4_ROW_1D || layout > NVFP4_BLK_2D) return NVFP4_ERR_ENUM;
+    if (round != NVFP4_RNE && round != NVFP4_SR) return NVFP4_ERR_ENUM;
+    if (out->elem != NVFP4_MX_E4M3 && out->elem != NVFP4_MX_E2M1) return NVFP4_ERR_ENUM;
+    if (layout != NVFP4_ROW_1D && layout != NVFP4_COL_1D) return NVFP4_ERR_UNSUPPORTED;
+    if (rows < 0 || cols < 0 || ld < cols) return NVFP4_ERR_SHAPE;
+    const bool col = layout == NVFP4_COL_1D;
+    if ((col ? rows : cols) % 32) return NVFP4_ERR_SHAPE;
+    const int64_t orows = col ? cols : rows, ocols = col ? rows : cols;
+    if (out->rows != orows || out->cols != ocols) return NVFP4_ERR_SHAPE;
+    const bool empty = rows == 0 || cols == 0;
+    if (!empty && (!x || !out->codes || !out->scales)) return NVFP4_ERR_NULL;
+    if (!aligned(x, 16) || (ld * (int64_t)dtype_size(dt)) % 16 || !aligned(out->codes, 16))
+        return NVFP4_ERR_ALIGN;
+    if (col ? cdiv(rows, 256) > kMaxGridY : cdiv(cols, 512) > 0x7FFFFFFF) return NVFP4_ERR_UNSUPPORTED;
+    hipError_t e = launch_mx_quantize(x, dt == NVFP4_BF16, rows, cols, ld, col ? kLayoutCol : kLayoutRow,
+                                      out->elem == NVFP4_MX_E4M3 ? kMxE4M3 : kMxE2M1, round == NVFP4_SR,
+                                      sr_seed, out->codes, out->scales, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
+}
+
+nvfp4_status nvfp4_mx_dequantize(const nvfp4_mx_tensor* q, void* y, nvfp4_dtype dt, int64_t ld,
+                                 void* stream) {
+    if (!q) return NVFP4_ERR_NULL;
+    if (!valid_dtype(dt)) return NVFP4_ERR_ENUM;
+    if (q->elem != NVFP4_MX_E4M3 && q->elem != NVFP4_MX_E2M1) return NVFP4_ERR_ENUM;
+    if (q->rows < 0 || q->cols < 0 || q->cols % 32 || ld < q->cols) return NVFP4_ERR_SHAPE;
+    const bool empty = q->rows == 0 || q->cols == 0;
+    if (!empty && (!y || !q->codes || !q->scales)) return NVFP4_ERR_NULL;
+    if (!aligned(y, 16) || (ld * (int64_t)dtype_size(dt)) % 16 || !aligned(q->codes, 16))
+        return NVFP4_ERR_ALIGN;
+    if (cdiv(q->cols / 16, 64) > 0x7FFFFFFF) return NVFP4_ERR_UNSUPPORTED;
+    hipError_t e = launch_mx_dequantize(q->codes, q->scales, q->elem == NVFP4_MX_E4M3 ? kMxE4M3 : kMxE2M1,
+                                        q->rows, q->cols, y, dt == NVFP4_BF16, ld,
+                                        static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
+}
+
 const char* nvfp4_status_string(nvfp4_status s) {
     switch (s) {
         case NVFP4_OK: return "ok";

@@ -21,15 +21,22 @@ NVFP4_ROW_1D, NVFP4_COL_1D, NVFP4_ROW_COL_1D, NVFP4_BLK_2D = 0, 1, 2, 3
 NVFP4_RNE, NVFP4_SR = 0, 1
 NVFP4_EPI_NONE, NVFP4_EPI_SWIGLU = 0, 1
 NVFP4_SCALE_1D, NVFP4_SCALE_2D = 0, 1
+NVFP4_MX_E4M3, NVFP4_MX_E2M1 = 0, 1
 
 EXPORTED = ["nvfp4_quantize_workspace_size", "nvfp4_quantize", "nvfp4_requantize", "nvfp4_dequantize",
-            "nvfp4_gemm", "nvfp4_grouped_gemm", "nvfp4_status_string", "nvfp4_version"]
+            "nvfp4_gemm", "nvfp4_grouped_gemm", "nvfp4_mx_quantize", "nvfp4_mx_dequantize",
+            "nvfp4_status_string", "nvfp4_version"]
 
 
 class CTensor(ctypes.Structure):
     _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
                 ("tensor_scale", ctypes.c_void_p), ("rows", ctypes.c_int64),
                 ("cols", ctypes.c_int64), ("scale_mode", ctypes.c_int32)]
+
+
+class CMXTensor(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("rows", ctypes.c_int64),
+                ("cols", ctypes.c_int64), ("elem", ctypes.c_int32)]
 
 
 class CQuantOpts(ctypes.Structure):
@@ -59,6 +66,11 @@ def _load():
     L.nvfp4_grouped_gemm.argtypes = [i32, ctypes.POINTER(CTensor), vp, ctypes.POINTER(CTensor), vp,
                                      i32, i64, i32, vp, vp, sz, vp]
     L.nvfp4_grouped_gemm.restype = i32
+    L.nvfp4_mx_quantize.argtypes = [vp, i32, i64, i64, i64, i32, i32, ctypes.c_uint64,
+                                    ctypes.POINTER(CMXTensor), vp]
+    L.nvfp4_mx_quantize.restype = i32
+    L.nvfp4_mx_dequantize.argtypes = [ctypes.POINTER(CMXTensor), vp, i32, i64, vp]
+    L.nvfp4_mx_dequantize.restype = i32
     L.nvfp4_status_string.argtypes = [i32]
     L.nvfp4_status_string.restype = ctypes.c_char_p
     L.nvfp4_version.argtypes = []
@@ -234,4 +246,56 @@ def nvfp4_grouped_gemm(A, offsets, B, groups, epilogue=NVFP4_EPI_NONE, out_dtype
                                 _dtype_code(out.dtype), ldc, epilogue, _ptr(amax_out), None, 0,
                                 _stream(stream))
     _check("nvfp4_grouped_gemm", st)
+    return out
+
+
+# ---------------------------------------------------------------- MX formats
+@dataclass
+class MXTensor:
+    """codes uint8 ([rows, cols] for E4M3, [rows, cols/2] for E2M1) and E8M0
+    scales uint8 [rows, cols/32] -- device tensors."""
+    codes: torch.Tensor
+    scales: torch.Tensor
+    rows: int
+    cols: int
+    elem: int = NVFP4_MX_E4M3
+
+    def c(self):
+        return CMXTensor(self.codes.data_ptr(), self.scales.data_ptr(), self.rows, self.cols, self.elem)
+
+    @staticmethod
+    def empty(rows, cols, elem=NVFP4_MX_E4M3, device="cuda"):
+        codes = torch.empty((rows, cols if elem == NVFP4_MX_E4M3 else cols // 2), dtype=torch.uint8,
+                            device=device)
+        scales = torch.empty((rows, cols // 32), dtype=torch.uint8, device=device)
+        return MXTensor(codes, scales, rows, cols, elem)
+
+
+def nvfp4_mx_quantize(x, layout=NVFP4_ROW_1D, elem=NVFP4_MX_E4M3, round=NVFP4_RNE, sr_seed=0, out=None,
+                      stream=None):
+    """MX-quantize a 2-D device tensor (float32 or bfloat16, unit column
+    stride) along rows (ROW_1D) or columns (COL_1D; the result describes the
+    transpose)."""
+    assert x.dim() == 2 and x.stride(1) == 1
+    rows, cols = x.shape
+    ld = x.stride(0) if rows > 1 else max(cols, x.stride(0))
+    if out is None:
+        r, c = (cols, rows) if layout == NVFP4_COL_1D else (rows, cols)
+        out = MXTensor.empty(r, c, elem, x.device)
+    ct = out.c()
+    st = lib.nvfp4_mx_quantize(ctypes.c_void_p(x.data_ptr()), _dtype_code(x.dtype), rows, cols, ld, layout,
+                               round, sr_seed, ctypes.byref(ct), _stream(stream))
+    _check("nvfp4_mx_quantize", st)
+    return out
+
+
+def nvfp4_mx_dequantize(q, dtype=torch.float32, out=None, stream=None):
+    if out is None:
+        out = torch.empty((q.rows, q.cols), dtype=dtype, device=q.codes.device)
+    assert out.stride(1) == 1
+    ld = out.stride(0) if q.rows > 1 else max(q.cols, out.stride(0))
+    ct = q.c()
+    st = lib.nvfp4_mx_dequantize(ctypes.byref(ct), ctypes.c_void_p(out.data_ptr()), _dtype_code(out.dtype), ld,
+                                 _stream(stream))
+    _check("nvfp4_mx_dequantize", st)
     return out

@@ -214,6 +214,62 @@ nvfp4_status nvfp4_grouped_gemm(int32_t G, const nvfp4_tensor* A, const int64_t*
                                 nvfp4_dtype c_dt, int64_t ldc, nvfp4_epilogue ep, float* amax_out,
                                 void* ws, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * MX formats (OCP Microscaling).  The pages name MXFP8 (the backward-pass
+ * format at Thinking Machines: iitak.ru page, "Как это работает"), MXFP4 (the
+ * Open Compute Project format NVFP4 is compared with: asector.ru page,
+ * "Эксперименты и сравнение с FP8") and an 8.25-bit transit format for expert
+ * outputs (iitak.ru page, "Но"), without defining them.  This library reads
+ * them as OCP Microscaling:
+ *   - 32 consecutive elements along the block dimension share an E8M0 scale
+ *     byte b = s + 127 (value 2^s), s = floor(log2(max|V|)) - emax, emax = 8
+ *     for E4M3 elements and 2 for E2M1, clamped to [-127, 127]; s = -127 for
+ *     an all-zero block;
+ *   - element code: y = fl(|V| * 2^-s), rounded onto E4M3 (as the NVFP4 scale
+ *     byte: bias 7, largest 448 = 0x7E) or E2M1 to nearest-even, or
+ *     stochastically (round up iff r < f * 65536 with r the 16-bit Philox
+ *     draw of the element, as for NVFP4, stream 4 for ROW_1D and 5 for
+ *     COL_1D); y beyond the largest value saturates (448 or 6); the sign is
+ *     copied (bit 7 for E4M3, bit 3 for E2M1);
+ *   - E4M3 with 32-element blocks costs 8 + 8/32 = 8.25 bits per element.
+ * ---------------------------------------------------------------------- */
+typedef enum { NVFP4_MX_E4M3 = 0, NVFP4_MX_E2M1 = 1 } nvfp4_mx_elem;
+
+/* An MX tensor of logical shape rows x cols (stored orientation).
+ *   codes:  E4M3: rows x cols bytes; E2M1: rows x cols/2 bytes, even column
+ *           in bits 3:0; row-major.
+ *   scales: rows x cols/32 E8M0 bytes (2^(byte - 127); byte 0xFF is not
+ *           produced and dequantizes to an unspecified value). */
+typedef struct {
+    uint8_t* codes;
+    uint8_t* scales;
+    int64_t rows;
+    int64_t cols;
+    int32_t elem; /* nvfp4_mx_elem */
+} nvfp4_mx_tensor;
+
+/* MX-quantize x (rows x cols, dtype dt, row stride ld elements) into out,
+ * whose elem field selects the element format.
+ *   ROW_1D: blocks along rows; out is rows x cols; cols % 32 == 0.
+ *   COL_1D: blocks along columns; out is cols x rows (x transposed);
+ *           rows % 32 == 0.
+ *   other layouts return NVFP4_ERR_UNSUPPORTED.
+ * No tensor scale and no workspace.  Requirements: ld >= cols,
+ * ld * sizeof(dtype) % 16 == 0, x and out->codes 16-byte aligned; out->rows
+ * and out->cols as the layout implies.  rows == 0 or cols == 0 is a no-op.
+ * Errors as for nvfp4_quantize. */
+nvfp4_status nvfp4_mx_quantize(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols, int64_t ld,
+                               nvfp4_layout layout, nvfp4_round round, uint64_t sr_seed,
+                               nvfp4_mx_tensor* out, void* stream);
+
+/* y = value(code) * 2^(scale byte - 127) as one binary32 rounding (exact
+ * unless the result leaves the binary32 normal range); BF16 output is the
+ * nearest-even BF16 of that binary32 value.  y is q->rows x q->cols, row
+ * stride ld elements.  Requirements: q->cols % 32 == 0, ld >= q->cols,
+ * ld * sizeof(dtype) % 16 == 0, y and q->codes 16-byte aligned. */
+nvfp4_status nvfp4_mx_dequantize(const nvfp4_mx_tensor* q, void* y, nvfp4_dtype dt, int64_t ld,
+                                 void* stream);
+
 /* Static description of a status code. */
 const char* nvfp4_status_string(nvfp4_status s);
 

@@ -153,3 +153,41 @@ def test_grouped_gemm_rejects_bad_arguments(nv):
     assert call(args(amax=65536)) == 5               # amax only with SwiGLU
     a2 = _t(100, 64, 1)
     assert call(args(A=ctypes.byref(a2))) == 3 or call(args(A=ctypes.byref(a2))) == 5
+
+
+def test_mx_rejects_bad_arguments(nv):
+    E = dict(NULL=1, ENUM=2, SHAPE=3, ALIGN=4, UNSUP=5)
+
+    def q(x=65536, dt=1, rows=64, cols=64, ld=64, layout=0, rnd=0, out=(64, 64), elem=0, codes=4096):
+        t = nv.CMXTensor(codes, 8192, out[0], out[1], elem) if out is not None else None
+        return nv.lib.nvfp4_mx_quantize(x, dt, rows, cols, ld, layout, rnd, 1,
+                                        ctypes.byref(t) if t is not None else None, None)
+
+    assert q(out=None) == E["NULL"]
+    assert q(x=None) == E["NULL"]
+    assert q(dt=3) == E["ENUM"]
+    assert q(layout=7) == E["ENUM"]
+    assert q(rnd=2) == E["ENUM"]
+    assert q(elem=2) == E["ENUM"]
+    assert q(layout=2) == E["UNSUP"]                       # ROW_COL is not offered for MX
+    assert q(layout=3) == E["UNSUP"]
+    assert q(cols=48, ld=48, out=(64, 48)) == E["SHAPE"]   # cols % 32 (ROW)
+    assert q(rows=48, layout=1, out=(64, 48)) == E["SHAPE"]  # rows % 32 (COL)
+    assert q(layout=1, rows=64, cols=96, ld=96, out=(64, 96)) == E["SHAPE"]  # COL output is the transpose
+    assert q(ld=32) == E["SHAPE"]
+    assert q(ld=68) == E["ALIGN"]                          # 136 bytes
+    assert q(codes=4096 + 8) == E["ALIGN"]
+    assert q(rows=0, x=None, codes=None, out=(0, 64)) == 0  # empty: a no-op
+
+    def dq(rows=64, cols=64, elem=0, y=65536, dt=0, ld=64):
+        t = nv.CMXTensor(4096, 8192, rows, cols, elem)
+        return nv.lib.nvfp4_mx_dequantize(ctypes.byref(t), y, dt, ld, None)
+
+    assert nv.lib.nvfp4_mx_dequantize(None, 65536, 0, 64, None) == E["NULL"]
+    assert dq(elem=5) == E["ENUM"]
+    assert dq(dt=9) == E["ENUM"]
+    assert dq(cols=48, ld=48) == E["SHAPE"]
+    assert dq(ld=32) == E["SHAPE"]
+    assert dq(y=None) == E["NULL"]
+    assert dq(y=65536 + 4) == E["ALIGN"]
+    assert dq(ld=66) == E["ALIGN"]                          # 264 bytes (fp32)
