@@ -9,4 +9,5 @@ from .nvfp4 import (  # noqa: F401
     nvfp4_quantize, nvfp4_quantize_workspace_size, nvfp4_requantize, nvfp4_dequantize, nvfp4_gemm,
     nvfp4_grouped_gemm,
     MXTensor, NVFP4_MX_E4M3, NVFP4_MX_E2M1, nvfp4_mx_quantize, nvfp4_mx_dequantize,
+    nvfp4_mx_gemm,
 )

@@ -23,7 +23,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libnvfp4.so")
 BUILD = os.path.join(HERE, "_build")
-SOURCES = ["quantize.hip", "gemm.hip", "mx.hip", "nvfp4_api.hip"]
+SOURCES = ["quantize.hip", "gemm.hip", "mx.hip", "mx_gemm.hip", "nvfp4_api.hip"]
 ARCH = os.environ.get("NVFP4_OFFLOAD_ARCH", "gfx950")
 
 

@@ -256,6 +256,33 @@ nvfp4_status nvfp4_mx_dequantize(const nvfp4_mx_tensor* q, void* y, nvfp4_dtype 
     return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
 
+nvfp4_status nvfp4_mx_gemm(const nvfp4_mx_tensor* A, const nvfp4_mx_tensor* B, void* C, nvfp4_dtype c_dt,
+                           int64_t ldc, void* stream) {
+    if (!A || !B) return NVFP4_ERR_NULL;
+    if (!valid_dtype(c_dt)) return NVFP4_ERR_ENUM;
+    for (const nvfp4_mx_tensor* t : {A, B}) {
+        if (t->elem != NVFP4_MX_E4M3 && t->elem != NVFP4_MX_E2M1) return NVFP4_ERR_ENUM;
+        if (t->rows < 0 || t->cols < 0 || t->cols % 32) return NVFP4_ERR_SHAPE;
+    }
+    if (A->cols != B->cols) return NVFP4_ERR_SHAPE;
+    if (A->elem != B->elem) return NVFP4_ERR_UNSUPPORTED;
+    const int64_t M = A->rows, N = B->rows, K = A->cols;
+    if (K % 64) return NVFP4_ERR_UNSUPPORTED;
+    if (ldc < N) return NVFP4_ERR_SHAPE;
+    if (M > 0 && N > 0) {
+        if (!C) return NVFP4_ERR_NULL;
+        if (K > 0 && (!A->codes || !A->scales || !B->codes || !B->scales)) return NVFP4_ERR_NULL;
+    }
+    if (!aligned(C, dtype_size(c_dt)) || !aligned(A->codes, 16) || !aligned(B->codes, 16) ||
+        !aligned(A->scales, 2) || !aligned(B->scales, 2))
+        return NVFP4_ERR_ALIGN;
+    if (cdiv(M, 256) > kMaxGridY) return NVFP4_ERR_UNSUPPORTED;
+    hipError_t e = launch_mx_gemm(A->codes, A->scales, B->codes, B->scales,
+                                  A->elem == NVFP4_MX_E4M3 ? kMxE4M3 : kMxE2M1, M, N, K, C, c_dt == NVFP4_BF16,
+                                  ldc, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
+}
+
 const char* nvfp4_status_string(nvfp4_status s) {
     switch (s) {
         case NVFP4_OK: return "ok";

@@ -191,3 +191,26 @@ def test_mx_rejects_bad_arguments(nv):
     assert dq(y=None) == E["NULL"]
     assert dq(y=65536 + 4) == E["ALIGN"]
     assert dq(ld=66) == E["ALIGN"]                          # 264 bytes (fp32)
+
+
+def test_mx_gemm_rejects_bad_arguments(nv):
+    E = dict(NULL=1, ENUM=2, SHAPE=3, ALIGN=4, UNSUP=5)
+
+    def g(ma=(64, 128, 0), mb=(32, 128, 0), C=65536, dt=0, ldc=32, ac=4096, asc=8192):
+        a = nv.CMXTensor(ac, asc, ma[0], ma[1], ma[2])
+        b = nv.CMXTensor(4096, 8192, mb[0], mb[1], mb[2])
+        return nv.lib.nvfp4_mx_gemm(ctypes.byref(a), ctypes.byref(b), C, dt, ldc, None)
+
+    assert nv.lib.nvfp4_mx_gemm(None, None, 65536, 0, 32, None) == E["NULL"]
+    assert g(dt=4) == E["ENUM"]
+    assert g(ma=(64, 128, 3)) == E["ENUM"]
+    assert g(ma=(64, 96, 0), mb=(32, 96, 0)) == E["UNSUP"]       # K % 64 == 32
+    assert g(ma=(64, 80, 0), mb=(32, 80, 0)) == E["SHAPE"]       # K % 32
+    assert g(mb=(32, 192, 0)) == E["SHAPE"]                      # K mismatch
+    assert g(mb=(32, 128, 1)) == E["UNSUP"]                      # mixed element formats
+    assert g(ldc=16) == E["SHAPE"]
+    assert g(C=None) == E["NULL"]
+    assert g(C=65536 + 2) == E["ALIGN"]
+    assert g(ac=4096 + 4) == E["ALIGN"]
+    assert g(asc=8192 + 1) == E["ALIGN"]
+    assert g(ma=(-1, 128, 0)) == E["SHAPE"]

@@ -1,0 +1,168 @@
+"""GPU parity of the MX GEMM (scaled matrix cores) against the oracle's plain
+definition: exactly dequantized MX operands, float64 products and sums
+(block-scaled tensor-core compute: "Nvidia добивается успеха с 4-битным
+форматом NVFP4", asector.ru, section "NVFP4 и Blackwell"; MXFP8 in the
+backward pass: "Thinking Machines ускорила обучение Inkling 2 Small
+4-битными числами", iitak.ru, section "Как это работает").
+
+Tolerance.  The oracle's sum is exact up to float64 rounding.  On the GPU an
+E2M1 step (64 products of at most 4 significant bits each) is summed exactly,
+and the per-step results are added in binary32; an E4M3 step is summed with
+about 13 significant bits relative to the step's largest product (measured
+on the hardware: error up to ~2^-12 of that product; adding a step's result
+into the accumulator is a binary32 addition).  Hence, per output,
+    |gpu - oracle| <= 2^-11 * sum over K steps of max_k |a_k b_k|   (E4M3 only)
+                      + max(1e-5, steps * 2^-24) * sum_k |a_k b_k|
+plus half a BF16 unit of the reference for BF16 outputs.  Operands whose
+products are all multiples of one power of two, with few significant bits,
+have exactly representable sums: there both formats must match exactly."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+from parity_utils import bf16_tensor_to_bits, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+ELEMS = [O.MX_FP8, O.MX_FP4]
+
+
+@pytest.fixture(scope="module")
+def nv():
+    return require_gpu()
+
+
+def up(nv, q):
+    return nv.MXTensor(torch.from_numpy(np.ascontiguousarray(q.codes)).cuda(),
+                       torch.from_numpy(np.ascontiguousarray(q.scales)).cuda(), q.rows, q.cols, q.elem)
+
+
+def step_max_sum(A, B, mi, ni):
+    """sum over 64-wide K steps of max |a_k b_k| for entries (mi, ni); A, B
+    exact float64 dequantizations."""
+    K = A.shape[1]
+    out = np.zeros(len(mi))
+    for s in range(0, len(mi), 4096):
+        P = np.abs(A[mi[s:s + 4096]] * B[ni[s:s + 4096]])
+        out[s:s + 4096] = P.reshape(P.shape[0], K // 64, 64).max(-1).sum(-1)
+    return out
+
+
+def tolerance(elem, K, W_, smax, cref, bf16):
+    tol = max(1e-5, (K // 64) * 2.0 ** -24) * W_
+    if elem == O.MX_FP8:
+        tol = tol + 2.0 ** -11 * smax
+    if bf16:
+        a = np.abs(cref)
+        e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+        tol = tol + np.where(a > 0, 2.0 ** (e - 8), 0.0)
+    return tol
+
+
+def check(nv, qa, qb, bf16=False, entries=None, exact=False, what=""):
+    C = nv.nvfp4_mx_gemm(up(nv, qa), up(nv, qb), out_dtype=torch.bfloat16 if bf16 else torch.float32)
+    torch.cuda.synchronize()
+    if bf16:
+        G = W.bf16_bits_to_f32(bf16_tensor_to_bits(C)).astype(np.float64)
+    else:
+        G = C.cpu().numpy().astype(np.float64)
+    M, N, K = qa.rows, qb.rows, qa.cols
+    if entries is None:
+        mi, ni = (a.ravel() for a in np.meshgrid(np.arange(M), np.arange(N), indexing="ij"))
+        Cref, Wref = O.mx_gemm(qa, qb)
+        Cref, Wref = Cref.ravel(), Wref.ravel()
+    else:
+        mi, ni = entries
+        Cref, Wref = O.mx_gemm(qa, qb, entries=(mi, ni))
+    got = G[mi, ni]
+    if exact:
+        ref = Cref.astype(np.float32).astype(np.float64) if not bf16 else Cref
+        assert np.array_equal(got, ref), f"{what}: exact case differs at {np.argmax(got != ref)}"
+        return
+    A = O.mx_dequantize(qa, 2)
+    B = O.mx_dequantize(qb, 2)
+    smax = step_max_sum(A, B, mi, ni) if qa.elem == O.MX_FP8 else 0.0
+    tol = tolerance(qa.elem, K, Wref, smax, Cref, bf16)
+    err = np.abs(got - Cref)
+    bad = np.flatnonzero(err > tol)
+    assert bad.size == 0, (f"{what}: {bad.size} entries off, first ({mi[bad[0]]}, {ni[bad[0]]}) "
+                           f"gpu={got[bad[0]]!r} ref={Cref[bad[0]]!r} tol={tol[bad[0]] if np.ndim(tol) else tol!r}")
+
+
+def mxq(x, elem, seed=0, rnd=O.RNE):
+    return O.mx_quantize(np.ascontiguousarray(x, dtype=np.float32), O.F32, O.ROW_1D, elem, rnd, seed=seed)
+
+
+@pytest.mark.parametrize("elem", ELEMS)
+@pytest.mark.parametrize("shape", [(64, 64, 64), (300, 260, 512), (256, 512, 4096)])
+def test_mx_gemm_exact_case(nv, elem, shape):
+    """Elements in {0, +-1/2, +-1, +-2} with every block maximum 2: equal
+    block scales, products on one power-of-two grid, sums below 2^15 -- the
+    GPU result must equal the exact product."""
+    M, N, K = shape
+    g = W.rng(M + N + K)
+    v = np.array([0, .5, 1, 2, -.5, -1, -2], np.float32)
+    xa, xb = g.choice(v, (M, K)), g.choice(v, (N, K))
+    xa[:, ::32] = 2.0
+    xb[:, ::32] = -2.0
+    for bf16 in (False, True):
+        check(nv, mxq(xa, elem), mxq(xb, elem), bf16=bf16, exact=not bf16, what=f"exact {shape} bf16={bf16}")
+
+
+@pytest.mark.parametrize("elem", ELEMS)
+@pytest.mark.parametrize("kind", ["normal", "t3", "spiky"])
+@pytest.mark.parametrize("shape", [(1, 1, 64), (33, 65, 128), (300, 260, 512), (512, 320, 1024)])
+def test_mx_gemm_matches_oracle(nv, elem, kind, shape):
+    M, N, K = shape
+    seed = M * 3 + N * 5 + K
+    if kind == "normal":
+        xa, xb = W.normal((M, K), 1.0, seed=seed), W.normal((N, K), 1.0, seed=seed + 1)
+    elif kind == "t3":
+        xa, xb = W.student_t((M, K), 3.0, seed=seed), W.student_t((N, K), 3.0, seed=seed + 1)
+    else:
+        xa = W.with_spikes(W.normal((M, K), 1.0, seed=seed), 1e-3, 100.0, seed=seed + 2)
+        xb = W.with_spikes(W.normal((N, K), 1.0, seed=seed + 1), 1e-3, 100.0, seed=seed + 3)
+    qa, qb = mxq(xa, elem, seed, O.SR), mxq(xb, elem, seed + 1, O.SR)
+    for bf16 in (False, True):
+        check(nv, qa, qb, bf16=bf16, what=f"{kind} {shape} elem={elem} bf16={bf16}")
+
+
+@pytest.mark.parametrize("elem", ELEMS)
+def test_mx_gemm_scale_spread(nv, elem):
+    """Rows and K blocks scaled by 2^-40 .. 2^40 (block scales across most of
+    the E8M0 range within one output's sum)."""
+    M, N, K = 96, 160, 1024
+    g = W.rng(77)
+    xa = W.normal((M, K), 1.0, seed=78) * (np.float32(2.0) ** g.integers(-40, 40, (M, K // 32)).repeat(32, 1))
+    xb = W.normal((N, K), 1.0, seed=79) * (np.float32(2.0) ** g.integers(-40, 40, (N, K // 32)).repeat(32, 1))
+    check(nv, mxq(xa, elem), mxq(xb, elem), what="scale spread")
+
+
+@pytest.mark.parametrize("elem", ELEMS)
+def test_mx_gemm_zero_k_and_empty(nv, elem):
+    a = nv.MXTensor.empty(70, 0, elem)
+    b = nv.MXTensor.empty(50, 0, elem)
+    C = nv.nvfp4_mx_gemm(a, b)
+    torch.cuda.synchronize()
+    assert C.shape == (70, 50) and not C.any()
+    e = nv.MXTensor.empty(0, 64, elem)
+    C = nv.nvfp4_mx_gemm(e, nv.MXTensor.empty(8, 64, elem))
+    torch.cuda.synchronize()
+    assert C.shape == (0, 8)
+
+
+@pytest.mark.parametrize("elem", ELEMS)
+def test_mx_gemm_8192_sampled(nv, elem):
+    """8192 x 8192 x 8192 (the benchmarked launch), operands quantized by the
+    oracle from Student-t(3) BF16 data: 1024 random entries plus the corners
+    of the output against the oracle's per-entry sums."""
+    n = 8192
+    xa = W.bf16_bits_to_f32(W.f32_to_bf16_bits(W.student_t((n, n), 3.0, seed=8200)))
+    xb = W.bf16_bits_to_f32(W.f32_to_bf16_bits(W.student_t((n, n), 3.0, seed=8201)))
+    qa, qb = mxq(xa, elem, 8202, O.SR), mxq(xb, elem, 8203, O.SR)
+    g = W.rng(8204)
+    mi = np.concatenate([g.integers(0, n, 1024), [0, 0, n - 1, n - 1, 255, 256]])
+    ni = np.concatenate([g.integers(0, n, 1024), [0, n - 1, 0, n - 1, 256, 255]])
+    check(nv, qa, qb, entries=(mi, ni), what="8192 sampled")
