@@ -21,9 +21,14 @@ Also reported, on the same JSON line:
                   blocks + SR operands) and the 32-expert MoE forward
                   (up-projection with SwiGLU, quantize, down-projection), in
                   TFLOP/s against the FP16 MFMA peak they run on and the FP4
-                  peak.
+                  peak;
+  mx           -- the MX formats: MXFP8 / MXFP4 quantize and dequantize of the
+                  step's tensor, the 8.25-bit expert-output codec (MXFP8 row
+                  encode of a 65536 x 7168 BF16 tensor and its BF16 decode),
+                  and the MX GEMMs on the scaled matrix cores (TFLOP/s against
+                  the FP8 or FP4 peak).
 
-python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-gemm] [--no-cpu-baseline]
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-gemm] [--no-mx] [--no-cpu-baseline]
 """
 import argparse
 import hashlib
@@ -39,6 +44,7 @@ METRIC = "NVFP4 quantize GB/s + block-scaled GEMM TFLOP/s, % of MI355X peaks"
 HBM_PEAK_GBS = 8000.0
 FP16_PEAK_TFLOPS = 2500.0
 FP4_PEAK_TFLOPS = 10100.0
+FP8_PEAK_TFLOPS = 5000.0
 N = 8192
 NBUF = 4
 
@@ -94,6 +100,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-gemm", action="store_true")
+    ap.add_argument("--no-mx", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=20)
     ap.add_argument("--pmc-driver", action="store_true",
@@ -233,8 +240,14 @@ def main():
                         "frac_hbm": round(v["frac_hbm"], 4)} for k, v in kern.items()},
     }
 
+    if not args.no_mx:
+        result["mx"] = bench_mx_quant(nv, torch, xs, reps)
     del xs
     torch.cuda.empty_cache()
+    if not args.no_mx:
+        result["mx"].update(bench_mx_codec(nv, W, np, torch, reps))
+        if not args.no_gemm:
+            result["mx"].update(bench_mx_gemm(nv, W, np, torch, reps=max(3, reps // 4)))
     if not args.no_gemm:
         result["gemm"] = bench_gemm(nv, W, np, torch, reps=max(3, reps // 4))
 
@@ -355,6 +368,87 @@ def bench_gemm(nv, W, np, torch, reps):
     entry("moe_down_65536x7168x2048", down_flop, down_ms)
     entry("moe_expert_forward_total", up_flop + down_flop, up_ms + q_ms + down_ms)
     out["moe_expert_forward_total"]["quantize_h_ms"] = round(q_ms, 4)
+    return out
+
+
+def _gbs(name, nbytes, ms):
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {name: {"ms": round(ms, 5), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+                   "bytes": nbytes}}
+
+
+def bench_mx_quant(nv, torch, xs, reps):
+    """MX quantize / dequantize of the step's 8192 x 8192 BF16 tensors (no
+    amax pass: MX scales are per block only).  Bytes: input + codes + E8M0
+    scales (quantize); codes + scales + BF16 output (dequantize)."""
+    log("mx: quantize")
+    E = N * N
+    E4, E2 = nv.NVFP4_MX_E4M3, nv.NVFP4_MX_E2M1
+    out = {}
+    q = {E4: nv.MXTensor.empty(N, N, E4), E2: nv.MXTensor.empty(N, N, E2)}
+    code_bytes = {E4: E, E2: E // 2}
+    for name, lay, elem, rnd in [("mx_e4m3_row_rne", nv.NVFP4_ROW_1D, E4, nv.NVFP4_RNE),
+                                 ("mx_e4m3_row_sr", nv.NVFP4_ROW_1D, E4, nv.NVFP4_SR),
+                                 ("mx_e4m3_col_rne", nv.NVFP4_COL_1D, E4, nv.NVFP4_RNE),
+                                 ("mx_e4m3_col_sr", nv.NVFP4_COL_1D, E4, nv.NVFP4_SR),
+                                 ("mx_e2m1_row_rne", nv.NVFP4_ROW_1D, E2, nv.NVFP4_RNE),
+                                 ("mx_e2m1_row_sr", nv.NVFP4_ROW_1D, E2, nv.NVFP4_SR),
+                                 ("mx_e2m1_col_sr", nv.NVFP4_COL_1D, E2, nv.NVFP4_SR)]:
+        ms = time_events(lambda i: nv.nvfp4_mx_quantize(xs[i % NBUF], layout=lay, elem=elem, round=rnd,
+                                                        sr_seed=9 + i, out=q[elem]), reps, torch)
+        out.update(_gbs(name, E * 2 + code_bytes[elem] + E // 32, ms))
+    y = torch.empty((N, N), dtype=torch.bfloat16, device="cuda")
+    for name, elem in [("mx_dequant_e4m3_bf16", E4), ("mx_dequant_e2m1_bf16", E2)]:
+        ms = time_events(lambda i: nv.nvfp4_mx_dequantize(q[elem], out=y), reps, torch)
+        out.update(_gbs(name, code_bytes[elem] + E // 32 + E * 2, ms))
+    return out
+
+
+def bench_mx_codec(nv, W, np, torch, reps):
+    """The 8.25-bit expert-output codec at the MoE output shape (65536 x 7168
+    BF16, the down-projection's output of 16384 tokens x top-4): MXFP8 row
+    encode (8 + 8/32 bits per number) and the BF16 decode.  Student-t(3)
+    rows (an 8192-row seeded block repeated 8 times)."""
+    log("mx: codec")
+    rows, cols = 65536, 7168
+    blk = bf16_device(W.f32_to_bf16_bits(W.student_t((8192, cols), 3.0, seed=7000)), torch, np)
+    Y = blk.repeat(rows // 8192, 1)
+    del blk
+    E = rows * cols
+    q = nv.MXTensor.empty(rows, cols, nv.NVFP4_MX_E4M3)
+    y = torch.empty_like(Y)
+    out = {}
+    ms = time_events(lambda i: nv.nvfp4_mx_quantize(Y, out=q), reps, torch)
+    out.update(_gbs("codec_encode_65536x7168", E * 2 + E + E // 32, ms))
+    ms = time_events(lambda i: nv.nvfp4_mx_dequantize(q, out=y), reps, torch)
+    out.update(_gbs("codec_decode_65536x7168", E + E // 32 + E * 2, ms))
+    out["codec_encode_65536x7168"]["bits_per_number"] = 8.25
+    out["codec_encode_65536x7168"]["payload_bytes"] = E + E // 32
+    del Y, y, q
+    torch.cuda.empty_cache()
+    return out
+
+
+def bench_mx_gemm(nv, W, np, torch, reps):
+    """MX GEMMs on the scaled matrix cores, operands MX-quantized on the GPU
+    from seeded BF16 data (SR)."""
+    out = {}
+
+    def mxq(shape, seed, elem):
+        x = bf16_device(W.f32_to_bf16_bits(W.student_t(shape, 3.0, seed=seed)), torch, np)
+        return nv.nvfp4_mx_quantize(x, elem=elem, round=nv.NVFP4_SR, sr_seed=seed + 1)
+
+    for elem, tag, peak in [(nv.NVFP4_MX_E4M3, "e4m3", FP8_PEAK_TFLOPS), (nv.NVFP4_MX_E2M1, "e2m1", FP4_PEAK_TFLOPS)]:
+        for (M, Nn, K, dt) in [(8192, 8192, 8192, torch.float32), (20480, 5120, 8192, torch.float32)]:
+            log(f"mx gemm {tag} {M}x{Nn}x{K}")
+            A, B = mxq((M, K), 7100, elem), mxq((Nn, K), 7200, elem)
+            C = torch.empty((M, Nn), dtype=dt, device="cuda")
+            ms = time_events(lambda i: nv.nvfp4_mx_gemm(A, B, out=C), reps, torch)
+            tf = 2 * M * Nn * K / (ms * 1e-3) / 1e12
+            out[f"mx_gemm_{tag}_{M}x{Nn}x{K}"] = {"ms": round(ms, 4), "TFLOP/s": round(tf, 1),
+                                                 "frac_peak": round(tf / peak, 4), "peak_TFLOP/s": peak}
+            del A, B, C
+            torch.cuda.empty_cache()
     return out
 
 

@@ -42,8 +42,9 @@
 // then wait for the wave's own loads of the next step, the workgroup barrier,
 // the fragment reads of the next step (into the other register set) and the
 // loads of the step four ahead into the slot just released, then the other 8
-// MFMAs.  The step count is padded to even with a leading step of zero
-// operands, so the two register sets alternate statically.
+// MFMAs.  The step count is padded to a multiple of 4 with leading steps whose
+// slots are zero-filled, so slots and register sets have static names and the
+// loop body has no branch.
 #include "launch.hpp"
 #include "nvfp4_device.hpp"
 
@@ -73,9 +74,10 @@ struct MxGeo {
     static constexpr int FMT = ELEM == kMxE4M3 ? 0 : 4;   // matrix-core operand format
 };
 
-// Physical chunk of logical chunk c in slot row r.  E4M3 (4 chunks): the 8
-// rows of any 8 consecutive lanes, and the 16 rows of any 16, fall on distinct
-// (row bank offset, chunk) pairs; E2M1 (2 chunks) likewise.
+// Physical chunk of logical chunk c in slot row r (a function of row bits
+// 1..4 only).  E4M3 (4 chunks): the 8 rows of any 8 consecutive lanes, and the
+// 16 rows of any 16, fall on distinct (row bank offset, chunk) pairs; E2M1 (2
+// chunks) likewise.
 template <int CPR>
 __device__ __forceinline__ int mx_chunk(int r, int c) {
     return CPR == 4 ? c ^ (((r >> 1) ^ (r >> 3)) & 3) : c ^ (((r >> 2) ^ (r >> 3)) & 1);
@@ -88,30 +90,36 @@ struct MxGemmArgs {
     int64_t ldc;
 };
 
+// Global sources of a workgroup's ring loads: wave-uniform bases (the tile's
+// first A and B rows) and 32-bit per-lane byte offsets from them (the tile
+// spans 256 rows, so offsets stay below 256 row lengths).
 template <int ELEM>
 struct MxSrc {
-    const uint8_t* a[MxGeo<ELEM>::LOADS];
-    const uint8_t* b[MxGeo<ELEM>::LOADS];
-    const uint8_t *as, *bs;
+    const uint8_t *ac, *bc, *as, *bs;
+    uint32_t a[MxGeo<ELEM>::LOADS];
+    uint32_t b[MxGeo<ELEM>::LOADS];
+    uint32_t sa, sb;
 };
 
 template <int ELEM>
 __device__ __forceinline__ void mx_ring_load(const MxSrc<ELEM>& src, int64_t kc, uint8_t* slot, int w) {
     using G = MxGeo<ELEM>;
-    const int64_t co = kc * G::RB, so = kc * 2;
+    const uint8_t* ac = src.ac + kc * G::RB;
+    const uint8_t* bc = src.bc + kc * G::RB;
 #pragma unroll
     for (int t = 0; t < G::LOADS; ++t)
-        __builtin_amdgcn_global_load_lds((gmem_t*)(src.a[t] + co), (lmem_t*)(slot + (64 * w + G::RPL * t) * G::RB),
+        __builtin_amdgcn_global_load_lds((gmem_t*)(ac + src.a[t]), (lmem_t*)(slot + (64 * w + G::RPL * t) * G::RB),
                                          16, 0, 0);
 #pragma unroll
     for (int t = 0; t < G::LOADS; ++t)
-        __builtin_amdgcn_global_load_lds((gmem_t*)(src.b[t] + co),
+        __builtin_amdgcn_global_load_lds((gmem_t*)(bc + src.b[t]),
                                          (lmem_t*)(slot + G::CODES + (64 * w + G::RPL * t) * G::RB), 16, 0, 0);
     // a 1- or 2-byte global_load_lds writes lane i's data zero-extended into
     // the dword at base + 4 i, so each row's two scale bytes take a dword
-    __builtin_amdgcn_global_load_lds((gmem_t*)(src.as + so), (lmem_t*)(slot + 2 * G::CODES + 256 * w), 2, 0, 0);
-    __builtin_amdgcn_global_load_lds((gmem_t*)(src.bs + so), (lmem_t*)(slot + 2 * G::CODES + G::SC + 256 * w), 2,
-                                     0, 0);
+    __builtin_amdgcn_global_load_lds((gmem_t*)(src.as + 2 * kc + src.sa), (lmem_t*)(slot + 2 * G::CODES + 256 * w),
+                                     2, 0, 0);
+    __builtin_amdgcn_global_load_lds((gmem_t*)(src.bs + 2 * kc + src.sb),
+                                     (lmem_t*)(slot + 2 * G::CODES + G::SC + 256 * w), 2, 0, 0);
 }
 
 // s_waitcnt immediate (gfx9 encoding): at most n vector memory operations of
@@ -125,23 +133,43 @@ struct MxFrags {
     int sa[4], sb[4];
 };
 
-// Fragment of slot row r (operand base `ops`) for lane half h.
+// A lane's byte offsets inside a slot for its fragment rows of MFMA tile 0
+// (rows arow0 + l32 of A and brow0 + l32 of B): codes of its two chunks per
+// operand and its scale byte.  Tile i adds 32 i rows, which leaves the chunk
+// swizzle unchanged (it depends on row bits 1..4 only), so every fragment
+// read is one of these offsets plus a compile-time constant.
+struct MxLaneOffsets {
+    int a_lo, a_hi, b_lo, b_hi, sa, sb;
+};
+
 template <int ELEM>
-__device__ __forceinline__ v8i_t mx_frag(const uint8_t* ops, int r, int h) {
+__device__ __forceinline__ MxLaneOffsets mx_lane_offsets(int arow0, int brow0, int l32, int h) {
     using G = MxGeo<ELEM>;
-    const uint8_t* row = ops + r * G::RB;
-    const uint4 lo = *reinterpret_cast<const uint4*>(row + 16 * mx_chunk<G::CPR>(r, h));
+    MxLaneOffsets o;
+    const int ra = arow0 + l32, rb = brow0 + l32;
+    o.a_lo = ra * G::RB + 16 * mx_chunk<G::CPR>(l32, h);
+    o.b_lo = G::CODES + rb * G::RB + 16 * mx_chunk<G::CPR>(l32, h);
+    o.a_hi = ra * G::RB + 16 * mx_chunk<G::CPR>(l32, (2 + h) & (G::CPR - 1));
+    o.b_hi = G::CODES + rb * G::RB + 16 * mx_chunk<G::CPR>(l32, (2 + h) & (G::CPR - 1));
+    o.sa = 2 * G::CODES + 4 * ra + h;
+    o.sb = 2 * G::CODES + G::SC + 4 * rb + h;
+    return o;
+}
+
+template <int ELEM>
+__device__ __forceinline__ v8i_t mx_frag(const uint8_t* slot, int lo, int hi) {
+    const uint4 q = *reinterpret_cast<const uint4*>(slot + lo);
     v8i_t v;
-    v[0] = (int)lo.x;
-    v[1] = (int)lo.y;
-    v[2] = (int)lo.z;
-    v[3] = (int)lo.w;
+    v[0] = (int)q.x;
+    v[1] = (int)q.y;
+    v[2] = (int)q.z;
+    v[3] = (int)q.w;
     if constexpr (ELEM == kMxE4M3) {
-        const uint4 hi = *reinterpret_cast<const uint4*>(row + 16 * mx_chunk<G::CPR>(r, 2 + h));
-        v[4] = (int)hi.x;
-        v[5] = (int)hi.y;
-        v[6] = (int)hi.z;
-        v[7] = (int)hi.w;
+        const uint4 r = *reinterpret_cast<const uint4*>(slot + hi);
+        v[4] = (int)r.x;
+        v[5] = (int)r.y;
+        v[6] = (int)r.z;
+        v[7] = (int)r.w;
     } else {
         v[4] = v[5] = v[6] = v[7] = 0;
     }
@@ -149,29 +177,51 @@ __device__ __forceinline__ v8i_t mx_frag(const uint8_t* ops, int r, int h) {
 }
 
 template <int ELEM>
-__device__ __forceinline__ void mx_read_frags(const uint8_t* slot, int arow0, int brow0, int l32, int h, bool zero,
-                                              MxFrags& f) {
+__device__ __forceinline__ void mx_read_frags(const uint8_t* slot, const MxLaneOffsets& o, MxFrags& f) {
     using G = MxGeo<ELEM>;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int ra = arow0 + 32 * i + l32, rb = brow0 + 32 * i + l32;
-        f.a[i] = mx_frag<ELEM>(slot, ra, h);
-        f.b[i] = mx_frag<ELEM>(slot + G::CODES, rb, h);
-        f.sa[i] = slot[2 * G::CODES + 4 * ra + h];
-        f.sb[i] = slot[2 * G::CODES + G::SC + 4 * rb + h];
-    }
-    if (zero) {  // a padding step: zero A operands make every product 0
-#pragma unroll
-        for (int i = 0; i < 4; ++i) f.a[i] = v8i_t{0, 0, 0, 0, 0, 0, 0, 0};
+        const int dc = 32 * i * G::RB, ds = 32 * i * 4;
+        f.a[i] = mx_frag<ELEM>(slot + dc, o.a_lo, o.a_hi);
+        f.b[i] = mx_frag<ELEM>(slot + dc, o.b_lo, o.b_hi);
+        f.sa[i] = slot[o.sa + ds];
+        f.sb[i] = slot[o.sb + ds];
     }
 }
+
+// A padding step's slot, all of it set to zero (codes +0, scale bytes 2^-127:
+// every product of the step is +0; leaving the B half or the scale bytes
+// uninitialized could pair a zero with a NaN pattern), written by the whole
+// workgroup.
+template <int ELEM>
+__device__ __forceinline__ void mx_zero_slot(uint8_t* slot) {
+    using G = MxGeo<ELEM>;
+    static_assert((2 * G::CODES) % (256 * 16) == 0 && 2 * G::SC == 256 * 8, "zero-fill geometry");
+    // codes of A and B occupy [0, 2 CODES): 16-byte stores; scale bytes
+    // [2 CODES, 2 CODES + 2 SC): 8 bytes per thread
+#pragma unroll
+    for (int k = 0; k < 2 * G::CODES / (256 * 16); ++k)
+        *reinterpret_cast<uint4*>(slot + 16 * (threadIdx.x + 256 * k)) = make_uint4(0u, 0u, 0u, 0u);
+    *reinterpret_cast<uint2*>(slot + 2 * G::CODES + 8 * threadIdx.x) = make_uint2(0u, 0u);
+}
+
+// s_waitcnt immediate: all LDS operations of this wave done, vector memory
+// and export counters untouched.
+constexpr unsigned mx_lgkmcnt_zero() { return 15u | (3u << 14) | (7u << 4); }
 
 template <int ELEM, bool OUT_BF16>
 __global__ void __launch_bounds__(256, 1) k_mx_gemm(MxGemmArgs p) {
     using G = MxGeo<ELEM>;
-    __shared__ __attribute__((aligned(16))) uint8_t lds[kMxRing * G::SLOT];
+    // four slots as four variables: the compiler then sees that a slot being
+    // read is not one that in-flight global_load_lds writes target, and waits
+    // only where the code says so (one shared array makes it wait for every
+    // outstanding load before each LDS read)
+    __shared__ __attribute__((aligned(16))) uint8_t ring0[G::SLOT];
+    __shared__ __attribute__((aligned(16))) uint8_t ring1[G::SLOT];
+    __shared__ __attribute__((aligned(16))) uint8_t ring2[G::SLOT];
+    __shared__ __attribute__((aligned(16))) uint8_t ring3[G::SLOT];
     const int tid = threadIdx.x;
-    const int lane = tid & 63, w = tid >> 6;
+    const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar LDS bases
     const int wm = w >> 1, wn = w & 1;
     const int h = lane >> 5, l32 = lane & 31;
     const int64_t M = p.M, N = p.N, K = p.K;
@@ -180,15 +230,19 @@ __global__ void __launch_bounds__(256, 1) k_mx_gemm(MxGemmArgs p) {
 
     // per-lane sources (rows past the end are clamped re-reads, never stored)
     MxSrc<ELEM> src;
+    src.ac = p.ac + m0 * kb;
+    src.bc = p.bc + n0 * kb;
+    src.as = p.as + m0 * ks;
+    src.bs = p.bs + n0 * ks;
 #pragma unroll
     for (int t = 0; t < G::LOADS; ++t) {
         const int r = 64 * w + G::RPL * t + lane / G::CPR;
         const int c = mx_chunk<G::CPR>(r, lane % G::CPR);  // the swizzle is an involution
-        src.a[t] = p.ac + min(m0 + r, M - 1) * kb + 16 * c;
-        src.b[t] = p.bc + min(n0 + r, N - 1) * kb + 16 * c;
+        src.a[t] = (uint32_t)((min(m0 + r, M - 1) - m0) * kb + 16 * c);
+        src.b[t] = (uint32_t)((min(n0 + r, N - 1) - n0) * kb + 16 * c);
     }
-    src.as = p.as + min(m0 + 64 * w + lane, M - 1) * ks;
-    src.bs = p.bs + min(n0 + 64 * w + lane, N - 1) * ks;
+    src.sa = (uint32_t)((min(m0 + 64 * w + lane, M - 1) - m0) * ks);
+    src.sb = (uint32_t)((min(n0 + 64 * w + lane, N - 1) - n0) * ks);
 
     v16f_t acc[4][4];
 #pragma unroll
@@ -201,35 +255,47 @@ __global__ void __launch_bounds__(256, 1) k_mx_gemm(MxGemmArgs p) {
     const int arow0 = 128 * wm, brow0 = 128 * wn;
     const int64_t nsteps = K / kMxStepK;
     if (nsteps > 0) {
-        const int64_t pad = nsteps & 1, nj = nsteps + pad, last = nsteps - 1;
+        // steps run four at a time (static slot names); the count is padded to
+        // a multiple of 4 with leading steps whose slots hold zeros
+        // (filled once here: the loop itself has no branch, so the compiler
+        // keeps each step's MFMAs between its barriers)
+        const int64_t pad = (4 - nsteps % 4) % 4, nj = nsteps + pad, last = nsteps - 1;
+        // (a padding slot is never reloaded before its step has been read)
         auto kc_of = [&](int64_t j) {
             const int64_t kc = j - pad;
             return kc < 0 ? (int64_t)0 : (kc > last ? last : kc);
         };
-#pragma unroll
-        for (int j = 0; j < kMxRing; ++j) mx_ring_load<ELEM>(src, kc_of(j), lds + j * G::SLOT, w);
+        if (pad > 0) mx_zero_slot<ELEM>(ring0); else mx_ring_load<ELEM>(src, kc_of(0), ring0, w);
+        if (pad > 1) mx_zero_slot<ELEM>(ring1); else mx_ring_load<ELEM>(src, kc_of(1), ring1, w);
+        if (pad > 2) mx_zero_slot<ELEM>(ring2); else mx_ring_load<ELEM>(src, kc_of(2), ring2, w);
+        mx_ring_load<ELEM>(src, kc_of(3), ring3, w);
+        // step 0 landed (pads come first, so if step 0 is loaded so are 1..3)
+        // and the zero fills done, then the barrier
         __builtin_amdgcn_s_waitcnt(mx_vmcnt_at_most(3 * G::LPS));
+        __builtin_amdgcn_s_waitcnt(mx_lgkmcnt_zero());
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
 
+        const MxLaneOffsets lo = mx_lane_offsets<ELEM>(arow0, brow0, l32, h);
         MxFrags fx, fy;
-        mx_read_frags<ELEM>(lds, arow0, brow0, l32, h, pad > 0, fx);
+        mx_read_frags<ELEM>(ring0, lo, fx);
 
-        auto step = [&](int64_t j, MxFrags& fc, MxFrags& fn) {
+        auto step = [&](int64_t j, uint8_t* cur, uint8_t* nxt, MxFrags& fc, MxFrags& fn) {
 #pragma unroll
             for (int m = 0; m < 16; ++m) {
                 if (m == 8) {
                     // own loads of step j + 1 landed (j + 2, j + 3 may still be
-                    // in flight); after the barrier every wave's part of it is
-                    // in LDS and every wave has read step j's slot
+                    // in flight; a padding step j + 1 loaded nothing and so
+                    // needs no wait); after the barrier every wave's part of
+                    // it is in LDS and every wave has read step j's slot
                     __builtin_amdgcn_sched_barrier(0);
                     __builtin_amdgcn_s_waitcnt(mx_vmcnt_at_most(2 * G::LPS));
                     asm volatile("" ::: "memory");
                     __builtin_amdgcn_s_barrier();
                     asm volatile("" ::: "memory");
-                    mx_read_frags<ELEM>(lds + ((j + 1) & 3) * G::SLOT, arow0, brow0, l32, h, j + 1 < pad, fn);
-                    mx_ring_load<ELEM>(src, kc_of(j + 4), lds + (j & 3) * G::SLOT, w);
+                    mx_read_frags<ELEM>(nxt, lo, fn);
+                    mx_ring_load<ELEM>(src, kc_of(j + 4), cur, w);
                     __builtin_amdgcn_sched_barrier(0);
                 }
                 const int i = m >> 2, jj = m & 3;
@@ -237,9 +303,11 @@ __global__ void __launch_bounds__(256, 1) k_mx_gemm(MxGemmArgs p) {
                     fc.a[i], fc.b[jj], acc[i][jj], G::FMT, G::FMT, 0, fc.sa[i], 0, fc.sb[jj]);
             }
         };
-        for (int64_t j = 0; j < nj; j += 2) {
-            step(j, fx, fy);
-            step(j + 1, fy, fx);
+        for (int64_t j = 0; j < nj; j += 4) {
+            step(j, ring0, ring1, fx, fy);
+            step(j + 1, ring1, ring2, fy, fx);
+            step(j + 2, ring2, ring3, fx, fy);
+            step(j + 3, ring3, ring0, fy, fx);
         }
         // the last look-ahead loads (clamped re-reads) land before the
         // workgroup's LDS is released
@@ -249,6 +317,231 @@ __global__ void __launch_bounds__(256, 1) k_mx_gemm(MxGemmArgs p) {
     // accumulator r of tile (i, j): row 32 i + 8 (r / 4) + 4 h + r % 4, column
     // 32 j + l32 of the wave tile
     const int64_t mw = m0 + arow0, nw = n0 + brow0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t c = nw + 32 * j + l32;
+            if (c >= N) continue;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int64_t m = mw + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+                if (m < M) {
+                    if (OUT_BF16)
+                        static_cast<uint16_t*>(p.C)[m * p.ldc + c] =
+                            (uint16_t)__builtin_bit_cast(uint16_t, (__bf16)acc[i][j][r]);
+                    else
+                        static_cast<float*>(p.C)[m * p.ldc + c] = acc[i][j][r];
+                }
+            }
+        }
+}
+
+// ============================================================ full-line kernel
+// For K % 1024 == 0 with 16-byte-aligned scale rows (every benchmarked shape):
+// the same tile and MFMA schedule, but the memory traffic shaped for gfx950's
+// caches, where each distinct cache line a wave-wide load touches costs
+// about the same whatever part of it is used:
+//   - a ring slot holds 128 bytes of every tile row (a whole line): 2 K steps
+//     of E4M3 or 4 of E2M1 ("a chunk"); two slots, the next chunk's loads in
+//     flight while the current chunk is consumed;
+//   - scale bytes arrive 16 per row (8 K steps) per load, one group ahead,
+//     into two small buffers, from which each step reads its lane's 8 bytes
+//     along with the fragments;
+//   - 16-byte chunk c of slot row r sits at chunk c ^ (r % 8) ^ ((r / 8) % 4)
+//     (bits 0..4 of r), which spreads the fragment reads over every bank for
+//     8 lanes (32 banks) and for 16 lanes (64 banks).
+// The body is unrolled over 16 K steps (8 E4M3 or 4 E2M1 chunks, 2 scale
+// groups), so every slot and buffer has a static name and there is no
+// padding.
+template <int ELEM>
+struct MxFull {
+    static constexpr int SPC = ELEM == kMxE4M3 ? 2 : 4;  // K steps per chunk
+    static constexpr int CODES = kMxTile * 128;          // code bytes per operand per slot
+    static constexpr int SCB = kMxTile * 16;             // scale bytes per operand per group buffer
+    static constexpr int FMT = ELEM == kMxE4M3 ? 0 : 4;
+};
+
+// (row bits 0..4 only: fragment rows 32 apart share it)
+__device__ __forceinline__ int mx_full_swz(int r) { return (r ^ ((r >> 3) & 3)) & 7; }
+
+// Per-lane byte offsets of the ring loads: code row r of load t in chunk 0
+// (add 128 per chunk), scale row (add 16 per group).
+struct MxFullSrc {
+    const uint8_t *ac, *bc, *as, *bs;
+    uint32_t a[8], b[8];
+    uint32_t sa, sb;
+};
+
+template <int ELEM>
+__device__ __forceinline__ void mx_full_chunk_load(const MxFullSrc& src, int64_t chunk, uint8_t* slot, int w) {
+    using F = MxFull<ELEM>;
+    const uint8_t* ac = src.ac + chunk * 128;
+    const uint8_t* bc = src.bc + chunk * 128;
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+        __builtin_amdgcn_global_load_lds((gmem_t*)(ac + src.a[t]), (lmem_t*)(slot + (64 * w + 8 * t) * 128), 16, 0, 0);
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+        __builtin_amdgcn_global_load_lds((gmem_t*)(bc + src.b[t]), (lmem_t*)(slot + F::CODES + (64 * w + 8 * t) * 128),
+                                         16, 0, 0);
+}
+
+template <int ELEM>
+__device__ __forceinline__ void mx_full_scale_load(const MxFullSrc& src, int64_t group, uint8_t* buf, int w) {
+    using F = MxFull<ELEM>;
+    __builtin_amdgcn_global_load_lds((gmem_t*)(src.as + group * 16 + src.sa), (lmem_t*)(buf + 64 * w * 16), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((gmem_t*)(src.bs + group * 16 + src.sb), (lmem_t*)(buf + F::SCB + 64 * w * 16),
+                                     16, 0, 0);
+}
+
+// Fragments of K step t of a chunk (A and B, tiles 0..3).
+template <int ELEM>
+__device__ __forceinline__ void mx_full_frags(const uint8_t* slot, int t, int rowa, int rowb, int sw, int h, v8i_t (&a)[4],
+                                              v8i_t (&b)[4]) {
+    using F = MxFull<ELEM>;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if constexpr (ELEM == kMxE4M3) {
+            const int clo = (4 * t + h) ^ sw, chi = (4 * t + 2 + h) ^ sw;
+            const uint4 alo = *reinterpret_cast<const uint4*>(slot + (rowa + 32 * i) * 128 + 16 * clo);
+            const uint4 ahi = *reinterpret_cast<const uint4*>(slot + (rowa + 32 * i) * 128 + 16 * chi);
+            const uint4 blo = *reinterpret_cast<const uint4*>(slot + F::CODES + (rowb + 32 * i) * 128 + 16 * clo);
+            const uint4 bhi = *reinterpret_cast<const uint4*>(slot + F::CODES + (rowb + 32 * i) * 128 + 16 * chi);
+            a[i] = v8i_t{(int)alo.x, (int)alo.y, (int)alo.z, (int)alo.w, (int)ahi.x, (int)ahi.y, (int)ahi.z, (int)ahi.w};
+            b[i] = v8i_t{(int)blo.x, (int)blo.y, (int)blo.z, (int)blo.w, (int)bhi.x, (int)bhi.y, (int)bhi.z, (int)bhi.w};
+        } else {
+            const int c = (2 * t + h) ^ sw;
+            const uint4 aq = *reinterpret_cast<const uint4*>(slot + (rowa + 32 * i) * 128 + 16 * c);
+            const uint4 bq = *reinterpret_cast<const uint4*>(slot + F::CODES + (rowb + 32 * i) * 128 + 16 * c);
+            a[i] = v8i_t{(int)aq.x, (int)aq.y, (int)aq.z, (int)aq.w, 0, 0, 0, 0};
+            b[i] = v8i_t{(int)bq.x, (int)bq.y, (int)bq.z, (int)bq.w, 0, 0, 0, 0};
+        }
+    }
+}
+
+// Scale bytes of K step g (0..7) of a group for the lane's 4 A and 4 B rows:
+// byte 2 g + h of each row's 16.
+template <int ELEM>
+__device__ __forceinline__ void mx_full_scales(const uint8_t* buf, int g, int rowa, int rowb, int h, int (&sa)[4],
+                                               int (&sb)[4]) {
+    using F = MxFull<ELEM>;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        sa[i] = buf[(rowa + 32 * i) * 16 + 2 * g + h];
+        sb[i] = buf[F::SCB + (rowb + 32 * i) * 16 + 2 * g + h];
+    }
+}
+
+template <int ELEM, bool OUT_BF16>
+__global__ void __launch_bounds__(256, 1) k_mx_gemm_full(MxGemmArgs p) {
+    using F = MxFull<ELEM>;
+    constexpr int SPC = F::SPC;
+    __shared__ __attribute__((aligned(16))) uint8_t slot0[2 * F::CODES];
+    __shared__ __attribute__((aligned(16))) uint8_t slot1[2 * F::CODES];
+    __shared__ __attribute__((aligned(16))) uint8_t scb0[2 * F::SCB];
+    __shared__ __attribute__((aligned(16))) uint8_t scb1[2 * F::SCB];
+    const int tid = threadIdx.x;
+    // the wave index is uniform: held in a scalar register, the LDS
+    // destinations of the ring loads need no vector registers
+    const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = w >> 1, wn = w & 1;
+    const int h = lane >> 5, l32 = lane & 31;
+    const int64_t M = p.M, N = p.N, K = p.K;
+    const int64_t m0 = (int64_t)blockIdx.y * kMxTile, n0 = (int64_t)blockIdx.x * kMxTile;
+    const int64_t kb = ELEM == kMxE4M3 ? K : K / 2, ks = K / 32;
+
+    MxFullSrc src;
+    src.ac = p.ac + m0 * kb;
+    src.bc = p.bc + n0 * kb;
+    src.as = p.as + m0 * ks;
+    src.bs = p.bs + n0 * ks;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const int r = 64 * w + 8 * t + (lane >> 3);
+        const int c = (lane & 7) ^ mx_full_swz(r);  // the swizzle is an involution
+        src.a[t] = (uint32_t)((min(m0 + r, M - 1) - m0) * kb + 16 * c);
+        src.b[t] = (uint32_t)((min(n0 + r, N - 1) - n0) * kb + 16 * c);
+    }
+    src.sa = (uint32_t)((min(m0 + 64 * w + lane, M - 1) - m0) * ks);
+    src.sb = (uint32_t)((min(n0 + 64 * w + lane, N - 1) - n0) * ks);
+
+    v16f_t acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    const int rowa = 128 * wm + l32, rowb = 128 * wn + l32;
+    const int sw = mx_full_swz(l32);
+    const int64_t nchunks = K / (64 * SPC), ngroups = K / 512, nsteps = K / 64;
+    auto cclamp = [&](int64_t c) { return c < nchunks ? c : nchunks - 1; };
+    auto gclamp = [&](int64_t g) { return g < ngroups ? g : ngroups - 1; };
+
+    // prologue: scale groups 0 and 1, chunks 0 and 1 (K >= 1024, so all exist)
+    mx_full_scale_load<ELEM>(src, 0, scb0, w);
+    mx_full_scale_load<ELEM>(src, 1, scb1, w);
+    mx_full_chunk_load<ELEM>(src, 0, slot0, w);
+    mx_full_chunk_load<ELEM>(src, 1, slot1, w);
+    __builtin_amdgcn_s_waitcnt(mx_vmcnt_at_most(16));  // all but chunk 1
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+
+    v8i_t fa[2][4], fb[2][4];
+    int sa[2][4], sb[2][4];
+    mx_full_scales<ELEM>(scb0, 0, rowa, rowb, h, sa[0], sb[0]);
+    mx_full_frags<ELEM>(slot0, 0, rowa, rowb, sw, h, fa[0], fb[0]);
+
+    for (int64_t it = 0; it < nsteps; it += 16) {
+        const int64_t chunk0 = it / SPC, group0 = it / 8;
+#pragma unroll
+        for (int s = 0; s < 16; ++s) {
+            const int cc = s / SPC, t = s % SPC, g = s % 8, cur = s & 1;
+            uint8_t* slot = (cc & 1) ? slot1 : slot0;
+            uint8_t* other = (cc & 1) ? slot0 : slot1;
+            uint8_t* gbuf = (s / 8) ? scb1 : scb0;  // this step's scale group
+#pragma unroll
+            for (int m = 0; m < 16; ++m) {
+                if (m == 8) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (t == SPC - 1) {
+                        // the next chunk's loads (and any scale group issued
+                        // before them) landed; after the barrier every wave
+                        // has read all of this chunk's slot
+                        __builtin_amdgcn_s_waitcnt(mx_vmcnt_at_most(0));
+                        asm volatile("" ::: "memory");
+                        __builtin_amdgcn_s_barrier();
+                        asm volatile("" ::: "memory");
+                        if (g == 7) {
+                            // the next step opens the other scale group; every
+                            // wave is done with this group's buffer, which
+                            // takes the group after next
+                            uint8_t* nb = (s == 7) ? scb1 : scb0;
+                            mx_full_scales<ELEM>(nb, 0, rowa, rowb, h, sa[cur ^ 1], sb[cur ^ 1]);
+                            mx_full_scale_load<ELEM>(src, gclamp(group0 + s / 8 + 2), gbuf, w);
+                        } else {
+                            mx_full_scales<ELEM>(gbuf, g + 1, rowa, rowb, h, sa[cur ^ 1], sb[cur ^ 1]);
+                        }
+                        mx_full_frags<ELEM>(other, 0, rowa, rowb, sw, h, fa[cur ^ 1], fb[cur ^ 1]);
+                        mx_full_chunk_load<ELEM>(src, cclamp(chunk0 + cc + 2), slot, w);
+                    } else {
+                        mx_full_scales<ELEM>(gbuf, g + 1, rowa, rowb, h, sa[cur ^ 1], sb[cur ^ 1]);
+                        mx_full_frags<ELEM>(slot, t + 1, rowa, rowb, sw, h, fa[cur ^ 1], fb[cur ^ 1]);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                const int i = m >> 2, jj = m & 3;
+                acc[i][jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    fa[cur][i], fb[cur][jj], acc[i][jj], F::FMT, F::FMT, 0, sa[cur][i], 0, sb[cur][jj]);
+            }
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(mx_vmcnt_at_most(0));
+
+    const int64_t mw = m0 + 128 * wm, nw = n0 + 128 * wn;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -279,7 +572,15 @@ hipError_t launch_mx_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const
     if (M == 0 || N == 0) return hipSuccess;
     MxGemmArgs p{a_codes, a_scales, b_codes, b_scales, M, N, K, C, ldc};
     dim3 grid((unsigned)mx_cdiv(N, kMxTile), (unsigned)mx_cdiv(M, kMxTile));
-#define NVFP4_MXG(E, BF) hipLaunchKernelGGL((k_mx_gemm<E, BF>), grid, dim3(256), 0, s, p)
+    const bool full = K % 1024 == 0 && K > 0 && (reinterpret_cast<uintptr_t>(a_scales) & 15) == 0 &&
+                      (reinterpret_cast<uintptr_t>(b_scales) & 15) == 0;
+#define NVFP4_MXG(E, BF)                                                                 \
+    do {                                                                                 \
+        if (full)                                                                        \
+            hipLaunchKernelGGL((k_mx_gemm_full<E, BF>), grid, dim3(256), 0, s, p);       \
+        else                                                                             \
+            hipLaunchKernelGGL((k_mx_gemm<E, BF>), grid, dim3(256), 0, s, p);            \
+    } while (0)
     if (elem == kMxE4M3) {
         if (c_bf16) NVFP4_MXG(kMxE4M3, true); else NVFP4_MXG(kMxE4M3, false);
     } else {
