@@ -72,9 +72,29 @@ def time_events(fn, reps, torch):
     return e0.elapsed_time(e1) / reps
 
 
-def kernel_source_hash():
+# Source files each measured kernel is built from: a traffic record taken on
+# other sources is stale and reported as null.
+KERNEL_SOURCES = {
+    "quant": ("quantize.hip", "nvfp4_device.hpp"),
+    "requant": ("quantize.hip", "nvfp4_device.hpp"),
+    "dequant": ("quantize.hip", "nvfp4_device.hpp"),
+    "gemm": ("gemm.hip", "nvfp4_device.hpp"),
+    "mx_gemm": ("mx_gemm.hip",),
+    "mx": ("mx.hip", "nvfp4_device.hpp"),
+    "codec": ("mx.hip", "nvfp4_device.hpp"),
+}
+
+
+def sources_of(kernel_key):
+    for prefix in sorted(KERNEL_SOURCES, key=len, reverse=True):
+        if kernel_key.startswith(prefix):
+            return KERNEL_SOURCES[prefix]
+    raise KeyError(kernel_key)
+
+
+def kernel_source_hash(kernel_key):
     h = hashlib.sha256()
-    for f in ("quantize.hip", "nvfp4_device.hpp", "gemm.hip"):
+    for f in sources_of(kernel_key):
         with open(os.path.join(ROOT, "bit_block_scaled_quantize_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -88,10 +108,10 @@ def traffic_for(kernel_key):
         return None
     with open(path) as fh:
         t = json.load(fh)
-    if t.get("source_hash") != kernel_source_hash():
-        return None
     k = t.get("kernels", {}).get(kernel_key)
-    return None if k is None else k.get("hbm_bytes_per_launch")
+    if k is None or k.get("source_hash") != kernel_source_hash(kernel_key):
+        return None
+    return k.get("hbm_bytes_per_launch")
 
 
 def main():
@@ -104,9 +124,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=20)
     ap.add_argument("--pmc-driver", action="store_true",
-                    help="for rocprofv3 --pmc runs: a 256 MiB device copy (calibration), then each "
-                         "step kernel alone, 3 launches each, then (unless --no-gemm) the forward "
-                         "GEMM twice, and exit")
+                    help="for rocprofv3 --pmc runs: a 1 GiB device copy (calibration), then each "
+                         "step kernel alone, the column re-quantization and the MX quantize / "
+                         "dequantize kernels, 3 launches each, then (unless --no-gemm) the forward "
+                         "GEMM and the two 8192^3 MX GEMMs twice each, and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -237,7 +258,7 @@ def main():
                    "bytes_per_step": step_bytes, "input_buffers": NBUF},
         "roofline": roofline,
         "kernels": {k: {"ms": round(v["ms"], 5), "GB/s": round(v["gbs"], 1),
-                        "frac_hbm": round(v["frac_hbm"], 4)} for k, v in kern.items()},
+                        "frac_hbm": round(v["frac_hbm"], 4), "hbm_bytes": traffic_for(k)} for k, v in kern.items()},
     }
 
     if not args.no_mx:
@@ -280,6 +301,24 @@ def pmc_driver(nv, torch, xs, amax, R, C, R2, C2, Q2d, yr):
     for i in range(3):
         nv.nvfp4_dequantize(R, out=yr)
     torch.cuda.synchronize()
+    # re-quantization along columns of the row-quantized tensor (SR, amax given)
+    Rq = nv.nvfp4_quantize(xs[0], round=1, sr_seed=3)
+    ramax = torch.zeros(1, dtype=torch.float32, device="cuda")
+    nv.nvfp4_requantize(Rq, out=C, amax_out=ramax)
+    torch.cuda.synchronize()
+    for i in range(3):
+        nv.nvfp4_requantize(Rq, round=1, sr_seed=6 + i, amax_in=ramax, out=C)
+    torch.cuda.synchronize()
+    # MX quantize / dequantize
+    E4, E2 = nv.NVFP4_MX_E4M3, nv.NVFP4_MX_E2M1
+    q4, q2 = nv.MXTensor.empty(N, N, E4), nv.MXTensor.empty(N, N, E2)
+    for lay, elem, rnd, q in [(ROW, E4, 0, q4), (ROW, E4, 1, q4), (COL, E4, 1, q4), (ROW, E2, 0, q2), (ROW, E2, 1, q2)]:
+        for i in range(3):
+            nv.nvfp4_mx_quantize(xs[i], layout=lay, elem=elem, round=rnd, sr_seed=5, out=q)
+        torch.cuda.synchronize()
+    for i in range(3):
+        nv.nvfp4_mx_dequantize(q4, out=yr)
+    torch.cuda.synchronize()
 
 
 def pmc_driver_gemm(nv, W, np, torch):
@@ -293,6 +332,19 @@ def pmc_driver_gemm(nv, W, np, torch):
     for _ in range(2):
         nv.nvfp4_gemm(X, Wt, out=Y)
     torch.cuda.synchronize()
+    del X, Wt, Y
+    # MX GEMMs 8192^3, FP32 out
+    for elem in (nv.NVFP4_MX_E4M3, nv.NVFP4_MX_E2M1):
+        A = nv.nvfp4_mx_quantize(bf16_device(W.f32_to_bf16_bits(W.student_t((8192, 8192), 3.0, seed=7100)), torch, np),
+                                 elem=elem)
+        B = nv.nvfp4_mx_quantize(bf16_device(W.f32_to_bf16_bits(W.student_t((8192, 8192), 3.0, seed=7200)), torch, np),
+                                 elem=elem)
+        C = torch.empty((8192, 8192), dtype=torch.float32, device="cuda")
+        torch.cuda.synchronize()
+        for _ in range(2):
+            nv.nvfp4_mx_gemm(A, B, out=C)
+        torch.cuda.synchronize()
+        del A, B, C
 
 
 def bench_gemm(nv, W, np, torch, reps):
@@ -374,7 +426,7 @@ def bench_gemm(nv, W, np, torch, reps):
 def _gbs(name, nbytes, ms):
     gbs = nbytes / (ms * 1e-3) / 1e9
     return {name: {"ms": round(ms, 5), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
-                   "bytes": nbytes}}
+                   "bytes": nbytes, "hbm_bytes": traffic_for(name)}}
 
 
 def bench_mx_quant(nv, torch, xs, reps):
