@@ -734,12 +734,19 @@ __global__ void __launch_bounds__(256) k_amax_req(const uint8_t* __restrict__ ic
     store_partial(a, partial);
 }
 
-// Workgroup (x, y) takes rows 256 y .. + 255 and kReqTiles consecutive tiles of
-// 32 columns from 32 kReqTiles x.  Thread t loads row t's codes and
-// multipliers of all its tiles up front, then per tile dequantizes its 32
-// values into binary32 in the LDS layout of the FP32 column tile, and the
-// column phase runs exactly as for FP32 input.
-constexpr int kReqTiles = 4;
+// Workgroup (x, y) takes rows 256 y .. + 255 and kReqTiles = 8 consecutive
+// tiles of 32 columns from 256 x: per row 128 bytes of codes (one whole cache
+// line) and 16 scale bytes.
+//   load: thread t reads 16-byte code chunk t % 8 of rows t / 8 + 32 k
+//     (k = 0..7), so 8 lanes cover one row's line, and row t's 16 scale
+//     bytes; the codes go to LDS raw, chunk c of row r at chunk c ^ (r % 8);
+//   per tile: thread t takes row t's chunk of that tile (32 codes) and its two
+//     multipliers, dequantizes them into binary32 in the LDS layout of the
+//     FP32 column tile, and the column phase runs exactly as for FP32 input.
+// Workgroups are grouped by XCD in runs of 8 tiles along x (xcd_tile), so the
+// 8 workgroups that share each 128-byte line of scale bytes read it through
+// one L2.
+constexpr int kReqTiles = 8;
 
 template <bool SR, bool RHT>
 __global__ void __launch_bounds__(256) k_requant_col(const uint8_t* __restrict__ icodes,
@@ -749,51 +756,87 @@ __global__ void __launch_bounds__(256) k_requant_col(const uint8_t* __restrict__
                                                      int n_part, uint64_t seed, uint32_t sign_mask,
                                                      uint8_t* __restrict__ ccodes,
                                                      uint8_t* __restrict__ cscales,
-                                                     float* __restrict__ cts, float* amax_out) {
+                                                     float* __restrict__ cts, float* amax_out,
+                                                     int xcd_group) {
     constexpr int STRIDE = ColTile<float>::STRIDE;  // 32 binary32 columns + padding
     __shared__ __attribute__((aligned(16))) uint8_t tile[256 * STRIDE];
+    __shared__ __attribute__((aligned(16))) uint8_t raw[256 * 128];
     const int t = threadIdx.x;
-    const int64_t R0 = (int64_t)blockIdx.y * 256, Cb = (int64_t)blockIdx.x * (32 * kReqTiles);
-    // Rows past the end read a clamped in-range row (their band is never
-    // encoded); a tile with 16 valid columns (cols % 32 == 16) reads its valid
-    // half twice, and tiles past the last column read the last 16 columns
-    // (those copies are never encoded either).
-    const int64_t gr = min(R0 + t, rows - 1);
-    uint2 lo[kReqTiles], hi[kReqTiles];
-    uint32_t s0[kReqTiles], s1[kReqTiles];
+    const TileXY tl = xcd_tile(xcd_group);
+    const int64_t R0 = tl.y * 256, Cb = tl.x * (32 * kReqTiles);
+    const int64_t cb = cols / 2, sb = cols / 16;  // code and scale bytes per row
+
+    // ---- codes: chunk c = t % 8 of rows t / 8 + 32 k.  Rows past the end
+    // read a clamped in-range row (their bands are never encoded); a chunk
+    // with only 16 valid columns (cols % 32 == 16) reads its valid half twice,
+    // and chunks past the last column read the row's first chunk (neither
+    // copy is ever encoded).
+    const int c = t & 7;
+    const int64_t C0 = Cb + 32 * c;
+    const int64_t coff = C0 < cols ? C0 / 2 : 0;
+    const bool whole = C0 + 32 <= cols;
+    uint4 q[8];
 #pragma unroll
-    for (int k = 0; k < kReqTiles; ++k) {
-        const int64_t C0 = Cb + 32 * k;
-        const int64_t cl = C0 < cols ? C0 : cols - 16;
-        const bool two = cl + 32 <= cols;
-        const uint8_t* cp = icodes + gr * (cols / 2) + cl / 2;
-        const uint8_t* sp = iscales + gr * (cols / 16) + cl / 16;
-        lo[k] = *reinterpret_cast<const uint2*>(cp);
-        hi[k] = *reinterpret_cast<const uint2*>(cp + (two ? 8 : 0));
-        s0[k] = sp[0];
-        s1[k] = sp[two ? 1 : 0];
+    for (int k = 0; k < 8; ++k) {
+        const int64_t gr = min(R0 + (t >> 3) + 32 * k, rows - 1);
+        const uint8_t* cp = icodes + gr * cb + coff;
+        if (whole) {
+            q[k] = *reinterpret_cast<const uint4*>(cp);
+        } else {
+            const uint2 lo = *reinterpret_cast<const uint2*>(cp);
+            q[k] = make_uint4(lo.x, lo.y, lo.x, lo.y);
+        }
+    }
+    // ---- scale bytes of row t for the 8 tiles (clamped like the codes)
+    const int64_t sr = min(R0 + t, rows - 1);
+    uint32_t sv[4];
+    if (sb % 16 == 0 && (reinterpret_cast<uintptr_t>(iscales) & 15) == 0 && Cb + 256 <= cols) {
+        const uint4 v = *reinterpret_cast<const uint4*>(iscales + sr * sb + Cb / 16);
+        sv[0] = v.x; sv[1] = v.y; sv[2] = v.z; sv[3] = v.w;
+    } else {
+        uint8_t b[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int64_t sc = Cb / 16 + j;
+            b[j] = iscales[sr * sb + (sc < sb ? sc : sb - 1)];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            sv[j] = b[4 * j] | (b[4 * j + 1] << 8) | (b[4 * j + 2] << 16) | ((uint32_t)b[4 * j + 3] << 24);
     }
     const float st_in = its[0];
     const TensorScale ts = prologue(amax_src, n_part, cts, nullptr, amax_out);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const int r = (t >> 3) + 32 * k;
+        *reinterpret_cast<uint4*>(raw + r * 128 + 16 * (c ^ (r & 7))) = q[k];
+    }
+    __syncthreads();
+
     const int sw = (t >> 4) & 15;
     uint8_t* rowp = tile + t * STRIDE;
 #pragma unroll
     for (int k = 0; k < kReqTiles; ++k) {
-        const int64_t C0 = Cb + 32 * k;
-        if (C0 >= cols) break;  // uniform across the workgroup
+        const int64_t T0 = Cb + 32 * k;
+        if (T0 >= cols) break;  // uniform across the workgroup
         if (k > 0) __syncthreads();  // the previous tile's column reads are done
+        const uint4 w = *reinterpret_cast<const uint4*>(raw + t * 128 + 16 * (k ^ (t & 7)));
+        const uint32_t sw2 = sv[k >> 1] >> (16 * (k & 1));
+        const float m0 = e4m3_value(sw2 & 0xFFu), m1 = e4m3_value((sw2 >> 8) & 0xFFu);
         float v[32];
-        dequant8(lo[k].x, e4m3_value(s0[k]), st_in, v);
-        dequant8(lo[k].y, e4m3_value(s0[k]), st_in, v + 8);
-        dequant8(hi[k].x, e4m3_value(s1[k]), st_in, v + 16);
-        dequant8(hi[k].y, e4m3_value(s1[k]), st_in, v + 24);
+        dequant8(w.x, m0, st_in, v);
+        dequant8(w.y, m0, st_in, v + 8);
+        // a tile with 16 valid columns (the last, when cols % 32 == 16) has its
+        // valid half copied into the upper half: never encoded
+        dequant8(w.z, T0 + 32 <= cols ? m1 : m0, st_in, v + 16);
+        dequant8(w.w, T0 + 32 <= cols ? m1 : m0, st_in, v + 24);
 #pragma unroll
         for (int j = 0; j < 16; ++j)
             *reinterpret_cast<uint2*>(rowp + 8 * (j ^ sw)) =
                 make_uint2(__float_as_uint(v[2 * j]), __float_as_uint(v[2 * j + 1]));
         __syncthreads();
         if (R0 + 16 * (t & 15) < rows)  // (a band past the end: no column work, but stay for the barriers)
-            tile_col_blocks<float, SR, RHT>(tile, R0, C0, rows, cols, ts, seed, sign_mask, ccodes, cscales);
+            tile_col_blocks<float, SR, RHT>(tile, R0, T0, rows, cols, ts, seed, sign_mask, ccodes, cscales);
     }
 }
 
@@ -946,9 +989,11 @@ hipError_t launch_requantize(const uint8_t* icodes, const uint8_t* iscales, cons
         np = (int)gx;
     }
     dim3 g((unsigned)cdiv(cols, 32 * kReqTiles), (unsigned)cdiv(rows, 256));
+    // runs of 8 tiles along x share their scale-byte lines: one XCD each
+    const int xg = g.x % 8 == 0 ? 8 : 1;
 #define NVFP4_REQ(SRV, RHTV)                                                                       \
     hipLaunchKernelGGL((k_requant_col<SRV, RHTV>), g, dim3(256), 0, s, icodes, iscales, its, rows, \
-                       cols, amax, np, seed, mask, out->codes, out->scales, out->ts, amax_out)
+                       cols, amax, np, seed, mask, out->codes, out->scales, out->ts, amax_out, xg)
     if (sr) {
         if (rht) NVFP4_REQ(true, true); else NVFP4_REQ(true, false);
     } else {
