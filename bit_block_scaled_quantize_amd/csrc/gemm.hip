@@ -632,6 +632,209 @@ __global__ void __launch_bounds__(256, 1) k_gemm_ring(GemmArgs p) {
     epilogue<GROUPED, SWIGLU, OUT_BF16>(p, acc, m0, m_end, g, wm, wn, h, l32, lane);
 }
 
+// ============================================================ full-line kernel
+// For K % 512 == 0 with 16-byte-aligned scale rows (every benchmarked shape):
+// the ring kernel's tile, fragment conversion and MFMA interleave, with the
+// operands moved in whole cache lines.  Each distinct line a wave-wide load
+// touches costs about the same whatever part of it is used, and the ring
+// kernel's 32-byte code and 4-byte scale pieces per row and step made the
+// loads 12% of its time.  Here a slot holds 128 bytes of codes per tile row
+// (256 K elements, 4 K steps) and that chunk's 16 scale bytes per row -- one
+// 16-byte load per row -- for both operands; two slots, the next chunk's loads
+// in flight during a whole chunk (4 steps of 64 MFMAs), one barrier per chunk.
+// 16-byte code chunk c of slot row r sits at chunk c ^ (r % 8) ^ ((r / 8) % 4)
+// (row bits 0..4; fragment rows 32 apart share it), which spreads the
+// fragment reads over every bank.
+constexpr int kFullCodes = kBM * 128;  // code bytes per operand per slot
+constexpr int kFullSc = kBM * 16;      // scale bytes per operand per slot
+
+// One ring slot: four separate LDS arrays (A codes, B codes, A scales, B
+// scales).  Declared per slot as distinct variables, so the compiler can tell
+// the slot being read from the one in-flight loads target; the same-operand
+// arrays of the two slots end up 32 KiB (codes) or 4 KiB (scales) apart, so
+// one address register per fragment row serves both slots through the LDS
+// instruction's immediate offset.
+struct FullSlot {
+    uint8_t* a_codes;
+    uint8_t* b_codes;
+    uint8_t* a_sc;
+    uint8_t* b_sc;
+};
+
+__device__ __forceinline__ int full_swz(int r) { return (r ^ ((r >> 3) & 3)) & 7; }
+
+// Wave-uniform bases and 32-bit per-lane byte offsets of the chunk-0 sources:
+// code loads t = 0..7 (tile rows 64 w + 8 t + L / 8, chunk L % 8), scale rows
+// 64 w + L.
+struct FullSrc {
+    const uint8_t *ac, *bc, *as, *bs;
+    uint32_t a[8], b[8];
+    uint32_t sa, sb;
+};
+constexpr int kFullLoadsPerChunk = 18;
+
+__device__ __forceinline__ void full_load(const FullSrc& src, int64_t chunk, const FullSlot& slot, int w) {
+    const uint8_t* ac = src.ac + chunk * 128;
+    const uint8_t* bc = src.bc + chunk * 128;
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+        __builtin_amdgcn_global_load_lds((gmem_t*)(ac + src.a[t]), (lmem_t*)(slot.a_codes + (64 * w + 8 * t) * 128), 16,
+                                         0, 0);
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+        __builtin_amdgcn_global_load_lds((gmem_t*)(bc + src.b[t]), (lmem_t*)(slot.b_codes + (64 * w + 8 * t) * 128), 16,
+                                         0, 0);
+    __builtin_amdgcn_global_load_lds((gmem_t*)(src.as + chunk * 16 + src.sa), (lmem_t*)(slot.a_sc + 64 * w * 16), 16, 0,
+                                     0);
+    __builtin_amdgcn_global_load_lds((gmem_t*)(src.bs + chunk * 16 + src.sb), (lmem_t*)(slot.b_sc + 64 * w * 16), 16, 0,
+                                     0);
+}
+
+// Raw fragments of K step t (0..3) of a chunk: lane (l32, h) takes the
+// step's codes K = 32 h .. 32 h + 31 (logical chunk 2 t + h) and the scale
+// bytes of blocks 2 h, 2 h + 1, as in the ring kernel.
+__device__ __forceinline__ void full_read_frags(const FullSlot& slot, int t, int arow0, const int (&brow)[4], int l32,
+                                                int h, RawFrags& f) {
+    const int pc = (2 * t + h) ^ full_swz(l32);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = arow0 + 32 * i + l32;
+        f.c[i] = *reinterpret_cast<const uint4*>(&slot.a_codes[r * 128 + 16 * pc]);
+        f.sb[i] = *reinterpret_cast<const uint16_t*>(&slot.a_sc[r * 16 + 4 * t + 2 * h]);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int r = brow[j] + l32;
+        f.c[4 + j] = *reinterpret_cast<const uint4*>(&slot.b_codes[r * 128 + 16 * pc]);
+        f.sb[4 + j] = *reinterpret_cast<const uint16_t*>(&slot.b_sc[r * 16 + 4 * t + 2 * h]);
+    }
+    f.zero = false;
+}
+
+template <bool GROUPED, bool SWIGLU, bool OUT_BF16>
+__global__ void __launch_bounds__(256, 1) k_gemm_full(GemmArgs p) {
+    __shared__ __attribute__((aligned(16))) uint8_t a0c[kFullCodes];
+    __shared__ __attribute__((aligned(16))) uint8_t a1c[kFullCodes];
+    __shared__ __attribute__((aligned(16))) uint8_t b0c[kFullCodes];
+    __shared__ __attribute__((aligned(16))) uint8_t b1c[kFullCodes];
+    __shared__ __attribute__((aligned(16))) uint8_t a0s[kFullSc];
+    __shared__ __attribute__((aligned(16))) uint8_t a1s[kFullSc];
+    __shared__ __attribute__((aligned(16))) uint8_t b0s[kFullSc];
+    __shared__ __attribute__((aligned(16))) uint8_t b1s[kFullSc];
+    const FullSlot slot0{a0c, b0c, a0s, b0s}, slot1{a1c, b1c, a1s, b1s};
+    const int tid = threadIdx.x;
+    // the wave index is uniform: held in a scalar register, the LDS
+    // destinations of the loads need no vector registers
+    const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = w >> 1, wn = w & 1;
+    const int h = lane >> 5, l32 = lane & 31;
+
+    const TileRows tr = tile_rows<GROUPED>(p);
+    if (!tr.ok) return;  // uniform across the workgroup
+    const int64_t m0 = tr.m0, m_end = tr.m_end;
+    const int g = tr.g;
+    const int64_t K = p.K, kc2 = K / 2, ks = K / 16;
+    const int64_t bbase = GROUPED ? (int64_t)g * p.N : 0;
+
+    FullSrc src;
+    src.ac = p.A.codes + m0 * kc2;
+    src.bc = p.B.codes + bbase * kc2;
+    src.as = p.A.scales;
+    src.bs = p.B.scales;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const int r = 64 * w + 8 * t + (lane >> 3);
+        const int c = (lane & 7) ^ full_swz(r);  // the swizzle is an involution
+        src.a[t] = (uint32_t)((min(m0 + r, m_end - 1) - m0) * kc2 + 16 * c);
+        src.b[t] = (uint32_t)((b_row<SWIGLU>(p, bbase, r) - bbase) * kc2 + 16 * c);
+    }
+    {
+        const int r = 64 * w + lane;
+        const int64_t ga = min(m0 + r, m_end - 1), gb = b_row<SWIGLU>(p, bbase, r);
+        src.sa = (uint32_t)((p.A.scale_2d ? ga / 16 : ga) * ks);
+        src.sb = (uint32_t)((p.B.scale_2d ? gb / 16 : gb) * ks);
+    }
+    const int arow0 = 128 * wm;
+    int brow[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) brow[j] = b_tile_row<SWIGLU>(wn, j);
+
+    float16_t acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    const int64_t nchunks = K / 256;  // even: K % 512 == 0
+    auto cclamp = [&](int64_t c) { return c < nchunks ? c : nchunks - 1; };
+    full_load(src, 0, slot0, w);
+    full_load(src, 1, slot1, w);
+    __builtin_amdgcn_s_waitcnt(vmcnt_at_most(kFullLoadsPerChunk));  // chunk 0 landed
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+
+    RawFrags fx, fy;            // raw fragments of the current / next step (alternating)
+    uint32_t op[2][8][4];       // converted fragments, double-buffered by substep
+    full_read_frags(slot0, 0, arow0, brow, l32, h, fx);
+    scale_frags(fx);
+#pragma unroll
+    for (int o = 0; o < 8; ++o)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) op[0][o][q] = frag_piece(fx, o, 0, q);
+
+    // K step t (0..3) of the chunk in `cur`; `other` holds the next chunk
+    auto step = [&](int64_t chunk, int t, const FullSlot& cur, const FullSlot& other, RawFrags& fc, RawFrags& fn) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int ob = s & 1;
+            if (s == 2) {
+                if (t == 3) {
+                    // the next chunk's loads landed; after the barrier every
+                    // wave has read all of `cur`, which takes chunk + 2
+                    __builtin_amdgcn_s_waitcnt(vmcnt_at_most(0));
+                    asm volatile("" ::: "memory");
+                    __builtin_amdgcn_s_barrier();
+                    asm volatile("" ::: "memory");
+                    full_read_frags(other, 0, arow0, brow, l32, h, fn);
+                    full_load(src, cclamp(chunk + 2), cur, w);
+                } else {
+                    full_read_frags(cur, t + 1, arow0, brow, l32, h, fn);
+                }
+            }
+            if (s == 3) scale_frags(fn);  // first use of the next step's fragments
+#pragma unroll
+            for (int m = 0; m < 16; ++m) {
+                const int i = m >> 2, jj = m & 3;
+                acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                    __builtin_bit_cast(half8_t, op[ob][i]), __builtin_bit_cast(half8_t, op[ob][4 + jj]),
+                    acc[i][jj], 0, 0, 0);
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const int piece = 2 * m + u, o = piece >> 2, q = piece & 3;
+                    op[ob ^ 1][o][q] = s < 3 ? frag_piece(fc, o, s + 1, q) : frag_piece(fn, o, 0, q);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    };
+    for (int64_t ch = 0; ch < nchunks; ch += 2) {
+        step(ch, 0, slot0, slot1, fx, fy);
+        step(ch, 1, slot0, slot1, fy, fx);
+        step(ch, 2, slot0, slot1, fx, fy);
+        step(ch, 3, slot0, slot1, fy, fx);
+        step(ch + 1, 0, slot1, slot0, fx, fy);
+        step(ch + 1, 1, slot1, slot0, fy, fx);
+        step(ch + 1, 2, slot1, slot0, fx, fy);
+        step(ch + 1, 3, slot1, slot0, fy, fx);
+    }
+    // the last look-ahead loads (clamped re-reads) land before the LDS is released
+    __builtin_amdgcn_s_waitcnt(vmcnt_at_most(0));
+    epilogue<GROUPED, SWIGLU, OUT_BF16>(p, acc, m0, m_end, g, wm, wn, h, l32, lane);
+}
+
 __global__ void k_zero_float(float* p) {
     if (threadIdx.x == 0) p[0] = 0.0f;
 }
@@ -644,6 +847,16 @@ inline bool fast_path(const Operand& A, const Operand& B, int64_t K) {
     return K % kBK == 0 && (reinterpret_cast<uintptr_t>(A.scales) & 3) == 0 &&
            (reinterpret_cast<uintptr_t>(B.scales) & 3) == 0;
 }
+
+// The full-line kernel: 512-multiple K, 16-byte-aligned scale rows, and
+// per-lane byte offsets that fit 32 bits (B's rows of one group and either
+// operand's scale rows).
+inline bool full_path(const Operand& A, const Operand& B, int64_t a_rows, int64_t b_rows, int64_t K) {
+    const uint64_t lim = (uint64_t)1 << 32;
+    return K > 0 && K % 512 == 0 && (reinterpret_cast<uintptr_t>(A.scales) & 15) == 0 &&
+           (reinterpret_cast<uintptr_t>(B.scales) & 15) == 0 && (uint64_t)b_rows * (uint64_t)(K / 2) < lim &&
+           (uint64_t)a_rows * (uint64_t)(K / 16) < lim && (uint64_t)b_rows * (uint64_t)(K / 16) < lim;
+}
 }  // namespace
 
 hipError_t launch_gemm(const Operand& A, const Operand& B, int64_t M, int64_t N, int64_t K,
@@ -651,7 +864,12 @@ hipError_t launch_gemm(const Operand& A, const Operand& B, int64_t M, int64_t N,
     if (M == 0 || N == 0) return hipSuccess;
     GemmArgs p{A, B, M, N, K, C, ldc, nullptr, 1, nullptr};
     dim3 grid((unsigned)cdiv(N, kBN), (unsigned)cdiv(M, kBM));
-    if (fast_path(A, B, K)) {
+    if (full_path(A, B, M, N, K)) {
+        if (c_bf16)
+            hipLaunchKernelGGL((k_gemm_full<false, false, true>), grid, dim3(256), 0, s, p);
+        else
+            hipLaunchKernelGGL((k_gemm_full<false, false, false>), grid, dim3(256), 0, s, p);
+    } else if (fast_path(A, B, K)) {
         if (c_bf16)
             hipLaunchKernelGGL((k_gemm_ring<false, false, true>), grid, dim3(256), 0, s, p);
         else
@@ -675,9 +893,12 @@ hipError_t launch_grouped_gemm(int G, const Operand& A, const int64_t* offsets, 
     // every group wastes at most one partial tile
     const int64_t mtiles = cdiv(total_rows, kBM) + G;
     const bool fast = fast_path(A, B, K);
+    const bool full = full_path(A, B, total_rows, n_per_group, K);
 #define NVFP4_GROUPED(SW, BF)                                                                   \
     do {                                                                                        \
-        if (fast)                                                                               \
+        if (full)                                                                               \
+            hipLaunchKernelGGL((k_gemm_full<true, SW, BF>), grid, dim3(256), 0, s, p);         \
+        else if (fast)                                                                          \
             hipLaunchKernelGGL((k_gemm_ring<true, SW, BF>), grid, dim3(256), 0, s, p);         \
         else                                                                                    \
             hipLaunchKernelGGL((k_gemm<true, SW, BF, false>), grid, dim3(256), 0, s, p);       \
