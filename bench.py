@@ -6,7 +6,9 @@ from Student-t(3) is quantized to NVFP4 along rows and along columns
 stochastic rounding, in separate calls and in the fused row+column call; the
 first call computes the tensor amax and publishes it (amax_out), the other
 five reuse it (amax_in), as a pipeline quantizing one tensor several ways
-would; the row and column results are then dequantized back to BF16.
+would; the row and column results are then dequantized back to BF16.  The
+step is timed as HIP graph replays (one graph per input buffer, captured from
+the same calls; --no-graph times eager launches; both are reported).
 `value` is the algorithmic bytes of the step (input read once + codes +
 scales per quantize call; codes + scales + output per dequantize call; the
 amax pass is not credited) divided by the step time, in GB/s.  Inputs rotate over 4 device buffers (512 MiB) so that
@@ -121,6 +123,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-gemm", action="store_true")
     ap.add_argument("--no-mx", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time the step as eager launches instead of HIP graph replays")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=20)
     ap.add_argument("--pmc-driver", action="store_true",
@@ -187,17 +191,34 @@ def main():
         nv.nvfp4_dequantize(R, out=yr)
         nv.nvfp4_dequantize(C, out=yc)
 
-    log("warmup")
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    log("timed steps")
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms = (t1 - t0) * 1e3 / args.steps
+    def timed(run):
+        for i in range(args.warmup):
+            run(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            run(i)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        return (t1 - t0) * 1e3 / args.steps
+
+    log("eager steps")
+    eager_ms = timed(step)
+    if args.no_graph:
+        ms = eager_ms
+    else:
+        # The step is a fixed sequence of launches: one HIP graph per input
+        # buffer (captured from the same calls, seeds fixed per buffer)
+        # replays it without the host-side gaps between launches.
+        log("graph capture and timed steps")
+        graphs = []
+        for b in range(NBUF):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(b)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        ms = timed(lambda i: graphs[i % NBUF].replay())
     value = step_bytes / (ms * 1e-3) / 1e9
 
     # ---- per-kernel durations (amax given, so each call is one kernel)
@@ -255,7 +276,9 @@ def main():
                    "input": "bf16", "step": [k for k, *_ in step_ops] + ["dequant_row_bf16",
                                                                        "dequant_col_bf16"],
                    "amax": "computed once per tensor by the first call (amax_out) and reused by the others (amax_in)",
-                   "bytes_per_step": step_bytes, "input_buffers": NBUF},
+                   "bytes_per_step": step_bytes, "input_buffers": NBUF,
+                   "launch": "eager" if args.no_graph else "hip_graph_replay",
+                   "eager_ms_per_step": round(eager_ms, 4)},
         "roofline": roofline,
         "kernels": {k: {"ms": round(v["ms"], 5), "GB/s": round(v["gbs"], 1),
                         "frac_hbm": round(v["frac_hbm"], 4), "hbm_bytes": traffic_for(k)} for k, v in kern.items()},

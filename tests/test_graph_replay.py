@@ -1,0 +1,89 @@
+"""HIP graph capture of the library's calls: a sequence covering every entry
+point (quantize with its amax pass and with a given amax, the fused and 2D
+layouts, dequantize, re-quantization, MX quantize/dequantize, both GEMMs and
+the grouped GEMM with its SwiGLU epilogue and amax) is captured once and
+replayed several times, with eager work that overwrites every output in
+between; every replay must reproduce the eager results bit for bit.  The
+library records only kernel launches (no memsets), which is what makes its
+calls capturable."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+from parity_utils import require_gpu, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def nv():
+    return require_gpu()
+
+
+def test_sequence_graph_replays_match_eager(nv):
+    R, C = 512, 768
+    x = to_device(W.f32_to_bf16_bits(W.student_t((R, C), 3.0, seed=31)))
+    dev = "cuda"
+    ws = torch.empty(nv.nvfp4_quantize_workspace_size(R, C) // 4 + 4, dtype=torch.float32, device=dev)
+    amax = torch.zeros(1, dtype=torch.float32, device=dev)
+    qr = nv.NVFP4Tensor.empty(R, C)
+    qc = nv.NVFP4Tensor.empty(C, R)
+    q2r, q2c = nv.NVFP4Tensor.empty(R, C), nv.NVFP4Tensor.empty(C, R)
+    qb = nv.NVFP4Tensor.empty(R, C, nv.NVFP4_SCALE_2D)
+    rq = nv.NVFP4Tensor.empty(C, R)
+    y = torch.empty((R, C), dtype=torch.bfloat16, device=dev)
+    mq = nv.MXTensor.empty(R, C, nv.NVFP4_MX_E4M3)
+    my = torch.empty((R, C), dtype=torch.float32, device=dev)
+    gc = torch.empty((R, R), dtype=torch.float32, device=dev)
+    mc = torch.empty((R, R), dtype=torch.float32, device=dev)
+    # grouped: 3 groups over the 512 rows, weights 3 x 64 x 768 (SwiGLU: F = 32)
+    offs = torch.tensor([0, 100, 100, 512], dtype=torch.int64, device=dev)
+    wq = nv.nvfp4_quantize(to_device(W.f32_to_bf16_bits(W.normal((192, C), 0.02, seed=32))),
+                           layout=nv.NVFP4_BLK_2D)
+    wstack = nv.NVFP4Tensor(wq.codes, wq.scales, wq.tensor_scale.repeat(3).contiguous(), 192, C,
+                            nv.NVFP4_SCALE_2D)
+    h = torch.empty((R, 32), dtype=torch.bfloat16, device=dev)
+    hmax = torch.zeros(1, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    def seq():
+        nv.nvfp4_quantize(x, round=nv.NVFP4_SR, sr_seed=1, out=qr, workspace=ws, amax_out=amax)
+        nv.nvfp4_quantize(x, layout=nv.NVFP4_COL_1D, round=nv.NVFP4_SR, sr_seed=2, out=qc, amax_in=amax)
+        nv.nvfp4_quantize(x, layout=nv.NVFP4_ROW_COL_1D, round=nv.NVFP4_SR, sr_seed=3, out=(q2r, q2c),
+                          amax_in=amax)
+        nv.nvfp4_quantize(x, layout=nv.NVFP4_BLK_2D, out=qb, workspace=ws)
+        nv.nvfp4_dequantize(qr, out=y)
+        nv.nvfp4_requantize(qr, round=nv.NVFP4_SR, sr_seed=4, hadamard=True, hadamard_seed=5, out=rq,
+                            workspace=ws)
+        nv.nvfp4_mx_quantize(x, round=nv.NVFP4_SR, sr_seed=6, out=mq)
+        nv.nvfp4_mx_dequantize(mq, out=my)
+        nv.nvfp4_gemm(qr, q2r, out=gc)
+        nv.nvfp4_mx_gemm(mq, mq, out=mc)
+        nv.nvfp4_grouped_gemm(qr, offs, wstack, 3, epilogue=nv.NVFP4_EPI_SWIGLU, out=h, amax_out=hmax)
+
+    outputs = [amax, qr.codes, qr.scales, qr.tensor_scale, qc.codes, qc.scales, q2r.codes, q2r.scales,
+               q2c.codes, q2c.scales, qb.codes, qb.scales, qb.tensor_scale, y, rq.codes, rq.scales,
+               rq.tensor_scale, mq.codes, mq.scales, my, gc, mc, h, hmax]
+
+    seq()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in outputs]
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        seq()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        # eager work between replays: overwrite every output
+        for t in outputs:
+            t.view(torch.uint8).fill_(0x5A + rep)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k, (t, r) in enumerate(zip(outputs, ref)):
+            assert torch.equal(t.view(torch.uint8), r.view(torch.uint8)), f"replay {rep}: output {k} differs"
+    # and the eager results are the oracle's (one spot check: the row quantization)
+    q = O.quantize(x.cpu().view(torch.int16).numpy().view(np.uint16), O.BF16, O.ROW_1D, O.SR, sr_seed=1)
+    assert np.array_equal(ref[1].cpu().numpy(), q.codes) and np.array_equal(ref[2].cpu().numpy(), q.scales)
