@@ -53,6 +53,13 @@ namespace nvfp4 {
 namespace {
 
 typedef int v8i_t __attribute__((ext_vector_type(8)));
+typedef int v4i_t __attribute__((ext_vector_type(4)));
+
+// 16 bytes of LDS as one vector load (one ds_read_b128 that keeps the
+// access's memory information; a struct load is split into dwords and
+// re-merged, and the compiler then lost track of which slot a read touches
+// and waited for every outstanding load before it).
+__device__ __forceinline__ v4i_t lds16(const uint8_t* p) { return *reinterpret_cast<const v4i_t*>(p); }
 typedef float v16f_t __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(1))) void gmem_t;
 typedef __attribute__((address_space(3))) void lmem_t;
@@ -402,20 +409,19 @@ __device__ __forceinline__ void mx_full_frags(const uint8_t* slot, int t, int ro
     using F = MxFull<ELEM>;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+        const uint8_t* ra = slot + (rowa + 32 * i) * 128;
+        const uint8_t* rb = slot + F::CODES + (rowb + 32 * i) * 128;
         if constexpr (ELEM == kMxE4M3) {
             const int clo = (4 * t + h) ^ sw, chi = (4 * t + 2 + h) ^ sw;
-            const uint4 alo = *reinterpret_cast<const uint4*>(slot + (rowa + 32 * i) * 128 + 16 * clo);
-            const uint4 ahi = *reinterpret_cast<const uint4*>(slot + (rowa + 32 * i) * 128 + 16 * chi);
-            const uint4 blo = *reinterpret_cast<const uint4*>(slot + F::CODES + (rowb + 32 * i) * 128 + 16 * clo);
-            const uint4 bhi = *reinterpret_cast<const uint4*>(slot + F::CODES + (rowb + 32 * i) * 128 + 16 * chi);
-            a[i] = v8i_t{(int)alo.x, (int)alo.y, (int)alo.z, (int)alo.w, (int)ahi.x, (int)ahi.y, (int)ahi.z, (int)ahi.w};
-            b[i] = v8i_t{(int)blo.x, (int)blo.y, (int)blo.z, (int)blo.w, (int)bhi.x, (int)bhi.y, (int)bhi.z, (int)bhi.w};
+            const v4i_t alo = lds16(ra + 16 * clo), ahi = lds16(ra + 16 * chi);
+            const v4i_t blo = lds16(rb + 16 * clo), bhi = lds16(rb + 16 * chi);
+            a[i] = v8i_t{alo[0], alo[1], alo[2], alo[3], ahi[0], ahi[1], ahi[2], ahi[3]};
+            b[i] = v8i_t{blo[0], blo[1], blo[2], blo[3], bhi[0], bhi[1], bhi[2], bhi[3]};
         } else {
             const int c = (2 * t + h) ^ sw;
-            const uint4 aq = *reinterpret_cast<const uint4*>(slot + (rowa + 32 * i) * 128 + 16 * c);
-            const uint4 bq = *reinterpret_cast<const uint4*>(slot + F::CODES + (rowb + 32 * i) * 128 + 16 * c);
-            a[i] = v8i_t{(int)aq.x, (int)aq.y, (int)aq.z, (int)aq.w, 0, 0, 0, 0};
-            b[i] = v8i_t{(int)bq.x, (int)bq.y, (int)bq.z, (int)bq.w, 0, 0, 0, 0};
+            const v4i_t aq = lds16(ra + 16 * c), bq = lds16(rb + 16 * c);
+            a[i] = v8i_t{aq[0], aq[1], aq[2], aq[3], 0, 0, 0, 0};
+            b[i] = v8i_t{bq[0], bq[1], bq[2], bq[3], 0, 0, 0, 0};
         }
     }
 }
@@ -444,7 +450,8 @@ __global__ void __launch_bounds__(256, 1) k_mx_gemm_full(MxGemmArgs p) {
     const int tid = threadIdx.x;
     // the wave index is uniform: held in a scalar register, the LDS
     // destinations of the ring loads need no vector registers
-    const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // (& 3: the compiler then knows every LDS offset below stays inside its slot)
+    const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6) & 3;
     const int wm = w >> 1, wn = w & 1;
     const int h = lane >> 5, l32 = lane & 31;
     const int64_t M = p.M, N = p.N, K = p.K;
