@@ -40,7 +40,7 @@ def quant_host(x, layout, rnd=O.RNE, seed=0):
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 16), (32, 32, 64), (100, 70, 80), (130, 260, 1040),
                                    (300, 128, 4112), (257, 129, 48), (64, 256, 192), (96, 160, 320),
-                                   (260, 300, 1024)])
+                                   (260, 300, 1024), (300, 260, 512), (33, 530, 1536)])
 @pytest.mark.parametrize("bmode", [O.ROW_1D, O.BLK_2D])
 @pytest.mark.parametrize("out", ["f32", "bf16"])
 def test_gemm_small(nv, M, N, K, bmode, out):
@@ -154,6 +154,19 @@ def test_grouped_gemm_small(nv, counts, bmode):
     check(out_to_f64(C), Cref, Wref, False, f"grouped {counts}")
 
 
+@pytest.mark.parametrize("counts", [[5, 0, 130, 64], [128, 128, 1, 255, 17]])
+@pytest.mark.parametrize("bmode", [O.ROW_1D, O.BLK_2D])
+def test_grouped_gemm_full_line_path(nv, counts, bmode):
+    """K = 512: the full-line kernel (whole 128-byte code lines per row),
+    ragged and empty groups, both scale layouts of the weights."""
+    N, K = 96, 512
+    offs, A, Bs = _grouped_inputs(counts, N, K, seed=sum(counts) + 11, bmode=bmode)
+    C = nv.nvfp4_grouped_gemm(q_to_device(A, nv), torch.from_numpy(offs).cuda(), _stack_device(Bs, nv),
+                              len(counts), out_dtype=torch.bfloat16)
+    Cref, Wref = O.grouped_gemm(A, offs, Bs)
+    check(out_to_f64(C), Cref, Wref, True, f"grouped full-line {counts}")
+
+
 def _swiglu_tol(G_, U_, Wg, Wu):
     from scipy.special import expit
     s = expit(G_)
@@ -183,6 +196,10 @@ def check_swiglu(nv, counts, F, K, seed):
 
 def test_grouped_swiglu_small(nv):
     check_swiglu(nv, [70, 0, 129, 33], F=80, K=160, seed=21)
+
+
+def test_grouped_swiglu_full_line_path(nv):
+    check_swiglu(nv, [70, 0, 129, 33], F=80, K=1024, seed=22)
 
 
 def test_swiglu_then_quantize_is_oracle_exact(nv):
