@@ -194,14 +194,22 @@ struct BlockScale {
     float R;
 };
 
-// Block multiplier: u = A_b / (6 s_t) rounded to E4M3; S = e4m3(u) * s_t;
-// R = 1/S (0 when S is 0, which makes every magnitude 0).
-__device__ __forceinline__ BlockScale block_scale(float amax_b, float six_st, float st) {
+// Multiplier of E4M3 byte b for a tensor with scale s_t: S = e4m3(b) * s_t,
+// R = 1/S (0 when S is 0, which makes every magnitude 0).  A block's S is one
+// of the 127 values S(b), so a workgroup computes R(b) once per byte into a
+// table (the same binary32 operations) and blocks look it up instead of
+// dividing.  Byte 0x7F (NaN) gives 0 and is never produced by e4m3_encode.
+__device__ __forceinline__ float block_multiplier(uint32_t b, float st) {
+    const float S = e4m3_value(b) * st;
+    return S > 0.0f ? 1.0f / S : 0.0f;
+}
+
+// Block scale: u = A_b / (6 s_t) rounded to E4M3 (the byte), R from the
+// tensor's multiplier table rtab[128].
+__device__ __forceinline__ BlockScale block_scale(float amax_b, float six_st, const float* rtab) {
     BlockScale bs;
-    float u = amax_b / six_st;
-    bs.byte = e4m3_encode(u);
-    float S = e4m3_value(bs.byte) * st;
-    bs.R = S > 0.0f ? 1.0f / S : 0.0f;
+    bs.byte = e4m3_encode(amax_b / six_st);
+    bs.R = rtab[bs.byte];
     return bs;
 }
 
@@ -244,7 +252,38 @@ __device__ __forceinline__ uint32_t sr_seed(uint32_t word, int high_half) {
 //   Blocks with R = inf (S below 2^-128), or whose scaled values could
 //   overflow (amax_b * R >= 2^100, possible only with a caller-supplied A_t
 //   below the true one), take the plain VALU path of e2m1_rne / e2m1_sr.
-template <bool SR, int N>
+// Codes of the 8 values p[0..7] by stochastic rounding into one word (see
+// encode).  FOLD computes z = ceil(fl(|t| * R23)) with R23 = R * 2^23, one
+// multiply instead of two; the caller guarantees that this equals
+// ceil(fl(|t| * R) * 2^23).
+template <bool FOLD>
+__device__ __forceinline__ uint32_t sr_word8(const float* p, float R, const uint32_t* wk) {
+    typedef float f2_t __attribute__((ext_vector_type(2)));
+    const float R23 = R * 0x1p23f;
+    uint32_t ce[4], co[4];
+#pragma unroll
+    for (int J = 0; J < 4; ++J) {
+        const float z0 = FOLD ? __builtin_ceilf(fabsf(p[2 * J]) * R23)
+                              : __builtin_ceilf((fabsf(p[2 * J]) * R) * 0x1p23f);
+        const float z1 = FOLD ? __builtin_ceilf(fabsf(p[2 * J + 1]) * R23)
+                              : __builtin_ceilf((fabsf(p[2 * J + 1]) * R) * 0x1p23f);
+        // the second slot's value is left unspecified: its nibble is masked off
+        const float any = __builtin_nondeterministic_value(z0);
+        const f2_t e = {__uint_as_float(__float_as_uint(z0) | (__float_as_uint(p[2 * J]) & 0x80000000u)), any};
+        const f2_t o = {__uint_as_float(__float_as_uint(z1) | (__float_as_uint(p[2 * J + 1]) & 0x80000000u)), any};
+        ce[J] = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, e, sr_seed(wk[J], 0), 0x1p23f, 0);
+        co[J] = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, o, sr_seed(wk[J], 1), 0x1p23f, 0);
+    }
+    // perm(b, a, lo2): byte 0 of a -> byte 0, byte 0 of b -> byte 1, bytes 2 and 3 zero
+    const uint32_t lo2 = 0x0C0C0400u;
+    const uint32_t ev = (__builtin_amdgcn_perm(ce[1], ce[0], lo2) |
+                         (__builtin_amdgcn_perm(ce[3], ce[2], lo2) << 16)) & 0x0F0F0F0Fu;
+    const uint32_t od = (__builtin_amdgcn_perm(co[1], co[0], lo2) |
+                         (__builtin_amdgcn_perm(co[3], co[2], lo2) << 16)) & 0x0F0F0F0Fu;
+    return ev | (od << 4);
+}
+
+template <bool SR, int N, bool FOLD = false>
 __device__ __forceinline__ void encode(const float* v, BlockScale bs, float amax_b, const uint32_t* w,
                                        uint32_t* out) {
     typedef float f2_t __attribute__((ext_vector_type(2)));
@@ -262,38 +301,30 @@ __device__ __forceinline__ void encode(const float* v, BlockScale bs, float amax
         }
         return;
     }
+    if (!SR) {
 #pragma unroll
-    for (int k = 0; k < N / 8; ++k) {
-        const float* p = v + 8 * k;
-        if (!SR) {
+        for (int k = 0; k < N / 8; ++k) {
+            const float* p = v + 8 * k;
             uint32_t c = 0u;
             c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, p[0] * bs.R, p[1] * bs.R, 1.0f, 0);
             c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, p[2] * bs.R, p[3] * bs.R, 1.0f, 1);
             c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, p[4] * bs.R, p[5] * bs.R, 1.0f, 2);
             c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, p[6] * bs.R, p[7] * bs.R, 1.0f, 3);
             out[k] = c;
-        } else {
-            uint32_t ce[4], co[4];
-            const uint32_t* wk = w + 4 * k;
-#pragma unroll
-            for (int J = 0; J < 4; ++J) {
-                const float z0 = __builtin_ceilf((fabsf(p[2 * J]) * bs.R) * 0x1p23f);
-                const float z1 = __builtin_ceilf((fabsf(p[2 * J + 1]) * bs.R) * 0x1p23f);
-                // the second slot's value is left unspecified: its nibble is masked off
-                const float any = __builtin_nondeterministic_value(z0);
-                const f2_t e = {__uint_as_float(__float_as_uint(z0) | (__float_as_uint(p[2 * J]) & 0x80000000u)), any};
-                const f2_t o = {__uint_as_float(__float_as_uint(z1) | (__float_as_uint(p[2 * J + 1]) & 0x80000000u)), any};
-                ce[J] = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, e, sr_seed(wk[J], 0), 0x1p23f, 0);
-                co[J] = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, o, sr_seed(wk[J], 1), 0x1p23f, 0);
-            }
-            // perm(b, a, lo2): byte 0 of a -> byte 0, byte 0 of b -> byte 1, bytes 2 and 3 zero
-            const uint32_t lo2 = 0x0C0C0400u;
-            const uint32_t ev = (__builtin_amdgcn_perm(ce[1], ce[0], lo2) |
-                                 (__builtin_amdgcn_perm(ce[3], ce[2], lo2) << 16)) & 0x0F0F0F0Fu;
-            const uint32_t od = (__builtin_amdgcn_perm(co[1], co[0], lo2) |
-                                 (__builtin_amdgcn_perm(co[3], co[2], lo2) << 16)) & 0x0F0F0F0Fu;
-            out[k] = ev | (od << 4);
         }
+        return;
+    }
+    // FOLD (BF16 inputs, no transform): every nonzero |t| is at least 2^-133.
+    // With R = 0 or 2^-16 <= R < 2^100, fl(|t| * R) is 0 only for t = 0; when
+    // it is normal, scaling by 2^23 commutes with the rounding, and when it is
+    // subnormal both forms give z = 1.  So the single multiply by R * 2^23 gives
+    // the same z.  The wave takes that path when every active lane qualifies.
+    if (FOLD && __all(bs.R == 0.0f || (bs.R >= 0x1p-16f && bs.R < 0x1p100f))) {
+#pragma unroll
+        for (int k = 0; k < N / 8; ++k) out[k] = sr_word8<true>(v + 8 * k, bs.R, w + 4 * k);
+    } else {
+#pragma unroll
+        for (int k = 0; k < N / 8; ++k) out[k] = sr_word8<false>(v + 8 * k, bs.R, w + 4 * k);
     }
 }
 

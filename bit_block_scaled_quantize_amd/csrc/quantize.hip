@@ -203,18 +203,25 @@ __global__ void k_write_tensor_scale(const float* amax_in, float* ts0, float* ts
     if (amax_out) amax_out[0] = a;
 }
 
-// Shared prologue: reduce A_t, derive s_t, and let workgroup 0 publish s_t
-// and A_t.
+// Shared prologue: reduce A_t, derive s_t, fill the workgroup's table of
+// block multipliers (one entry per E4M3 byte), and let workgroup 0 publish s_t
+// and A_t.  Every thread of the (256-thread) workgroup must call it: it ends
+// with a barrier.
 struct TensorScale {
     float st, six_st;
+    const float* rtab;  // 128 block multipliers in LDS
 };
 
 __device__ __forceinline__ TensorScale prologue(const float* amax_src, int n_partials, float* ts0,
                                                 float* ts1, float* amax_out) {
+    __shared__ float rtab[128];
     const float a = tensor_amax_of(amax_src, n_partials);
     TensorScale t;
     t.st = tensor_scale_of(a);
     t.six_st = 6.0f * t.st;
+    if (threadIdx.x < 128) rtab[threadIdx.x] = block_multiplier(threadIdx.x, t.st);
+    __syncthreads();
+    t.rtab = rtab;
     if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
         if (ts0) ts0[0] = t.st;
         if (ts1) ts1[0] = t.st;
@@ -262,7 +269,7 @@ __device__ __forceinline__ void pair_block_scales(float& a0, float& a1, bool odd
                                                   BlockScale& b0, BlockScale& b1) {
     a0 = fmaxf(a0, __shfl_xor(a0, 1, 64));
     a1 = fmaxf(a1, __shfl_xor(a1, 1, 64));
-    const BlockScale mine = block_scale(odd ? a1 : a0, ts.six_st, ts.st);
+    const BlockScale mine = block_scale(odd ? a1 : a0, ts.six_st, ts.rtab);
     BlockScale other;
     other.R = __shfl_xor(mine.R, 1, 64);
     other.byte = (uint32_t)__shfl_xor((int)mine.byte, 1, 64);
@@ -321,7 +328,7 @@ __global__ void __launch_bounds__(256) k_quant_row(const T* __restrict__ x, int6
             for (int k = 0; k < 2; ++k) {
                 if (r + k >= rows) break;
                 uint32_t w[1];
-                encode<SR, 8>(v[k], bs[k], a[k], wd[k], w);
+                encode<SR, 8, sizeof(T) == 2 && !RHT>(v[k], bs[k], a[k], wd[k], w);
                 *reinterpret_cast<uint32_t*>(codes + (r + k) * (cols / 2) + c / 2) = w[0];
                 if (odd == (k == 1)) scales[(r + k) * (cols / 16) + c / 16] = (uint8_t)bs[k].byte;
             }
@@ -408,7 +415,7 @@ __device__ __forceinline__ void tile_row_blocks(const uint4 (&raw)[8], int64_t R
         float mine_a = a[i0];
 #pragma unroll
         for (int k = 1; k < LPB; ++k) mine_a = (q == k) ? a[i0 + k] : mine_a;
-        const BlockScale mine = block_scale(mine_a, ts.six_st, ts.st);
+        const BlockScale mine = block_scale(mine_a, ts.six_st, ts.rtab);
         const int base = lane - q;
 #pragma unroll
         for (int k = 0; k < LPB; ++k) {
@@ -442,7 +449,9 @@ __device__ __forceinline__ void tile_row_blocks(const uint4 (&raw)[8], int64_t R
 #pragma unroll
             for (int e = CH; e < 8; ++e) v[e] = 0.0f;
             uint32_t w[1];
-            encode<SR, 8>(v, bs[k + h], a[k + h], wd[h], w);
+            // no single-multiply SR path here: in the fused kernel it would
+            // raise register use past the 168 VGPRs of three waves per SIMD
+            encode<SR, 8, false>(v, bs[k + h], a[k + h], wd[h], w);
             uint8_t* dst = rcodes + rr * (cols / 2) + gc / 2;
             if (CH == 8) *reinterpret_cast<uint32_t*>(dst) = w[0];
             else *reinterpret_cast<uint16_t*>(dst) = (uint16_t)w[0];
@@ -503,18 +512,20 @@ __device__ __forceinline__ void tile_col_blocks(const uint8_t* tile, int64_t R0,
         for (int i = 0; i < 16; ++i) col[i] = unit_elem<T>(q[i], e);
         if (RHT) hadamard16(col, sign_mask);
         const float ab = absmax16(col);
-        const BlockScale bs = block_scale(ab, ts.six_st, ts.st);
+        const BlockScale bs = block_scale(ab, ts.six_st, ts.rtab);
         uint32_t wd[8];
         if (SR) philox_words16(seed, kStreamCol, (uint64_t)(c * rows + r0), wd);
         uint32_t w[2];
-        encode<SR, 16>(col, bs, ab, wd, w);
+        encode<SR, 16, sizeof(T) == 2 && !RHT>(col, bs, ab, wd, w);
         *reinterpret_cast<uint2*>(ccodes + c * (rows / 2) + r0 / 2) = make_uint2(w[0], w[1]);
         cscales[c * (rows / 16) + r0 / 16] = (uint8_t)bs.byte;
     }
 }
 
+// At least three waves per SIMD: the fused stochastic-rounding instance must
+// stay within 168 VGPRs.
 template <typename T, bool DO_ROW, bool SR, bool RHT>
-__global__ void __launch_bounds__(256) k_quant_colt(const T* __restrict__ x, int64_t rows,
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) k_quant_colt(const T* __restrict__ x, int64_t rows,
                                                     int64_t cols, int64_t ld,
                                                     const float* __restrict__ amax_src, int n_part,
                                                     uint64_t seed, uint32_t sign_mask,
@@ -592,7 +603,7 @@ __global__ void __launch_bounds__(256) k_quant_2d(const T* __restrict__ x, int64
         // active or both inactive, since cols % 16 == 0)
         a = fmaxf(a, __shfl_xor(a, 1, 64));
         if (!active) return;
-        BlockScale bs = block_scale(a, ts.six_st, ts.st);
+        BlockScale bs = block_scale(a, ts.six_st, ts.rtab);
         if ((lane & 1) == 0) scales[rband * (cols / 16) + c / 16] = (uint8_t)bs.byte;
 #pragma unroll
         for (int i = 0; i < 16; i += 2) {
@@ -602,7 +613,7 @@ __global__ void __launch_bounds__(256) k_quant_2d(const T* __restrict__ x, int64
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 uint32_t w[1];
-                encode<SR, 8>(v[i + h], bs, a, wd[h], w);
+                encode<SR, 8, sizeof(T) == 2>(v[i + h], bs, a, wd[h], w);
                 *reinterpret_cast<uint32_t*>(codes + (r + h) * (cols / 2) + c / 2) = w[0];
             }
         }

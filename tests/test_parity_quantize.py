@@ -130,6 +130,46 @@ def test_understated_amax(nv, layout):
                     assert_q_equal(got[i], ref[i], f"amax_in={amax_in} {layout}/{i} {rnd} {dt}")
 
 
+@pytest.mark.parametrize("layout", [O.ROW_1D, O.COL_1D, O.ROW_COL_1D, O.BLK_2D])
+def test_sr_large_blocks_with_smallest_subnormals(nv, layout):
+    """BF16 stochastic rounding with blocks whose multiplier R is below 2^-17:
+    in every other 16x16 square the diagonal holds 1e6 (the tensor amax) and
+    the rest the smallest BF16 subnormal 2^-133, so each row, column and 2D
+    block of the square mixes the two.  There |t|*R < 2^-150 rounds to 0 and
+    the code must be 0 under every draw; computing the scaled value as
+    |t|*(R*2^23) instead would round up on a zero draw.  The other squares
+    hold ordinary values, so waves mix both kinds of block.  The test first
+    counts, with the oracle's own draws, the subnormal elements whose draw is
+    0 (at least one per layout), so the case is really exercised."""
+    n = 1024
+    x = W.normal((n, n), 1.0, seed=4242)
+    tiny = np.float32(2.0 ** -133)
+    mask = np.zeros((n, n), dtype=bool)
+    for bi in range(n // 16):
+        for bj in range(n // 16):
+            if (bi + bj) % 2:
+                continue
+            sq = x[16 * bi:16 * bi + 16, 16 * bj:16 * bj + 16]
+            sq[:] = tiny
+            np.fill_diagonal(sq, 1.0e6)
+            m = mask[16 * bi:16 * bi + 16, 16 * bj:16 * bj + 16]
+            m[:] = True
+            np.fill_diagonal(m, False)
+    xb = W.f32_to_bf16_bits(x)
+    assert np.all(xb[mask] == 0x0001)
+    seed = 61
+    rr, cc = np.nonzero(mask)
+    # output index and random stream of each layout: row blocks 0, column blocks 1, squares 2
+    spec = {O.ROW_1D: [(0, rr * n + cc)], O.COL_1D: [(1, cc * n + rr)],
+            O.ROW_COL_1D: [(0, rr * n + cc), (1, cc * n + rr)], O.BLK_2D: [(2, rr * n + cc)]}[layout]
+    for stream, idx in spec:
+        zero_draws = sum(1 for i in idx.tolist() if O.draw16(seed, stream, i) == 0)
+        assert zero_draws >= 1, f"stream {stream}: no subnormal element draws 0"
+    got, ref = run_both(nv, xb, O.BF16, layout, O.SR, seed=seed)
+    for i in range(len(ref)):
+        assert_q_equal(got[i], ref[i], f"large blocks {layout}/{i}")
+
+
 def test_zero_and_empty_tensors(nv):
     x = np.zeros((32, 32), dtype=np.float32)
     got, ref = run_both(nv, x, O.F32, O.ROW_1D, O.SR)
