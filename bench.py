@@ -30,7 +30,12 @@ Also reported, on the same JSON line:
                   and the MX GEMMs on the scaled matrix cores (TFLOP/s against
                   the FP8 or FP4 peak).
 
-python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-gemm] [--no-mx] [--no-cpu-baseline]
+The first call computes the amax; after it the three stochastic-rounding calls
+run on a second stream beside the nearest-even and dequantize calls (--streams
+1 runs every call in order on one stream).  After timing, the step's outputs
+are checked bit for bit against the one-stream order.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--streams 2] [--no-gemm] [--no-mx] [--no-cpu-baseline]
 """
 import argparse
 import hashlib
@@ -125,6 +130,10 @@ def main():
     ap.add_argument("--no-mx", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
                     help="time the step as eager launches instead of HIP graph replays")
+    ap.add_argument("--streams", type=int, default=2, choices=(1, 2),
+                    help="2 (default): after the first call, the three stochastic-rounding calls run "
+                         "on a second stream beside the nearest-even and dequantize calls; 1: every "
+                         "call in order on one stream")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=20)
     ap.add_argument("--pmc-driver", action="store_true",
@@ -153,6 +162,9 @@ def main():
 
     R, C = nv.NVFP4Tensor.empty(N, N, device=dev), nv.NVFP4Tensor.empty(N, N, device=dev)
     R2, C2 = nv.NVFP4Tensor.empty(N, N, device=dev), nv.NVFP4Tensor.empty(N, N, device=dev)
+    # outputs of the stochastic-rounding calls of the step
+    Rs, Cs = nv.NVFP4Tensor.empty(N, N, device=dev), nv.NVFP4Tensor.empty(N, N, device=dev)
+    R2s, C2s = nv.NVFP4Tensor.empty(N, N, device=dev), nv.NVFP4Tensor.empty(N, N, device=dev)
     Q2d = nv.NVFP4Tensor.empty(N, N, nv.NVFP4_SCALE_2D, device=dev)
     yr = torch.empty((N, N), dtype=torch.bfloat16, device=dev)
     yc = torch.empty((N, N), dtype=torch.bfloat16, device=dev)
@@ -178,18 +190,35 @@ def main():
     step_bytes = sum(op[3] for op in step_ops) + 2 * dq
 
     amax_step = torch.zeros(1, dtype=torch.float32, device=dev)
+    # The calls of a step are independent once the first has published the
+    # amax.  The stochastic-rounding ones are bound by VALU issue, the others
+    # by HBM, so with --streams 2 they run on a second stream (default
+    # priority) beside the nearest-even and dequantize calls, which overlaps
+    # the two kinds of kernel; the step ends when both streams are done.
+    side = torch.cuda.Stream() if args.streams == 2 else None
+    sr_calls = [(ROW, Rs), (COL, Cs), (RC, (R2s, C2s))]
 
-    def step(i):
+    def step(i, streams=args.streams):
         x = xs[i % NBUF]
-        for k, (_, lay, rnd, _) in enumerate(step_ops):
-            out = (R2, C2) if lay == RC else (C if lay == COL else R)
-            if k == 0:
-                nv.nvfp4_quantize(x, layout=lay, round=rnd, sr_seed=77 + i, out=out, workspace=ws,
-                                  amax_out=amax_step)
-            else:
-                nv.nvfp4_quantize(x, layout=lay, round=rnd, sr_seed=77 + i, out=out, amax_in=amax_step)
+        main = torch.cuda.current_stream()
+        nv.nvfp4_quantize(x, layout=ROW, round=RNE, out=R, workspace=ws, amax_out=amax_step)
+        if streams == 2:
+            side.wait_stream(main)
+            with torch.cuda.stream(side):
+                for lay, out in sr_calls:
+                    nv.nvfp4_quantize(x, layout=lay, round=SR, sr_seed=77 + i, out=out, amax_in=amax_step)
+        else:
+            for lay, out in sr_calls:
+                nv.nvfp4_quantize(x, layout=lay, round=SR, sr_seed=77 + i, out=out, amax_in=amax_step)
+        nv.nvfp4_quantize(x, layout=COL, round=RNE, out=C, amax_in=amax_step)
+        nv.nvfp4_quantize(x, layout=RC, round=RNE, out=(R2, C2), amax_in=amax_step)
         nv.nvfp4_dequantize(R, out=yr)
         nv.nvfp4_dequantize(C, out=yc)
+        if streams == 2:
+            main.wait_stream(side)
+
+    step_outputs = [t for q in (R, C, R2, C2, Rs, Cs, R2s, C2s) for t in (q.codes, q.scales, q.tensor_scale)]
+    step_outputs += [yr, yc, amax_step]
 
     def timed(run):
         for i in range(args.warmup):
@@ -219,6 +248,20 @@ def main():
             graphs.append(g)
         torch.cuda.synchronize()
         ms = timed(lambda i: graphs[i % NBUF].replay())
+    # the timed form of the step computes what the calls in order on one
+    # stream compute, bit for bit
+    if args.no_graph:
+        step(0)
+    else:
+        graphs[0].replay()
+    torch.cuda.synchronize()
+    got = [t.clone() for t in step_outputs]
+    step(0, streams=1)
+    torch.cuda.synchronize()
+    for k, (a, b) in enumerate(zip(got, step_outputs)):
+        if not torch.equal(a.view(torch.uint8), b.view(torch.uint8)):
+            raise RuntimeError(f"step output {k} differs between the timed step and the one-stream step")
+    del got
     value = step_bytes / (ms * 1e-3) / 1e9
 
     # ---- per-kernel durations (amax given, so each call is one kernel)
@@ -278,6 +321,7 @@ def main():
                    "amax": "computed once per tensor by the first call (amax_out) and reused by the others (amax_in)",
                    "bytes_per_step": step_bytes, "input_buffers": NBUF,
                    "launch": "eager" if args.no_graph else "hip_graph_replay",
+                   "streams": args.streams,
                    "eager_ms_per_step": round(eager_ms, 4)},
         "roofline": roofline,
         "kernels": {k: {"ms": round(v["ms"], 5), "GB/s": round(v["gbs"], 1),
