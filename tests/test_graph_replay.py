@@ -1,4 +1,4 @@
-"""HIP graph capture of the library's calls: a sequence covering every entry
+"""HIP graph capture and two-stream use of the library's calls: a sequence covering every entry
 point (quantize with its amax pass and with a given amax, the fused and 2D
 layouts, dequantize, re-quantization, MX quantize/dequantize, both GEMMs and
 the grouped GEMM with its SwiGLU epilogue and amax) is captured once and
@@ -87,3 +87,51 @@ def test_sequence_graph_replays_match_eager(nv):
     # and the eager results are the oracle's (one spot check: the row quantization)
     q = O.quantize(x.cpu().view(torch.int16).numpy().view(np.uint16), O.BF16, O.ROW_1D, O.SR, sr_seed=1)
     assert np.array_equal(ref[1].cpu().numpy(), q.codes) and np.array_equal(ref[2].cpu().numpy(), q.scales)
+
+
+def test_two_streams_match_one_stream(nv):
+    """The library keeps no state between calls: the same calls split over two
+    streams (default priority), overlapping, give bit-identical outputs to
+    the calls in order on one stream."""
+    R, C = 1024, 1536
+    dev = "cuda"
+    x = to_device(W.f32_to_bf16_bits(W.student_t((R, C), 3.0, seed=41)))
+    ws = torch.empty(nv.nvfp4_quantize_workspace_size(R, C) // 4 + 4, dtype=torch.float32, device=dev)
+    amax = torch.zeros(1, dtype=torch.float32, device=dev)
+    qa, qb = nv.NVFP4Tensor.empty(R, C), nv.NVFP4Tensor.empty(C, R)
+    q2r, q2c = nv.NVFP4Tensor.empty(R, C), nv.NVFP4Tensor.empty(C, R)
+    qd = nv.NVFP4Tensor.empty(R, C, nv.NVFP4_SCALE_2D)
+    rq = nv.NVFP4Tensor.empty(C, R)
+    mq = nv.MXTensor.empty(R, C, nv.NVFP4_MX_E2M1)
+    y = torch.empty((R, C), dtype=torch.bfloat16, device=dev)
+    g = torch.empty((R, R), dtype=torch.float32, device=dev)
+    side = torch.cuda.Stream()
+    outputs = [amax, qa.codes, qa.scales, qb.codes, qb.scales, q2r.codes, q2r.scales, q2c.codes, q2c.scales,
+               qd.codes, qd.scales, rq.codes, rq.scales, rq.tensor_scale, mq.codes, mq.scales, y, g]
+
+    def run(split):
+        main = torch.cuda.current_stream()
+        nv.nvfp4_quantize(x, round=nv.NVFP4_SR, sr_seed=1, out=qa, workspace=ws, amax_out=amax)
+        other = side if split else main
+        other.wait_stream(main)
+        with torch.cuda.stream(other):
+            nv.nvfp4_quantize(x, layout=nv.NVFP4_COL_1D, round=nv.NVFP4_SR, sr_seed=2, out=qb, amax_in=amax)
+            nv.nvfp4_requantize(qa, round=nv.NVFP4_SR, sr_seed=3, out=rq, workspace=ws)
+            nv.nvfp4_mx_quantize(x, round=nv.NVFP4_SR, sr_seed=4, out=mq)
+        nv.nvfp4_quantize(x, layout=nv.NVFP4_ROW_COL_1D, out=(q2r, q2c), amax_in=amax)
+        nv.nvfp4_quantize(x, layout=nv.NVFP4_BLK_2D, out=qd, amax_in=amax)
+        nv.nvfp4_dequantize(qa, out=y)
+        nv.nvfp4_gemm(qa, q2r, out=g)
+        main.wait_stream(other)
+
+    run(False)
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in outputs]
+    for rep in range(3):
+        for t in outputs:
+            t.view(torch.uint8).fill_(0xA5)
+        torch.cuda.synchronize()
+        run(True)
+        torch.cuda.synchronize()
+        for k, (t, r) in enumerate(zip(outputs, ref)):
+            assert torch.equal(t.view(torch.uint8), r.view(torch.uint8)), f"rep {rep}: output {k} differs"
