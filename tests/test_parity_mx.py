@@ -108,6 +108,46 @@ def test_mx_quantize_strided_input(nv, elem):
         assert_mx_equal(q.codes.cpu().numpy(), q.scales.cpu().numpy(), ref, f"strided layout={layout}")
 
 
+@pytest.mark.parametrize("elem", ELEMS)
+@pytest.mark.parametrize("layout", [O.ROW_1D, O.COL_1D])
+def test_mx_sr_large_blocks_with_smallest_subnormals(nv, elem, layout):
+    """BF16 stochastic rounding with block scales 2^s, s = 17: in every other
+    32 x 32 square the diagonal holds 2^25 (E4M3) or 2^19 (E2M1) and the rest
+    the smallest BF16 subnormal 2^-133, so every row and column block mixes
+    the two.  Then |v| * 2^-s = 2^-150 rounds to 0 and the code must be 0
+    under every draw; one multiply by 2^-s times 2^29 (or 2^23) would round up
+    on a zero draw.  Other squares hold ordinary values, so waves mix both
+    kinds of block.  The test first counts, with the oracle's draws, the
+    subnormal elements whose draw is 0 (at least one), so the case is really
+    exercised."""
+    n = 1024
+    x = W.normal((n, n), 1.0, seed=4343)
+    big = np.float32(2.0 ** 25 if elem == O.MX_FP8 else 2.0 ** 19)
+    tiny = np.float32(2.0 ** -133)
+    mask = np.zeros((n, n), dtype=bool)
+    for bi in range(n // 32):
+        for bj in range(n // 32):
+            if (bi + bj) % 2:
+                continue
+            sq = x[32 * bi:32 * bi + 32, 32 * bj:32 * bj + 32]
+            sq[:] = tiny
+            np.fill_diagonal(sq, big)
+            m = mask[32 * bi:32 * bi + 32, 32 * bj:32 * bj + 32]
+            m[:] = True
+            np.fill_diagonal(m, False)
+    xb = W.f32_to_bf16_bits(x)
+    assert np.all(xb[mask] == 0x0001)
+    seed = 62
+    rr, cc = np.nonzero(mask)
+    # random streams of the MX layouts: 4 row blocks, 5 column blocks; index in the output tensor
+    stream, idx = (4, rr * n + cc) if layout == O.ROW_1D else (5, cc * n + rr)
+    zero_draws = sum(1 for i in idx.tolist() if O.draw16(seed, stream, i) == 0)
+    assert zero_draws >= 1, "no subnormal element draws 0"
+    _, codes, scales = gpu_mx(nv, xb, O.BF16, layout, elem, O.SR, seed)
+    ref = O.mx_quantize(xb, O.BF16, layout, elem, O.SR, seed=seed)
+    assert_mx_equal(codes, scales, ref, f"large blocks {layout} elem={elem}")
+
+
 def test_mx_empty(nv):
     x = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
     q = nv.nvfp4_mx_quantize(x)
