@@ -1,0 +1,28 @@
+"""bench.py's contract on the CPU: a run on more than one GPU is refused with
+a message (before anything touches a GPU), and the CPU baseline -- the oracle
+timed on a bounded sample of the step -- reports the fields the result line
+carries."""
+import os
+import subprocess
+import sys
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], cwd=ROOT,
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+def test_cpu_baseline_fields():
+    import bench
+    import workloads as W
+    cb = bench.cpu_baseline(np, W)
+    assert set(cb) == {"value", "unit", "cores", "kind", "sample"}
+    assert cb["kind"] == "oracle" and cb["unit"] == "GB/s" and cb["cores"] == 1
+    assert cb["value"] > 0 and "rows 0..2047" in cb["sample"]
