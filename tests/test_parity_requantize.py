@@ -78,17 +78,19 @@ def test_requantize_empty(nv):
 
 @pytest.mark.parametrize("had", [False, True])
 def test_requantize_8192_sampled(nv, had):
-    """8192 x 8192: the forward tensor quantized along rows on the GPU, then
-    re-quantized along columns with stochastic rounding (the benchmarked
-    call): the tensor scale against the oracle's amax of the whole
-    dequantized tensor, and 64-row bands of the output against the oracle
-    with the band's own random-draw indices."""
+    """8192 x 8192: the forward tensor quantized along rows on the GPU (equal
+    to the oracle's row quantization), then re-quantized along columns with
+    stochastic rounding (the benchmarked call): the tensor scale against the
+    oracle's amax of the whole dequantized tensor, and 64-row bands of the
+    output against the oracle with the band's own random-draw indices.  The
+    oracle works from its own row quantization."""
     n = 8192
     xb = W.f32_to_bf16_bits(W.student_t((n, n), 3.0, seed=7000))
     qd = nv.nvfp4_quantize(to_device(xb), round=nv.NVFP4_SR, sr_seed=7001)
     r = q_to_host(nv.nvfp4_requantize(qd, round=nv.NVFP4_SR, sr_seed=7002, hadamard=had,
                                       hadamard_seed=7003))
-    q = q_to_host(qd)
+    q = O.quantize(xb, O.BF16, O.ROW_1D, O.SR, sr_seed=7001)
+    assert_q_equal(q_to_host(qd), q, "row quantization")
     xd = O.dequantize(q, O.F32)
     amax = O.amax(xd, O.F32, O.COL_1D, hadamard=had, hadamard_seed=7003)
     assert r.ts == O.tensor_scale(amax)
