@@ -208,12 +208,13 @@ __global__ void __launch_bounds__(256) k_mx_row(const T* __restrict__ x, int64_t
 template <typename T, int ELEM, bool SR>
 __global__ void __launch_bounds__(256) k_mx_col(const T* __restrict__ x, int64_t rows, int64_t cols,
                                                 int64_t ld, uint64_t seed, uint8_t* __restrict__ codes,
-                                                uint8_t* __restrict__ scales) {
+                                                uint8_t* __restrict__ scales, int xcd_group) {
     constexpr int CH = 16 / (int)sizeof(T), TWC = 128 / (int)sizeof(T), UE = 8 / (int)sizeof(T);
     constexpr int STRIDE = 136;
     __shared__ __attribute__((aligned(16))) uint8_t tile[256 * STRIDE];
     const int t = threadIdx.x;
-    const int64_t R0 = (int64_t)blockIdx.y * 256, C0 = (int64_t)blockIdx.x * TWC;
+    const TileXY tl = xcd_tile(xcd_group);
+    const int64_t R0 = tl.y * 256, C0 = tl.x * TWC;
 
     const int ch = t & 7, lr0 = t >> 3;
     const int64_t gc = C0 + CH * ch;
@@ -346,7 +347,14 @@ hipError_t mx_quantize_typed(const T* x, int64_t rows, int64_t cols, int64_t ld,
         hipLaunchKernelGGL((k_mx_row<T, ELEM, SR>), g, dim3(256), 0, s, x, rows, cols, ld, seed, codes, scales);
     } else {
         dim3 g((unsigned)mx_cdiv(cols, 128 / (int64_t)sizeof(T)), (unsigned)mx_cdiv(rows, 256));
-        hipLaunchKernelGGL((k_mx_col<T, ELEM, SR>), g, dim3(256), 0, s, x, rows, cols, ld, seed, codes, scales);
+        // nearest-even: runs of tiles along a tile row share one XCD, as for
+        // the NVFP4 column tiles (E4M3 8192^2 bf16: 40.0 -> 38.8 us); with
+        // stochastic rounding the grouping measured 8% slower
+        const int xg = SR ? 1
+                       : (g.x % (16 * sizeof(T)) == 0) ? (int)(16 * sizeof(T))
+                       : (g.x % (2 * sizeof(T)) == 0) ? (int)(2 * sizeof(T)) : 1;
+        hipLaunchKernelGGL((k_mx_col<T, ELEM, SR>), g, dim3(256), 0, s, x, rows, cols, ld, seed, codes, scales,
+                           xg);
     }
     return hipGetLastError();
 }

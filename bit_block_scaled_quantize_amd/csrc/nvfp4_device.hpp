@@ -409,4 +409,32 @@ __device__ __forceinline__ float absmax16(const float v[16]) {
     return a;
 }
 
+// ---------------------------------------------------------------- tiles
+// Tile of the calling workgroup.  Workgroups are handed to the eight XCDs
+// round robin in dispatch order, and each XCD has its own L2.  With
+// xcd_group = G (> 1; G divides the grid width), each run of G consecutive
+// tiles along a tile row is served by workgroups of one XCD: within every
+// block of 8 G dispatched workgroups, workgroup L takes tile
+// G * (L % 8) + (L / 8) % G of the block.  Output lines that those G tiles
+// write in parts (row codes and scales of the fused layout) are then
+// completed in one L2, and the G tiles' row segments are read by one L2 as
+// one contiguous stretch.  A last partial block keeps the identity order.
+struct TileXY {
+    int64_t x, y;
+};
+
+__device__ __forceinline__ TileXY xcd_tile(int xcd_group) {
+    const int64_t gx = gridDim.x;
+    int64_t L = (int64_t)blockIdx.y * gx + blockIdx.x;
+    if (xcd_group > 1) {
+        const int64_t blk = 8 * (int64_t)xcd_group;
+        if (L < ((int64_t)gridDim.y * gx) / blk * blk)
+            L = L / blk * blk + xcd_group * (L % 8) + (L / 8) % xcd_group;
+    }
+    TileXY r;
+    r.x = L % gx;
+    r.y = L / gx;
+    return r;
+}
+
 }  // namespace nvfp4
