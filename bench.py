@@ -341,6 +341,8 @@ def main():
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(np, W)
+        if not args.no_gemm:
+            result["gemm"]["cpu_oracle_forward_8192x20480x5120_sampled"] = cpu_oracle_gemm(np, W)
     print(json.dumps(result), flush=True)
 
 
@@ -571,11 +573,11 @@ def bench_mx_gemm(nv, W, np, torch, reps):
     return out
 
 
-def cpu_baseline(np, W):
-    """The oracle on rows 0..2047 of the step's input (a quarter of the
-    tensor): the same quantize calls and dequantizations, single thread."""
+def cpu_baseline(np, W, rows=N):
+    """The oracle on rows 0 .. rows-1 of the 8192 x 8192 step input (by default
+    the whole tensor, about 13 s on the GPU machine's host): the same quantize
+    calls and dequantizations as the step, single thread."""
     import oracle as O
-    rows = 2048
     x = W.f32_to_bf16_bits(W.student_t((N, N), 3.0, seed=1000))[:rows].copy()
     E = rows * N
     t0 = time.perf_counter()
@@ -592,8 +594,39 @@ def cpu_baseline(np, W):
     dq = E // 2 + E // 16 + 4 + E * 2
     b = 4 * q1 + 2 * q2 + 2 * dq
     return {"value": round(b / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"rows 0..{rows - 1} of the 8192x8192 step input; the full step's quantize and "
+            "sample": f"rows 0..{rows - 1} of the {N}x{N} step input"
+                      f"{' (the whole tensor)' if rows == N else ''}: the step's quantize and "
                       f"dequantize calls; {dt:.1f} s single-threaded"}
+
+
+def cpu_oracle_gemm(np, W, n_entries=8192):
+    """The oracle GEMM (exact dequantization, float64 dot products) on sampled
+    output entries of the forward shape 8192 x 20480 x 5120 (X Student-t(3)
+    row blocks, W N(0, 0.02) 16x16 blocks), single thread.  The operand rows
+    the entries need are quantized by the oracle beforehand (not timed); the
+    per-entry time is extrapolated to the whole output."""
+    import oracle as O
+    M, Nn, K = 8192, 20480, 5120
+    x = W.f32_to_bf16_bits(W.student_t((M, K), 3.0, seed=4000))
+    w = W.f32_to_bf16_bits(W.normal((Nn, K), 0.02, seed=4001))
+    g = W.rng(4002)
+    # columns from 128 random 16-row bands of W, so the untimed operand
+    # quantization stays small
+    mi = g.integers(0, M, n_entries)
+    ni = 16 * g.choice(Nn // 16, 128, replace=False)[g.integers(0, 128, n_entries)] + g.integers(0, 16, n_entries)
+    mu, ml = np.unique(mi, return_inverse=True)
+    A = O.quantize(np.ascontiguousarray(x[mu]), O.BF16, O.ROW_1D, amax_in=O.amax(x, O.BF16, O.ROW_1D))
+    bands = np.unique(ni // 16)
+    B = O.quantize(np.concatenate([w[16 * b:16 * b + 16] for b in bands]), O.BF16, O.BLK_2D,
+                   amax_in=O.amax(w, O.BF16, O.BLK_2D))
+    nl = np.searchsorted(bands, ni // 16) * 16 + ni % 16
+    t0 = time.perf_counter()
+    O.gemm(A, B, entries=(ml, nl))
+    dt = time.perf_counter() - t0
+    full_s = dt / n_entries * M * Nn
+    return {"entries": n_entries, "seconds": round(dt, 3), "cores": 1, "kind": "oracle",
+            "extrapolated_full_seconds": round(full_s, 1),
+            "extrapolated_TFLOP/s": round(2 * M * Nn * K / full_s / 1e12, 6)}
 
 
 if __name__ == "__main__":

@@ -22,7 +22,7 @@ def test_more_than_one_gpu_is_refused():
 def test_cpu_baseline_fields():
     import bench
     import workloads as W
-    cb = bench.cpu_baseline(np, W)
+    cb = bench.cpu_baseline(np, W, rows=256)
     assert set(cb) == {"value", "unit", "cores", "kind", "sample"}
     assert cb["kind"] == "oracle" and cb["unit"] == "GB/s" and cb["cores"] == 1
-    assert cb["value"] > 0 and "rows 0..2047" in cb["sample"]
+    assert cb["value"] > 0 and "rows 0..255" in cb["sample"]
