@@ -436,6 +436,27 @@ def bench_gemm(nv, W, np, torch, reps):
                      "frac_fp16_mfma_peak": round(tf / FP16_PEAK_TFLOPS, 4),
                      "frac_fp4_mfma_peak": round(tf / FP4_PEAK_TFLOPS, 4)}
 
+    log("gemm: 256^3")
+    # M = N = K = 256, FP32 N(0,1) with 0.1% x50 outliers; A along rows, B
+    # (K x N) along K, RNE, FP32 out: quantize both operands and multiply
+    # (latency-bound; one launch per call, amax computed by each quantize)
+    a = torch.from_numpy(W.with_spikes(W.normal((256, 256), 1.0, seed=1), 1e-3, 50.0, seed=2)).cuda()
+    b = torch.from_numpy(W.with_spikes(W.normal((256, 256), 1.0, seed=3), 1e-3, 50.0, seed=4)).cuda()
+    Aq = nv.nvfp4_quantize(a)
+    Bq = nv.nvfp4_quantize(b, layout=nv.NVFP4_COL_1D)
+    C = torch.empty((256, 256), dtype=torch.float32, device="cuda")
+    entry("gemm_256x256x256_f32", 2 * 256 ** 3, time_events(lambda i: nv.nvfp4_gemm(Aq, Bq, out=C), reps, torch))
+
+    ws = torch.empty((nv.nvfp4_quantize_workspace_size(256, 256) + 15) // 16 * 4, dtype=torch.float32,
+                     device="cuda")
+
+    def c1(i):
+        nv.nvfp4_quantize(a, out=Aq, workspace=ws)
+        nv.nvfp4_quantize(b, layout=nv.NVFP4_COL_1D, out=Bq, workspace=ws)
+        nv.nvfp4_gemm(Aq, Bq, out=C)
+    out["gemm_256x256x256_f32"]["quantize_both_and_gemm_ms"] = round(time_events(c1, reps, torch), 4)
+    del a, b, Aq, Bq, C, ws
+
     log("gemm: forward")
     X = nv.nvfp4_quantize(gen((8192, 5120), 4000, "t3"))
     Wt = nv.nvfp4_quantize(gen((20480, 5120), 4001, "w"), layout=nv.NVFP4_BLK_2D)
