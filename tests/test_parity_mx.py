@@ -98,6 +98,21 @@ def test_mx_quantize_matches_oracle(nv, elem, rnd, dtype, layout, shape):
 
 
 @pytest.mark.parametrize("elem", ELEMS)
+@pytest.mark.parametrize("rnd", [O.RNE, O.SR])
+@pytest.mark.parametrize("dtype", [O.BF16, O.F32])
+def test_mx_col_tiles_xcd_remap_with_partial_block(nv, elem, rnd, dtype):
+    """2304 x 2048 along columns: a 32 x 9 grid of 256-row tiles for bf16
+    (64 x 9 for fp32); with nearest-even rounding whole blocks of 8 x 32
+    (8 x 64) dispatched workgroups take remapped tiles and the last, partial
+    block keeps the dispatch order."""
+    x = W.student_t((2304, 2048), 3.0, seed=91)
+    xin = W.f32_to_bf16_bits(x) if dtype == O.BF16 else x
+    _, codes, scales = gpu_mx(nv, xin, dtype, O.COL_1D, elem, rnd, 92)
+    ref = O.mx_quantize(xin, dtype, O.COL_1D, elem, rnd, seed=92)
+    assert_mx_equal(codes, scales, ref, f"mx remap elem={elem} rnd={rnd} dtype={dtype}")
+
+
+@pytest.mark.parametrize("elem", ELEMS)
 def test_mx_quantize_strided_input(nv, elem):
     """A row stride wider than the row (a column slice of a wider tensor)."""
     x = W.f32_to_bf16_bits(W.normal((64, 96), 1.0, seed=3))

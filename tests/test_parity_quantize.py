@@ -83,6 +83,20 @@ def test_rowcol_and_2d(nv, dtype, rnd, shape):
     assert_q_equal(got[0], ref[0], f"2d {shape}")
 
 
+@pytest.mark.parametrize("dtype", [O.BF16, O.F32])
+@pytest.mark.parametrize("layout,rnd", [(O.COL_1D, O.RNE), (O.COL_1D, O.SR), (O.ROW_COL_1D, O.RNE),
+                                        (O.ROW_COL_1D, O.SR)])
+def test_col_tiles_xcd_remap_with_partial_block(nv, dtype, layout, rnd):
+    """2288 x 2048: a 32 x 9 grid of 256-row column tiles for bf16 (64 x 9 for
+    fp32), so whole blocks of 8 x 32 (8 x 64) dispatched workgroups take
+    remapped tiles while the last, partial block keeps the dispatch order;
+    the last tile row is partial (240 rows)."""
+    x = make_input(2288, 2048, dtype, seed=77)
+    got, ref = run_both(nv, x, dtype, layout, rnd, seed=78)
+    for i, (g, r) in enumerate(zip(got, ref)):
+        assert_q_equal(g, r, f"remap {layout}/{rnd}/{i}")
+
+
 def test_fused_rowcol_equals_separate_calls(nv):
     x = make_input(128, 192, O.BF16, seed=3)
     xd = to_device(x)
