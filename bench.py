@@ -18,7 +18,11 @@ Also reported, on the same JSON line:
   roofline     -- the dominant kernel of the step, timed alone with HIP events
                   on the launch stream, against the 8 TB/s HBM peak;
   cpu_baseline -- the CPU oracle on a bounded sample of the same step;
-  gemm         -- the block-scaled GEMMs: forward 8192x20480x5120 (BF16 out),
+  kernels      -- each step kernel timed alone, the 16x16-block, dequantize,
+                  re-quantization and amax kernels, and (with the GEMMs) the
+                  8192 x 20480 gradient's Hadamard + column-block + SR
+                  quantization, amax given and computed;
+  gemm         -- the block-scaled GEMMs: the 256^3 case, forward 8192x20480x5120 (BF16 out),
                   weight-gradient 20480x5120x8192 (FP32 out, Hadamard + column
                   blocks + SR operands) and the 32-expert MoE forward
                   (up-projection with SwiGLU, quantize, down-projection), in
@@ -337,7 +341,12 @@ def main():
         if not args.no_gemm:
             result["mx"].update(bench_mx_gemm(nv, W, np, torch, reps=max(3, reps // 4)))
     if not args.no_gemm:
-        result["gemm"] = bench_gemm(nv, W, np, torch, reps=max(3, reps // 4))
+        extra = {}
+        result["gemm"] = bench_gemm(nv, W, np, torch, reps=max(3, reps // 4), kern_extra=extra)
+        for k, v in extra.items():
+            gbs = v["bytes"] / (v["ms"] * 1e-3) / 1e9
+            result["kernels"][k] = {"ms": round(v["ms"], 5), "GB/s": round(gbs, 1),
+                                    "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "hbm_bytes": None}
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(np, W)
@@ -416,7 +425,7 @@ def pmc_driver_gemm(nv, W, np, torch):
         del A, B, C
 
 
-def bench_gemm(nv, W, np, torch, reps):
+def bench_gemm(nv, W, np, torch, reps, kern_extra=None):
     """Block-scaled GEMM throughput at the forward, weight-gradient and MoE
     shapes; operands are quantized on the GPU from seeded inputs."""
     out = {}
@@ -466,7 +475,25 @@ def bench_gemm(nv, W, np, torch, reps):
     del X, Wt, Y
     log("gemm: wgrad")
     kw = dict(layout=nv.NVFP4_COL_1D, round=nv.NVFP4_SR, hadamard=True, hadamard_seed=5200)
-    dYq = nv.nvfp4_quantize(gen((8192, 20480), 5000, "spiky"), sr_seed=5100, **kw)
+    dy = gen((8192, 20480), 5000, "spiky")
+    dYq = nv.nvfp4_quantize(dy, sr_seed=5100, **kw)
+    if kern_extra is not None:
+        # the gradient's own quantization (320 MiB, larger than the Infinity
+        # Cache): 16-point Hadamard along tokens, column blocks, SR; with the
+        # amax given, and with the transformed tensor's amax computed first
+        eg = 8192 * 20480
+        amax_h = torch.zeros(1, dtype=torch.float32, device="cuda")
+        ws_h = torch.empty((nv.nvfp4_quantize_workspace_size(8192, 20480) + 15) // 16 * 4,
+                           dtype=torch.float32, device="cuda")
+        nv.nvfp4_quantize(dy, sr_seed=5100, amax_out=amax_h, out=dYq, workspace=ws_h, **kw)
+        qb = eg * 2 + eg // 2 + eg // 16 + 4
+        kern_extra["quant_col_sr_hadamard_8192x20480"] = dict(ms=time_events(
+            lambda i: nv.nvfp4_quantize(dy, sr_seed=5100 + i, amax_in=amax_h, out=dYq, **kw), reps, torch), bytes=qb)
+        kern_extra["quant_col_sr_hadamard_8192x20480_with_amax"] = dict(ms=time_events(
+            lambda i: nv.nvfp4_quantize(dy, sr_seed=5100 + i, out=dYq, workspace=ws_h, **kw), reps, torch), bytes=qb)
+        nv.nvfp4_quantize(dy, sr_seed=5100, out=dYq, workspace=ws_h, **kw)
+        del ws_h, amax_h
+    del dy
     Xq = nv.nvfp4_quantize(gen((8192, 5120), 5002, "spiky"), sr_seed=5101, **kw)
     dW = torch.empty((20480, 5120), dtype=torch.float32, device="cuda")
     entry("wgrad_20480x5120x8192_f32", 2 * 20480 * 5120 * 8192,
