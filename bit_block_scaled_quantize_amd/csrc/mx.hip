@@ -278,33 +278,41 @@ __global__ void __launch_bounds__(256) k_mx_col(const T* __restrict__ x, int64_t
 // ============================================================ dequantize
 // y = value(code) * 2^(byte - 127), one binary32 rounding (ldexp; exact
 // unless the result leaves the normal range), BF16 output rounded to nearest
-// even from that binary32 value.  A lane expands 16 code bytes (16 E4M3 or 32
-// E2M1 elements) of each of 4 rows; the 64 lanes of a wave cover 1024 code
-// bytes of a row.
+// even from that binary32 value.  A lane expands 16 elements (16 E4M3 code
+// bytes or 8 E2M1 ones) of each of 4 rows; the 64 lanes of a wave cover 1024
+// elements of a row.  (E2M1 with 32 elements per lane, the same 16-byte
+// loads, ran at half the workgroups and took 44 instead of 35 us on 8192^2.)
 template <int ELEM, typename TOut>
 __global__ void __launch_bounds__(256) k_mx_dequant(const uint8_t* __restrict__ codes,
                                                     const uint8_t* __restrict__ scales, int64_t rows,
                                                     int64_t cols, TOut* __restrict__ y, int64_t ld) {
-    constexpr int EPL = ELEM == kMxE4M3 ? 16 : 32;  // elements per lane
+    constexpr int EPL = 16;                           // elements per lane
+    constexpr int CB = ELEM == kMxE4M3 ? 16 : 8;      // their code bytes
     const int64_t row_bytes = ELEM == kMxE4M3 ? cols : cols / 2;
     const int64_t b = (int64_t)blockIdx.x * 64 + (threadIdx.x & 63);
     if (b >= cols / EPL) return;
     const int64_t nrg = (rows + 15) / 16;
     for (int64_t rg = blockIdx.y; rg < nrg; rg += gridDim.y) {
         const int64_t r0 = rg * 16 + 4 * (threadIdx.x >> 6);
-        uint4 cw[4];
+        uint32_t cw[4][4];
         int sx[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int64_t r = r0 + i < rows ? r0 + i : rows - 1;  // clamped; never stored
-            cw[i] = *reinterpret_cast<const uint4*>(codes + r * row_bytes + 16 * b);
+            if constexpr (CB == 16) {
+                const uint4 q = *reinterpret_cast<const uint4*>(codes + r * row_bytes + CB * b);
+                cw[i][0] = q.x; cw[i][1] = q.y; cw[i][2] = q.z; cw[i][3] = q.w;
+            } else {
+                const uint2 q = *reinterpret_cast<const uint2*>(codes + r * row_bytes + CB * b);
+                cw[i][0] = q.x; cw[i][1] = q.y; cw[i][2] = 0u; cw[i][3] = 0u;
+            }
             sx[i] = (int)scales[r * (cols / 32) + (b * EPL) / 32] - 127;
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int64_t r = r0 + i;
             if (r >= rows) break;
-            const uint32_t wv[4] = {cw[i].x, cw[i].y, cw[i].z, cw[i].w};
+            const uint32_t* wv = cw[i];
             float o[EPL];
 #pragma unroll
             for (int k = 0; k < EPL / 2; ++k) {
@@ -385,8 +393,7 @@ hipError_t launch_mx_quantize(const void* x, bool bf16, int64_t rows, int64_t co
 hipError_t launch_mx_dequantize(const uint8_t* codes, const uint8_t* scales, int elem, int64_t rows,
                                 int64_t cols, void* y, bool bf16, int64_t ld, hipStream_t s) {
     if (rows == 0 || cols == 0) return hipSuccess;
-    const int epl = elem == kMxE4M3 ? 16 : 32;
-    dim3 g((unsigned)mx_cdiv(cols / epl, 64), mx_grid_y(mx_cdiv(rows, 16)));
+    dim3 g((unsigned)mx_cdiv(cols / 16, 64), mx_grid_y(mx_cdiv(rows, 16)));
 #define NVFP4_MXDQ(E, TO) \
     hipLaunchKernelGGL((k_mx_dequant<E, TO>), g, dim3(256), 0, s, codes, scales, rows, cols, static_cast<TO*>(y), ld)
     if (elem == kMxE4M3) {
