@@ -267,15 +267,12 @@ __device__ __forceinline__ uint32_t sr_word8(const float* p, float R, const uint
                               : __builtin_ceilf((fabsf(p[2 * J]) * R) * 0x1p23f);
         const float z1 = FOLD ? __builtin_ceilf(fabsf(p[2 * J + 1]) * R23)
                               : __builtin_ceilf((fabsf(p[2 * J + 1]) * R) * 0x1p23f);
-        // the second slot's nibble is masked off; it is fed the seed, which
-        // is computed anyway, so the register pair needs no extra move
-        const uint32_t se = sr_seed(wk[J], 0), so = sr_seed(wk[J], 1);
-        const f2_t e = {__uint_as_float(__float_as_uint(z0) | (__float_as_uint(p[2 * J]) & 0x80000000u)),
-                        __uint_as_float(se)};
-        const f2_t o = {__uint_as_float(__float_as_uint(z1) | (__float_as_uint(p[2 * J + 1]) & 0x80000000u)),
-                        __uint_as_float(so)};
-        ce[J] = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, e, se, 0x1p23f, 0);
-        co[J] = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, o, so, 0x1p23f, 0);
+        // the second slot's value is left unspecified: its nibble is masked off
+        const float any = __builtin_nondeterministic_value(z0);
+        const f2_t e = {__uint_as_float(__float_as_uint(z0) | (__float_as_uint(p[2 * J]) & 0x80000000u)), any};
+        const f2_t o = {__uint_as_float(__float_as_uint(z1) | (__float_as_uint(p[2 * J + 1]) & 0x80000000u)), any};
+        ce[J] = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, e, sr_seed(wk[J], 0), 0x1p23f, 0);
+        co[J] = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, o, sr_seed(wk[J], 1), 0x1p23f, 0);
     }
     // perm(b, a, lo2): byte 0 of a -> byte 0, byte 0 of b -> byte 1, bytes 2 and 3 zero
     const uint32_t lo2 = 0x0C0C0400u;

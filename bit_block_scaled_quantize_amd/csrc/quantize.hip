@@ -449,7 +449,9 @@ __device__ __forceinline__ void tile_row_blocks(const uint4 (&raw)[8], int64_t R
 #pragma unroll
             for (int e = CH; e < 8; ++e) v[e] = 0.0f;
             uint32_t w[1];
-            encode<SR, 8, sizeof(T) == 2>(v, bs[k + h], a[k + h], wd[h], w);
+            // no single-multiply SR path here: in the fused kernel it would
+            // raise register use past the 168 VGPRs of three waves per SIMD
+            encode<SR, 8, false>(v, bs[k + h], a[k + h], wd[h], w);
             uint8_t* dst = rcodes + rr * (cols / 2) + gc / 2;
             if (CH == 8) *reinterpret_cast<uint32_t*>(dst) = w[0];
             else *reinterpret_cast<uint16_t*>(dst) = (uint16_t)w[0];
@@ -615,20 +617,19 @@ __global__ void __launch_bounds__(256) k_dequant(const uint8_t* __restrict__ cod
         const int64_t r0 = rg * 16 + 4 * (threadIdx.x >> 6);
         uint2 cw[4];
         uint32_t sb[4];
+        // rows past the end read the last row (never stored), and the scale
+        // row is r >> 4 for 16x16 blocks, so the loads carry no branch and
+        // issue back to back
+        const int sshift = scale_2d ? 4 : 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int64_t r = r0 + i;
-            cw[i] = make_uint2(0u, 0u);
-            sb[i] = 0u;
-            if (r < rows) {
-                cw[i] = *reinterpret_cast<const uint2*>(codes + (r * nb + b) * 8);
-                sb[i] = scale_2d ? scales[(r / 16) * nb + b] : scales[r * nb + b];
-            }
+            const int64_t r = r0 + i < rows ? r0 + i : rows - 1;
+            cw[i] = *reinterpret_cast<const uint2*>(codes + (r * nb + b) * 8);
+            sb[i] = scales[(r >> sshift) * nb + b];
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int64_t r = r0 + i;
-            if (r >= rows) break;
             const float sv = e4m3_value(sb[i]);
             float o[16];
 #pragma unroll
@@ -637,6 +638,7 @@ __global__ void __launch_bounds__(256) k_dequant(const uint8_t* __restrict__ cod
                 o[2 * k] = (p.x * sv) * st;
                 o[2 * k + 1] = (p.y * sv) * st;
             }
+            if (r >= rows) continue;  // (only the stores are predicated)
             TOut* qp = y + r * ld + b * 16;
             if constexpr (sizeof(TOut) == 2) {
                 uint32_t pk[8];
