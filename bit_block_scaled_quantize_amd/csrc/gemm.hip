@@ -711,6 +711,22 @@ __device__ __forceinline__ void full_read_frags(const FullSlot& slot, int t, int
     f.zero = false;
 }
 
+// Fragment o (0..3: A tiles, 4..7: B tiles) of full_read_frags, on its own.
+__device__ __forceinline__ void full_read_frag(const FullSlot& slot, int t, int arow0, const int (&brow)[4], int l32,
+                                               int h, int o, RawFrags& f) {
+    const int pc = (2 * t + h) ^ full_swz(l32);
+    if (o < 4) {
+        const int r = arow0 + 32 * o + l32;
+        f.c[o] = *reinterpret_cast<const uint4*>(&slot.a_codes[r * 128 + 16 * pc]);
+        f.sb[o] = *reinterpret_cast<const uint16_t*>(&slot.a_sc[r * 16 + 4 * t + 2 * h]);
+    } else {
+        const int r = brow[o - 4] + l32;
+        f.c[o] = *reinterpret_cast<const uint4*>(&slot.b_codes[r * 128 + 16 * pc]);
+        f.sb[o] = *reinterpret_cast<const uint16_t*>(&slot.b_sc[r * 16 + 4 * t + 2 * h]);
+    }
+    f.zero = false;
+}
+
 template <bool GROUPED, bool SWIGLU, bool OUT_BF16>
 __global__ void __launch_bounds__(256, 1) k_gemm_full(GemmArgs p) {
     __shared__ __attribute__((aligned(16))) uint8_t a0c[kFullCodes];
@@ -798,10 +814,7 @@ __global__ void __launch_bounds__(256, 1) k_gemm_full(GemmArgs p) {
                     asm volatile("" ::: "memory");
                     __builtin_amdgcn_s_barrier();
                     asm volatile("" ::: "memory");
-                    full_read_frags(other, 0, arow0, brow, l32, h, fn);
                     full_load(src, cclamp(chunk + 2), cur, w);
-                } else {
-                    full_read_frags(cur, t + 1, arow0, brow, l32, h, fn);
                 }
             }
             if (s == 3) scale_frags(fn);  // first use of the next step's fragments
@@ -815,6 +828,11 @@ __global__ void __launch_bounds__(256, 1) k_gemm_full(GemmArgs p) {
                 for (int u = 0; u < 2; ++u) {
                     const int piece = 2 * m + u, o = piece >> 2, q = piece & 3;
                     op[ob ^ 1][o][q] = s < 3 ? frag_piece(fc, o, s + 1, q) : frag_piece(fn, o, 0, q);
+                }
+                // the next step's fragments, one per MFMA over the first half of substep 2
+                if (s == 2 && m < 8) {
+                    if (t == 3) full_read_frag(other, 0, arow0, brow, l32, h, m, fn);
+                    else full_read_frag(cur, t + 1, arow0, brow, l32, h, m, fn);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
