@@ -354,7 +354,12 @@ __global__ void __launch_bounds__(256, 1) k_mx_gemm(MxGemmArgs p) {
 //     flight while the current chunk is consumed;
 //   - scale bytes arrive 16 per row (8 K steps) per load, one group ahead,
 //     into two small buffers, from which each step reads its lane's 8 bytes
-//     along with the fragments;
+//     for the next step at its start;
+//   - the next step's fragments are read one 16-byte piece after each MFMA
+//     (E4M3: 16 pieces; E2M1: 8, after every other MFMA), so the LDS reads
+//     spread over the whole step instead of queueing behind one another;
+//     a chunk's last step opens with the wait and barrier that hand its
+//     slot to the loads of the chunk after next;
 //   - 16-byte chunk c of slot row r sits at chunk c ^ (r % 8) ^ ((r / 8) % 4)
 //     (bits 0..4 of r), which spreads the fragment reads over every bank for
 //     8 lanes (32 banks) and for 16 lanes (64 banks).
@@ -423,6 +428,33 @@ __device__ __forceinline__ void mx_full_frags(const uint8_t* slot, int t, int ro
             a[i] = v8i_t{aq[0], aq[1], aq[2], aq[3], 0, 0, 0, 0};
             b[i] = v8i_t{bq[0], bq[1], bq[2], bq[3], 0, 0, 0, 0};
         }
+    }
+}
+
+// One piece of the fragments of K step t: E4M3 pieces 0..15 (A then B; tile
+// (o & 7) >> 1, low or high 16 bytes by o & 1), E2M1 pieces 0..7 (A then B,
+// tile o & 3).
+template <int ELEM>
+__device__ __forceinline__ void mx_full_frag_piece(const uint8_t* slot, int t, int rowa, int rowb, int sw, int h,
+                                                   int o, v8i_t (&a)[4], v8i_t (&b)[4]) {
+    using F = MxFull<ELEM>;
+    if constexpr (ELEM == kMxE4M3) {
+        const bool isb = o >= 8;
+        const int i = (o & 7) >> 1, hi = o & 1;
+        const uint8_t* r = isb ? slot + F::CODES + (rowb + 32 * i) * 128 : slot + (rowa + 32 * i) * 128;
+        const int c = (4 * t + 2 * hi + h) ^ sw;
+        const v4i_t q = lds16(r + 16 * c);
+        v8i_t& d = isb ? b[i] : a[i];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) d[4 * hi + e] = q[e];
+    } else {
+        const bool isb = o >= 4;
+        const int i = o & 3;
+        const uint8_t* r = isb ? slot + F::CODES + (rowb + 32 * i) * 128 : slot + (rowa + 32 * i) * 128;
+        const int c = (2 * t + h) ^ sw;
+        const v4i_t q = lds16(r + 16 * c);
+        v8i_t& d = isb ? b[i] : a[i];
+        d = v8i_t{q[0], q[1], q[2], q[3], 0, 0, 0, 0};
     }
 }
 
@@ -512,13 +544,14 @@ __global__ void __launch_bounds__(256, 1) k_mx_gemm_full(MxGemmArgs p) {
             uint8_t* gbuf = (s / 8) ? scb1 : scb0;  // this step's scale group
 #pragma unroll
             for (int m = 0; m < 16; ++m) {
-                if (m == 8) {
+                if (m == 0) {
                     __builtin_amdgcn_sched_barrier(0);
                     if (t == SPC - 1) {
-                        // the next chunk's loads (and any scale group issued
-                        // before them) landed; after the barrier every wave
-                        // has read all of this chunk's slot
-                        __builtin_amdgcn_s_waitcnt(mx_vmcnt_at_most(0));
+                        // this step's fragments are in registers and the next
+                        // chunk's loads (and any scale group issued before
+                        // them) landed; after the barrier every wave has read
+                        // all of this chunk's slot
+                        __builtin_amdgcn_s_waitcnt(mx_vmcnt_at_most(0) & mx_lgkmcnt_zero());
                         asm volatile("" ::: "memory");
                         __builtin_amdgcn_s_barrier();
                         asm volatile("" ::: "memory");
@@ -532,17 +565,22 @@ __global__ void __launch_bounds__(256, 1) k_mx_gemm_full(MxGemmArgs p) {
                         } else {
                             mx_full_scales<ELEM>(gbuf, g + 1, rowa, rowb, h, sa[cur ^ 1], sb[cur ^ 1]);
                         }
-                        mx_full_frags<ELEM>(other, 0, rowa, rowb, sw, h, fa[cur ^ 1], fb[cur ^ 1]);
                         mx_full_chunk_load<ELEM>(src, cclamp(chunk0 + cc + 2), slot, w);
                     } else {
                         mx_full_scales<ELEM>(gbuf, g + 1, rowa, rowb, h, sa[cur ^ 1], sb[cur ^ 1]);
-                        mx_full_frags<ELEM>(slot, t + 1, rowa, rowb, sw, h, fa[cur ^ 1], fb[cur ^ 1]);
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 }
                 const int i = m >> 2, jj = m & 3;
                 acc[i][jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                     fa[cur][i], fb[cur][jj], acc[i][jj], F::FMT, F::FMT, 0, sa[cur][i], 0, sb[cur][jj]);
+                // the next step's fragments, spread over this step's MFMAs
+                if (ELEM == kMxE4M3 || (m & 1) == 0) {
+                    const int o = ELEM == kMxE4M3 ? m : m >> 1;
+                    if (t == SPC - 1) mx_full_frag_piece<ELEM>(other, 0, rowa, rowb, sw, h, o, fa[cur ^ 1], fb[cur ^ 1]);
+                    else mx_full_frag_piece<ELEM>(slot, t + 1, rowa, rowb, sw, h, o, fa[cur ^ 1], fb[cur ^ 1]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
     }
