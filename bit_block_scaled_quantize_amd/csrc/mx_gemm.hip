@@ -354,7 +354,7 @@ __global__ void __launch_bounds__(256, 1) k_mx_gemm(MxGemmArgs p) {
 //     flight while the current chunk is consumed;
 //   - scale bytes arrive 16 per row (8 K steps) per load, one group ahead,
 //     into two small buffers, from which each step reads its lane's 8 bytes
-//     for the next step at its start;
+//     for the next step, one after each of its first 8 MFMAs;
 //   - the next step's fragments are read one 16-byte piece after each MFMA
 //     (E4M3: 16 pieces; E2M1: 8, after every other MFMA), so the LDS reads
 //     spread over the whole step instead of queueing behind one another;
@@ -471,6 +471,15 @@ __device__ __forceinline__ void mx_full_scales(const uint8_t* buf, int g, int ro
     }
 }
 
+// Scale byte q (0..3: A rows, 4..7: B rows) of K step g of a group.
+template <int ELEM>
+__device__ __forceinline__ void mx_full_scale_piece(const uint8_t* buf, int g, int rowa, int rowb, int h, int q,
+                                                    int (&sa)[4], int (&sb)[4]) {
+    using F = MxFull<ELEM>;
+    if (q < 4) sa[q] = buf[(rowa + 32 * q) * 16 + 2 * g + h];
+    else sb[q - 4] = buf[F::SCB + (rowb + 32 * (q - 4)) * 16 + 2 * g + h];
+}
+
 template <int ELEM, bool OUT_BF16>
 __global__ void __launch_bounds__(256, 1) k_mx_gemm_full(MxGemmArgs p) {
     using F = MxFull<ELEM>;
@@ -556,24 +565,23 @@ __global__ void __launch_bounds__(256, 1) k_mx_gemm_full(MxGemmArgs p) {
                         __builtin_amdgcn_s_barrier();
                         asm volatile("" ::: "memory");
                         if (g == 7) {
-                            // the next step opens the other scale group; every
-                            // wave is done with this group's buffer, which
-                            // takes the group after next
-                            uint8_t* nb = (s == 7) ? scb1 : scb0;
-                            mx_full_scales<ELEM>(nb, 0, rowa, rowb, h, sa[cur ^ 1], sb[cur ^ 1]);
+                            // every wave is done with this group's buffer,
+                            // which takes the group after next
                             mx_full_scale_load<ELEM>(src, gclamp(group0 + s / 8 + 2), gbuf, w);
-                        } else {
-                            mx_full_scales<ELEM>(gbuf, g + 1, rowa, rowb, h, sa[cur ^ 1], sb[cur ^ 1]);
                         }
                         mx_full_chunk_load<ELEM>(src, cclamp(chunk0 + cc + 2), slot, w);
-                    } else {
-                        mx_full_scales<ELEM>(gbuf, g + 1, rowa, rowb, h, sa[cur ^ 1], sb[cur ^ 1]);
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 }
                 const int i = m >> 2, jj = m & 3;
                 acc[i][jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                     fa[cur][i], fb[cur][jj], acc[i][jj], F::FMT, F::FMT, 0, sa[cur][i], 0, sb[cur][jj]);
+                // the next step's scale bytes (at a group's last step, from
+                // the other group's buffer), one after each of the first 8 MFMAs
+                if (m < 8) {
+                    if (g == 7) mx_full_scale_piece<ELEM>((s == 7) ? scb1 : scb0, 0, rowa, rowb, h, m, sa[cur ^ 1], sb[cur ^ 1]);
+                    else mx_full_scale_piece<ELEM>(gbuf, g + 1, rowa, rowb, h, m, sa[cur ^ 1], sb[cur ^ 1]);
+                }
                 // the next step's fragments, spread over this step's MFMAs
                 if (ELEM == kMxE4M3 || (m & 1) == 0) {
                     const int o = ELEM == kMxE4M3 ? m : m >> 1;
