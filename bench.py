@@ -111,10 +111,11 @@ def kernel_source_hash(kernel_key):
     return h.hexdigest()[:16]
 
 
-def traffic_for(kernel_key):
-    """HBM bytes per launch of `kernel_key` from the committed counter
-    summary, or None when absent or taken on different kernel sources."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+def profile_figure(fname, kernel_key, field):
+    """`field` of `kernel_key` in the committed counter summary
+    profiles/`fname`, or None when absent or taken on different kernel
+    sources."""
+    path = os.path.join(ROOT, "profiles", fname)
     if not os.path.exists(path):
         return None
     with open(path) as fh:
@@ -122,7 +123,18 @@ def traffic_for(kernel_key):
     k = t.get("kernels", {}).get(kernel_key)
     if k is None or k.get("source_hash") != kernel_source_hash(kernel_key):
         return None
-    return k.get("hbm_bytes_per_launch")
+    return k.get(field)
+
+
+def traffic_for(kernel_key):
+    """HBM bytes per launch (FETCH_SIZE and WRITE_SIZE, calibrated)."""
+    return profile_figure("traffic.json", kernel_key, "hbm_bytes_per_launch")
+
+
+def valu_issue_share_for(kernel_key):
+    """Share of cycles the kernel's SIMDs spend issuing VALU instructions
+    (SQ_INSTS_VALU x 4 / (SIMDs x cycles)): near 1, VALU issue bounds it."""
+    return profile_figure("valu.json", kernel_key, "valu_issue_share")
 
 
 def main():
@@ -312,7 +324,8 @@ def main():
     dk = kern[dom]
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(dk["gbs"], 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(dk["frac_hbm"], 4), "traffic": traffic_for(dom),
-                "avg_launch_ms": round(dk["ms"], 5), "algorithmic_bytes_per_launch": dk["bytes"]}
+                "avg_launch_ms": round(dk["ms"], 5), "algorithmic_bytes_per_launch": dk["bytes"],
+                "valu_issue_share": valu_issue_share_for(dom)}
 
     result = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,

@@ -26,3 +26,20 @@ def test_cpu_baseline_fields():
     assert set(cb) == {"value", "unit", "cores", "kind", "sample"}
     assert cb["kind"] == "oracle" and cb["unit"] == "GB/s" and cb["cores"] == 1
     assert cb["value"] > 0 and "rows 0..255" in cb["sample"]
+
+
+def test_profile_figures_follow_the_kernel_sources(tmp_path, monkeypatch):
+    """A counter figure is reported only while the kernel sources hash to
+    the value stored with it; otherwise, or without the file, it is None."""
+    import json
+    import bench
+    (tmp_path / "profiles").mkdir()
+    (tmp_path / "profiles" / "valu.json").write_text(json.dumps(
+        {"kernels": {"quant_row_sr": {"valu_issue_share": 0.8, "source_hash": "abc"}}}))
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda k: "abc")
+    assert bench.valu_issue_share_for("quant_row_sr") == 0.8
+    assert bench.valu_issue_share_for("quant_col_sr") is None
+    assert bench.traffic_for("quant_row_sr") is None  # no traffic.json here
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda k: "def")
+    assert bench.valu_issue_share_for("quant_row_sr") is None
