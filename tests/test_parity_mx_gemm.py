@@ -113,10 +113,12 @@ def test_mx_gemm_exact_case(nv, elem, shape):
 
 @pytest.mark.parametrize("elem", ELEMS)
 @pytest.mark.parametrize("kind", ["normal", "t3", "spiky"])
-@pytest.mark.parametrize("shape", [(1, 1, 64), (33, 65, 128), (300, 260, 512), (512, 320, 1024), (300, 260, 2048)])
+@pytest.mark.parametrize("shape", [(1, 1, 64), (33, 65, 128), (300, 260, 512), (512, 320, 1024), (300, 260, 2048),
+                                   (264, 200, 3072)])
 def test_mx_gemm_matches_oracle(nv, elem, kind, shape):
     """Ragged M and N; K below and at the 1024 multiple that selects the
-    full-line kernel (K = 1024, 2048) -- both kernels are covered."""
+    full-line kernel (K = 1024, 2048, and 3072: an odd number of its
+    16-step bodies) -- both kernels are covered."""
     M, N, K = shape
     seed = M * 3 + N * 5 + K
     if kind == "normal":
