@@ -294,22 +294,32 @@ def main():
         kern[name] = dict(ms=time_events(qk(lay, rnd, out), reps, torch), bytes=b)
     q2d = E * 2 + E // 2 + E // 256 + 4                  # 2D: one scale byte per 16 x 16 tile
     kern["quant_2d_rne"] = dict(ms=time_events(qk(nv.NVFP4_BLK_2D, RNE, Q2d), reps, torch), bytes=q2d)
-    kern["dequant_row_bf16"] = dict(ms=time_events(lambda i: nv.nvfp4_dequantize(R, out=yr), reps, torch),
-                                    bytes=dq)
+    # dequantize and re-quantize read NVFP4 tensors: one per input buffer, and
+    # one output per buffer, so consecutive launches touch different memory
+    # (4 x 36 MiB in, 4 x 128 MiB or 4 x 36 MiB out) instead of re-reading one
+    # tensor that stays in the 256 MB Infinity Cache
+    Rb = [nv.nvfp4_quantize(xs[b], layout=ROW, round=RNE, amax_in=amax[b]) for b in range(NBUF)]
+    yb = [torch.empty((N, N), dtype=torch.bfloat16, device=dev) for _ in range(NBUF)]
+    kern["dequant_row_bf16"] = dict(ms=time_events(
+        lambda i: nv.nvfp4_dequantize(Rb[i % NBUF], out=yb[i % NBUF]), reps, torch), bytes=dq)
+    del Rb, yb
     # re-quantization of the row-quantized tensor along columns (not part of the step):
     # codes + scales in, codes + scales out, 1.125 B/element
     rq = 2 * (E // 2 + E // 16 + 4)
-    Rq = nv.nvfp4_quantize(xs[0], layout=ROW, round=SR, sr_seed=3)
-    Cq = nv.NVFP4Tensor.empty(N, N, device=dev)
-    ramax = torch.zeros(1, dtype=torch.float32, device=dev)
-    nv.nvfp4_requantize(Rq, out=Cq, amax_out=ramax, workspace=ws)
-    ramax_h = torch.zeros(1, dtype=torch.float32, device=dev)
-    nv.nvfp4_requantize(Rq, out=Cq, hadamard=True, hadamard_seed=4, amax_out=ramax_h, workspace=ws)
+    Rq = [nv.nvfp4_quantize(xs[b], layout=ROW, round=SR, sr_seed=3 + b) for b in range(NBUF)]
+    Cq = [nv.NVFP4Tensor.empty(N, N, device=dev) for _ in range(NBUF)]
+    ramax = [torch.zeros(1, dtype=torch.float32, device=dev) for _ in range(NBUF)]
+    ramax_h = [torch.zeros(1, dtype=torch.float32, device=dev) for _ in range(NBUF)]
+    for b in range(NBUF):
+        nv.nvfp4_requantize(Rq[b], out=Cq[b], amax_out=ramax[b], workspace=ws)
+        nv.nvfp4_requantize(Rq[b], out=Cq[b], hadamard=True, hadamard_seed=4, amax_out=ramax_h[b], workspace=ws)
     kern["requant_col_sr"] = dict(ms=time_events(
-        lambda i: nv.nvfp4_requantize(Rq, round=SR, sr_seed=6 + i, amax_in=ramax, out=Cq), reps, torch), bytes=rq)
+        lambda i: nv.nvfp4_requantize(Rq[i % NBUF], round=SR, sr_seed=6 + i, amax_in=ramax[i % NBUF],
+                                      out=Cq[i % NBUF]), reps, torch), bytes=rq)
     kern["requant_col_sr_hadamard"] = dict(ms=time_events(
-        lambda i: nv.nvfp4_requantize(Rq, round=SR, sr_seed=6 + i, hadamard=True, hadamard_seed=4,
-                                      amax_in=ramax_h, out=Cq), reps, torch), bytes=rq)
+        lambda i: nv.nvfp4_requantize(Rq[i % NBUF], round=SR, sr_seed=6 + i, hadamard=True, hadamard_seed=4,
+                                      amax_in=ramax_h[i % NBUF], out=Cq[i % NBUF]), reps, torch), bytes=rq)
+    del Rq, Cq
     amax_ms = time_events(lambda i: nv.nvfp4_quantize(xs[i % NBUF], layout=ROW, out=R, workspace=ws),
                           reps, torch) - kern["quant_row_rne"]["ms"]
     kern["amax_pass"] = dict(ms=amax_ms, bytes=E * 2)
@@ -579,10 +589,14 @@ def bench_mx_quant(nv, torch, xs, reps):
         ms = time_events(lambda i: nv.nvfp4_mx_quantize(xs[i % NBUF], layout=lay, elem=elem, round=rnd,
                                                         sr_seed=9 + i, out=q[elem]), reps, torch)
         out.update(_gbs(name, E * 2 + code_bytes[elem] + E // 32, ms))
-    y = torch.empty((N, N), dtype=torch.bfloat16, device="cuda")
+    # dequantize: one MX tensor and one output per input buffer (rotated)
+    ys = [torch.empty((N, N), dtype=torch.bfloat16, device="cuda") for _ in range(NBUF)]
     for name, elem in [("mx_dequant_e4m3_bf16", E4), ("mx_dequant_e2m1_bf16", E2)]:
-        ms = time_events(lambda i: nv.nvfp4_mx_dequantize(q[elem], out=y), reps, torch)
+        qs = [nv.nvfp4_mx_quantize(xs[b], elem=elem) for b in range(NBUF)]
+        ms = time_events(lambda i: nv.nvfp4_mx_dequantize(qs[i % NBUF], out=ys[i % NBUF]), reps, torch)
         out.update(_gbs(name, code_bytes[elem] + E // 32 + E * 2, ms))
+        del qs
+    del ys
     return out
 
 

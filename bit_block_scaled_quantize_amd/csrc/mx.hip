@@ -5,9 +5,9 @@
 // Inkling 2 Small 4-битными числами", iitak.ru, section "Как это работает"),
 // MXFP4 is the Open Compute Project format NVFP4 is measured against
 // ("Nvidia добивается успеха с 4-битным форматом NVFP4", asector.ru, section
-// "Эксперименты и сравнение с FP8"), and expert outputs travel in an 8.25-bit
-// format (iitak.ru page, section "Но") -- 8-bit elements plus one 8-bit scale
-// per 32.  The reading implemented here is the OCP Microscaling definition:
+// "Перспективы и дальнейшие направления исследований"), and expert outputs
+// travel in an 8.25-bit format (iitak.ru page, section "Но") -- 8-bit
+// elements plus one 8-bit scale per 32.  The reading implemented here is the OCP Microscaling definition:
 //   - 32 consecutive elements along the block dimension share one E8M0 scale
 //     X = 2^s, s = floor(log2 max|V|) - emax (emax 8 for E4M3 elements, 2 for
 //     E2M1), clamped to [-127, 127], -127 for an all-zero block; the scale

@@ -268,6 +268,9 @@ nvfp4_status nvfp4_mx_gemm(const nvfp4_mx_tensor* A, const nvfp4_mx_tensor* B, v
     if (A->elem != B->elem) return NVFP4_ERR_UNSUPPORTED;
     const int64_t M = A->rows, N = B->rows, K = A->cols;
     if (K % 64) return NVFP4_ERR_UNSUPPORTED;
+    // the kernels keep per-lane byte offsets inside a 256-row tile in 32 bits
+    const uint64_t row_bytes = (uint64_t)(A->elem == NVFP4_MX_E4M3 ? K : K / 2);
+    if (256 * row_bytes >= ((uint64_t)1 << 32)) return NVFP4_ERR_UNSUPPORTED;
     if (ldc < N) return NVFP4_ERR_SHAPE;
     if (M > 0 && N > 0) {
         if (!C) return NVFP4_ERR_NULL;

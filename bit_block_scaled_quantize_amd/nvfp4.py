@@ -5,7 +5,9 @@ the HIP kernels behind the C ABI.  PyTorch supplies device memory (output
 tensors are allocated with torch) and the current HIP stream.  If the built
 library is missing, importing this module raises -- there is no fallback.
 """
+import contextlib
 import ctypes
+import functools
 import os
 from dataclasses import dataclass
 
@@ -104,6 +106,25 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _on(stream):
+    """Context in which a call's outputs and workspace are allocated: the
+    stream the kernels run on.  torch's caching allocator hands a freed block
+    back only to later allocations on the stream it was allocated on, so a
+    workspace released when the call returns cannot be reused by other work
+    while the kernels on `stream` still read it."""
+    return contextlib.nullcontext() if stream is None else torch.cuda.stream(stream)
+
+
+def _launches_on_stream(fn):
+    """Run the binding function fn with `stream` (keyword) as torch's current
+    stream, so that everything it allocates belongs to that stream."""
+    @functools.wraps(fn)
+    def call(*args, stream=None, **kw):
+        with _on(stream):
+            return fn(*args, stream=stream, **kw)
+    return call
+
+
 def _dtype_code(dt):
     if dt == torch.float32:
         return NVFP4_F32
@@ -144,6 +165,7 @@ def nvfp4_quantize_workspace_size(rows, cols, amax_in=None):
     return int(lib.nvfp4_quantize_workspace_size(rows, cols, ctypes.byref(o)))
 
 
+@_launches_on_stream
 def nvfp4_quantize(x, layout=NVFP4_ROW_1D, round=NVFP4_RNE, sr_seed=0, hadamard=False,
                    hadamard_seed=0, amax_in=None, out=None, workspace=None, amax_out=None,
                    stream=None):
@@ -184,6 +206,7 @@ def nvfp4_quantize(x, layout=NVFP4_ROW_1D, round=NVFP4_RNE, sr_seed=0, hadamard=
     return tuple(outs) if layout == NVFP4_ROW_COL_1D else outs[0]
 
 
+@_launches_on_stream
 def nvfp4_requantize(q, round=NVFP4_RNE, sr_seed=0, hadamard=False, hadamard_seed=0, amax_in=None,
                      out=None, workspace=None, amax_out=None, stream=None):
     """COL_1D re-quantization of a row-blocked NVFP4Tensor q (rows x cols):
@@ -206,6 +229,7 @@ def nvfp4_requantize(q, round=NVFP4_RNE, sr_seed=0, hadamard=False, hadamard_see
     return out
 
 
+@_launches_on_stream
 def nvfp4_dequantize(q, dtype=torch.float32, out=None, stream=None):
     if out is None:
         out = torch.empty((q.rows, q.cols), dtype=dtype, device=q.codes.device)
@@ -218,6 +242,7 @@ def nvfp4_dequantize(q, dtype=torch.float32, out=None, stream=None):
     return out
 
 
+@_launches_on_stream
 def nvfp4_gemm(A, B, out_dtype=torch.float32, out=None, stream=None):
     """C = A B^T (A: M x K, B: N x K NVFP4 tensors)."""
     if out is None:
@@ -231,6 +256,7 @@ def nvfp4_gemm(A, B, out_dtype=torch.float32, out=None, stream=None):
     return out
 
 
+@_launches_on_stream
 def nvfp4_grouped_gemm(A, offsets, B, groups, epilogue=NVFP4_EPI_NONE, out_dtype=torch.bfloat16,
                        out=None, amax_out=None, stream=None):
     """Per group g: rows offsets[g]..offsets[g+1]-1 of A times B_g^T (B stacks
@@ -273,6 +299,7 @@ class MXTensor:
         return MXTensor(codes, scales, rows, cols, elem)
 
 
+@_launches_on_stream
 def nvfp4_mx_quantize(x, layout=NVFP4_ROW_1D, elem=NVFP4_MX_E4M3, round=NVFP4_RNE, sr_seed=0, out=None,
                       stream=None):
     """MX-quantize a 2-D device tensor (float32 or bfloat16, unit column
@@ -291,6 +318,7 @@ def nvfp4_mx_quantize(x, layout=NVFP4_ROW_1D, elem=NVFP4_MX_E4M3, round=NVFP4_RN
     return out
 
 
+@_launches_on_stream
 def nvfp4_mx_dequantize(q, dtype=torch.float32, out=None, stream=None):
     if out is None:
         out = torch.empty((q.rows, q.cols), dtype=dtype, device=q.codes.device)
@@ -303,6 +331,7 @@ def nvfp4_mx_dequantize(q, dtype=torch.float32, out=None, stream=None):
     return out
 
 
+@_launches_on_stream
 def nvfp4_mx_gemm(A, B, out_dtype=torch.float32, out=None, stream=None):
     """C = A B^T (A: M x K, B: N x K MX tensors of one element format)."""
     if out is None:

@@ -218,8 +218,9 @@ nvfp4_status nvfp4_grouped_gemm(int32_t G, const nvfp4_tensor* A, const int64_t*
  * MX formats (OCP Microscaling).  The pages name MXFP8 (the backward-pass
  * format at Thinking Machines: iitak.ru page, "Как это работает"), MXFP4 (the
  * Open Compute Project format NVFP4 is compared with: asector.ru page,
- * "Эксперименты и сравнение с FP8") and an 8.25-bit transit format for expert
- * outputs (iitak.ru page, "Но"), without defining them.  This library reads
+ * "Перспективы и дальнейшие направления исследований") and an 8.25-bit
+ * transit format for expert outputs (iitak.ru page, "Но"), without defining
+ * them.  This library reads
  * them as OCP Microscaling:
  *   - 32 consecutive elements along the block dimension share an E8M0 scale
  *     byte b = s + 127 (value 2^s), s = floor(log2(max|V|)) - emax, emax = 8
@@ -278,7 +279,8 @@ nvfp4_status nvfp4_mx_dequantize(const nvfp4_mx_tensor* q, void* y, nvfp4_dtype 
  * keeps about 13 significant bits, relative to the step's largest product,
  * while it sums a step's 64 products (errors up to ~2^-12 of that product).
  * Requirements: K % 64 == 0 (K % 32 != 0 is ERR_SHAPE, K % 64 == 32 is
- * ERR_UNSUPPORTED), A->elem == B->elem (else ERR_UNSUPPORTED), ldc >= N,
+ * ERR_UNSUPPORTED), code bytes per row (K for E4M3, K/2 for E2M1) below
+ * 2^24 (else ERR_UNSUPPORTED), A->elem == B->elem (else ERR_UNSUPPORTED), ldc >= N,
  * codes 16-byte aligned, scales 2-byte aligned, C aligned to its element.
  * Source: asector.ru page, "NVFP4 и Blackwell" (block-scaled tensor-core
  * compute); iitak.ru page, "Как это работает" (MXFP8 in the backward pass). */

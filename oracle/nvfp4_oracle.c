@@ -455,9 +455,9 @@ double orc_swiglu(double g, double u) {
  * The pages name MXFP8 (the backward pass at Thinking Machines runs in it:
  * P3 "Как это работает"; Blackwell tensor cores support MXFP8/MXFP6/MXFP4:
  * P2 "NVFP4 и Blackwell"), MXFP4 (the Open Compute Project's 4-bit format
- * NVFP4 is compared with: P1; P2 "Эксперименты и сравнение с FP8") and an
- * 8.25-bit transit format for expert outputs (P3 "Но"), but define none of
- * them.  The reading here is the OCP Microscaling definition: blocks of 32
+ * NVFP4 is compared with: P1; P2 "Перспективы и дальнейшие направления
+ * исследований") and an 8.25-bit transit format for expert outputs (P3
+ * "Но"), but define none of them.  The reading here is the OCP Microscaling definition: blocks of 32
  * consecutive elements along the block dimension share one E8M0 scale
  * X = 2^s, s = floor(log2(max |V|)) - emax (emax = 8 for E4M3 elements,
  * 2 for E2M1), clamped to [-127, 127] (s = -127 for an all-zero block);

@@ -214,3 +214,7 @@ def test_mx_gemm_rejects_bad_arguments(nv):
     assert g(ac=4096 + 4) == E["ALIGN"]
     assert g(asc=8192 + 1) == E["ALIGN"]
     assert g(ma=(-1, 128, 0)) == E["SHAPE"]
+    # per-lane 32-bit byte offsets inside a 256-row tile: code rows below 2^24 bytes
+    K4 = 1 << 24                                                 # E4M3: 2^24 bytes per row
+    assert g(ma=(64, K4, 0), mb=(32, K4, 0)) == E["UNSUP"]
+    assert g(ma=(64, 2 * K4, 1), mb=(32, 2 * K4, 1)) == E["UNSUP"]   # E2M1: K/2 bytes per row

@@ -135,3 +135,34 @@ def test_two_streams_match_one_stream(nv):
         torch.cuda.synchronize()
         for k, (t, r) in enumerate(zip(outputs, ref)):
             assert torch.equal(t.view(torch.uint8), r.view(torch.uint8)), f"rep {rep}: output {k} differs"
+
+
+def test_stream_argument_keeps_workspace_on_that_stream(nv):
+    """Calls given stream= (not torch's current stream) allocate their outputs
+    and their amax workspace on that stream: work enqueued on the current
+    stream right after the call returns, which allocates and overwrites
+    memory, cannot receive the workspace the delayed kernels still read."""
+    R, C = 512, 1024
+    x = to_device(W.f32_to_bf16_bits(W.student_t((R, C), 3.0, seed=51)))
+    xh = x.cpu().view(torch.int16).numpy().view(np.uint16)
+    ref = O.quantize(xh, O.BF16, O.ROW_1D, O.SR, sr_seed=7)
+    ref_rq = O.requantize(ref, O.SR, sr_seed=8)
+    side = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            torch.cuda._sleep(50_000_000)  # a bounded spin: the calls below start late
+        q = nv.nvfp4_quantize(x, round=nv.NVFP4_SR, sr_seed=7, stream=side)
+        rq = nv.nvfp4_requantize(q, round=nv.NVFP4_SR, sr_seed=8, stream=side)
+        # the current stream now allocates and fills blocks of every small size
+        junk = [torch.full((n,), 3.0e38, dtype=torch.float32, device="cuda") for n in (128, 256, 512, 1024)]
+        torch.cuda.synchronize()
+        del junk
+        got = O.QTensor(q.codes.cpu().numpy(), q.scales.cpu().numpy(), float(q.tensor_scale[0].item()),
+                        q.rows, q.cols, q.scale_mode)
+        assert got.ts == ref.ts, f"rep {rep}: tensor scale {got.ts} != {ref.ts}"
+        assert np.array_equal(got.codes, ref.codes) and np.array_equal(got.scales, ref.scales)
+        assert float(rq.tensor_scale[0].item()) == ref_rq.ts
+        assert np.array_equal(rq.codes.cpu().numpy(), ref_rq.codes)
+        assert np.array_equal(rq.scales.cpu().numpy(), ref_rq.scales)

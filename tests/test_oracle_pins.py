@@ -422,6 +422,26 @@ def _exact_deq(q):
     return out
 
 
+@pytest.mark.parametrize("layout", [O.ROW_1D, O.BLK_2D])
+def test_dequantize_f64_and_f32_equal_rational_value(layout):
+    """The float64 dequantization is the exact value code x multiplier x s_t
+    (at most 30 significant bits, so float64 holds it), and the binary32 one
+    is that exact value rounded once; both checked element by element
+    against rational arithmetic on the page's value set and torch's E4M3."""
+    x = W.with_spikes(W.student_t((32, 64), 3.0, seed=60), 0.05, 300.0, seed=61)
+    x[3, :16] = 0.0                      # an all-zero block: multiplier byte 0
+    x[5, 16:32] *= 1e-6                  # a block with a subnormal-range multiplier
+    q = O.quantize(x, O.F32, layout, O.SR, sr_seed=62)
+    exact = _exact_deq(q)
+    d64 = O.dequantize_f64(q)
+    d32 = O.dequantize(q, O.F32)
+    for r in range(q.rows):
+        for c in range(q.cols):
+            assert Fraction(float(d64[r, c])) == exact[r][c], (r, c)
+            assert d32[r, c] == np.float32(float(exact[r][c])), (r, c)
+    assert len({float(v) for row in exact for v in row}) > 40   # many distinct values were checked
+
+
 @pytest.mark.parametrize("modes", [(O.ROW_1D, O.ROW_1D), (O.ROW_1D, O.BLK_2D), (O.COL_1D, O.COL_1D)])
 def test_gemm_brute_force_tiny(modes):
     M, N, K = 16, 16, 48

@@ -4,7 +4,8 @@ both block directions, both roundings and both input types; dequantized
 values bit for bit.  MXFP8 and MXFP4 are named on "Thinking Machines ускорила
 обучение Inkling 2 Small 4-битными числами" (iitak.ru, sections "Как это
 работает" and "Но") and "Nvidia добивается успеха с 4-битным форматом NVFP4"
-(asector.ru, "Эксперименты и сравнение с FP8"); the format details are the
+(asector.ru, "Перспективы и дальнейшие направления исследований"); the
+format details are the
 OCP reading both sides implement."""
 import numpy as np
 import pytest
