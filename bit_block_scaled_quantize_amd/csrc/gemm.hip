@@ -878,9 +878,20 @@ inline bool full_path(const Operand& A, const Operand& B, int64_t a_rows, int64_
 }  // namespace
 
 hipError_t launch_gemm(const Operand& A, const Operand& B, int64_t M, int64_t N, int64_t K,
-                       void* C, bool c_bf16, int64_t ldc, hipStream_t s) {
+                       void* C, bool c_bf16, int64_t ldc, bool swiglu, hipStream_t s) {
     if (M == 0 || N == 0) return hipSuccess;
     GemmArgs p{A, B, M, N, K, C, ldc, nullptr, 1, nullptr};
+    if (swiglu) {
+        // gate column j and up column F + j share a tile: 128 output columns per tile
+        dim3 grid((unsigned)cdiv(N / 2, kBN / 2), (unsigned)cdiv(M, kBM));
+        if (full_path(A, B, M, N, K))
+            hipLaunchKernelGGL((k_gemm_full<false, true, true>), grid, dim3(256), 0, s, p);
+        else if (fast_path(A, B, K))
+            hipLaunchKernelGGL((k_gemm_ring<false, true, true>), grid, dim3(256), 0, s, p);
+        else
+            hipLaunchKernelGGL((k_gemm<false, true, true, false>), grid, dim3(256), 0, s, p);
+        return hipGetLastError();
+    }
     dim3 grid((unsigned)cdiv(N, kBN), (unsigned)cdiv(M, kBM));
     if (full_path(A, B, M, N, K)) {
         if (c_bf16)

@@ -50,9 +50,11 @@ struct Operand {
     int scale_2d;
 };
 
-// C (M x N, ldc) = A * B^T; c_bf16 selects the output type.
+// C (M x N, ldc) = A * B^T; c_bf16 selects the output type.  swiglu: N = 2F,
+// C (M x F, BF16) = gate * sigmoid(gate) * up with gate = columns [0, F) and
+// up = columns [F, 2F) of A * B^T.
 hipError_t launch_gemm(const Operand& A, const Operand& B, int64_t M, int64_t N, int64_t K,
-                       void* C, bool c_bf16, int64_t ldc, hipStream_t s);
+                       void* C, bool c_bf16, int64_t ldc, bool swiglu, hipStream_t s);
 
 // Grouped GEMM over G groups (see nvfp4_grouped_gemm).  n_per_group = rows of
 // one group's weight matrix; swiglu halves the output width.

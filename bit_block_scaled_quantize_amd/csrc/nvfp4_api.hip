@@ -71,8 +71,7 @@ nvfp4_status nvfp4_quantize(const void* x, nvfp4_dtype dt, int64_t rows, int64_t
     const bool col_blocks = layout == NVFP4_COL_1D || layout == NVFP4_ROW_COL_1D || layout == NVFP4_BLK_2D;
     if (row_blocks && cols % 16) return NVFP4_ERR_SHAPE;
     if (col_blocks && rows % 16) return NVFP4_ERR_SHAPE;
-    if (opts->hadamard && (layout == NVFP4_BLK_2D || layout == NVFP4_ROW_COL_1D))
-        return NVFP4_ERR_UNSUPPORTED;
+    if (opts->hadamard && layout == NVFP4_BLK_2D) return NVFP4_ERR_UNSUPPORTED;
     const bool empty = rows == 0 || cols == 0;
     if (!empty && !x) return NVFP4_ERR_NULL;
     if (!aligned(x, 16) || (ld * (int64_t)dtype_size(dt)) % 16) return NVFP4_ERR_ALIGN;
@@ -160,18 +159,23 @@ nvfp4_status nvfp4_gemm(const nvfp4_tensor* A, const nvfp4_tensor* B, void* C, n
     if (!A || !B) return NVFP4_ERR_NULL;
     if (!valid_dtype(c_dt)) return NVFP4_ERR_ENUM;
     if (ep != NVFP4_EPI_NONE && ep != NVFP4_EPI_SWIGLU) return NVFP4_ERR_ENUM;
-    if (ep != NVFP4_EPI_NONE) return NVFP4_ERR_UNSUPPORTED;
     nvfp4_status st = check_operand(A);
     if (st != NVFP4_OK) return st;
     st = check_operand(B);
     if (st != NVFP4_OK) return st;
     if (A->cols != B->cols) return NVFP4_ERR_SHAPE;
     const int64_t M = A->rows, N = B->rows, K = A->cols;
-    if (ldc < N) return NVFP4_ERR_SHAPE;
-    if (M > 0 && N > 0 && !C) return NVFP4_ERR_NULL;
+    const bool swiglu = ep == NVFP4_EPI_SWIGLU;
+    if (swiglu) {
+        if (N % 2 || (N / 2) % 16) return NVFP4_ERR_SHAPE;
+        if (c_dt != NVFP4_BF16) return NVFP4_ERR_UNSUPPORTED;
+    }
+    const int64_t ncols = swiglu ? N / 2 : N;
+    if (ldc < ncols) return NVFP4_ERR_SHAPE;
+    if (M > 0 && ncols > 0 && !C) return NVFP4_ERR_NULL;
     if (!aligned(C, dtype_size(c_dt))) return NVFP4_ERR_ALIGN;
     if (cdiv(M, 128) > kMaxGridY) return NVFP4_ERR_UNSUPPORTED;
-    hipError_t e = launch_gemm(as_operand(A), as_operand(B), M, N, K, C, c_dt == NVFP4_BF16, ldc,
+    hipError_t e = launch_gemm(as_operand(A), as_operand(B), M, N, K, C, c_dt == NVFP4_BF16, ldc, swiglu,
                                static_cast<hipStream_t>(stream));
     return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }

@@ -866,6 +866,20 @@ template <typename T>
 hipError_t quantize_typed(const T* x, int64_t rows, int64_t cols, int64_t ld, int layout, bool sr,
                           uint64_t seed, bool rht, uint64_t hseed, const float* amax_in,
                           float* amax_out, const QOut* out, float* ws, hipStream_t s) {
+    if (layout == kLayoutRowCol && rht) {
+        // The two outputs quantize two different tensors: x transformed along
+        // rows (row blocks) and x transformed down columns (column blocks),
+        // each with its own A_t; amax_in / amax_out hold those two values, the
+        // row output's first.  The two calls run in stream order, so the
+        // second amax pass reuses the workspace after the first call is done
+        // with it.
+        hipError_t e = quantize_typed(x, rows, cols, ld, kLayoutRow, sr, seed, true, hseed, amax_in,
+                                      amax_out, &out[0], ws, s);
+        if (e != hipSuccess) return e;
+        return quantize_typed(x, rows, cols, ld, kLayoutCol, sr, seed, true, hseed,
+                              amax_in ? amax_in + 1 : nullptr, amax_out ? amax_out + 1 : nullptr,
+                              &out[1], ws, s);
+    }
     const uint32_t mask = rht ? hadamard_sign_mask(hseed) : 0u;
     if (rows == 0 || cols == 0) {
         hipLaunchKernelGGL(k_write_tensor_scale, dim3(1), dim3(1), 0, s, amax_in, out[0].ts,

@@ -243,15 +243,17 @@ def nvfp4_dequantize(q, dtype=torch.float32, out=None, stream=None):
 
 
 @_launches_on_stream
-def nvfp4_gemm(A, B, out_dtype=torch.float32, out=None, stream=None):
-    """C = A B^T (A: M x K, B: N x K NVFP4 tensors)."""
+def nvfp4_gemm(A, B, out_dtype=torch.float32, out=None, epilogue=NVFP4_EPI_NONE, stream=None):
+    """C = A B^T (A: M x K, B: N x K NVFP4 tensors); with NVFP4_EPI_SWIGLU
+    (N = 2F, bfloat16 output) C = gate * sigmoid(gate) * up, M x F."""
+    ncols = B.rows // 2 if epilogue == NVFP4_EPI_SWIGLU else B.rows
     if out is None:
-        out = torch.empty((A.rows, B.rows), dtype=out_dtype, device=A.codes.device)
+        out = torch.empty((A.rows, ncols), dtype=out_dtype, device=A.codes.device)
     assert out.stride(1) == 1
-    ldc = out.stride(0) if A.rows > 1 else max(B.rows, out.stride(0))
+    ldc = out.stride(0) if A.rows > 1 else max(ncols, out.stride(0))
     ca, cb = A.c(), B.c()
     st = lib.nvfp4_gemm(ctypes.byref(ca), ctypes.byref(cb), ctypes.c_void_p(out.data_ptr()),
-                        _dtype_code(out.dtype), ldc, NVFP4_EPI_NONE, _stream(stream))
+                        _dtype_code(out.dtype), ldc, epilogue, _stream(stream))
     _check("nvfp4_gemm", st)
     return out
 

@@ -133,9 +133,13 @@ size_t nvfp4_quantize_workspace_size(int64_t rows, int64_t cols, const nvfp4_qua
  *   ROW_1D:     out[0] is rows x cols, SCALE_1D; cols % 16 == 0.
  *   COL_1D:     out[0] is cols x rows (x transposed), SCALE_1D; rows % 16 == 0.
  *   ROW_COL_1D: out[0] as ROW_1D and out[1] as COL_1D, sharing one A_t;
- *               rows % 16 == 0 and cols % 16 == 0; no Hadamard transform.
+ *               rows % 16 == 0 and cols % 16 == 0.  With the Hadamard
+ *               transform the two outputs quantize two different tensors, x
+ *               transformed along rows (out[0]) and x transformed down
+ *               columns (out[1]), each with its own A_t: amax_in and
+ *               amax_out then point at two floats, out[0]'s first.
  *   BLK_2D:     out[0] is rows x cols, SCALE_2D; both dims % 16 == 0; no
- *               Hadamard transform.
+ *               Hadamard transform (UNSUPPORTED).
  * The Hadamard transform runs along the block dimension (along rows for
  * ROW_1D, along columns for COL_1D).  Each out[i] must carry codes, scales
  * and tensor_scale pointers and the rows/cols/scale_mode the layout implies
@@ -182,10 +186,16 @@ nvfp4_status nvfp4_requantize(const nvfp4_tensor* in, const nvfp4_quant_opts* op
  * binary32 over exactly dequantized products; C (M x N, row stride ldc
  * elements, dtype c_dt) = (s_A * s_B) * sum_k (v_A sb_A)(v_B sb_B).
  * Each operand may be SCALE_1D or SCALE_2D.  K % 16 == 0, M, N >= 0,
- * ldc >= N, C 16-byte aligned, codes 16-byte aligned.  ep must be
- * NVFP4_EPI_NONE here (SwiGLU is offered by the grouped GEMM).
+ * ldc >= N, C 16-byte aligned, codes 16-byte aligned.
+ *   EPI_NONE:   as above.
+ *   EPI_SWIGLU: N = 2F with F % 16 == 0; gate = columns [0, F), up = columns
+ *               [F, 2F) of A * B^T; C (M x F, ldc >= F) = gate *
+ *               sigmoid(gate) * up, and c_dt must be BF16 (else
+ *               UNSUPPORTED).  The grouped GEMM offers the same epilogue
+ *               with the largest |C| written to amax_out.
  * Source: asector.ru page, "NVFP4 и Blackwell" (scaled compute with
- * high-precision accumulation). */
+ * high-precision accumulation); iitak.ru page, "Детали" (the expert layers
+ * whose feed-forward the SwiGLU epilogue closes). */
 nvfp4_status nvfp4_gemm(const nvfp4_tensor* A, const nvfp4_tensor* B, void* C, nvfp4_dtype c_dt,
                         int64_t ldc, nvfp4_epilogue ep, void* stream);
 

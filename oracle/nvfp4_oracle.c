@@ -303,7 +303,6 @@ int orc_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64_t l
                  uint8_t* codes2, uint8_t* scales2, float* ts2) {
     if (rows < 0 || cols < 0 || ld < cols) return 1;
     if (layout == ORC_BLK_2D && hadamard) return 2;
-    if (layout == ORC_ROW_COL_1D && hadamard) return 2;
     if ((layout == ORC_ROW_1D || layout == ORC_ROW_COL_1D || layout == ORC_BLK_2D) && cols % 16) return 3;
     if ((layout == ORC_COL_1D || layout == ORC_ROW_COL_1D || layout == ORC_BLK_2D) && rows % 16) return 3;
 
@@ -319,13 +318,19 @@ int orc_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64_t l
         return 0;
     }
     if (layout == ORC_ROW_COL_1D) {
-        float* t = oriented(x, dtype, rows, cols, ld, 0, 0, 0);
-        float* tt = oriented(x, dtype, rows, cols, ld, 1, 0, 0);
+        /* Both orientations of one tensor.  Without the transform they share
+         * one A_t.  With it, the row output is ROW_1D of the tensor transformed
+         * along rows and the column output COL_1D of the tensor transformed
+         * along columns: two different tensors, each with its own A_t
+         * (amax_in then holds two values, the row output's first). */
+        float* t = oriented(x, dtype, rows, cols, ld, 0, hadamard, hadamard_seed);
+        float* tt = oriented(x, dtype, rows, cols, ld, 1, hadamard, hadamard_seed);
         if ((!t || !tt) && rows > 0 && cols > 0) { free(t); free(tt); return 4; }
-        float a = amax_in ? *amax_in : amax_of(t, rows * cols);
+        float a = amax_in ? amax_in[0] : amax_of(t, rows * cols);
+        float a2 = !hadamard ? a : amax_in ? amax_in[1] : amax_of(tt, rows * cols);
         quantize_rows(t, rows, cols, a, round, sr_seed, ORC_STREAM_ROW, index_base, codes, scales,
                       ts);
-        quantize_rows(tt, cols, rows, a, round, sr_seed, ORC_STREAM_COL, index_base, codes2,
+        quantize_rows(tt, cols, rows, a2, round, sr_seed, ORC_STREAM_COL, index_base, codes2,
                       scales2, ts2);
         free(t);
         free(tt);

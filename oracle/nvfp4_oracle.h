@@ -82,7 +82,11 @@ void orc_rht16(const float in[16], uint32_t sign_mask, float out[16]);
  * ROW_1D / BLK_2D outputs: codes rows x cols/2, scales rows x cols/16 (1D)
  * or rows/16 x cols/16 (2D).  COL_1D outputs describe the transpose:
  * codes cols x rows/2, scales cols x rows/16.  ROW_COL_1D writes the row
- * output to (codes, scales, ts) and the column output to (codes2, ...).
+ * output to (codes, scales, ts) and the column output to (codes2, ...); with
+ * the Hadamard transform the row output quantizes x transformed along rows
+ * and the column output x transformed along columns, each with its own A_t,
+ * and amax_in (when given) points at those two values, the row output's
+ * first.
  * index_base is added to every element's linear output index before its
  * random draw, so that a band of a larger tensor can be recomputed alone
  * (0 for a whole tensor).

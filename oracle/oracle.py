@@ -198,7 +198,8 @@ def quantize(x, dtype, layout, rnd=RNE, sr_seed=0, hadamard=False, hadamard_seed
     else:
         codes2 = scales2 = None
         ts2 = None
-    amax_arr = None if amax_in is None else np.array([amax_in], dtype=np.float32)
+    # one A_t, or (ROW_COL_1D with the transform) a pair: row output, column output
+    amax_arr = None if amax_in is None else np.array(np.atleast_1d(amax_in), dtype=np.float32)
     nul8 = ctypes.POINTER(ctypes.c_uint8)()
     nulf = ctypes.POINTER(ctypes.c_float)()
     rc = lib().orc_quantize(

@@ -76,7 +76,8 @@ def test_quantize_rejects_bad_arguments(nv):
     assert _quant(nv, ld=36) == E["ALIGN"]                                     # 72 bytes
     assert _quant(nv, x=65536 + 2) == E["ALIGN"]
     assert _quant(nv, layout=3, had=1, outs=[_t(32, 32, 1)]) == E["UNSUP"]
-    assert _quant(nv, layout=2, had=1, outs=[_t(32, 32), _t(32, 32)]) == E["UNSUP"]
+    # ROW_COL_1D with the transform is supported; its outputs are still checked
+    assert _quant(nv, layout=2, had=1, outs=[_t(32, 32), _t(16, 32)]) == E["SHAPE"]
     assert _quant(nv, outs=[_t(32, 32, 1)]) == E["SHAPE"]                     # wrong scale mode
     assert _quant(nv, layout=1, outs=[_t(32, 64)]) == E["SHAPE"]              # COL output shape
     assert _quant(nv, outs=[_t(32, 32, codes=None)]) == E["NULL"]
@@ -125,7 +126,10 @@ def test_gemm_rejects_bad_arguments(nv):
     g = nv.lib.nvfp4_gemm
     assert g(None, ctypes.byref(b), 65536, 0, 32, 0, None) == 1
     assert g(ctypes.byref(a), ctypes.byref(b), 65536, 9, 32, 0, None) == 2
-    assert g(ctypes.byref(a), ctypes.byref(b), 65536, 0, 32, 1, None) == 5     # SwiGLU is grouped-only
+    assert g(ctypes.byref(a), ctypes.byref(b), 65536, 0, 32, 1, None) == 5     # SwiGLU: BF16 output only
+    assert g(ctypes.byref(a), ctypes.byref(b), 65536, 1, 15, 1, None) == 3     # SwiGLU: ldc < F = 16
+    b48 = _t(48, 64)
+    assert g(ctypes.byref(a), ctypes.byref(b48), 65536, 1, 24, 1, None) == 3   # SwiGLU: F = 24 not % 16
     b2 = _t(32, 48)
     assert g(ctypes.byref(a), ctypes.byref(b2), 65536, 0, 32, 0, None) == 3    # K mismatch
     assert g(ctypes.byref(a), ctypes.byref(b), 65536, 0, 16, 0, None) == 3     # ldc < N

@@ -546,3 +546,24 @@ def test_requantize_of_grid_exact_tensor_is_the_transpose(rnd):
 
     assert np.array_equal(nibbles(r.codes), nibbles(q.codes).T)
 
+
+
+def test_rowcol_hadamard_is_row_and_col_of_their_own_transforms():
+    """ROW_COL_1D with the Hadamard transform: the row output is ROW_1D of x
+    transformed along rows, the column output COL_1D of x transformed along
+    columns (both pinned above against scipy's Sylvester matrix), each with
+    the A_t of its own transformed tensor; a given pair of A_t is used as
+    (row output, column output)."""
+    x = W.f32_to_bf16_bits(W.with_spikes(W.student_t((64, 96), 3.0, seed=70), 0.01, 80.0, seed=71))
+    for rnd in (O.RNE, O.SR):
+        r, c = O.quantize(x, O.BF16, O.ROW_COL_1D, rnd, sr_seed=5, hadamard=True, hadamard_seed=9)
+        r1 = O.quantize(x, O.BF16, O.ROW_1D, rnd, sr_seed=5, hadamard=True, hadamard_seed=9)
+        c1 = O.quantize(x, O.BF16, O.COL_1D, rnd, sr_seed=5, hadamard=True, hadamard_seed=9)
+        for a, b in ((r, r1), (c, c1)):
+            assert a.ts == b.ts and np.array_equal(a.codes, b.codes) and np.array_equal(a.scales, b.scales)
+        assert r.ts == O.tensor_scale(O.amax(x, O.BF16, O.ROW_1D, True, 9))
+        assert c.ts == O.tensor_scale(O.amax(x, O.BF16, O.COL_1D, True, 9))
+        assert r.ts != c.ts
+        r2, c2 = O.quantize(x, O.BF16, O.ROW_COL_1D, rnd, sr_seed=5, hadamard=True, hadamard_seed=9,
+                            amax_in=(100.0, 200.0))
+        assert r2.ts == O.tensor_scale(100.0) and c2.ts == O.tensor_scale(200.0)

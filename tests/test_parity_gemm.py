@@ -269,6 +269,26 @@ def test_grouped_swiglu_full_line_path(nv):
     check_swiglu(nv, [70, 0, 129, 33], F=80, K=1024, seed=22)
 
 
+@pytest.mark.parametrize("M,F,K", [(70, 80, 160), (257, 48, 192), (300, 144, 1024)])
+@pytest.mark.parametrize("bmode", [O.ROW_1D, O.BLK_2D])
+def test_gemm_swiglu_epilogue(nv, M, F, K, bmode):
+    """The plain GEMM's SwiGLU epilogue (B = [gate; up], 2F rows): each of
+    the three kernels (K % 64 != 0, K % 64 == 0, K % 512 == 0) against the
+    oracle's SwiGLU of its own GEMM, within the GEMM bound carried through
+    h = g sigmoid(g) u."""
+    a = W.with_spikes(W.student_t((M, K), 3.0, seed=M + F), 1e-3, 50.0, seed=2)
+    A = quant_host(a, O.ROW_1D)
+    B = quant_host(W.normal((2 * F, K), 0.02, seed=K + F), bmode)
+    H = nv.nvfp4_gemm(q_to_device(A, nv), q_to_device(B, nv), out_dtype=torch.bfloat16,
+                      epilogue=nv.NVFP4_EPI_SWIGLU)
+    assert tuple(H.shape) == (M, F)
+    Cref, Wref = O.gemm(A, B)
+    G_, U_ = Cref[:, :F], Cref[:, F:]
+    err = np.abs(out_to_f64(H) - O.swiglu(G_, U_))
+    tol = _swiglu_tol(G_, U_, Wref[:, :F], Wref[:, F:])
+    assert (err <= tol).all(), f"swiglu gemm: {np.sum(err > tol)} entries out of tolerance"
+
+
 def test_swiglu_then_quantize_is_oracle_exact(nv):
     """The quantize step after the SwiGLU epilogue: the GPU quantizes its BF16
     H with the amax the epilogue produced; the oracle quantizes its own H

@@ -84,6 +84,30 @@ def test_rowcol_and_2d(nv, dtype, rnd, shape):
 
 
 @pytest.mark.parametrize("dtype", [O.BF16, O.F32])
+@pytest.mark.parametrize("rnd", [O.RNE, O.SR])
+@pytest.mark.parametrize("shape", [(16, 16), (48, 80), (208, 1040), (1040, 96)])
+def test_rowcol_hadamard(nv, dtype, rnd, shape):
+    """ROW_COL_1D with the Hadamard transform: the row output quantizes x
+    transformed along rows, the column output x transformed down columns,
+    each with its own A_t (computed, then given as a pair and published
+    through amax_out as a pair)."""
+    x = make_input(*shape, dtype, seed=shape[0] * 3 + shape[1], kind="spiky")
+    got, ref = run_both(nv, x, dtype, O.ROW_COL_1D, rnd, seed=13, had=True, hseed=321)
+    assert_q_equal(got[0], ref[0], f"rowcol+had/row {shape}")
+    assert_q_equal(got[1], ref[1], f"rowcol+had/col {shape}")
+    assert got[0].ts != got[1].ts or shape == (16, 16)
+    pair = torch.tensor([3.5, 700.0], dtype=torch.float32, device="cuda")
+    out_pair = torch.zeros(2, dtype=torch.float32, device="cuda")
+    gr, gc = nv.nvfp4_quantize(to_device(x), layout=nv.NVFP4_ROW_COL_1D, round=rnd, sr_seed=13,
+                               hadamard=True, hadamard_seed=321, amax_in=pair, amax_out=out_pair)
+    rr, rc = O.quantize(x, dtype, O.ROW_COL_1D, rnd, sr_seed=13, hadamard=True, hadamard_seed=321,
+                        amax_in=(3.5, 700.0))
+    assert_q_equal(q_to_host(gr), rr, f"rowcol+had given pair/row {shape}")
+    assert_q_equal(q_to_host(gc), rc, f"rowcol+had given pair/col {shape}")
+    assert out_pair.cpu().tolist() == [3.5, 700.0]
+
+
+@pytest.mark.parametrize("dtype", [O.BF16, O.F32])
 @pytest.mark.parametrize("layout,rnd", [(O.COL_1D, O.RNE), (O.COL_1D, O.SR), (O.ROW_COL_1D, O.RNE),
                                         (O.ROW_COL_1D, O.SR)])
 def test_col_tiles_xcd_remap_with_partial_block(nv, dtype, layout, rnd):
