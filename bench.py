@@ -648,39 +648,80 @@ def bench_mx_gemm(nv, W, np, torch, reps):
     return out
 
 
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(np, W, rows=N):
     """The oracle on rows 0 .. rows-1 of the 8192 x 8192 step input (by default
-    the whole tensor, about 13 s on the GPU machine's host): the same quantize
-    calls and dequantizations as the step, single thread."""
+    the whole tensor): the same quantize calls and dequantizations as the
+    step, first as single oracle calls on one core (about 13 s on the GPU
+    box's host), then band by band on every core this process may use
+    (oracle/banded.py: the unchanged oracle called once per independent band
+    in threads), whose outputs must equal the single-core ones byte for
+    byte.  `value` is the all-core rate; the single-core rate is reported
+    beside it."""
     import oracle as O
+    from oracle import banded as OB
     x = W.f32_to_bf16_bits(W.student_t((N, N), 3.0, seed=1000))[:rows].copy()
     E = rows * N
-    t0 = time.perf_counter()
-    for lay in (O.ROW_1D, O.COL_1D):
+
+    def run(quantize, dequantize, **kw):
+        outs = []
+        for lay in (O.ROW_1D, O.COL_1D):
+            for rnd in (O.RNE, O.SR):
+                outs.append(quantize(x, O.BF16, lay, rnd, sr_seed=77, **kw))
         for rnd in (O.RNE, O.SR):
-            O.quantize(x, O.BF16, lay, rnd, sr_seed=77)
-    for rnd in (O.RNE, O.SR):
-        qr, qc = O.quantize(x, O.BF16, O.ROW_COL_1D, rnd, sr_seed=77)
-    O.dequantize(qr, O.BF16)
-    O.dequantize(qc, O.BF16)
-    dt = time.perf_counter() - t0
+            qr, qc = quantize(x, O.BF16, O.ROW_COL_1D, rnd, sr_seed=77, **kw)
+            outs += [qr, qc]
+        outs.append(dequantize(outs[0], O.BF16, **kw))
+        outs.append(dequantize(outs[2], O.BF16, **kw))
+        return outs
+
+    t0 = time.perf_counter()
+    single = run(O.quantize, O.dequantize)
+    t_single = time.perf_counter() - t0
+    threads = OB.default_threads()
+    t0 = time.perf_counter()
+    multi = run(OB.quantize, OB.dequantize, threads=threads)
+    t_multi = time.perf_counter() - t0
+    for a, b in zip(single, multi):
+        if isinstance(a, np.ndarray):
+            same = np.array_equal(a, b)
+        else:
+            same = a.ts == b.ts and np.array_equal(a.codes, b.codes) and np.array_equal(a.scales, b.scales)
+        if not same:
+            raise RuntimeError("the banded oracle differs from the single-call oracle")
     q1 = E * 2 + E // 2 + E // 16 + 4
     q2 = E * 2 + 2 * (E // 2 + E // 16) + 8
     dq = E // 2 + E // 16 + 4 + E * 2
     b = 4 * q1 + 2 * q2 + 2 * dq
-    return {"value": round(b / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+    return {"value": round(b / t_multi / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "single_core_value": round(b / t_single / 1e9, 4),
+            "cpu_model": cpu_model(), "host_cpus_visible": os.cpu_count(),
             "sample": f"rows 0..{rows - 1} of the {N}x{N} step input"
                       f"{' (the whole tensor)' if rows == N else ''}: the step's quantize and "
-                      f"dequantize calls; {dt:.1f} s single-threaded"}
+                      f"dequantize calls; {t_single:.1f} s as single oracle calls on one core, "
+                      f"{t_multi:.2f} s band by band on {threads} threads (identical outputs)"}
 
 
 def cpu_oracle_gemm(np, W, n_entries=8192):
     """The oracle GEMM (exact dequantization, float64 dot products) on sampled
     output entries of the forward shape 8192 x 20480 x 5120 (X Student-t(3)
-    row blocks, W N(0, 0.02) 16x16 blocks), single thread.  The operand rows
+    row blocks, W N(0, 0.02) 16x16 blocks).  The operand rows
     the entries need are quantized by the oracle beforehand (not timed); the
-    per-entry time is extrapolated to the whole output."""
+    per-entry time is extrapolated to the whole output.  Timed on one core,
+    then with the entries split over every core this process may use."""
     import oracle as O
+    from oracle import banded as OB
     M, Nn, K = 8192, 20480, 5120
     x = W.f32_to_bf16_bits(W.student_t((M, K), 3.0, seed=4000))
     w = W.f32_to_bf16_bits(W.normal((Nn, K), 0.02, seed=4001))
@@ -696,12 +737,21 @@ def cpu_oracle_gemm(np, W, n_entries=8192):
                    amax_in=O.amax(w, O.BF16, O.BLK_2D))
     nl = np.searchsorted(bands, ni // 16) * 16 + ni % 16
     t0 = time.perf_counter()
-    O.gemm(A, B, entries=(ml, nl))
+    c1, _ = O.gemm(A, B, entries=(ml, nl))
     dt = time.perf_counter() - t0
+    threads = OB.default_threads()
+    t0 = time.perf_counter()
+    cn, _ = OB.gemm_entries(A, B, ml, nl, threads=threads)
+    dtn = time.perf_counter() - t0
+    if not np.array_equal(c1, cn):
+        raise RuntimeError("the threaded oracle GEMM differs from the single-call one")
     full_s = dt / n_entries * M * Nn
-    return {"entries": n_entries, "seconds": round(dt, 3), "cores": 1, "kind": "oracle",
-            "extrapolated_full_seconds": round(full_s, 1),
-            "extrapolated_TFLOP/s": round(2 * M * Nn * K / full_s / 1e12, 6)}
+    full_n = dtn / n_entries * M * Nn
+    return {"entries": n_entries, "seconds": round(dtn, 3), "cores": threads, "kind": "oracle",
+            "extrapolated_full_seconds": round(full_n, 1),
+            "extrapolated_TFLOP/s": round(2 * M * Nn * K / full_n / 1e12, 6),
+            "single_core_seconds": round(dt, 3),
+            "single_core_extrapolated_full_seconds": round(full_s, 1)}
 
 
 if __name__ == "__main__":

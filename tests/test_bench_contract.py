@@ -22,10 +22,12 @@ def test_more_than_one_gpu_is_refused():
 def test_cpu_baseline_fields():
     import bench
     import workloads as W
+    from oracle import banded
     cb = bench.cpu_baseline(np, W, rows=256)
-    assert set(cb) == {"value", "unit", "cores", "kind", "sample"}
-    assert cb["kind"] == "oracle" and cb["unit"] == "GB/s" and cb["cores"] == 1
-    assert cb["value"] > 0 and "rows 0..255" in cb["sample"]
+    assert {"value", "unit", "cores", "kind", "sample", "single_core_value", "cpu_model"} <= set(cb)
+    assert cb["kind"] == "oracle" and cb["unit"] == "GB/s" and cb["cores"] == banded.default_threads()
+    assert cb["value"] > 0 and cb["single_core_value"] > 0 and "rows 0..255" in cb["sample"]
+    assert "identical outputs" in cb["sample"]
 
 
 def test_profile_figures_follow_the_kernel_sources(tmp_path, monkeypatch):
