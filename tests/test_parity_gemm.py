@@ -240,7 +240,8 @@ def _swiglu_tol(G_, U_, Wg, Wu):
     dh_dg = np.abs(s * (1.0 + G_ * (1.0 - s)) * U_)
     dh_du = np.abs(G_ * s)
     h = np.abs(G_ * s * U_)
-    e = np.floor(np.log2(np.where(h > 0, h, 1.0)))
+    # one BF16 rounding: half a spacing, at least the subnormal spacing 2^-133
+    e = np.maximum(np.floor(np.log2(np.where(h > 0, h, 1.0))), -126.0)
     ulp = np.where(h > 0, 2.0 ** (e - 7), 2.0 ** -133)
     return dh_dg * 1e-5 * Wg + dh_du * 1e-5 * Wu + 1e-6 * h + ulp
 

@@ -261,77 +261,3 @@ def test_gpu_idempotence(nv):
     amax = torch.tensor([float(np.abs(x).max())], device="cuda")
     q2 = nv.nvfp4_quantize(y, amax_in=amax)
     assert_q_equal(q_to_host(q2), q_to_host(q), "idempotence")
-
-
-# ---------------------------------------------------------- full-size samples
-def _band_ref(x, layout, rnd, seed, amax, b0, width, had=False, hseed=0):
-    """Oracle output rows b0 .. b0+width of the full tensor's quantization:
-    the matching input band with the full tensor's amax and the band's
-    position as the base of its random-draw indices."""
-    rows, cols = x.shape
-    if layout == O.COL_1D:
-        sub = np.ascontiguousarray(x[:, b0:b0 + width])
-        base = b0 * rows
-    else:
-        sub = np.ascontiguousarray(x[b0:b0 + width])
-        base = b0 * cols
-    return O.quantize(sub, O.BF16, layout, rnd, sr_seed=seed, hadamard=had, hadamard_seed=hseed,
-                      amax_in=amax, index_base=base)
-
-
-def _check_bands(g, x, layout, rnd, seed, amax, bands, width=64, had=False, hseed=0):
-    for b0 in bands:
-        ref = _band_ref(x, layout, rnd, seed, amax, b0, width, had, hseed)
-        assert np.array_equal(g.codes[b0:b0 + width], ref.codes), f"codes band {b0}"
-        sc = g.scales[b0 // 16:(b0 + width) // 16] if layout == O.BLK_2D else g.scales[b0:b0 + width]
-        assert np.array_equal(sc, ref.scales), f"scales band {b0}"
-
-
-@pytest.mark.parametrize("layout,rnd", [(O.ROW_1D, O.RNE), (O.ROW_1D, O.SR), (O.COL_1D, O.RNE),
-                                        (O.COL_1D, O.SR), (O.BLK_2D, O.RNE), (O.BLK_2D, O.SR)])
-def test_activation_8192_sampled(nv, layout, rnd):
-    """8192 x 8192 BF16 Student-t(3), the launch configuration the benchmark
-    times: the tensor scale against the oracle's amax of the whole tensor,
-    and bands of the output against the oracle."""
-    n = 8192
-    x = make_input(n, n, O.BF16, seed=1000 + layout)
-    q = nv.nvfp4_quantize(to_device(x), layout=layout, round=rnd, sr_seed=1100)
-    g = q_to_host(q)
-    amax = O.amax(x, O.BF16, layout)
-    assert g.ts == O.tensor_scale(amax)
-    _check_bands(g, x, layout, rnd, 1100, amax, (0, 4096 + 48, n - 64))
-
-
-def test_activation_8192_rowcol_sampled(nv):
-    n = 8192
-    x = make_input(n, n, O.BF16, seed=1010)
-    r, c = nv.nvfp4_quantize(to_device(x), layout=nv.NVFP4_ROW_COL_1D, round=nv.NVFP4_SR,
-                             sr_seed=1200)
-    gr, gc = q_to_host(r), q_to_host(c)
-    amax = O.amax(x, O.BF16, O.ROW_1D)
-    assert gr.ts == gc.ts == O.tensor_scale(amax)
-    _check_bands(gr, x, O.ROW_1D, O.SR, 1200, amax, (0, n - 64))
-    _check_bands(gc, x, O.COL_1D, O.SR, 1200, amax, (0, 2000, n - 64))
-
-
-def test_weight_2d_20480x5120_sampled(nv):
-    """Weight 20480 x 5120 BF16 N(0, 0.02), 16 x 16 blocks, RNE."""
-    x = make_input(20480, 5120, O.BF16, seed=2000, kind="w")
-    g = q_to_host(nv.nvfp4_quantize(to_device(x), layout=nv.NVFP4_BLK_2D))
-    amax = O.amax(x, O.BF16, O.BLK_2D)
-    assert g.ts == O.tensor_scale(amax)
-    _check_bands(g, x, O.BLK_2D, O.RNE, 0, amax, (0, 10240, 20480 - 64))
-
-
-@pytest.mark.parametrize("rows,cols,seed", [(8192, 20480, 3000), (8192, 5120, 3010)])
-def test_wgrad_hadamard_col_sr_sampled(nv, rows, cols, seed):
-    """dY 8192 x 20480 and X 8192 x 5120, N(0,1) with 0.01% x100 spikes:
-    Hadamard along tokens, column blocks, stochastic rounding."""
-    x = W.f32_to_bf16_bits(W.with_spikes(W.normal((rows, cols), 1.0, seed=seed), 1e-4, 100.0,
-                                         seed=seed + 1))
-    q = q_to_host(nv.nvfp4_quantize(to_device(x), layout=nv.NVFP4_COL_1D, round=nv.NVFP4_SR,
-                                    sr_seed=seed + 100, hadamard=True, hadamard_seed=seed + 200))
-    amax = O.amax(x, O.BF16, O.COL_1D, hadamard=True, hadamard_seed=seed + 200)
-    assert q.ts == O.tensor_scale(amax)
-    _check_bands(q, x, O.COL_1D, O.SR, seed + 100, amax, (0, cols // 2 + 16, cols - 64), had=True,
-                 hseed=seed + 200)
