@@ -5,9 +5,18 @@
 
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "launch.hpp"
 
 using namespace nvfp4;
+
+// Scratch of nvfp4_quantize_noalloc: the amax pass's per-workgroup partial
+// maxima (at most kMaxPartials floats for a tensor of any size, 2 KiB).  Each
+// device the library runs on holds its own copy until the process ends.  In
+// host code `scratch` names a host-side stand-in, not device memory: kernels
+// get the device address that hipGetSymbolAddress returns for the device.
+static __device__ __align__(256) float scratch[kMaxPartials];
 
 namespace {
 
@@ -58,9 +67,14 @@ size_t nvfp4_quantize_workspace_size(int64_t rows, int64_t cols, const nvfp4_qua
     return kQuantWorkspaceBytes;
 }
 
-nvfp4_status nvfp4_quantize(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols, int64_t ld,
-                            const nvfp4_quant_opts* opts, nvfp4_tensor* out, void* ws,
-                            size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks of nvfp4_quantize other than the workspace; NVFP4_OK when
+// the request can be launched.
+nvfp4_status check_quantize(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols, int64_t ld,
+                            const nvfp4_quant_opts* opts, nvfp4_tensor* out) {
     if (!opts || !out) return NVFP4_ERR_NULL;
     if (!valid_dtype(dt)) return NVFP4_ERR_ENUM;
     const int layout = opts->layout;
@@ -92,22 +106,81 @@ nvfp4_status nvfp4_quantize(const void* x, nvfp4_dtype dt, int64_t rows, int64_t
     if ((layout == NVFP4_COL_1D || layout == NVFP4_ROW_COL_1D) && cdiv(rows, 256) > kMaxGridY)
         return NVFP4_ERR_UNSUPPORTED;
     if (layout == NVFP4_BLK_2D && cdiv(rows, 64) > kMaxGridY) return NVFP4_ERR_UNSUPPORTED;
+    return NVFP4_OK;
+}
 
-    if (!empty && !opts->amax_in) {
-        if (!ws) return NVFP4_ERR_WORKSPACE;
-        if (ws_bytes < kQuantWorkspaceBytes) return NVFP4_ERR_WORKSPACE;
-        if (!aligned(ws, 16)) return NVFP4_ERR_ALIGN;
-    }
-
+nvfp4_status launch_checked_quantize(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols,
+                                     int64_t ld, const nvfp4_quant_opts* opts, nvfp4_tensor* out,
+                                     float* ws, void* stream) {
+    const int layout = opts->layout;
     QOut o[2];
     o[0] = QOut{out[0].codes, out[0].scales, out[0].tensor_scale};
     if (layout == NVFP4_ROW_COL_1D) o[1] = QOut{out[1].codes, out[1].scales, out[1].tensor_scale};
     else o[1] = QOut{nullptr, nullptr, nullptr};
     hipError_t e = launch_quantize(x, dt == NVFP4_BF16, rows, cols, ld, layout, opts->round == NVFP4_SR,
                                    opts->sr_seed, opts->hadamard != 0, opts->hadamard_seed,
-                                   opts->amax_in, opts->amax_out, o, static_cast<float*>(ws),
-                                   static_cast<hipStream_t>(stream));
+                                   opts->amax_in, opts->amax_out, o, ws, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the device `stream` belongs to, looked up
+// once per device with that device current; NULL on failure.
+float* scratch_on_device_of(hipStream_t stream) {
+    int dev = -1;
+    if (stream) {
+        if (hipStreamGetDevice(stream, &dev) != hipSuccess) return nullptr;
+    } else if (hipGetDevice(&dev) != hipSuccess) {
+        return nullptr;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        int cur = -1;
+        if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+        if (cur != dev && hipSetDevice(dev) != hipSuccess) return nullptr;
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) (void)hipSetDevice(cur);
+        if (e != hipSuccess || !p) return nullptr;
+        g_scratch_ptr[dev] = static_cast<float*>(p);
+    }
+    return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+nvfp4_status nvfp4_quantize(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols, int64_t ld,
+                            const nvfp4_quant_opts* opts, nvfp4_tensor* out, void* ws,
+                            size_t ws_bytes, void* stream) {
+    nvfp4_status st = check_quantize(x, dt, rows, cols, ld, opts, out);
+    if (st != NVFP4_OK) return st;
+    if (rows > 0 && cols > 0 && !opts->amax_in) {
+        if (!ws) return NVFP4_ERR_WORKSPACE;
+        if (ws_bytes < kQuantWorkspaceBytes) return NVFP4_ERR_WORKSPACE;
+        if (!aligned(ws, 16)) return NVFP4_ERR_ALIGN;
+    }
+    return launch_checked_quantize(x, dt, rows, cols, ld, opts, out, static_cast<float*>(ws), stream);
+}
+
+nvfp4_status nvfp4_quantize_noalloc(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols, int64_t ld,
+                                    const nvfp4_quant_opts* opts, nvfp4_tensor* out, void* stream) {
+    nvfp4_status st = check_quantize(x, dt, rows, cols, ld, opts, out);
+    if (st != NVFP4_OK) return st;
+    // the amax pass writes at most kMaxPartials partials whatever the size, so
+    // no request needs more scratch than the array holds
+    static_assert(sizeof(scratch) >= kQuantWorkspaceBytes, "scratch smaller than the quantize workspace");
+    float* ws = nullptr;
+    if (rows > 0 && cols > 0 && !opts->amax_in) {
+        ws = scratch_on_device_of(static_cast<hipStream_t>(stream));
+        if (!ws) return NVFP4_ERR_HIP;
+    }
+    return launch_checked_quantize(x, dt, rows, cols, ld, opts, out, ws, stream);
 }
 
 nvfp4_status nvfp4_requantize(const nvfp4_tensor* in, const nvfp4_quant_opts* opts, nvfp4_tensor* out,

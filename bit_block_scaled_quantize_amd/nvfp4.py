@@ -25,7 +25,8 @@ NVFP4_EPI_NONE, NVFP4_EPI_SWIGLU = 0, 1
 NVFP4_SCALE_1D, NVFP4_SCALE_2D = 0, 1
 NVFP4_MX_E4M3, NVFP4_MX_E2M1 = 0, 1
 
-EXPORTED = ["nvfp4_quantize_workspace_size", "nvfp4_quantize", "nvfp4_requantize", "nvfp4_dequantize",
+EXPORTED = ["nvfp4_quantize_workspace_size", "nvfp4_quantize", "nvfp4_quantize_noalloc", "nvfp4_requantize",
+            "nvfp4_dequantize",
             "nvfp4_gemm", "nvfp4_grouped_gemm", "nvfp4_mx_quantize", "nvfp4_mx_dequantize", "nvfp4_mx_gemm",
             "nvfp4_status_string", "nvfp4_version"]
 
@@ -58,6 +59,9 @@ def _load():
     L.nvfp4_quantize.argtypes = [vp, i32, i64, i64, i64, ctypes.POINTER(CQuantOpts),
                                  ctypes.POINTER(CTensor), vp, sz, vp]
     L.nvfp4_quantize.restype = i32
+    L.nvfp4_quantize_noalloc.argtypes = [vp, i32, i64, i64, i64, ctypes.POINTER(CQuantOpts),
+                                         ctypes.POINTER(CTensor), vp]
+    L.nvfp4_quantize_noalloc.restype = i32
     L.nvfp4_dequantize.argtypes = [ctypes.POINTER(CTensor), vp, i32, i64, vp]
     L.nvfp4_dequantize.restype = i32
     L.nvfp4_requantize.argtypes = [ctypes.POINTER(CTensor), ctypes.POINTER(CQuantOpts),
@@ -203,6 +207,28 @@ def nvfp4_quantize(x, layout=NVFP4_ROW_1D, round=NVFP4_RNE, sr_seed=0, hadamard=
     st = lib.nvfp4_quantize(ctypes.c_void_p(x.data_ptr()), _dtype_code(x.dtype), rows, cols, ld,
                             ctypes.byref(opts), arr, _ptr(workspace), ws_bytes, _stream(stream))
     _check("nvfp4_quantize", st)
+    return tuple(outs) if layout == NVFP4_ROW_COL_1D else outs[0]
+
+
+def nvfp4_quantize_noalloc(x, out, layout=NVFP4_ROW_1D, round=NVFP4_RNE, sr_seed=0, hadamard=False,
+                           hadamard_seed=0, amax_in=None, amax_out=None, stream=None):
+    """nvfp4_quantize into preallocated outputs (`out`: one NVFP4Tensor, or a
+    pair for NVFP4_ROW_COL_1D) with no workspace: the library's static
+    device scratch holds the amax partials, so neither the library nor this
+    wrapper allocates anything."""
+    assert x.dim() == 2 and x.stride(1) == 1
+    rows, cols = x.shape
+    ld = x.stride(0) if rows > 1 else max(cols, x.stride(0))
+    outs = list(out) if isinstance(out, (list, tuple)) else [out]
+    arr = (CTensor * 2)()
+    for i, t in enumerate(outs):
+        arr[i] = t.c()
+    opts = CQuantOpts(layout, round, sr_seed, int(bool(hadamard)), hadamard_seed,
+                      None if amax_in is None else amax_in.data_ptr(),
+                      None if amax_out is None else amax_out.data_ptr())
+    st = lib.nvfp4_quantize_noalloc(ctypes.c_void_p(x.data_ptr()), _dtype_code(x.dtype), rows, cols, ld,
+                                    ctypes.byref(opts), arr, _stream(stream))
+    _check("nvfp4_quantize_noalloc", st)
     return tuple(outs) if layout == NVFP4_ROW_COL_1D else outs[0]
 
 

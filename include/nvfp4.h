@@ -154,6 +154,23 @@ nvfp4_status nvfp4_quantize(const void* x, nvfp4_dtype dt, int64_t rows, int64_t
                             const nvfp4_quant_opts* opts, nvfp4_tensor* out, void* ws,
                             size_t ws_bytes, void* stream);
 
+/* nvfp4_quantize for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments without the workspace, the same results bit for bit.
+ * The amax pass keeps its per-workgroup partial maxima in a static device
+ * array of the library (512 floats, 2 KiB, one copy per device, held until
+ * the process ends) instead of a caller workspace.  That need does not grow
+ * with the tensor, so no size is rejected for it.  Nothing is allocated or
+ * freed, and nothing needs clearing between calls (every partial a call
+ * reads was written by that call).  All calls on one device share the array:
+ * calls that overlap in time on one device (on different streams, or from
+ * different threads without ordering) race and give unspecified results;
+ * calls ordered on one stream do not.  The first call on a device looks the
+ * array's address up (hipGetSymbolAddress); NVFP4_ERR_HIP if that fails.
+ * Errors otherwise as for nvfp4_quantize. */
+nvfp4_status nvfp4_quantize_noalloc(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols, int64_t ld,
+                                    const nvfp4_quant_opts* opts, nvfp4_tensor* out, void* stream);
+
 /* Dequantize q into y (q->rows x q->cols in the stored orientation, element
  * dtype `dt`, row stride `ld` elements): y = e2m1(code) * e4m3(scale) *
  * tensor_scale, computed as one binary32 rounding (the first product is

@@ -222,3 +222,24 @@ def test_mx_gemm_rejects_bad_arguments(nv):
     K4 = 1 << 24                                                 # E4M3: 2^24 bytes per row
     assert g(ma=(64, K4, 0), mb=(32, K4, 0)) == E["UNSUP"]
     assert g(ma=(64, 2 * K4, 1), mb=(32, 2 * K4, 1)) == E["UNSUP"]   # E2M1: K/2 bytes per row
+
+
+def test_quantize_noalloc_rejects_bad_arguments(nv):
+    """The allocation-free variant validates like nvfp4_quantize (before it
+    looks anything up on a device)."""
+    E = dict(NULL=1, ENUM=2, SHAPE=3, ALIGN=4, UNSUP=5)
+
+    def q(x=65536, dt=1, rows=32, cols=32, ld=32, layout=0, had=0, outs=None):
+        o = nv.CQuantOpts(layout, 0, 1, had, 2, None, None)
+        arr = (nv.CTensor * 2)()
+        for i, t in enumerate(outs or [_t(rows, cols)]):
+            arr[i] = t
+        return nv.lib.nvfp4_quantize_noalloc(x, dt, rows, cols, ld, ctypes.byref(o), arr, None)
+
+    assert nv.lib.nvfp4_quantize_noalloc(65536, 1, 32, 32, 32, None, None, None) == E["NULL"]
+    assert q(x=None) == E["NULL"]
+    assert q(dt=5) == E["ENUM"]
+    assert q(cols=24, ld=32, outs=[_t(32, 24)]) == E["SHAPE"]
+    assert q(ld=36) == E["ALIGN"]
+    assert q(layout=3, had=1, outs=[_t(32, 32, 1)]) == E["UNSUP"]
+    assert q(outs=[_t(32, 32, 1)]) == E["SHAPE"]
