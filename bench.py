@@ -626,24 +626,47 @@ def bench_mx_codec(nv, W, np, torch, reps):
 
 
 def bench_mx_gemm(nv, W, np, torch, reps):
-    """MX GEMMs on the scaled matrix cores, operands MX-quantized on the GPU
-    from seeded BF16 data (SR)."""
+    """MX GEMMs, operands MX-quantized on the GPU from seeded BF16 data (SR):
+    the native path on the scaled matrix cores (against the FP8 or FP4 peak)
+    and the exact path (exact products, binary32 sums, on the BF16 matrix
+    cores: against the BF16 peak).  For the native path the line also carries
+    its error relative to sum |a b| over the whole output: |native - exact| /
+    sum |a b|, where the exact path is within 1e-5 sum |a b| of the exact
+    product (its parity tests) and sum |a b| is the exact path's GEMM of the
+    operands with every sign bit cleared."""
     out = {}
 
     def mxq(shape, seed, elem):
         x = bf16_device(W.f32_to_bf16_bits(W.student_t(shape, 3.0, seed=seed)), torch, np)
         return nv.nvfp4_mx_quantize(x, elem=elem, round=nv.NVFP4_SR, sr_seed=seed + 1)
 
+    def magnitude(q, elem):
+        # the same MX tensor with every element's sign bit cleared
+        mask = 0x7F if elem == nv.NVFP4_MX_E4M3 else 0x77
+        return nv.MXTensor(torch.bitwise_and(q.codes, mask), q.scales, q.rows, q.cols, q.elem)
+
+    EX = nv.NVFP4_MX_ACC_EXACT
     for elem, tag, peak in [(nv.NVFP4_MX_E4M3, "e4m3", FP8_PEAK_TFLOPS), (nv.NVFP4_MX_E2M1, "e2m1", FP4_PEAK_TFLOPS)]:
         for (M, Nn, K, dt) in [(8192, 8192, 8192, torch.float32), (20480, 5120, 8192, torch.float32)]:
             log(f"mx gemm {tag} {M}x{Nn}x{K}")
             A, B = mxq((M, K), 7100, elem), mxq((Nn, K), 7200, elem)
             C = torch.empty((M, Nn), dtype=dt, device="cuda")
+            Ce = torch.empty((M, Nn), dtype=dt, device="cuda")
             ms = time_events(lambda i: nv.nvfp4_mx_gemm(A, B, out=C), reps, torch)
+            ms_x = time_events(lambda i: nv.nvfp4_mx_gemm(A, B, out=Ce, accum=EX), reps, torch)
             tf = 2 * M * Nn * K / (ms * 1e-3) / 1e12
-            out[f"mx_gemm_{tag}_{M}x{Nn}x{K}"] = {"ms": round(ms, 4), "TFLOP/s": round(tf, 1),
-                                                 "frac_peak": round(tf / peak, 4), "peak_TFLOP/s": peak}
-            del A, B, C
+            tf_x = 2 * M * Nn * K / (ms_x * 1e-3) / 1e12
+            nv.nvfp4_mx_gemm(magnitude(A, elem), magnitude(B, elem), out=C, accum=EX)   # C = sum |a b|
+            Cn = nv.nvfp4_mx_gemm(A, B)
+            rel = ((Cn.double() - Ce.double()).abs() / C.double().clamp_min(1e-300)).flatten()
+            out[f"mx_gemm_{tag}_{M}x{Nn}x{K}"] = {
+                "ms": round(ms, 4), "TFLOP/s": round(tf, 1), "frac_peak": round(tf / peak, 4),
+                "peak_TFLOP/s": peak,
+                "native_error_vs_sum_abs_ab": {"max": float(rel.max()), "median": float(rel.median()),
+                                               "meets_1e-5": bool(rel.max() <= 1e-5)},
+                "exact": {"ms": round(ms_x, 4), "TFLOP/s": round(tf_x, 1),
+                          "frac_bf16_peak": round(tf_x / FP16_PEAK_TFLOPS, 4)}}
+            del A, B, C, Ce, Cn, rel
             torch.cuda.empty_cache()
     return out
 

@@ -8,6 +8,7 @@ from .nvfp4 import (  # noqa: F401
     NVFP4_RNE, NVFP4_SR, NVFP4_EPI_NONE, NVFP4_EPI_SWIGLU, NVFP4_SCALE_1D, NVFP4_SCALE_2D,
     nvfp4_quantize, nvfp4_quantize_noalloc, nvfp4_quantize_workspace_size, nvfp4_requantize, nvfp4_dequantize, nvfp4_gemm,
     nvfp4_grouped_gemm,
-    MXTensor, NVFP4_MX_E4M3, NVFP4_MX_E2M1, nvfp4_mx_quantize, nvfp4_mx_dequantize,
+    MXTensor, NVFP4_MX_E4M3, NVFP4_MX_E2M1, NVFP4_MX_ACC_NATIVE, NVFP4_MX_ACC_EXACT,
+    nvfp4_mx_quantize, nvfp4_mx_dequantize,
     nvfp4_mx_gemm,
 )

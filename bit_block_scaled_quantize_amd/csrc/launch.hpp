@@ -73,8 +73,10 @@ hipError_t launch_mx_dequantize(const uint8_t* codes, const uint8_t* scales, int
                                 int64_t cols, void* y, bool bf16, int64_t ld, hipStream_t s);
 
 // C (M x N, ldc) = A * B^T for MX operands of one element format; K % 64 == 0.
+// exact: every product exact and binary32 accumulation (BF16 matrix cores on
+// exactly rescaled elements) instead of the scaled matrix cores.
 hipError_t launch_mx_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
                           const uint8_t* b_scales, int elem, int64_t M, int64_t N, int64_t K, void* C,
-                          bool c_bf16, int64_t ldc, hipStream_t s);
+                          bool c_bf16, int64_t ldc, bool exact, hipStream_t s);
 
 }  // namespace nvfp4

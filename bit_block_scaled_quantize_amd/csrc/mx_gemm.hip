@@ -344,6 +344,243 @@ __global__ void __launch_bounds__(256, 1) k_mx_gemm(MxGemmArgs p) {
         }
 }
 
+// ============================================================ exact accumulation
+// For callers that need the NVFP4 GEMM's accuracy (|C - exact| within
+// 1e-5 sum |a b|) from MX operands: the scaled matrix core keeps only ~13 bits
+// while it sums a K step of E4M3 products, so here every element is converted
+// exactly to BF16 and the BF16 matrix core (v_mfma_f32_32x32x16_bf16) forms
+// exact products and sums them in binary32, as the NVFP4 GEMM does in FP16.
+// BF16 keeps binary32's 8 exponent bits, so an element carries its block
+// scale as a power of two relative to the largest block scale of its row:
+// A'[m][k] = v * 2^(b[m][kb] - R[m]), R[m] = max over kb of the scale byte
+// b[m][kb]; then C[m][n] = 2^(R_A[m] + R_B[n] - 254) * sum_k A'[m][k] B'[n][k]
+// (E8M0 bytes carry a bias of 127).  One gfx950 scaled convert
+// (v_cvt_scalef32_pk_bf16_fp8 / _fp4) turns two codes into two BF16 values
+// times that power of two; its f32 scale operand contributes its exponent
+// only, so the operand is built as 2^e directly.  Every product is exact while
+// the rescaled elements and their products stay in the normal ranges of BF16
+// and binary32: a nonzero E4M3 element is at least 2^-9 (E2M1: 2^-1), so it
+// suffices that for each block the two rows' distances below their largest
+// scales add up to at most 108 binades (E2M1: 124) -- e.g. every row's
+// nonzero blocks within 2^54 of its largest.  A block more than 2^126 below
+// is scaled by 2^-126 (a clamp that keeps the operand a normal binary32).
+//
+// Pipeline: the ring kernel's (four 64-step slots of raw codes and scale
+// bytes, loaded by global_load_lds three steps ahead, one barrier per step),
+// with each 64-wide K step run as four 16-wide substeps of 16 BF16 MFMAs per
+// wave; a lane converts its 8 elements of each fragment for the substep just
+// before its MFMAs.  Substep q takes bytes 8q .. 8q+7 of the lane's E4M3
+// fragment (block q / 2 of the step) or nibbles 8q .. 8q+7 of its E2M1
+// fragment (block h); A and B use the same map, so the products pair the
+// same K.  The largest scale byte of each tile row is found once, in the
+// prologue, from the rows' scale bytes.
+typedef __bf16 v8bf_t __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf_t __attribute__((ext_vector_type(2)));
+
+// Largest byte of p[0 .. n).
+__device__ __forceinline__ int row_max_byte(const uint8_t* p, int64_t n) {
+    uint32_t m = 0u;
+    int64_t k = 0;
+    if ((reinterpret_cast<uintptr_t>(p) & 15) == 0) {
+        for (; k + 16 <= n; k += 16) {
+            const uint4 v = *reinterpret_cast<const uint4*>(p + k);
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int d = 0; d < 4; ++d)
+                m = max(m, max(max(w[d] & 0xFFu, (w[d] >> 8) & 0xFFu), max((w[d] >> 16) & 0xFFu, w[d] >> 24)));
+        }
+    }
+    for (; k < n; ++k) m = max(m, (uint32_t)p[k]);
+    return (int)m;
+}
+
+// 2^(b - r) as a binary32 scale operand (b <= r), at least 2^-126.
+__device__ __forceinline__ float pow2_rel(int b, int r) {
+    return __uint_as_float((uint32_t)(127 + max(b - r, -126)) << 23);
+}
+
+// The lane's 8 elements of substep q of its fragment f, as BF16 times sc.
+template <int ELEM>
+__device__ __forceinline__ v8bf_t exact_piece(const v8i_t& f, int q, float sc) {
+    v2bf_t p0, p1, p2, p3;
+    if constexpr (ELEM == kMxE4M3) {
+        const uint32_t d0 = (uint32_t)f[2 * q], d1 = (uint32_t)f[2 * q + 1];
+        p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, sc, false);
+        p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, sc, true);
+        p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, sc, false);
+        p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, sc, true);
+    } else {
+        const uint32_t d = (uint32_t)f[q];
+        p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, sc, 0);
+        p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, sc, 1);
+        p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, sc, 2);
+        p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, sc, 3);
+    }
+    return v8bf_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+// Raw fragments of a step (as mx_read_frags) with the scale bytes an exact
+// conversion needs: E4M3 lanes hold elements of both blocks of the step (the
+// row's two bytes, block 0 in bits 0..7), E2M1 lanes of block h only.
+template <int ELEM>
+__device__ __forceinline__ void mx_read_frags_exact(const uint8_t* slot, const MxLaneOffsets& o, MxFrags& f) {
+    using G = MxGeo<ELEM>;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int dc = 32 * i * G::RB, ds = 32 * i * 4;
+        f.a[i] = mx_frag<ELEM>(slot + dc, o.a_lo, o.a_hi);
+        f.b[i] = mx_frag<ELEM>(slot + dc, o.b_lo, o.b_hi);
+        if constexpr (ELEM == kMxE4M3) {
+            // o.sa - h is the row's dword: bytes 0 and 1 are blocks 0 and 1
+            f.sa[i] = *reinterpret_cast<const uint16_t*>(slot + o.sa - (o.sa & 3) + ds);
+            f.sb[i] = *reinterpret_cast<const uint16_t*>(slot + o.sb - (o.sb & 3) + ds);
+        } else {
+            f.sa[i] = slot[o.sa + ds];
+            f.sb[i] = slot[o.sb + ds];
+        }
+    }
+}
+
+template <int ELEM, bool OUT_BF16>
+__global__ void __launch_bounds__(256, 1) k_mx_gemm_exact(MxGemmArgs p) {
+    using G = MxGeo<ELEM>;
+    __shared__ __attribute__((aligned(16))) uint8_t ring0[G::SLOT];
+    __shared__ __attribute__((aligned(16))) uint8_t ring1[G::SLOT];
+    __shared__ __attribute__((aligned(16))) uint8_t ring2[G::SLOT];
+    __shared__ __attribute__((aligned(16))) uint8_t ring3[G::SLOT];
+    __shared__ int rref[2 * kMxTile];  // largest scale byte of each tile row: A rows, then B rows
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = w >> 1, wn = w & 1;
+    const int h = lane >> 5, l32 = lane & 31;
+    const int64_t M = p.M, N = p.N, K = p.K;
+    const int64_t m0 = (int64_t)blockIdx.y * kMxTile, n0 = (int64_t)blockIdx.x * kMxTile;
+    const int64_t kb = ELEM == kMxE4M3 ? K : K / 2, ks = K / 32;
+
+    MxSrc<ELEM> src;
+    src.ac = p.ac + m0 * kb;
+    src.bc = p.bc + n0 * kb;
+    src.as = p.as + m0 * ks;
+    src.bs = p.bs + n0 * ks;
+#pragma unroll
+    for (int t = 0; t < G::LOADS; ++t) {
+        const int r = 64 * w + G::RPL * t + lane / G::CPR;
+        const int c = mx_chunk<G::CPR>(r, lane % G::CPR);
+        src.a[t] = (uint32_t)((min(m0 + r, M - 1) - m0) * kb + 16 * c);
+        src.b[t] = (uint32_t)((min(n0 + r, N - 1) - n0) * kb + 16 * c);
+    }
+    src.sa = (uint32_t)((min(m0 + 64 * w + lane, M - 1) - m0) * ks);
+    src.sb = (uint32_t)((min(n0 + 64 * w + lane, N - 1) - n0) * ks);
+
+    // each thread: the largest scale byte of one A row and one B row of the
+    // tile (rows past the end: the clamped row, never stored)
+    rref[tid] = row_max_byte(p.as + min(m0 + tid, M - 1) * ks, ks);
+    rref[kMxTile + tid] = row_max_byte(p.bs + min(n0 + tid, N - 1) * ks, ks);
+
+    v16f_t acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    const int arow0 = 128 * wm, brow0 = 128 * wn;
+    const int64_t nsteps = K / kMxStepK;
+    if (nsteps > 0) {
+        const int64_t pad = (4 - nsteps % 4) % 4, nj = nsteps + pad, last = nsteps - 1;
+        auto kc_of = [&](int64_t j) {
+            const int64_t kc = j - pad;
+            return kc < 0 ? (int64_t)0 : (kc > last ? last : kc);
+        };
+        if (pad > 0) mx_zero_slot<ELEM>(ring0); else mx_ring_load<ELEM>(src, kc_of(0), ring0, w);
+        if (pad > 1) mx_zero_slot<ELEM>(ring1); else mx_ring_load<ELEM>(src, kc_of(1), ring1, w);
+        if (pad > 2) mx_zero_slot<ELEM>(ring2); else mx_ring_load<ELEM>(src, kc_of(2), ring2, w);
+        mx_ring_load<ELEM>(src, kc_of(3), ring3, w);
+        __builtin_amdgcn_s_waitcnt(mx_vmcnt_at_most(3 * G::LPS));
+        __builtin_amdgcn_s_waitcnt(mx_lgkmcnt_zero());
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();  // (also publishes rref)
+        asm volatile("" ::: "memory");
+
+        int refa[4], refb[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            refa[i] = rref[arow0 + 32 * i + l32];
+            refb[i] = rref[kMxTile + brow0 + 32 * i + l32];
+        }
+        const MxLaneOffsets lo = mx_lane_offsets<ELEM>(arow0, brow0, l32, h);
+        MxFrags fx, fy;
+        mx_read_frags_exact<ELEM>(ring0, lo, fx);
+
+        auto step = [&](int64_t j, uint8_t* cur, uint8_t* nxt, MxFrags& fc, MxFrags& fn) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if (q == 2) {
+                    // as in the ring kernel, half way through the step: own
+                    // loads of step j + 1 landed, the barrier, then the next
+                    // step's fragments and the loads of step j + 4 into the
+                    // slot every wave has finished reading
+                    __builtin_amdgcn_sched_barrier(0);
+                    __builtin_amdgcn_s_waitcnt(mx_vmcnt_at_most(2 * G::LPS));
+                    asm volatile("" ::: "memory");
+                    __builtin_amdgcn_s_barrier();
+                    asm volatile("" ::: "memory");
+                    mx_read_frags_exact<ELEM>(nxt, lo, fn);
+                    mx_ring_load<ELEM>(src, kc_of(j + 4), cur, w);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                const int sh = ELEM == kMxE4M3 ? 8 * (q >> 1) : 0;
+                v8bf_t av[4], bv[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    av[i] = exact_piece<ELEM>(fc.a[i], q, pow2_rel((fc.sa[i] >> sh) & 0xFF, refa[i]));
+                    bv[i] = exact_piece<ELEM>(fc.b[i], q, pow2_rel((fc.sb[i] >> sh) & 0xFF, refb[i]));
+                }
+#pragma unroll
+                for (int m = 0; m < 16; ++m) {
+                    const int i = m >> 2, jj = m & 3;
+                    acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[jj], acc[i][jj], 0, 0, 0);
+                }
+            }
+        };
+        for (int64_t j = 0; j < nj; j += 4) {
+            step(j, ring0, ring1, fx, fy);
+            step(j + 1, ring1, ring2, fy, fx);
+            step(j + 2, ring2, ring3, fx, fy);
+            step(j + 3, ring3, ring0, fy, fx);
+        }
+        __builtin_amdgcn_s_waitcnt(mx_vmcnt_at_most(0));
+    } else {
+        __syncthreads();  // (K == 0: rref published for the epilogue)
+    }
+
+    // C = 2^(R_A[m] + R_B[n] - 254) * acc (exact unless C leaves binary32's
+    // normal range); accumulator r of tile (i, j): row 32 i + 8 (r / 4) + 4 h +
+    // r % 4, column 32 j + l32 of the wave tile
+    const int64_t mw = m0 + arow0, nw = n0 + brow0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t c = nw + 32 * j + l32;
+            if (c >= N) continue;
+            const int rb = rref[kMxTile + brow0 + 32 * j + l32];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int rl = arow0 + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+                const int64_t m = m0 + rl;
+                if (m < M) {
+                    const float v = ldexpf(acc[i][j][r], rref[rl] + rb - 254);
+                    if (OUT_BF16)
+                        static_cast<uint16_t*>(p.C)[m * p.ldc + c] = (uint16_t)__builtin_bit_cast(uint16_t, (__bf16)v);
+                    else
+                        static_cast<float*>(p.C)[m * p.ldc + c] = v;
+                }
+            }
+        }
+}
+
 // ============================================================ full-line kernel
 // For K % 1024 == 0 with 16-byte-aligned scale rows (every benchmarked shape):
 // the same tile and MFMA schedule, but the memory traffic shaped for gfx950's
@@ -621,10 +858,20 @@ inline int64_t mx_cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 hipError_t launch_mx_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
                           const uint8_t* b_scales, int elem, int64_t M, int64_t N, int64_t K, void* C,
-                          bool c_bf16, int64_t ldc, hipStream_t s) {
+                          bool c_bf16, int64_t ldc, bool exact, hipStream_t s) {
     if (M == 0 || N == 0) return hipSuccess;
     MxGemmArgs p{a_codes, a_scales, b_codes, b_scales, M, N, K, C, ldc};
     dim3 grid((unsigned)mx_cdiv(N, kMxTile), (unsigned)mx_cdiv(M, kMxTile));
+    if (exact) {
+#define NVFP4_MXX(E, BF) hipLaunchKernelGGL((k_mx_gemm_exact<E, BF>), grid, dim3(256), 0, s, p)
+        if (elem == kMxE4M3) {
+            if (c_bf16) NVFP4_MXX(kMxE4M3, true); else NVFP4_MXX(kMxE4M3, false);
+        } else {
+            if (c_bf16) NVFP4_MXX(kMxE2M1, true); else NVFP4_MXX(kMxE2M1, false);
+        }
+#undef NVFP4_MXX
+        return hipGetLastError();
+    }
     const bool full = K % 1024 == 0 && K > 0 && (reinterpret_cast<uintptr_t>(a_scales) & 15) == 0 &&
                       (reinterpret_cast<uintptr_t>(b_scales) & 15) == 0;
 #define NVFP4_MXG(E, BF)                                                                 \

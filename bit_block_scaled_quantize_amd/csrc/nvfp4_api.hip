@@ -334,9 +334,10 @@ nvfp4_status nvfp4_mx_dequantize(const nvfp4_mx_tensor* q, void* y, nvfp4_dtype 
 }
 
 nvfp4_status nvfp4_mx_gemm(const nvfp4_mx_tensor* A, const nvfp4_mx_tensor* B, void* C, nvfp4_dtype c_dt,
-                           int64_t ldc, void* stream) {
+                           int64_t ldc, int32_t accum, void* stream) {
     if (!A || !B) return NVFP4_ERR_NULL;
     if (!valid_dtype(c_dt)) return NVFP4_ERR_ENUM;
+    if (accum != NVFP4_MX_ACC_NATIVE && accum != NVFP4_MX_ACC_EXACT) return NVFP4_ERR_ENUM;
     for (const nvfp4_mx_tensor* t : {A, B}) {
         if (t->elem != NVFP4_MX_E4M3 && t->elem != NVFP4_MX_E2M1) return NVFP4_ERR_ENUM;
         if (t->rows < 0 || t->cols < 0 || t->cols % 32) return NVFP4_ERR_SHAPE;
@@ -359,7 +360,7 @@ nvfp4_status nvfp4_mx_gemm(const nvfp4_mx_tensor* A, const nvfp4_mx_tensor* B, v
     if (cdiv(M, 256) > kMaxGridY) return NVFP4_ERR_UNSUPPORTED;
     hipError_t e = launch_mx_gemm(A->codes, A->scales, B->codes, B->scales,
                                   A->elem == NVFP4_MX_E4M3 ? kMxE4M3 : kMxE2M1, M, N, K, C, c_dt == NVFP4_BF16,
-                                  ldc, static_cast<hipStream_t>(stream));
+                                  ldc, accum == NVFP4_MX_ACC_EXACT, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
 

@@ -24,6 +24,7 @@ NVFP4_RNE, NVFP4_SR = 0, 1
 NVFP4_EPI_NONE, NVFP4_EPI_SWIGLU = 0, 1
 NVFP4_SCALE_1D, NVFP4_SCALE_2D = 0, 1
 NVFP4_MX_E4M3, NVFP4_MX_E2M1 = 0, 1
+NVFP4_MX_ACC_NATIVE, NVFP4_MX_ACC_EXACT = 0, 1
 
 EXPORTED = ["nvfp4_quantize_workspace_size", "nvfp4_quantize", "nvfp4_quantize_noalloc", "nvfp4_requantize",
             "nvfp4_dequantize",
@@ -77,7 +78,7 @@ def _load():
     L.nvfp4_mx_quantize.restype = i32
     L.nvfp4_mx_dequantize.argtypes = [ctypes.POINTER(CMXTensor), vp, i32, i64, vp]
     L.nvfp4_mx_dequantize.restype = i32
-    L.nvfp4_mx_gemm.argtypes = [ctypes.POINTER(CMXTensor), ctypes.POINTER(CMXTensor), vp, i32, i64, vp]
+    L.nvfp4_mx_gemm.argtypes = [ctypes.POINTER(CMXTensor), ctypes.POINTER(CMXTensor), vp, i32, i64, i32, vp]
     L.nvfp4_mx_gemm.restype = i32
     L.nvfp4_status_string.argtypes = [i32]
     L.nvfp4_status_string.restype = ctypes.c_char_p
@@ -360,14 +361,16 @@ def nvfp4_mx_dequantize(q, dtype=torch.float32, out=None, stream=None):
 
 
 @_launches_on_stream
-def nvfp4_mx_gemm(A, B, out_dtype=torch.float32, out=None, stream=None):
-    """C = A B^T (A: M x K, B: N x K MX tensors of one element format)."""
+def nvfp4_mx_gemm(A, B, out_dtype=torch.float32, out=None, accum=NVFP4_MX_ACC_NATIVE, stream=None):
+    """C = A B^T (A: M x K, B: N x K MX tensors of one element format);
+    accum NVFP4_MX_ACC_NATIVE (scaled matrix cores) or NVFP4_MX_ACC_EXACT
+    (exact products, binary32 sums)."""
     if out is None:
         out = torch.empty((A.rows, B.rows), dtype=out_dtype, device=A.codes.device)
     assert out.stride(1) == 1
     ldc = out.stride(0) if A.rows > 1 else max(B.rows, out.stride(0))
     ca, cb = A.c(), B.c()
     st = lib.nvfp4_mx_gemm(ctypes.byref(ca), ctypes.byref(cb), ctypes.c_void_p(out.data_ptr()),
-                           _dtype_code(out.dtype), ldc, _stream(stream))
+                           _dtype_code(out.dtype), ldc, accum, _stream(stream))
     _check("nvfp4_mx_gemm", st)
     return out

@@ -298,13 +298,31 @@ nvfp4_status nvfp4_mx_quantize(const void* x, nvfp4_dtype dt, int64_t rows, int6
 nvfp4_status nvfp4_mx_dequantize(const nvfp4_mx_tensor* q, void* y, nvfp4_dtype dt, int64_t ld,
                                  void* stream);
 
+/* How nvfp4_mx_gemm accumulates.
+ *   NATIVE: gfx950's scaled matrix cores take the codes and scale bytes as
+ *           they are (the fastest path).  The OCP Microscaling definition
+ *           leaves the internal precision of a block dot product to the
+ *           implementation; this hardware sums the 64 products of a K step
+ *           exactly for E2M1 operands, but for E4M3 operands keeps about 13
+ *           significant bits relative to the step's largest product (errors
+ *           up to ~2^-12 of it, measured), so E4M3 results do NOT meet the
+ *           1e-5 * sum |a b| accuracy of nvfp4_gemm.
+ *   EXACT:  every element is converted exactly to BF16 times a power of two
+ *           relative to its row's largest block scale, and the BF16 matrix
+ *           cores form every product exactly and sum in binary32, as
+ *           nvfp4_gemm does: |C - sum of exact products| within
+ *           1e-5 * sum |a b| (+ half a BF16 ulp for BF16 output), at about
+ *           the FP16 matrix-core rate.  Exact products need the rescaled
+ *           elements and their products in the normal ranges of BF16 and
+ *           binary32: it suffices that in every row of A and of B the nonzero
+ *           blocks' scales lie within 2^54 of the row's largest, and that C
+ *           stays within binary32's range. */
+typedef enum { NVFP4_MX_ACC_NATIVE = 0, NVFP4_MX_ACC_EXACT = 1 } nvfp4_mx_accum;
+
 /* C = A * B^T for MX tensors A (M x K) and B (N x K) of the same element
- * format, on gfx950's scaled matrix cores: C[m][n] = sum over K of
- * (v_A 2^s_A)(v_B 2^s_B), FP32 accumulation, written as F32 or BF16 (nearest
- * even) to C (M x N, row stride ldc elements).  Accuracy: E2M1 products are
- * summed exactly within each 64-wide K step; with E4M3 operands the hardware
- * keeps about 13 significant bits, relative to the step's largest product,
- * while it sums a step's 64 products (errors up to ~2^-12 of that product).
+ * format: C[m][n] = sum over K of (v_A 2^s_A)(v_B 2^s_B), accumulated as
+ * `accum` (nvfp4_mx_accum) selects, written as F32 or BF16 (nearest even) to
+ * C (M x N, row stride ldc elements).
  * Requirements: K % 64 == 0 (K % 32 != 0 is ERR_SHAPE, K % 64 == 32 is
  * ERR_UNSUPPORTED), code bytes per row (K for E4M3, K/2 for E2M1) below
  * 2^24 (else ERR_UNSUPPORTED), A->elem == B->elem (else ERR_UNSUPPORTED), ldc >= N,
@@ -312,7 +330,7 @@ nvfp4_status nvfp4_mx_dequantize(const nvfp4_mx_tensor* q, void* y, nvfp4_dtype 
  * Source: asector.ru page, "NVFP4 и Blackwell" (block-scaled tensor-core
  * compute); iitak.ru page, "Как это работает" (MXFP8 in the backward pass). */
 nvfp4_status nvfp4_mx_gemm(const nvfp4_mx_tensor* A, const nvfp4_mx_tensor* B, void* C, nvfp4_dtype c_dt,
-                           int64_t ldc, void* stream);
+                           int64_t ldc, int32_t accum, void* stream);
 
 /* Static description of a status code. */
 const char* nvfp4_status_string(nvfp4_status s);

@@ -200,13 +200,15 @@ def test_mx_rejects_bad_arguments(nv):
 def test_mx_gemm_rejects_bad_arguments(nv):
     E = dict(NULL=1, ENUM=2, SHAPE=3, ALIGN=4, UNSUP=5)
 
-    def g(ma=(64, 128, 0), mb=(32, 128, 0), C=65536, dt=0, ldc=32, ac=4096, asc=8192):
+    def g(ma=(64, 128, 0), mb=(32, 128, 0), C=65536, dt=0, ldc=32, ac=4096, asc=8192, acc=0):
         a = nv.CMXTensor(ac, asc, ma[0], ma[1], ma[2])
         b = nv.CMXTensor(4096, 8192, mb[0], mb[1], mb[2])
-        return nv.lib.nvfp4_mx_gemm(ctypes.byref(a), ctypes.byref(b), C, dt, ldc, None)
+        return nv.lib.nvfp4_mx_gemm(ctypes.byref(a), ctypes.byref(b), C, dt, ldc, acc, None)
 
-    assert nv.lib.nvfp4_mx_gemm(None, None, 65536, 0, 32, None) == E["NULL"]
+    assert nv.lib.nvfp4_mx_gemm(None, None, 65536, 0, 32, 0, None) == E["NULL"]
     assert g(dt=4) == E["ENUM"]
+    assert g(acc=2) == E["ENUM"]
+    assert g(acc=-1) == E["ENUM"]
     assert g(ma=(64, 128, 3)) == E["ENUM"]
     assert g(ma=(64, 96, 0), mb=(32, 96, 0)) == E["UNSUP"]       # K % 64 == 32
     assert g(ma=(64, 80, 0), mb=(32, 80, 0)) == E["SHAPE"]       # K % 32
@@ -222,6 +224,7 @@ def test_mx_gemm_rejects_bad_arguments(nv):
     K4 = 1 << 24                                                 # E4M3: 2^24 bytes per row
     assert g(ma=(64, K4, 0), mb=(32, K4, 0)) == E["UNSUP"]
     assert g(ma=(64, 2 * K4, 1), mb=(32, 2 * K4, 1)) == E["UNSUP"]   # E2M1: K/2 bytes per row
+    assert g(ma=(64, K4, 0), mb=(32, K4, 0), acc=1) == E["UNSUP"]     # the exact path shares the limit
 
 
 def test_quantize_noalloc_rejects_bad_arguments(nv):
