@@ -93,6 +93,7 @@ KERNEL_SOURCES = {
     "mx_gemm": ("mx_gemm.hip",),
     "mx": ("mx.hip", "nvfp4_device.hpp"),
     "codec": ("mx.hip", "nvfp4_device.hpp"),
+    "amax": ("quantize.hip", "nvfp4_device.hpp"),
 }
 
 
@@ -156,7 +157,9 @@ def main():
                     help="for rocprofv3 --pmc runs: a 1 GiB device copy (calibration), then each "
                          "step kernel alone, the column re-quantization and the MX quantize / "
                          "dequantize kernels, 3 launches each, then (unless --no-gemm) the forward "
-                         "GEMM and the two 8192^3 MX GEMMs twice each, and exit")
+                         "GEMM, the two 8192^3 MX GEMMs and the exact-accumulation E4M3 one twice "
+                         "each, and the 8192x20480 gradient's Hadamard + column + SR quantization "
+                         "(with its amax pass) twice, and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -434,7 +437,7 @@ def pmc_driver_gemm(nv, W, np, torch):
         nv.nvfp4_gemm(X, Wt, out=Y)
     torch.cuda.synchronize()
     del X, Wt, Y
-    # MX GEMMs 8192^3, FP32 out
+    # MX GEMMs 8192^3, FP32 out (native; then E4M3 with exact accumulation)
     for elem in (nv.NVFP4_MX_E4M3, nv.NVFP4_MX_E2M1):
         A = nv.nvfp4_mx_quantize(bf16_device(W.f32_to_bf16_bits(W.student_t((8192, 8192), 3.0, seed=7100)), torch, np),
                                  elem=elem)
@@ -445,7 +448,20 @@ def pmc_driver_gemm(nv, W, np, torch):
         for _ in range(2):
             nv.nvfp4_mx_gemm(A, B, out=C)
         torch.cuda.synchronize()
+        if elem == nv.NVFP4_MX_E4M3:
+            for _ in range(2):
+                nv.nvfp4_mx_gemm(A, B, out=C, accum=nv.NVFP4_MX_ACC_EXACT)
+            torch.cuda.synchronize()
         del A, B, C
+    # the 8192 x 20480 gradient's transformed amax (down columns) and its
+    # Hadamard + column + SR quantization, two calls
+    dy = bf16_device(W.f32_to_bf16_bits(W.with_spikes(W.normal((8192, 20480), 1.0, seed=5000), 1e-4, 100.0,
+                                                      seed=5001)), torch, np)
+    for i in range(2):
+        nv.nvfp4_quantize(dy, layout=nv.NVFP4_COL_1D, round=nv.NVFP4_SR, sr_seed=5100 + i, hadamard=True,
+                          hadamard_seed=5200)
+    torch.cuda.synchronize()
+    del dy
 
 
 def bench_gemm(nv, W, np, torch, reps, kern_extra=None):

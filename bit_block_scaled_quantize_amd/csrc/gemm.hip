@@ -741,7 +741,10 @@ __global__ void __launch_bounds__(256, 1) k_gemm_full(GemmArgs p) {
     const int tid = threadIdx.x;
     // the wave index is uniform: held in a scalar register, the LDS
     // destinations of the loads need no vector registers
-    const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // (the two forms of the lane index are equal; with either one alone, one
+    // of the SwiGLU instances got a dead register spill from the allocator)
+    const int lane = GROUPED ? (int)__lane_id() : (tid & 63);
     const int wm = w >> 1, wn = w & 1;
     const int h = lane >> 5, l32 = lane & 31;
 
@@ -850,7 +853,10 @@ __global__ void __launch_bounds__(256, 1) k_gemm_full(GemmArgs p) {
     }
     // the last look-ahead loads (clamped re-reads) land before the LDS is released
     __builtin_amdgcn_s_waitcnt(vmcnt_at_most(0));
-    epilogue<GROUPED, SWIGLU, OUT_BF16>(p, acc, m0, m_end, g, wm, wn, h, l32, lane);
+    // the tile's rows and group found again rather than kept through the loop
+    // (held there, they cost the grouped SwiGLU instance a spilled register)
+    const TileRows te = tile_rows<GROUPED>(p);
+    epilogue<GROUPED, SWIGLU, OUT_BF16>(p, acc, te.m0, te.m_end, te.g, wm, wn, h, l32, (int)(threadIdx.x & 63));
 }
 
 __global__ void k_zero_float(float* p) {

@@ -164,8 +164,8 @@ __global__ void __launch_bounds__(256) k_mx_row(const T* __restrict__ x, int64_t
             float m = 0.0f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(v[k][e]));
-            m = fmaxf(m, __shfl_xor(m, 1, 64));
-            a[k] = fmaxf(m, __shfl_xor(m, 2, 64));
+            m = fmaxf(m, lane_xor1(m));
+            a[k] = fmaxf(m, lane_xor2(m));
         }
         if (col_ok) {
             uint32_t wd[2][4];
@@ -258,7 +258,7 @@ __global__ void __launch_bounds__(256) k_mx_col(const T* __restrict__ x, int64_t
             }
         }
         float a = absmax16(col);
-        a = fmaxf(a, __shfl_xor(a, 1, 64));
+        a = fmaxf(a, lane_xor1(a));
         const int s = mx_scale_exp<ELEM>(a);
         uint32_t wd[8];
         if (SR) philox_words16(seed, kStreamMxCol, (uint64_t)(c * rows + r0), wd);

@@ -138,6 +138,35 @@ __device__ __forceinline__ uint32_t draw16(const uint32_t* w, int j) {
     return (j & 1) ? (w[j >> 1] >> 16) : (w[j >> 1] & 0xFFFFu);
 }
 
+// ---------------------------------------------------------------- lane exchanges
+// Exchanges inside aligned groups of four lanes as DPP quad permutes: the
+// value of another lane of the quad arrives as a VALU operand modifier
+// instead of through an LDS round trip (ds_bpermute).  Control word: output
+// lane i of each quad reads input lane (CTRL >> 2i) & 3.
+template <int CTRL>
+__device__ __forceinline__ uint32_t quad_perm(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, CTRL, 0xF, 0xF, true);
+}
+template <int CTRL>
+__device__ __forceinline__ float quad_perm(float x) {
+    return __uint_as_float(quad_perm<CTRL>(__float_as_uint(x)));
+}
+// The value of lane ^ 1 and of lane ^ 2.
+template <typename V>
+__device__ __forceinline__ V lane_xor1(V x) { return quad_perm<0xB1>(x); }
+template <typename V>
+__device__ __forceinline__ V lane_xor2(V x) { return quad_perm<0x4E>(x); }
+// The value of lane k of the caller's aligned group of G (2 or 4) lanes.
+template <int G, typename V>
+__device__ __forceinline__ V group_lane(V x, int k) {
+    if constexpr (G == 2) {
+        return k == 0 ? quad_perm<0xA0>(x) : quad_perm<0xF5>(x);  // [0,0,2,2], [1,1,3,3]
+    } else {
+        return k == 0 ? quad_perm<0x00>(x) : k == 1 ? quad_perm<0x55>(x)
+             : k == 2 ? quad_perm<0xAA>(x) : quad_perm<0xFF>(x);  // [k,k,k,k]
+    }
+}
+
 // ---------------------------------------------------------------- formats
 // binary32 value of an E4M3 byte (bias 7; exponent field 0 = multiples of 2^-9)
 // (the gfx950 FP8 -> binary32 convert is exact for every finite E4M3 byte)
@@ -375,6 +404,33 @@ __device__ __forceinline__ void hadamard16(float v[16], uint32_t sign_mask) {
     }
 #pragma unroll
     for (int j = 0; j < 16; ++j) v[j] = 0.25f * v[j];
+}
+
+// max_i |t_i| of t = hadamard16(v): the same values as transforming and then
+// taking the maximum magnitude, with less work.  For binary32 a and b, one of
+// |a + b| and |a - b| is |a| + |b| exactly and the other is smaller, and
+// rounding is monotone and sign-symmetric, so max(|fl(a + b)|, |fl(a - b)|) =
+// fl(|a| + |b|): the last butterfly stage collapses to one addition per pair.
+// fl(x / 4) is monotone in |x| too, so the multiply by 1/4 moves after the
+// maximum.
+__device__ __forceinline__ float hadamard16_absmax(float v[16], uint32_t sign_mask) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+        if ((sign_mask >> j) & 1u) v[j] = -v[j];
+#pragma unroll
+    for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            if (j & h) continue;
+            float a = v[j], b = v[j + h];
+            v[j] = a + b;
+            v[j + h] = a - b;
+        }
+    }
+    float m = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[j]) + fabsf(v[j + 8]));
+    return 0.25f * m;
 }
 
 // ---------------------------------------------------------------- loads

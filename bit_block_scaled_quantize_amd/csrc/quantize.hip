@@ -153,10 +153,7 @@ __global__ void __launch_bounds__(256) k_amax_hadamard_rows(const T* __restrict_
                 }
             }
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                hadamard16(v[u], sign_mask);
-                a = fmaxf(a, absmax16(v[u]));
-            }
+            for (int u = 0; u < 2; ++u) a = fmaxf(a, hadamard16_absmax(v[u], sign_mask));
         }
     }
     store_partial(a, partial);
@@ -186,8 +183,8 @@ __global__ void __launch_bounds__(256) k_amax_hadamard_cols(const T* __restrict_
             const int64_t valid = cols - j * CH;
 #pragma unroll
             for (int e = 0; e < CH; ++e) {
-                hadamard16(col[e], sign_mask);
-                if (e < valid) a = fmaxf(a, absmax16(col[e]));
+                const float t = hadamard16_absmax(col[e], sign_mask);
+                if (e < valid) a = fmaxf(a, t);
             }
         }
     }
@@ -253,7 +250,7 @@ __device__ __forceinline__ void hadamard8_pair(float v[8], uint32_t sign_mask, b
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        const float p = __shfl_xor(v[j], 1, 64);
+        const float p = lane_xor1(v[j]);
         v[j] = odd ? (p - v[j]) : (v[j] + p);
     }
 #pragma unroll
@@ -267,12 +264,12 @@ __device__ __forceinline__ void hadamard8_pair(float v[8], uint32_t sign_mask, b
 // block maxima.
 __device__ __forceinline__ void pair_block_scales(float& a0, float& a1, bool odd, const TensorScale& ts,
                                                   BlockScale& b0, BlockScale& b1) {
-    a0 = fmaxf(a0, __shfl_xor(a0, 1, 64));
-    a1 = fmaxf(a1, __shfl_xor(a1, 1, 64));
+    a0 = fmaxf(a0, lane_xor1(a0));
+    a1 = fmaxf(a1, lane_xor1(a1));
     const BlockScale mine = block_scale(odd ? a1 : a0, ts.six_st, ts.rtab);
     BlockScale other;
-    other.R = __shfl_xor(mine.R, 1, 64);
-    other.byte = (uint32_t)__shfl_xor((int)mine.byte, 1, 64);
+    other.R = lane_xor1(mine.R);
+    other.byte = lane_xor1(mine.byte);
     b0 = odd ? other : mine;
     b1 = odd ? mine : other;
 }
@@ -403,8 +400,8 @@ __device__ __forceinline__ void tile_row_blocks(const uint4 (&raw)[8], int64_t R
         float m = 0.0f;
 #pragma unroll
         for (int e = 0; e < CH; ++e) m = fmaxf(m, fabsf(chunk_elem<T>(raw[k], e)));
-#pragma unroll
-        for (int o = 1; o < LPB; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+        m = fmaxf(m, lane_xor1(m));
+        if (LPB == 4) m = fmaxf(m, lane_xor2(m));
         a[k] = m;
     }
     // lane q of a block derives the multipliers of rows k = q, q + LPB, ...;
@@ -416,11 +413,10 @@ __device__ __forceinline__ void tile_row_blocks(const uint4 (&raw)[8], int64_t R
 #pragma unroll
         for (int k = 1; k < LPB; ++k) mine_a = (q == k) ? a[i0 + k] : mine_a;
         const BlockScale mine = block_scale(mine_a, ts.six_st, ts.rtab);
-        const int base = lane - q;
 #pragma unroll
         for (int k = 0; k < LPB; ++k) {
-            bs[i0 + k].R = __shfl(mine.R, base + k, 64);
-            bs[i0 + k].byte = (uint32_t)__shfl((int)mine.byte, base + k, 64);
+            bs[i0 + k].R = group_lane<LPB>(mine.R, k);
+            bs[i0 + k].byte = group_lane<LPB>(mine.byte, k);
         }
     }
 #pragma unroll
@@ -575,7 +571,7 @@ __global__ void __launch_bounds__(256) k_quant_2d(const T* __restrict__ x, int64
             for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(v[i][e]));
         // the partner lane holds the other 8 columns of the square (both are
         // active or both inactive, since cols % 16 == 0)
-        a = fmaxf(a, __shfl_xor(a, 1, 64));
+        a = fmaxf(a, lane_xor1(a));
         if (!active) return;
         BlockScale bs = block_scale(a, ts.six_st, ts.rtab);
         if ((lane & 1) == 0) scales[rband * (cols / 16) + c / 16] = (uint8_t)bs.byte;
@@ -595,13 +591,14 @@ __global__ void __launch_bounds__(256) k_quant_2d(const T* __restrict__ x, int64
 }
 
 // ============================================================ dequantize
-// A lane expands one 16-element block of each of 4 rows (row group rg = 16
-// rows per workgroup); the 64 lanes of a wave cover 1024 columns from
-// 1024 * blockIdx.x: 8 code bytes and a scale byte in, 32 (bf16) or 64 (fp32)
-// bytes out per row.  Codes are expanded two at a time by the gfx950 FP4
-// unpack instruction (scale operand 1.0, so the values are exact), then
-// multiplied by the block multiplier (exact: at most 6 significant bits) and
-// by s_t (one rounding).
+// A lane expands half of a 16-element block (8 elements: one code word and
+// the block's multiplier) of each of 8 rows; the 64 lanes of a wave cover 32
+// blocks (512 columns) from 512 * blockIdx.x, so each wave-wide store writes
+// 1 KiB (bf16; 2 KiB as two stores for fp32) of one row contiguously and each
+// code load reads 256 contiguous bytes.  Codes are expanded two at a time by
+// the gfx950 FP4 unpack instruction (scale operand 1.0, so the values are
+// exact), then multiplied by the block multiplier (exact: at most 6
+// significant bits) and by s_t (one rounding).
 template <typename TOut>
 __global__ void __launch_bounds__(256) k_dequant(const uint8_t* __restrict__ codes,
                                                  const uint8_t* __restrict__ scales,
@@ -610,47 +607,44 @@ __global__ void __launch_bounds__(256) k_dequant(const uint8_t* __restrict__ cod
                                                  int64_t ld) {
     const float st = ts[0];
     const int64_t nb = cols / 16;
-    const int64_t b = (int64_t)blockIdx.x * 64 + (threadIdx.x & 63);
+    const int lane = threadIdx.x & 63;
+    const int hf = lane & 1;
+    const int64_t b = (int64_t)blockIdx.x * 32 + (lane >> 1);
     if (b >= nb) return;
-    const int64_t nrg = (rows + 15) / 16;
+    const int64_t nrg = (rows + 31) / 32;
+    const int sshift = scale_2d ? 4 : 0;
     for (int64_t rg = blockIdx.y; rg < nrg; rg += gridDim.y) {
-        const int64_t r0 = rg * 16 + 4 * (threadIdx.x >> 6);
-        uint2 cw[4];
-        uint32_t sb[4];
+        const int64_t r0 = rg * 32 + 8 * (threadIdx.x >> 6);
+        uint32_t cw[8], sb[8];
         // rows past the end read the last row (never stored), and the scale
         // row is r >> 4 for 16x16 blocks, so the loads carry no branch and
         // issue back to back
-        const int sshift = scale_2d ? 4 : 0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 8; ++i) {
             const int64_t r = r0 + i < rows ? r0 + i : rows - 1;
-            cw[i] = *reinterpret_cast<const uint2*>(codes + (r * nb + b) * 8);
+            cw[i] = *reinterpret_cast<const uint32_t*>(codes + (r * nb + b) * 8 + 4 * hf);
             sb[i] = scales[(r >> sshift) * nb + b];
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 8; ++i) {
             const int64_t r = r0 + i;
             const float sv = e4m3_value(sb[i]);
-            float o[16];
+            float o[8];
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                float2 p = e2m1x2_unpack(k < 4 ? cw[i].x : cw[i].y, k & 3);
+            for (int k = 0; k < 4; ++k) {
+                const float2 p = e2m1x2_unpack(cw[i], k);
                 o[2 * k] = (p.x * sv) * st;
                 o[2 * k + 1] = (p.y * sv) * st;
             }
             if (r >= rows) continue;  // (only the stores are predicated)
-            TOut* qp = y + r * ld + b * 16;
+            TOut* qp = y + r * ld + b * 16 + 8 * hf;
             if constexpr (sizeof(TOut) == 2) {
-                uint32_t pk[8];
-#pragma unroll
-                for (int j = 0; j < 8; ++j) pk[j] = pack_bf16x2(o[2 * j], o[2 * j + 1]);
-                uint4* qq = reinterpret_cast<uint4*>(qp);
-                qq[0] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-                qq[1] = make_uint4(pk[4], pk[5], pk[6], pk[7]);
+                *reinterpret_cast<uint4*>(qp) = make_uint4(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]),
+                                                           pack_bf16x2(o[4], o[5]), pack_bf16x2(o[6], o[7]));
             } else {
                 float4* qq = reinterpret_cast<float4*>(qp);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) qq[j] = make_float4(o[4 * j], o[4 * j + 1], o[4 * j + 2], o[4 * j + 3]);
+                qq[0] = make_float4(o[0], o[1], o[2], o[3]);
+                qq[1] = make_float4(o[4], o[5], o[6], o[7]);
             }
         }
     }
@@ -706,8 +700,7 @@ __global__ void __launch_bounds__(256) k_amax_req(const uint8_t* __restrict__ ic
                 float col[16];
 #pragma unroll
                 for (int i = 0; i < 16; ++i) col[i] = v[i][e];
-                hadamard16(col, sign_mask);
-                a = fmaxf(a, absmax16(col));
+                a = fmaxf(a, hadamard16_absmax(col, sign_mask));
             }
         } else {
 #pragma unroll
@@ -1012,7 +1005,7 @@ hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, const 
                              int64_t rows, int64_t cols, bool scale_2d, void* y, bool bf16,
                              int64_t ld, hipStream_t s) {
     if (rows == 0 || cols == 0) return hipSuccess;
-    dim3 g((unsigned)cdiv(cols / 16, 64), grid_y(cdiv(rows, 16)));
+    dim3 g((unsigned)cdiv(cols / 16, 32), grid_y(cdiv(rows, 32)));
     if (bf16)
         hipLaunchKernelGGL(k_dequant<uint16_t>, g, dim3(256), 0, s, codes, scales, ts, rows, cols,
                            (int)scale_2d, static_cast<uint16_t*>(y), ld);

@@ -13,7 +13,9 @@ indices its elements have in the whole output tensor, so the assembled result
 is byte for byte the single call's (tests/test_oracle_banded.py checks that).
 A_t itself is the maximum of the bands' maxima (orc_amax per band).
 ROW_COL_1D is the ROW_1D and COL_1D outputs, which is how the oracle defines
-it.  Nothing here does any of the method's arithmetic.
+it.  The GEMM references split their output rows (or listed entries) the same
+way: every output entry is its own oracle dot product.  Nothing here does any
+of the method's arithmetic.
 """
 import concurrent.futures
 import ctypes
@@ -175,3 +177,65 @@ def gemm_entries(A, B, m_idx, n_idx, threads=None):
 
     _run(one, bands(mi.size, 4 * threads), threads)
     return C, Wt
+
+
+def _row_slice_mx(q, r0, r1):
+    return O.MXTensor(np.ascontiguousarray(q.codes[r0:r1]), np.ascontiguousarray(q.scales[r0:r1]),
+                      r1 - r0, q.cols, q.elem)
+
+
+def _gemm_rows(gemm, slice_rows, A, B, entries, threads):
+    threads = threads or default_threads()
+    if entries is not None:
+        mi = np.ascontiguousarray(entries[0], dtype=np.int64)
+        ni = np.ascontiguousarray(entries[1], dtype=np.int64)
+        C = np.zeros(mi.size, dtype=np.float64)
+        Wt = np.zeros(mi.size, dtype=np.float64)
+
+        def one(e0, e1):
+            C[e0:e1], Wt[e0:e1] = gemm(A, B, entries=(mi[e0:e1], ni[e0:e1]))
+
+        _run(one, bands(mi.size, 4 * threads), threads)
+        return C, Wt
+    C = np.zeros((A.rows, B.rows), dtype=np.float64)
+    Wt = np.zeros((A.rows, B.rows), dtype=np.float64)
+
+    def one(r0, r1):
+        C[r0:r1], Wt[r0:r1] = gemm(slice_rows(A, r0, r1), B)
+
+    _run(one, bands(A.rows, 4 * threads, 16), threads)
+    return C, Wt
+
+
+def gemm(A, B, entries=None, threads=None):
+    """O.gemm with the output rows (or the listed entries) split over
+    threads; the same (C, W).  For the whole output A must be row-blocked
+    (SCALE_1D) or split on 16-row bands (SCALE_2D)."""
+    def rows_of(q, r0, r1):
+        if q.scale_mode == O.SCALE_2D:
+            assert r0 % 16 == 0 and (r1 % 16 == 0 or r1 == q.rows)
+        return O.row_slice(q, r0, r1)
+    return _gemm_rows(O.gemm, rows_of, A, B, entries, threads)
+
+
+def mx_gemm(A, B, entries=None, threads=None):
+    """O.mx_gemm with the output rows (or the listed entries) split over
+    threads; the same (C, W)."""
+    return _gemm_rows(O.mx_gemm, _row_slice_mx, A, B, entries, threads)
+
+
+def mx_quantize(x, dtype, elem, rnd=O.RNE, seed=0, threads=None):
+    """O.mx_quantize (ROW_1D) band by band over rows, each band with the
+    random-draw index base of its first row; the same result."""
+    x = np.ascontiguousarray(x)
+    rows, cols = x.shape
+    threads = threads or default_threads()
+    out = O.MXTensor(np.zeros((rows, cols if elem == O.MX_FP8 else cols // 2), dtype=np.uint8),
+                     np.zeros((rows, cols // 32), dtype=np.uint8), rows, cols, elem)
+
+    def one(r0, r1):
+        q = O.mx_quantize(x[r0:r1], dtype, O.ROW_1D, elem, rnd, seed=seed, index_base=r0 * cols)
+        out.codes[r0:r1], out.scales[r0:r1] = q.codes, q.scales
+
+    _run(one, bands(rows, 4 * threads), threads)
+    return out

@@ -78,3 +78,22 @@ def test_banded_gemm_entries():
     c, w = B.gemm_entries(A, Bq, mi, ni, threads=4)
     c1, w1 = O.gemm(A, Bq, entries=(mi, ni))
     assert np.array_equal(c, c1) and np.array_equal(w, w1)
+
+
+def test_banded_gemms_and_mx_quantize():
+    A = O.quantize(_x(70, 96, O.F32, seed=31), O.F32, O.ROW_1D)
+    Bq = O.quantize(W.normal((48, 96), 0.02, seed=32), O.F32, O.BLK_2D)
+    for got, ref in zip(B.gemm(A, Bq, threads=3), O.gemm(A, Bq)):
+        assert np.array_equal(got, ref)
+    x = _x(96, 128, O.F32, seed=33)
+    for elem in (O.MX_FP8, O.MX_FP4):
+        for rnd in (O.RNE, O.SR):
+            q = B.mx_quantize(x, O.F32, elem, rnd, seed=34, threads=5)
+            r = O.mx_quantize(x, O.F32, O.ROW_1D, elem, rnd, seed=34)
+            assert np.array_equal(q.codes, r.codes) and np.array_equal(q.scales, r.scales)
+        qb = O.mx_quantize(_x(40, 128, O.F32, seed=35), O.F32, O.ROW_1D, elem)
+        for got, ref in zip(B.mx_gemm(r, qb, threads=4), O.mx_gemm(r, qb)):
+            assert np.array_equal(got, ref)
+        mi, ni = np.array([0, 5, 95, 3]), np.array([1, 39, 0, 7])
+        for got, ref in zip(B.mx_gemm(r, qb, entries=(mi, ni), threads=2), O.mx_gemm(r, qb, entries=(mi, ni))):
+            assert np.array_equal(got, ref)

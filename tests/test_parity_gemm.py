@@ -7,6 +7,7 @@ import torch
 
 import oracle as O
 import workloads as W
+from oracle import banded as OB
 from parity_utils import (assert_q_equal, bf16_tensor_to_bits, gemm_tol, q_to_device, q_to_host,
                           require_gpu, to_device)
 
@@ -52,7 +53,7 @@ def test_gemm_small(nv, M, N, K, bmode, out):
     A, B = quant_host(a, O.ROW_1D), quant_host(b, bmode)
     C = nv.nvfp4_gemm(q_to_device(A, nv), q_to_device(B, nv),
                       out_dtype=torch.float32 if out == "f32" else torch.bfloat16)
-    Cref, Wref = O.gemm(A, B)
+    Cref, Wref = OB.gemm(A, B)
     check(out_to_f64(C), Cref, Wref, out == "bf16", f"gemm {M}x{N}x{K}")
 
 
@@ -72,7 +73,7 @@ def test_gemm_exact_unit_scales(nv):
     A = O.quantize(make(M), O.F32, O.ROW_1D, amax_in=2688.0)
     B = O.quantize(make(N), O.F32, O.ROW_1D, amax_in=2688.0)
     C = nv.nvfp4_gemm(q_to_device(A, nv), q_to_device(B, nv))
-    Cref, _ = O.gemm(A, B)
+    Cref, _ = OB.gemm(A, B)
     assert np.array_equal(out_to_f64(C), Cref)
 
 
@@ -90,7 +91,7 @@ def test_gemm_256_config(nv):
     Aref, Bref = O.quantize(a, O.F32, O.ROW_1D), O.quantize(b, O.F32, O.COL_1D)
     assert_q_equal(q_to_host(Ad), Aref, "A")
     assert_q_equal(q_to_host(Bd), Bref, "B")
-    Cref, Wref = O.gemm(Aref, Bref)
+    Cref, Wref = OB.gemm(Aref, Bref)
     check(out_to_f64(C), Cref, Wref, False, "gemm 256")
 
 
@@ -168,7 +169,7 @@ def test_forward_8192x20480x5120_sampled(nv):
     Bq, bands, nl = _oracle_bands(w, ni, O.amax(w, O.BF16, O.BLK_2D))
     _assert_gpu_rows(Xq, ru, Aq, "X rows")
     _assert_gpu_bands(Wq, bands, Bq, "W bands")
-    Cref, Wref = O.gemm(Aq, Bq, entries=(ml, nl))
+    Cref, Wref = OB.gemm(Aq, Bq, entries=(ml, nl))
     got = out_to_f64(Y)[mi, ni]
     check(got, Cref, Wref, True, "forward sampled")
 
@@ -189,7 +190,7 @@ def test_wgrad_20480x5120x8192_sampled(nv):
     Bq = _oracle_cols(x, nu, O.amax(x, O.BF16, O.COL_1D, hadamard=True, hadamard_seed=5200), 5101, 5200)
     _assert_gpu_rows(dYq, mu, Aq, "dY^T rows")
     _assert_gpu_rows(Xq, nu, Bq, "X^T rows")
-    Cref, Wref = O.gemm(Aq, Bq, entries=(ml, nl))
+    Cref, Wref = OB.gemm(Aq, Bq, entries=(ml, nl))
     check(out_to_f64(dW)[mi, ni], Cref, Wref, False, "wgrad sampled")
 
 
@@ -283,7 +284,7 @@ def test_gemm_swiglu_epilogue(nv, M, F, K, bmode):
     H = nv.nvfp4_gemm(q_to_device(A, nv), q_to_device(B, nv), out_dtype=torch.bfloat16,
                       epilogue=nv.NVFP4_EPI_SWIGLU)
     assert tuple(H.shape) == (M, F)
-    Cref, Wref = O.gemm(A, B)
+    Cref, Wref = OB.gemm(A, B)
     G_, U_ = Cref[:, :F], Cref[:, F:]
     err = np.abs(out_to_f64(H) - O.swiglu(G_, U_))
     tol = _swiglu_tol(G_, U_, Wref[:, :F], Wref[:, F:])
@@ -348,8 +349,8 @@ def test_moe_expert_forward_sampled(nv):
         _assert_gpu_bands(W1, bands, Bq, f"W1 bands of expert {g_}", row0=g_ * 2 * F, ts_index=g_)
         mi = np.repeat(np.arange(rows.size), cols.size)
         gl, ul = np.tile(local[:cols.size], rows.size), np.tile(local[cols.size:], rows.size)
-        Cg, Wg = O.gemm(Aq, Bq, entries=(mi, gl))
-        Cu, Wu = O.gemm(Aq, Bq, entries=(mi, ul))
+        Cg, Wg = OB.gemm(Aq, Bq, entries=(mi, gl))
+        Cu, Wu = OB.gemm(Aq, Bq, entries=(mi, ul))
         href = O.swiglu(Cg, Cu)
         tol = _swiglu_tol(Cg, Cu, Wg, Wu)
         got = Hh[np.repeat(rows, cols.size), np.tile(cols, rows.size)]
@@ -378,5 +379,5 @@ def test_moe_expert_forward_sampled(nv):
         Bq, bands, local = _oracle_bands(w2[g_], cols, O.amax(w2[g_], O.BF16, O.BLK_2D))
         _assert_gpu_bands(W2, bands, Bq, f"W2 bands of expert {g_}", row0=g_ * Hd, ts_index=g_)
         mi = np.repeat(rows, cols.size)
-        Cref, Wref = O.gemm(Hq, Bq, entries=(mi, np.tile(local, rows.size)))
+        Cref, Wref = OB.gemm(Hq, Bq, entries=(mi, np.tile(local, rows.size)))
         check(Yh[mi, np.tile(cols, rows.size)], Cref, Wref, True, f"down group {g_}")

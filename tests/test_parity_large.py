@@ -15,6 +15,7 @@ import pytest
 import torch
 
 import oracle as O
+from oracle import banded as OB
 import workloads as W
 from parity_utils import assert_q_equal, bf16_tensor_to_bits, gemm_tol, require_gpu
 
@@ -156,7 +157,7 @@ def test_gemm_output_past_2pow31_elements(nv):
     assert_q_equal(O.QTensor(Bq.codes.index_select(0, rb).cpu().numpy(),
                              Bq.scales.index_select(0, torch.from_numpy(bands).cuda()).cpu().numpy(),
                              float(Bq.tensor_scale[0].item()), 16 * bands.size, K, O.SCALE_2D), Br, "B bands")
-    Cref, Wref = O.gemm(Ar, Br, entries=(ml, nl))
+    Cref, Wref = OB.gemm(Ar, Br, entries=(ml, nl))
     tol = gemm_tol(Cref, Wref, False)
     bad = np.abs(got - Cref) > tol
     assert not bad.any(), f"{bad.sum()} entries out of tolerance, first at {(mi[bad][0], ni[bad][0])}"

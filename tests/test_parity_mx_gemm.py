@@ -32,6 +32,7 @@ import torch
 
 import oracle as O
 import workloads as W
+from oracle import banded as OB
 from parity_utils import bf16_tensor_to_bits, require_gpu
 
 pytestmark = pytest.mark.gpu
@@ -89,11 +90,11 @@ def check(nv, qa, qb, bf16=False, entries=None, exact=False, what="", accum=NATI
     M, N, K = qa.rows, qb.rows, qa.cols
     if entries is None:
         mi, ni = (a.ravel() for a in np.meshgrid(np.arange(M), np.arange(N), indexing="ij"))
-        Cref, Wref = O.mx_gemm(qa, qb)
+        Cref, Wref = OB.mx_gemm(qa, qb)
         Cref, Wref = Cref.ravel(), Wref.ravel()
     else:
         mi, ni = entries
-        Cref, Wref = O.mx_gemm(qa, qb, entries=(mi, ni))
+        Cref, Wref = OB.mx_gemm(qa, qb, entries=(mi, ni))
     got = G[mi, ni]
     if exact:
         ref = Cref.astype(np.float32).astype(np.float64) if not bf16 else Cref
@@ -110,7 +111,7 @@ def check(nv, qa, qb, bf16=False, entries=None, exact=False, what="", accum=NATI
 
 
 def mxq(x, elem, seed=0, rnd=O.RNE):
-    return O.mx_quantize(np.ascontiguousarray(x, dtype=np.float32), O.F32, O.ROW_1D, elem, rnd, seed=seed)
+    return OB.mx_quantize(np.ascontiguousarray(x, dtype=np.float32), O.F32, elem, rnd, seed=seed)
 
 
 @pytest.mark.parametrize("accum", ACCUMS)
