@@ -278,70 +278,68 @@ __global__ void __launch_bounds__(256) k_mx_col(const T* __restrict__ x, int64_t
 // ============================================================ dequantize
 // y = value(code) * 2^(byte - 127), one binary32 rounding (ldexp; exact
 // unless the result leaves the normal range), BF16 output rounded to nearest
-// even from that binary32 value.  A lane expands 16 elements (16 E4M3 code
-// bytes or 8 E2M1 ones) of each of 4 rows; the 64 lanes of a wave cover 1024
-// elements of a row.  (E2M1 with 32 elements per lane, the same 16-byte
-// loads, ran at half the workgroups and took 44 instead of 35 us on 8192^2.)
+// even from that binary32 value.  A lane expands 8 elements (8 E4M3 code
+// bytes or 4 E2M1 ones) of each of 8 rows; the 64 lanes of a wave cover 512
+// elements of a row, so each wave-wide store writes 1 KiB (bf16) of a row
+// contiguously.  (With 16 elements per lane its two 16-byte stores each
+// covered every other 16 bytes of 2 KiB: 8192^2 to BF16, alternating builds on
+// one box, E2M1 44.2 -> 35.3 us, E4M3 42.4 -> 40.2 us.)
 template <int ELEM, typename TOut>
 __global__ void __launch_bounds__(256) k_mx_dequant(const uint8_t* __restrict__ codes,
                                                     const uint8_t* __restrict__ scales, int64_t rows,
                                                     int64_t cols, TOut* __restrict__ y, int64_t ld) {
-    constexpr int EPL = 16;                           // elements per lane
-    constexpr int CB = ELEM == kMxE4M3 ? 16 : 8;      // their code bytes
+    constexpr int EPL = 8;                            // elements per lane
+    constexpr int CB = ELEM == kMxE4M3 ? 8 : 4;       // their code bytes
     const int64_t row_bytes = ELEM == kMxE4M3 ? cols : cols / 2;
     const int64_t b = (int64_t)blockIdx.x * 64 + (threadIdx.x & 63);
     if (b >= cols / EPL) return;
-    const int64_t nrg = (rows + 15) / 16;
+    const int64_t nrg = (rows + 31) / 32;
     for (int64_t rg = blockIdx.y; rg < nrg; rg += gridDim.y) {
-        const int64_t r0 = rg * 16 + 4 * (threadIdx.x >> 6);
-        uint32_t cw[4][4];
-        int sx[4];
+        const int64_t r0 = rg * 32 + 8 * (threadIdx.x >> 6);
+        uint32_t cw[8][2];
+        int sx[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 8; ++i) {
             const int64_t r = r0 + i < rows ? r0 + i : rows - 1;  // clamped; never stored
-            if constexpr (CB == 16) {
-                const uint4 q = *reinterpret_cast<const uint4*>(codes + r * row_bytes + CB * b);
-                cw[i][0] = q.x; cw[i][1] = q.y; cw[i][2] = q.z; cw[i][3] = q.w;
-            } else {
+            if constexpr (CB == 8) {
                 const uint2 q = *reinterpret_cast<const uint2*>(codes + r * row_bytes + CB * b);
-                cw[i][0] = q.x; cw[i][1] = q.y; cw[i][2] = 0u; cw[i][3] = 0u;
+                cw[i][0] = q.x; cw[i][1] = q.y;
+            } else {
+                cw[i][0] = *reinterpret_cast<const uint32_t*>(codes + r * row_bytes + CB * b);
+                cw[i][1] = 0u;
             }
             sx[i] = (int)scales[r * (cols / 32) + (b * EPL) / 32] - 127;
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 8; ++i) {
             const int64_t r = r0 + i;
             if (r >= rows) break;
-            const uint32_t* wv = cw[i];
             float o[EPL];
 #pragma unroll
             for (int k = 0; k < EPL / 2; ++k) {
                 float2 p;
                 if constexpr (ELEM == kMxE4M3) {
                     if (k & 1) {
-                        const auto f = __builtin_amdgcn_cvt_pk_f32_fp8((int)wv[k >> 1], true);
+                        const auto f = __builtin_amdgcn_cvt_pk_f32_fp8((int)cw[i][k >> 1], true);
                         p = make_float2(f[0], f[1]);
                     } else {
-                        const auto f = __builtin_amdgcn_cvt_pk_f32_fp8((int)wv[k >> 1], false);
+                        const auto f = __builtin_amdgcn_cvt_pk_f32_fp8((int)cw[i][k >> 1], false);
                         p = make_float2(f[0], f[1]);
                     }
                 } else {
-                    p = e2m1x2_unpack(wv[k >> 2], k & 3);
+                    p = e2m1x2_unpack(cw[i][0], k);
                 }
                 o[2 * k] = __builtin_amdgcn_ldexpf(p.x, sx[i]);
                 o[2 * k + 1] = __builtin_amdgcn_ldexpf(p.y, sx[i]);
             }
             TOut* qp = y + r * ld + b * EPL;
             if constexpr (sizeof(TOut) == 2) {
-                uint4* qq = reinterpret_cast<uint4*>(qp);
-#pragma unroll
-                for (int j = 0; j < EPL / 8; ++j)
-                    qq[j] = make_uint4(pack_bf16x2(o[8 * j], o[8 * j + 1]), pack_bf16x2(o[8 * j + 2], o[8 * j + 3]),
-                                       pack_bf16x2(o[8 * j + 4], o[8 * j + 5]), pack_bf16x2(o[8 * j + 6], o[8 * j + 7]));
+                *reinterpret_cast<uint4*>(qp) = make_uint4(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]),
+                                                           pack_bf16x2(o[4], o[5]), pack_bf16x2(o[6], o[7]));
             } else {
                 float4* qq = reinterpret_cast<float4*>(qp);
-#pragma unroll
-                for (int j = 0; j < EPL / 4; ++j) qq[j] = make_float4(o[4 * j], o[4 * j + 1], o[4 * j + 2], o[4 * j + 3]);
+                qq[0] = make_float4(o[0], o[1], o[2], o[3]);
+                qq[1] = make_float4(o[4], o[5], o[6], o[7]);
             }
         }
     }
@@ -393,7 +391,7 @@ hipError_t launch_mx_quantize(const void* x, bool bf16, int64_t rows, int64_t co
 hipError_t launch_mx_dequantize(const uint8_t* codes, const uint8_t* scales, int elem, int64_t rows,
                                 int64_t cols, void* y, bool bf16, int64_t ld, hipStream_t s) {
     if (rows == 0 || cols == 0) return hipSuccess;
-    dim3 g((unsigned)mx_cdiv(cols / 16, 64), mx_grid_y(mx_cdiv(rows, 16)));
+    dim3 g((unsigned)mx_cdiv(cols / 8, 64), mx_grid_y(mx_cdiv(rows, 32)));
 #define NVFP4_MXDQ(E, TO) \
     hipLaunchKernelGGL((k_mx_dequant<E, TO>), g, dim3(256), 0, s, codes, scales, rows, cols, static_cast<TO*>(y), ld)
     if (elem == kMxE4M3) {

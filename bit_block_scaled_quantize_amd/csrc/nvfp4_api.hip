@@ -326,7 +326,7 @@ nvfp4_status nvfp4_mx_dequantize(const nvfp4_mx_tensor* q, void* y, nvfp4_dtype 
     if (!empty && (!y || !q->codes || !q->scales)) return NVFP4_ERR_NULL;
     if (!aligned(y, 16) || (ld * (int64_t)dtype_size(dt)) % 16 || !aligned(q->codes, 16))
         return NVFP4_ERR_ALIGN;
-    if (cdiv(q->cols / 16, 64) > 0x7FFFFFFF) return NVFP4_ERR_UNSUPPORTED;
+    if (cdiv(q->cols / 8, 64) > 0x7FFFFFFF) return NVFP4_ERR_UNSUPPORTED;
     hipError_t e = launch_mx_dequantize(q->codes, q->scales, q->elem == NVFP4_MX_E4M3 ? kMxE4M3 : kMxE2M1,
                                         q->rows, q->cols, y, dt == NVFP4_BF16, ld,
                                         static_cast<hipStream_t>(stream));
