@@ -285,37 +285,53 @@ __device__ __forceinline__ uint32_t sr_seed(uint32_t word, int high_half) {
 // encode).  FOLD computes z = ceil(fl(|t| * R23)) with R23 = R * 2^23, one
 // multiply instead of two; the caller guarantees that this equals
 // ceil(fl(|t| * R) * 2^23).
+typedef float sr_f2_t __attribute__((ext_vector_type(2)));
+
+// The SR FP4 convert writing only byte SEL of acc (its op_sel bits 2 and 3
+// select the destination byte; the other three bytes keep their value).
+// Written as asm with acc tied in and out: the compiler's builtin for this
+// instruction treats the whole destination register as written.
+template <int SEL>
+__device__ __forceinline__ void cvt_sr_fp4_byte(uint32_t& acc, sr_f2_t v, uint32_t seed, float scale) {
+    if constexpr (SEL == 0)
+        asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, %3" : "+v"(acc) : "v"(v), "v"(seed), "s"(scale));
+    else if constexpr (SEL == 1)
+        asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, %3 op_sel:[0,0,1,0]" : "+v"(acc) : "v"(v), "v"(seed), "s"(scale));
+    else if constexpr (SEL == 2)
+        asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, %3 op_sel:[0,0,0,1]" : "+v"(acc) : "v"(v), "v"(seed), "s"(scale));
+    else
+        asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, %3 op_sel:[0,0,1,1]" : "+v"(acc) : "v"(v), "v"(seed), "s"(scale));
+}
+
 template <bool FOLD>
 __device__ __forceinline__ uint32_t sr_word8(const float* p, float R, const uint32_t* wk) {
-    typedef float f2_t __attribute__((ext_vector_type(2)));
     const float R23 = R * 0x1p23f;
-    uint32_t ce[4], co[4];
+    // byte J of ev / od: code of element 2J / 2J + 1 in the low nibble (the
+    // high nibble, from the unspecified second slot, is masked off); every
+    // byte is written, so the registers start unspecified
+    uint32_t ev = __builtin_nondeterministic_value(0u), od = __builtin_nondeterministic_value(0u);
 #pragma unroll
     for (int J = 0; J < 4; ++J) {
         const float z0 = FOLD ? __builtin_ceilf(fabsf(p[2 * J]) * R23)
                               : __builtin_ceilf((fabsf(p[2 * J]) * R) * 0x1p23f);
         const float z1 = FOLD ? __builtin_ceilf(fabsf(p[2 * J + 1]) * R23)
                               : __builtin_ceilf((fabsf(p[2 * J + 1]) * R) * 0x1p23f);
-        // the second slot's value is left unspecified: its nibble is masked off
         const float any = __builtin_nondeterministic_value(z0);
-        const f2_t e = {__uint_as_float(__float_as_uint(z0) | (__float_as_uint(p[2 * J]) & 0x80000000u)), any};
-        const f2_t o = {__uint_as_float(__float_as_uint(z1) | (__float_as_uint(p[2 * J + 1]) & 0x80000000u)), any};
-        ce[J] = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, e, sr_seed(wk[J], 0), 0x1p23f, 0);
-        co[J] = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, o, sr_seed(wk[J], 1), 0x1p23f, 0);
+        const sr_f2_t e = {__uint_as_float(__float_as_uint(z0) | (__float_as_uint(p[2 * J]) & 0x80000000u)), any};
+        const sr_f2_t o = {__uint_as_float(__float_as_uint(z1) | (__float_as_uint(p[2 * J + 1]) & 0x80000000u)), any};
+        switch (J) {
+            case 0: cvt_sr_fp4_byte<0>(ev, e, sr_seed(wk[J], 0), 0x1p23f); cvt_sr_fp4_byte<0>(od, o, sr_seed(wk[J], 1), 0x1p23f); break;
+            case 1: cvt_sr_fp4_byte<1>(ev, e, sr_seed(wk[J], 0), 0x1p23f); cvt_sr_fp4_byte<1>(od, o, sr_seed(wk[J], 1), 0x1p23f); break;
+            case 2: cvt_sr_fp4_byte<2>(ev, e, sr_seed(wk[J], 0), 0x1p23f); cvt_sr_fp4_byte<2>(od, o, sr_seed(wk[J], 1), 0x1p23f); break;
+            default: cvt_sr_fp4_byte<3>(ev, e, sr_seed(wk[J], 0), 0x1p23f); cvt_sr_fp4_byte<3>(od, o, sr_seed(wk[J], 1), 0x1p23f); break;
+        }
     }
-    // perm(b, a, lo2): byte 0 of a -> byte 0, byte 0 of b -> byte 1, bytes 2 and 3 zero
-    const uint32_t lo2 = 0x0C0C0400u;
-    const uint32_t ev = (__builtin_amdgcn_perm(ce[1], ce[0], lo2) |
-                         (__builtin_amdgcn_perm(ce[3], ce[2], lo2) << 16)) & 0x0F0F0F0Fu;
-    const uint32_t od = (__builtin_amdgcn_perm(co[1], co[0], lo2) |
-                         (__builtin_amdgcn_perm(co[3], co[2], lo2) << 16)) & 0x0F0F0F0Fu;
-    return ev | (od << 4);
+    return (ev & 0x0F0F0F0Fu) | ((od << 4) & 0xF0F0F0F0u);
 }
 
 template <bool SR, int N, bool FOLD = false>
 __device__ __forceinline__ void encode(const float* v, BlockScale bs, float amax_b, const uint32_t* w,
                                        uint32_t* out) {
-    typedef float f2_t __attribute__((ext_vector_type(2)));
     const bool slow = SR ? !(amax_b * bs.R < 0x1p100f) : __builtin_isinf(bs.R);
     if (__builtin_expect(slow, 0)) {
 #pragma unroll

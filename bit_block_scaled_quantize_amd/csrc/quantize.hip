@@ -445,9 +445,7 @@ __device__ __forceinline__ void tile_row_blocks(const uint4 (&raw)[8], int64_t R
 #pragma unroll
             for (int e = CH; e < 8; ++e) v[e] = 0.0f;
             uint32_t w[1];
-            // no single-multiply SR path here: in the fused kernel it would
-            // raise register use past the 168 VGPRs of three waves per SIMD
-            encode<SR, 8, false>(v, bs[k + h], a[k + h], wd[h], w);
+            encode<SR, 8, sizeof(T) == 2>(v, bs[k + h], a[k + h], wd[h], w);
             uint8_t* dst = rcodes + rr * (cols / 2) + gc / 2;
             if (CH == 8) *reinterpret_cast<uint32_t*>(dst) = w[0];
             else *reinterpret_cast<uint16_t*>(dst) = (uint16_t)w[0];
@@ -506,8 +504,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) k
                                                     uint8_t* __restrict__ cscales,
                                                     float* __restrict__ cts, float* amax_out,
                                                     int xcd_group) {
-    constexpr int CH = ColTile<T>::CH, TWC = ColTile<T>::TWC, UE = ColTile<T>::UE,
-                  STRIDE = ColTile<T>::STRIDE;
+    constexpr int CH = ColTile<T>::CH, TWC = ColTile<T>::TWC, STRIDE = ColTile<T>::STRIDE;
     __shared__ __attribute__((aligned(16))) uint8_t tile[256 * STRIDE];
     const int t = threadIdx.x;
     const TileXY tl = xcd_tile(xcd_group);
