@@ -790,13 +790,18 @@ __global__ void __launch_bounds__(256) k_requant_col(const uint8_t* __restrict__
 
     const int sw = (t >> 4) & 15;
     uint8_t* rowp = tile + t * STRIDE;
-#pragma unroll
+    // a rolled loop: unrolled, the eight copies of the column encoder made the
+    // kernel larger than the instruction cache
+#pragma unroll 1
     for (int k = 0; k < kReqTiles; ++k) {
         const int64_t T0 = Cb + 32 * k;
         if (T0 >= cols) break;  // uniform across the workgroup
         if (k > 0) __syncthreads();  // the previous tile's column reads are done
         const uint4 w = *reinterpret_cast<const uint4*>(raw + t * 128 + 16 * (k ^ (t & 7)));
-        const uint32_t sw2 = sv[k >> 1] >> (16 * (k & 1));
+        // (selects, not a dynamically indexed register array)
+        const int kp = k >> 1;
+        const uint32_t swd = kp == 0 ? sv[0] : kp == 1 ? sv[1] : kp == 2 ? sv[2] : sv[3];
+        const uint32_t sw2 = swd >> (16 * (k & 1));
         const float m0 = e4m3_value(sw2 & 0xFFu), m1 = e4m3_value((sw2 >> 8) & 0xFFu);
         float v[32];
         dequant8(w.x, m0, st_in, v);
