@@ -29,7 +29,8 @@
 // significant bits, small exponent spread) come out exact.  The tolerance of
 // the parity tests follows from this measured behaviour.
 //
-// Geometry and pipeline: a 256-thread workgroup owns a 256 x 256 output tile,
+// Ring kernel (any K % 64 == 0; the full-line kernel further down serves
+// K % 1024 == 0): a 256-thread workgroup owns a 256 x 256 output tile,
 // its four waves a 2 x 2 grid of 128 x 128 wave tiles (4 x 4 MFMAs per 64-wide
 // K step).  Raw codes and scale bytes of both operands travel from global
 // memory to LDS by global_load_lds (lane i of a load lands at base + size i)
@@ -66,7 +67,6 @@ typedef __attribute__((address_space(3))) void lmem_t;
 
 constexpr int kMxTile = 256;  // tile rows of A and of B
 constexpr int kMxStepK = 64;  // K elements per step (one MFMA K)
-constexpr int kMxRing = 4;
 
 template <int ELEM>
 struct MxGeo {
@@ -558,7 +558,7 @@ __global__ void __launch_bounds__(256, 1) k_mx_gemm_exact(MxGemmArgs p) {
     // C = 2^(R_A[m] + R_B[n] - 254) * acc (exact unless C leaves binary32's
     // normal range); accumulator r of tile (i, j): row 32 i + 8 (r / 4) + 4 h +
     // r % 4, column 32 j + l32 of the wave tile
-    const int64_t mw = m0 + arow0, nw = n0 + brow0;
+    const int64_t nw = n0 + brow0;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -583,23 +583,26 @@ __global__ void __launch_bounds__(256, 1) k_mx_gemm_exact(MxGemmArgs p) {
 
 // ============================================================ full-line kernel
 // For K % 1024 == 0 with 16-byte-aligned scale rows (every benchmarked shape):
-// the same tile and MFMA schedule, but the memory traffic shaped for gfx950's
+// the ring kernel's 256 x 256 tile with the memory traffic shaped for gfx950's
 // caches, where each distinct cache line a wave-wide load touches costs
-// about the same whatever part of it is used:
-//   - a ring slot holds 128 bytes of every tile row (a whole line): 2 K steps
-//     of E4M3 or 4 of E2M1 ("a chunk"); two slots, the next chunk's loads in
-//     flight while the current chunk is consumed;
+// about the same whatever part of it is used, and eight waves:
+//   - a slot holds 128 bytes of every tile row (a whole line): 2 K steps of
+//     E4M3 or 4 of E2M1 ("a chunk"); two slots, the next chunk's loads in
+//     flight while the current chunk is consumed; a chunk's last step opens
+//     with the wait and barrier that hand its slot to the loads of the chunk
+//     after next;
 //   - scale bytes arrive 16 per row (8 K steps) per load, one group ahead,
-//     into two small buffers, from which each step reads its lane's 8 bytes
-//     for the next step, one after each of its first 8 MFMAs;
-//   - the next step's fragments are read one 16-byte piece after each MFMA
-//     (E4M3: 16 pieces; E2M1: 8, after every other MFMA), so the LDS reads
-//     spread over the whole step instead of queueing behind one another;
-//     a chunk's last step opens with the wait and barrier that hand its
-//     slot to the loads of the chunk after next;
+//     into two small buffers;
 //   - 16-byte chunk c of slot row r sits at chunk c ^ (r % 8) ^ ((r / 8) % 4)
 //     (bits 0..4 of r), which spreads the fragment reads over every bank for
-//     8 lanes (32 banks) and for 16 lanes (64 banks).
+//     8 lanes (32 banks) and for 16 lanes (64 banks);
+//   - eight waves, two per SIMD, in a 2 x 4 grid of 128 x 64 wave tiles (4 x 2
+//     MFMA tiles, 128 accumulators per lane): while one wave of a SIMD waits
+//     for its LDS reads or at the barrier the other issues MFMAs.  Against
+//     four waves of 128 x 128 (one per SIMD, fragments double-buffered),
+//     8192^3 ran 0.552 -> 0.464 ms with E4M3 and 0.307 -> 0.287 ms with E2M1,
+//     20480 x 5120 x 8192 0.939 -> 0.788 and 0.534 -> 0.494 ms, outputs bit
+//     for bit the same (alternating A/B on one box).
 // The body is unrolled over 16 K steps (8 E4M3 or 4 E2M1 chunks, 2 scale
 // groups), so every slot and buffer has a static name and there is no
 // padding.
@@ -622,115 +625,122 @@ struct MxFullSrc {
     uint32_t sa, sb;
 };
 
+// Fragments are held once (no second register set): the next step's fragment
+// of an A tile is read right after the step's last MFMA on that tile, a B
+// fragment after its last MFMA, with the MFMAs ordered B tile by B tile so
+// that each read has at least three MFMAs of the step after to land.  Each
+// wave loads 32 rows of each operand per chunk and, per scale group, the 16
+// scale bytes of 32 A rows (lanes 0..31) and of 32 B rows (lanes 32..63):
+// wave w's 1 KiB of a group buffer holds A rows 32 w .. 32 w + 31, then B rows
+// 32 w .. 32 w + 31.
+// (each 32-bit lane offset passes through an empty asm statement at the load:
+// the compiler then cannot hoist the 64-bit per-lane addresses out of the
+// loop, where they would hold two registers each, and forms the address as a
+// scalar base plus the offset)
 template <int ELEM>
-__device__ __forceinline__ void mx_full_chunk_load(const MxFullSrc& src, int64_t chunk, uint8_t* slot, int w) {
+__device__ __forceinline__ void mx_full8_chunk_load(const MxFullSrc& src, int64_t chunk, uint8_t* slot, int w) {
     using F = MxFull<ELEM>;
     const uint8_t* ac = src.ac + chunk * 128;
     const uint8_t* bc = src.bc + chunk * 128;
 #pragma unroll
-    for (int t = 0; t < 8; ++t)
-        __builtin_amdgcn_global_load_lds((gmem_t*)(ac + src.a[t]), (lmem_t*)(slot + (64 * w + 8 * t) * 128), 16, 0, 0);
+    for (int t = 0; t < 4; ++t) {
+        uint32_t o = src.a[t];
+        asm volatile("" : "+v"(o));
+        __builtin_amdgcn_global_load_lds((gmem_t*)(ac + o), (lmem_t*)(slot + (32 * w + 8 * t) * 128), 16, 0, 0);
+    }
 #pragma unroll
-    for (int t = 0; t < 8; ++t)
-        __builtin_amdgcn_global_load_lds((gmem_t*)(bc + src.b[t]), (lmem_t*)(slot + F::CODES + (64 * w + 8 * t) * 128),
-                                         16, 0, 0);
-}
-
-template <int ELEM>
-__device__ __forceinline__ void mx_full_scale_load(const MxFullSrc& src, int64_t group, uint8_t* buf, int w) {
-    using F = MxFull<ELEM>;
-    __builtin_amdgcn_global_load_lds((gmem_t*)(src.as + group * 16 + src.sa), (lmem_t*)(buf + 64 * w * 16), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds((gmem_t*)(src.bs + group * 16 + src.sb), (lmem_t*)(buf + F::SCB + 64 * w * 16),
-                                     16, 0, 0);
-}
-
-// Fragments of K step t of a chunk (A and B, tiles 0..3).
-template <int ELEM>
-__device__ __forceinline__ void mx_full_frags(const uint8_t* slot, int t, int rowa, int rowb, int sw, int h, v8i_t (&a)[4],
-                                              v8i_t (&b)[4]) {
-    using F = MxFull<ELEM>;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint8_t* ra = slot + (rowa + 32 * i) * 128;
-        const uint8_t* rb = slot + F::CODES + (rowb + 32 * i) * 128;
-        if constexpr (ELEM == kMxE4M3) {
-            const int clo = (4 * t + h) ^ sw, chi = (4 * t + 2 + h) ^ sw;
-            const v4i_t alo = lds16(ra + 16 * clo), ahi = lds16(ra + 16 * chi);
-            const v4i_t blo = lds16(rb + 16 * clo), bhi = lds16(rb + 16 * chi);
-            a[i] = v8i_t{alo[0], alo[1], alo[2], alo[3], ahi[0], ahi[1], ahi[2], ahi[3]};
-            b[i] = v8i_t{blo[0], blo[1], blo[2], blo[3], bhi[0], bhi[1], bhi[2], bhi[3]};
-        } else {
-            const int c = (2 * t + h) ^ sw;
-            const v4i_t aq = lds16(ra + 16 * c), bq = lds16(rb + 16 * c);
-            a[i] = v8i_t{aq[0], aq[1], aq[2], aq[3], 0, 0, 0, 0};
-            b[i] = v8i_t{bq[0], bq[1], bq[2], bq[3], 0, 0, 0, 0};
-        }
+    for (int t = 0; t < 4; ++t) {
+        uint32_t o = src.b[t];
+        asm volatile("" : "+v"(o));
+        __builtin_amdgcn_global_load_lds((gmem_t*)(bc + o), (lmem_t*)(slot + F::CODES + (32 * w + 8 * t) * 128), 16,
+                                         0, 0);
     }
 }
 
-// One piece of the fragments of K step t: E4M3 pieces 0..15 (A then B; tile
-// (o & 7) >> 1, low or high 16 bytes by o & 1), E2M1 pieces 0..7 (A then B,
-// tile o & 3).
+// (A lanes and B lanes as two loads under complementary lane masks, each a
+// scalar base plus the lane's 32-bit offset)
+__device__ __forceinline__ void mx_full8_scale_load(const uint8_t* as, const uint8_t* bs, uint32_t so, int lane,
+                                                    int64_t group, uint8_t* buf, int w) {
+    uint32_t o = so;
+    asm volatile("" : "+v"(o));
+    if (lane < 32)
+        __builtin_amdgcn_global_load_lds((gmem_t*)(as + group * 16 + o), (lmem_t*)(buf + 1024 * w), 16, 0, 0);
+    else
+        __builtin_amdgcn_global_load_lds((gmem_t*)(bs + group * 16 + o), (lmem_t*)(buf + 1024 * w), 16, 0, 0);
+}
+
+// A lane's LDS byte offsets for the 8-wave kernel: code piece q of a fragment
+// row inside a slot (E4M3: q = 2 t + hi, t the step of the chunk, hi the upper
+// 16 bytes; E2M1: q = t) for A (tile 0 of the wave; tile i adds 4096 i) and
+// for B, and its scale byte inside a group buffer (A tile 0 / B tile 0, step
+// 0; tile i adds 1024 i, step g adds 2 g).  They are formed once and made
+// opaque to the compiler, so that every fragment read is one of them plus an
+// immediate instead of a register of its own per tile, step and slot.
+struct MxFull8Offsets {
+    uint32_t a[4], b[4];
+    uint32_t sa, sb;
+};
+
 template <int ELEM>
-__device__ __forceinline__ void mx_full_frag_piece(const uint8_t* slot, int t, int rowa, int rowb, int sw, int h,
-                                                   int o, v8i_t (&a)[4], v8i_t (&b)[4]) {
+__device__ __forceinline__ MxFull8Offsets mx_full8_offsets(int wm, int wn, int l32, int h) {
     using F = MxFull<ELEM>;
+    MxFull8Offsets o;
+    const int sw = mx_full_swz(l32);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int c = ELEM == kMxE4M3 ? (4 * (q >> 1) + 2 * (q & 1) + h) : (2 * q + h);
+        o.a[q] = (uint32_t)((128 * wm + l32) * 128 + 16 * (c ^ sw));
+        o.b[q] = (uint32_t)(F::CODES + (64 * wn + l32) * 128 + 16 * (c ^ sw));
+        asm volatile("" : "+v"(o.a[q]));
+        asm volatile("" : "+v"(o.b[q]));
+    }
+    o.sa = (uint32_t)(1024 * (4 * wm) + 16 * l32 + h);
+    o.sb = (uint32_t)(1024 * (2 * wn) + 512 + 16 * l32 + h);
+    asm volatile("" : "+v"(o.sa));
+    asm volatile("" : "+v"(o.sb));
+    return o;
+}
+
+// Fragment f of the next step (f = 0..3: A tile f, 4..5: B tile f - 4) from
+// step t of the slot, with its scale byte (step g of the group buffer).
+template <int ELEM>
+__device__ __forceinline__ void mx_full8_read(const uint8_t* slot, const uint8_t* sbuf, int t, int g, int f,
+                                              const MxFull8Offsets& o, v8i_t (&a)[4], v8i_t (&b)[2], int (&sa)[4],
+                                              int (&sb)[2]) {
+    const bool isb = f >= 4;
+    const int i = isb ? f - 4 : f;
+    v8i_t v;
     if constexpr (ELEM == kMxE4M3) {
-        const bool isb = o >= 8;
-        const int i = (o & 7) >> 1, hi = o & 1;
-        const uint8_t* r = isb ? slot + F::CODES + (rowb + 32 * i) * 128 : slot + (rowa + 32 * i) * 128;
-        const int c = (4 * t + 2 * hi + h) ^ sw;
-        const v4i_t q = lds16(r + 16 * c);
-        v8i_t& d = isb ? b[i] : a[i];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) d[4 * hi + e] = q[e];
+        const uint32_t lo = isb ? o.b[2 * t] : o.a[2 * t], hi = isb ? o.b[2 * t + 1] : o.a[2 * t + 1];
+        const v4i_t ql = lds16(slot + lo + 4096 * i), qh = lds16(slot + hi + 4096 * i);
+        v = v8i_t{ql[0], ql[1], ql[2], ql[3], qh[0], qh[1], qh[2], qh[3]};
     } else {
-        const bool isb = o >= 4;
-        const int i = o & 3;
-        const uint8_t* r = isb ? slot + F::CODES + (rowb + 32 * i) * 128 : slot + (rowa + 32 * i) * 128;
-        const int c = (2 * t + h) ^ sw;
-        const v4i_t q = lds16(r + 16 * c);
-        v8i_t& d = isb ? b[i] : a[i];
-        d = v8i_t{q[0], q[1], q[2], q[3], 0, 0, 0, 0};
+        const uint32_t off = isb ? o.b[t] : o.a[t];
+        const v4i_t q = lds16(slot + off + 4096 * i);
+        v = v8i_t{q[0], q[1], q[2], q[3], 0, 0, 0, 0};
     }
-}
-
-// Scale bytes of K step g (0..7) of a group for the lane's 4 A and 4 B rows:
-// byte 2 g + h of each row's 16.
-template <int ELEM>
-__device__ __forceinline__ void mx_full_scales(const uint8_t* buf, int g, int rowa, int rowb, int h, int (&sa)[4],
-                                               int (&sb)[4]) {
-    using F = MxFull<ELEM>;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        sa[i] = buf[(rowa + 32 * i) * 16 + 2 * g + h];
-        sb[i] = buf[F::SCB + (rowb + 32 * i) * 16 + 2 * g + h];
+    const int sbyte = sbuf[(isb ? o.sb : o.sa) + 1024 * i + 2 * g];
+    if (isb) {
+        b[i] = v;
+        sb[i] = sbyte;
+    } else {
+        a[i] = v;
+        sa[i] = sbyte;
     }
-}
-
-// Scale byte q (0..3: A rows, 4..7: B rows) of K step g of a group.
-template <int ELEM>
-__device__ __forceinline__ void mx_full_scale_piece(const uint8_t* buf, int g, int rowa, int rowb, int h, int q,
-                                                    int (&sa)[4], int (&sb)[4]) {
-    using F = MxFull<ELEM>;
-    if (q < 4) sa[q] = buf[(rowa + 32 * q) * 16 + 2 * g + h];
-    else sb[q - 4] = buf[F::SCB + (rowb + 32 * (q - 4)) * 16 + 2 * g + h];
 }
 
 template <int ELEM, bool OUT_BF16>
-__global__ void __launch_bounds__(256, 1) k_mx_gemm_full(MxGemmArgs p) {
+__global__ void __launch_bounds__(512, 1) k_mx_gemm_full8(MxGemmArgs p) {
     using F = MxFull<ELEM>;
     constexpr int SPC = F::SPC;
     __shared__ __attribute__((aligned(16))) uint8_t slot0[2 * F::CODES];
     __shared__ __attribute__((aligned(16))) uint8_t slot1[2 * F::CODES];
     __shared__ __attribute__((aligned(16))) uint8_t scb0[2 * F::SCB];
     __shared__ __attribute__((aligned(16))) uint8_t scb1[2 * F::SCB];
+    static_assert(2 * F::SCB == 8 * 1024, "scale group buffer: 1 KiB per wave");
     const int tid = threadIdx.x;
-    // the wave index is uniform: held in a scalar register, the LDS
-    // destinations of the ring loads need no vector registers
-    // (& 3: the compiler then knows every LDS offset below stays inside its slot)
-    const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6) & 3;
-    const int wm = w >> 1, wn = w & 1;
+    const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6) & 7;
+    const int wm = w >> 2, wn = w & 3;
     const int h = lane >> 5, l32 = lane & 31;
     const int64_t M = p.M, N = p.N, K = p.K;
     const int64_t m0 = (int64_t)blockIdx.y * kMxTile, n0 = (int64_t)blockIdx.x * kMxTile;
@@ -739,103 +749,99 @@ __global__ void __launch_bounds__(256, 1) k_mx_gemm_full(MxGemmArgs p) {
     MxFullSrc src;
     src.ac = p.ac + m0 * kb;
     src.bc = p.bc + n0 * kb;
-    src.as = p.as + m0 * ks;
-    src.bs = p.bs + n0 * ks;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-        const int r = 64 * w + 8 * t + (lane >> 3);
+    for (int t = 0; t < 4; ++t) {
+        const int r = 32 * w + 8 * t + (lane >> 3);
         const int c = (lane & 7) ^ mx_full_swz(r);  // the swizzle is an involution
         src.a[t] = (uint32_t)((min(m0 + r, M - 1) - m0) * kb + 16 * c);
         src.b[t] = (uint32_t)((min(n0 + r, N - 1) - n0) * kb + 16 * c);
     }
-    src.sa = (uint32_t)((min(m0 + 64 * w + lane, M - 1) - m0) * ks);
-    src.sb = (uint32_t)((min(n0 + 64 * w + lane, N - 1) - n0) * ks);
+    // this lane's scale row: A row 32 w + lane (lanes 0..31), B row 32 w + lane - 32,
+    // as an offset from the tile's first row
+    const uint8_t* s_as = p.as + m0 * ks;
+    const uint8_t* s_bs = p.bs + n0 * ks;
+    const uint32_t so = (uint32_t)(lane < 32 ? (min(m0 + 32 * w + lane, M - 1) - m0) * ks
+                                             : (min(n0 + 32 * w + (lane - 32), N - 1) - n0) * ks);
 
-    v16f_t acc[4][4];
+    v16f_t acc[4][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    const int rowa = 128 * wm + l32, rowb = 128 * wn + l32;
-    const int sw = mx_full_swz(l32);
-    const int64_t nchunks = K / (64 * SPC), ngroups = K / 512, nsteps = K / 64;
-    auto cclamp = [&](int64_t c) { return c < nchunks ? c : nchunks - 1; };
-    auto gclamp = [&](int64_t g) { return g < ngroups ? g : ngroups - 1; };
+    const MxFull8Offsets off = mx_full8_offsets<ELEM>(wm, wn, l32, h);
+    // (32-bit step, chunk and group counts: K < 2^31)
+    const int nchunks = (int)(K / (64 * SPC)), ngroups = (int)(K / 512), nsteps = (int)(K / 64);
+    auto cclamp = [&](int c) { return c < nchunks ? c : nchunks - 1; };
+    auto gclamp = [&](int g) { return g < ngroups ? g : ngroups - 1; };
 
     // prologue: scale groups 0 and 1, chunks 0 and 1 (K >= 1024, so all exist)
-    mx_full_scale_load<ELEM>(src, 0, scb0, w);
-    mx_full_scale_load<ELEM>(src, 1, scb1, w);
-    mx_full_chunk_load<ELEM>(src, 0, slot0, w);
-    mx_full_chunk_load<ELEM>(src, 1, slot1, w);
-    __builtin_amdgcn_s_waitcnt(mx_vmcnt_at_most(16));  // all but chunk 1
+    mx_full8_scale_load(s_as, s_bs, so, lane, 0, scb0, w);
+    mx_full8_scale_load(s_as, s_bs, so, lane, 1, scb1, w);
+    mx_full8_chunk_load<ELEM>(src, 0, slot0, w);
+    mx_full8_chunk_load<ELEM>(src, 1, slot1, w);
+    __builtin_amdgcn_s_waitcnt(mx_vmcnt_at_most(8));  // all but chunk 1
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
 
-    v8i_t fa[2][4], fb[2][4];
-    int sa[2][4], sb[2][4];
-    mx_full_scales<ELEM>(scb0, 0, rowa, rowb, h, sa[0], sb[0]);
-    mx_full_frags<ELEM>(slot0, 0, rowa, rowb, sw, h, fa[0], fb[0]);
+    v8i_t fa[4], fb[2];
+    int sa[4], sb[2];
+#pragma unroll
+    for (int f = 0; f < 6; ++f) mx_full8_read<ELEM>(slot0, scb0, 0, 0, f, off, fa, fb, sa, sb);
 
-    for (int64_t it = 0; it < nsteps; it += 16) {
-        const int64_t chunk0 = it / SPC, group0 = it / 8;
+    for (int it = 0; it < nsteps; it += 16) {
+        const int chunk0 = it / SPC, group0 = it / 8;
 #pragma unroll
         for (int s = 0; s < 16; ++s) {
-            const int cc = s / SPC, t = s % SPC, g = s % 8, cur = s & 1;
+            const int cc = s / SPC, t = s % SPC, g = s % 8;
             uint8_t* slot = (cc & 1) ? slot1 : slot0;
             uint8_t* other = (cc & 1) ? slot0 : slot1;
             uint8_t* gbuf = (s / 8) ? scb1 : scb0;  // this step's scale group
+            // where the next step's fragments and scale bytes are
+            const uint8_t* nslot = (t == SPC - 1) ? other : slot;
+            const int nt = (t == SPC - 1) ? 0 : t + 1;
+            const uint8_t* nsbuf = (g == 7) ? ((s == 7) ? scb1 : scb0) : gbuf;
+            const int ng = (g == 7) ? 0 : g + 1;
 #pragma unroll
-            for (int m = 0; m < 16; ++m) {
+            for (int m = 0; m < 8; ++m) {
                 if (m == 0) {
                     __builtin_amdgcn_sched_barrier(0);
                     if (t == SPC - 1) {
-                        // this step's fragments are in registers and the next
-                        // chunk's loads (and any scale group issued before
-                        // them) landed; after the barrier every wave has read
-                        // all of this chunk's slot
+                        // the next chunk's loads (and any scale group issued
+                        // before them) landed and this step's fragments are in
+                        // registers; after the barrier every wave has read all
+                        // of this chunk's slot
                         __builtin_amdgcn_s_waitcnt(mx_vmcnt_at_most(0) & mx_lgkmcnt_zero());
                         asm volatile("" ::: "memory");
                         __builtin_amdgcn_s_barrier();
                         asm volatile("" ::: "memory");
-                        if (g == 7) {
-                            // every wave is done with this group's buffer,
-                            // which takes the group after next
-                            mx_full_scale_load<ELEM>(src, gclamp(group0 + s / 8 + 2), gbuf, w);
-                        }
-                        mx_full_chunk_load<ELEM>(src, cclamp(chunk0 + cc + 2), slot, w);
+                        if (g == 7) mx_full8_scale_load(s_as, s_bs, so, lane, gclamp(group0 + s / 8 + 2), gbuf, w);
+                        mx_full8_chunk_load<ELEM>(src, cclamp(chunk0 + cc + 2), slot, w);
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 }
-                const int i = m >> 2, jj = m & 3;
-                acc[i][jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    fa[cur][i], fb[cur][jj], acc[i][jj], F::FMT, F::FMT, 0, sa[cur][i], 0, sb[cur][jj]);
-                // the next step's scale bytes (at a group's last step, from
-                // the other group's buffer), one after each of the first 8 MFMAs
-                if (m < 8) {
-                    if (g == 7) mx_full_scale_piece<ELEM>((s == 7) ? scb1 : scb0, 0, rowa, rowb, h, m, sa[cur ^ 1], sb[cur ^ 1]);
-                    else mx_full_scale_piece<ELEM>(gbuf, g + 1, rowa, rowb, h, m, sa[cur ^ 1], sb[cur ^ 1]);
-                }
-                // the next step's fragments, spread over this step's MFMAs
-                if (ELEM == kMxE4M3 || (m & 1) == 0) {
-                    const int o = ELEM == kMxE4M3 ? m : m >> 1;
-                    if (t == SPC - 1) mx_full_frag_piece<ELEM>(other, 0, rowa, rowb, sw, h, o, fa[cur ^ 1], fb[cur ^ 1]);
-                    else mx_full_frag_piece<ELEM>(slot, t + 1, rowa, rowb, sw, h, o, fa[cur ^ 1], fb[cur ^ 1]);
-                }
+                const int i = m & 3, j = m >> 2;
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    fa[i], fb[j], acc[i][j], F::FMT, F::FMT, 0, sa[i], 0, sb[j]);
+                // next step: B tile 0 after its last MFMA (m = 3), A tile i
+                // after its last (m = 4 + i), B tile 1 after m = 7
+                if (m == 3) mx_full8_read<ELEM>(nslot, nsbuf, nt, ng, 4, off, fa, fb, sa, sb);
+                if (m >= 4) mx_full8_read<ELEM>(nslot, nsbuf, nt, ng, m - 4, off, fa, fb, sa, sb);
+                if (m == 7) mx_full8_read<ELEM>(nslot, nsbuf, nt, ng, 5, off, fa, fb, sa, sb);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
     }
     __builtin_amdgcn_s_waitcnt(mx_vmcnt_at_most(0));
 
-    const int64_t mw = m0 + 128 * wm, nw = n0 + 128 * wn;
+    const int64_t mw = m0 + 128 * wm, nw = n0 + 64 * wn;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < 2; ++j) {
             const int64_t c = nw + 32 * j + l32;
             if (c >= N) continue;
 #pragma unroll
@@ -877,7 +883,7 @@ hipError_t launch_mx_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const
 #define NVFP4_MXG(E, BF)                                                                 \
     do {                                                                                 \
         if (full)                                                                        \
-            hipLaunchKernelGGL((k_mx_gemm_full<E, BF>), grid, dim3(256), 0, s, p);       \
+            hipLaunchKernelGGL((k_mx_gemm_full8<E, BF>), grid, dim3(512), 0, s, p);      \
         else                                                                             \
             hipLaunchKernelGGL((k_mx_gemm<E, BF>), grid, dim3(256), 0, s, p);            \
     } while (0)
