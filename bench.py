@@ -16,7 +16,10 @@ consecutive steps do not hit in the 256 MB Infinity Cache.
 
 Also reported, on the same JSON line:
   roofline     -- the dominant kernel of the step, timed alone with HIP events
-                  on the launch stream, against the 8 TB/s HBM peak;
+                  on the launch stream, against the 8 TB/s HBM peak (per-kernel
+                  figures are the median over interleaved rounds of back-to-back
+                  launches: the stochastic-rounding kernels' clocks move by up to
+                  ~15% between bursts; every round's figure is on the line);
   cpu_baseline -- the CPU oracle on a bounded sample of the same step;
   kernels      -- each step kernel timed alone, the 16x16-block, dequantize,
                   re-quantization and amax kernels, and (with the GEMMs) the
@@ -112,6 +115,19 @@ def kernel_source_hash(kernel_key):
     return h.hexdigest()[:16]
 
 
+def time_rounds(cases, reps, torch, rounds):
+    """Median over `rounds` rounds of time_events for each case, the cases
+    interleaved within a round: the stochastic-rounding kernels run at clocks
+    that the chip's power management moves by up to ~15% from one burst of
+    launches to the next, so one burst per kernel is not a stable figure.
+    Returns {name: (median ms, [ms of each round])}."""
+    got = {k: [] for k in cases}
+    for _ in range(rounds):
+        for k, fn in cases.items():
+            got[k].append(time_events(fn, reps, torch))
+    return {k: (float(sorted(v)[len(v) // 2]), v) for k, v in got.items()}
+
+
 def profile_figure(fname, kernel_key, field):
     """`field` of `kernel_key` in the committed counter summary
     profiles/`fname`, or None when absent or taken on different kernel
@@ -153,6 +169,9 @@ def main():
                          "call in order on one stream")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=20)
+    ap.add_argument("--kernel-rounds", type=int, default=5,
+                    help="per-kernel figures: median over this many interleaved rounds of --kernel-reps "
+                         "back-to-back launches")
     ap.add_argument("--pmc-driver", action="store_true",
                     help="for rocprofv3 --pmc runs: a 1 GiB device copy (calibration), then each "
                          "step kernel alone, the column re-quantization and the MX quantize / "
@@ -283,10 +302,11 @@ def main():
     del got
     value = step_bytes / (ms * 1e-3) / 1e9
 
-    # ---- per-kernel durations (amax given, so each call is one kernel)
+    # ---- per-kernel durations (amax given, so each call is one kernel), as the
+    # median of interleaved rounds of back-to-back launches
     log("per-kernel timing")
     reps = args.kernel_reps
-    kern = {}
+    cases, nbytes = {}, {}
 
     def qk(lay, rnd, out):
         return lambda i: nv.nvfp4_quantize(xs[i % NBUF], layout=lay, round=rnd, sr_seed=5,
@@ -294,18 +314,17 @@ def main():
 
     for name, lay, rnd, b in step_ops:
         out = (R2, C2) if lay == RC else (C if lay == COL else R)
-        kern[name] = dict(ms=time_events(qk(lay, rnd, out), reps, torch), bytes=b)
+        cases[name], nbytes[name] = qk(lay, rnd, out), b
     q2d = E * 2 + E // 2 + E // 256 + 4                  # 2D: one scale byte per 16 x 16 tile
-    kern["quant_2d_rne"] = dict(ms=time_events(qk(nv.NVFP4_BLK_2D, RNE, Q2d), reps, torch), bytes=q2d)
+    cases["quant_2d_rne"], nbytes["quant_2d_rne"] = qk(nv.NVFP4_BLK_2D, RNE, Q2d), q2d
     # dequantize and re-quantize read NVFP4 tensors: one per input buffer, and
     # one output per buffer, so consecutive launches touch different memory
     # (4 x 36 MiB in, 4 x 128 MiB or 4 x 36 MiB out) instead of re-reading one
     # tensor that stays in the 256 MB Infinity Cache
     Rb = [nv.nvfp4_quantize(xs[b], layout=ROW, round=RNE, amax_in=amax[b]) for b in range(NBUF)]
     yb = [torch.empty((N, N), dtype=torch.bfloat16, device=dev) for _ in range(NBUF)]
-    kern["dequant_row_bf16"] = dict(ms=time_events(
-        lambda i: nv.nvfp4_dequantize(Rb[i % NBUF], out=yb[i % NBUF]), reps, torch), bytes=dq)
-    del Rb, yb
+    cases["dequant_row_bf16"] = lambda i: nv.nvfp4_dequantize(Rb[i % NBUF], out=yb[i % NBUF])
+    nbytes["dequant_row_bf16"] = dq
     # re-quantization of the row-quantized tensor along columns (not part of the step):
     # codes + scales in, codes + scales out, 1.125 B/element
     rq = 2 * (E // 2 + E // 16 + 4)
@@ -316,15 +335,19 @@ def main():
     for b in range(NBUF):
         nv.nvfp4_requantize(Rq[b], out=Cq[b], amax_out=ramax[b], workspace=ws)
         nv.nvfp4_requantize(Rq[b], out=Cq[b], hadamard=True, hadamard_seed=4, amax_out=ramax_h[b], workspace=ws)
-    kern["requant_col_sr"] = dict(ms=time_events(
-        lambda i: nv.nvfp4_requantize(Rq[i % NBUF], round=SR, sr_seed=6 + i, amax_in=ramax[i % NBUF],
-                                      out=Cq[i % NBUF]), reps, torch), bytes=rq)
-    kern["requant_col_sr_hadamard"] = dict(ms=time_events(
-        lambda i: nv.nvfp4_requantize(Rq[i % NBUF], round=SR, sr_seed=6 + i, hadamard=True, hadamard_seed=4,
-                                      amax_in=ramax_h[i % NBUF], out=Cq[i % NBUF]), reps, torch), bytes=rq)
-    del Rq, Cq
-    amax_ms = time_events(lambda i: nv.nvfp4_quantize(xs[i % NBUF], layout=ROW, out=R, workspace=ws),
-                          reps, torch) - kern["quant_row_rne"]["ms"]
+    cases["requant_col_sr"] = lambda i: nv.nvfp4_requantize(Rq[i % NBUF], round=SR, sr_seed=6 + i,
+                                                            amax_in=ramax[i % NBUF], out=Cq[i % NBUF])
+    cases["requant_col_sr_hadamard"] = lambda i: nv.nvfp4_requantize(
+        Rq[i % NBUF], round=SR, sr_seed=6 + i, hadamard=True, hadamard_seed=4, amax_in=ramax_h[i % NBUF],
+        out=Cq[i % NBUF])
+    nbytes["requant_col_sr"] = nbytes["requant_col_sr_hadamard"] = rq
+    # the amax pass: the row quantize with its amax computed, less the kernel alone
+    cases["quant_row_rne_with_amax"] = lambda i: nv.nvfp4_quantize(xs[i % NBUF], layout=ROW, out=R, workspace=ws)
+    timed_k = time_rounds(cases, reps, torch, args.kernel_rounds)
+    del Rb, yb, Rq, Cq
+    kern = {k: dict(ms=timed_k[k][0], ms_rounds=[round(x, 5) for x in timed_k[k][1]], bytes=nbytes[k])
+            for k in nbytes}
+    amax_ms = timed_k["quant_row_rne_with_amax"][0] - timed_k["quant_row_rne"][0]
     kern["amax_pass"] = dict(ms=amax_ms, bytes=E * 2)
     for k, v in kern.items():
         v["gbs"] = v["bytes"] / (v["ms"] * 1e-3) / 1e9
@@ -338,6 +361,9 @@ def main():
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(dk["gbs"], 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(dk["frac_hbm"], 4), "traffic": traffic_for(dom),
                 "avg_launch_ms": round(dk["ms"], 5), "algorithmic_bytes_per_launch": dk["bytes"],
+                "timing": f"median over {args.kernel_rounds} interleaved rounds of the average of "
+                          f"{args.kernel_reps} back-to-back launches (HIP events on the launch stream)",
+                "avg_launch_ms_rounds": dk["ms_rounds"],
                 "valu_issue_share": valu_issue_share_for(dom)}
 
     result = {
@@ -355,11 +381,12 @@ def main():
                    "eager_ms_per_step": round(eager_ms, 4)},
         "roofline": roofline,
         "kernels": {k: {"ms": round(v["ms"], 5), "GB/s": round(v["gbs"], 1),
-                        "frac_hbm": round(v["frac_hbm"], 4), "hbm_bytes": traffic_for(k)} for k, v in kern.items()},
+                        "frac_hbm": round(v["frac_hbm"], 4), "hbm_bytes": traffic_for(k),
+                        **({"ms_rounds": v["ms_rounds"]} if "ms_rounds" in v else {})} for k, v in kern.items()},
     }
 
     if not args.no_mx:
-        result["mx"] = bench_mx_quant(nv, torch, xs, reps)
+        result["mx"] = bench_mx_quant(nv, torch, xs, reps, args.kernel_rounds)
     del xs
     torch.cuda.empty_cache()
     if not args.no_mx:
@@ -372,7 +399,8 @@ def main():
         for k, v in extra.items():
             gbs = v["bytes"] / (v["ms"] * 1e-3) / 1e9
             result["kernels"][k] = {"ms": round(v["ms"], 5), "GB/s": round(gbs, 1),
-                                    "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "hbm_bytes": None}
+                                    "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "hbm_bytes": traffic_for(k),
+                                    "ms_rounds": v["ms_rounds"]}
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(np, W)
@@ -526,10 +554,14 @@ def bench_gemm(nv, W, np, torch, reps, kern_extra=None):
                            dtype=torch.float32, device="cuda")
         nv.nvfp4_quantize(dy, sr_seed=5100, amax_out=amax_h, out=dYq, workspace=ws_h, **kw)
         qb = eg * 2 + eg // 2 + eg // 16 + 4
-        kern_extra["quant_col_sr_hadamard_8192x20480"] = dict(ms=time_events(
-            lambda i: nv.nvfp4_quantize(dy, sr_seed=5100 + i, amax_in=amax_h, out=dYq, **kw), reps, torch), bytes=qb)
-        kern_extra["quant_col_sr_hadamard_8192x20480_with_amax"] = dict(ms=time_events(
-            lambda i: nv.nvfp4_quantize(dy, sr_seed=5100 + i, out=dYq, workspace=ws_h, **kw), reps, torch), bytes=qb)
+        tg = time_rounds({
+            "quant_col_sr_hadamard_8192x20480":
+                lambda i: nv.nvfp4_quantize(dy, sr_seed=5100 + i, amax_in=amax_h, out=dYq, **kw),
+            "quant_col_sr_hadamard_8192x20480_with_amax":
+                lambda i: nv.nvfp4_quantize(dy, sr_seed=5100 + i, out=dYq, workspace=ws_h, **kw)},
+            10, torch, 3)
+        for k, (ms_k, rounds_k) in tg.items():
+            kern_extra[k] = dict(ms=ms_k, bytes=qb, ms_rounds=[round(x, 5) for x in rounds_k])
         nv.nvfp4_quantize(dy, sr_seed=5100, out=dYq, workspace=ws_h, **kw)
         del ws_h, amax_h
     del dy
@@ -585,7 +617,7 @@ def _gbs(name, nbytes, ms):
                    "bytes": nbytes, "hbm_bytes": traffic_for(name)}}
 
 
-def bench_mx_quant(nv, torch, xs, reps):
+def bench_mx_quant(nv, torch, xs, reps, rounds):
     """MX quantize / dequantize of the step's 8192 x 8192 BF16 tensors (no
     amax pass: MX scales are per block only).  Bytes: input + codes + E8M0
     scales (quantize); codes + scales + BF16 output (dequantize)."""
@@ -595,6 +627,7 @@ def bench_mx_quant(nv, torch, xs, reps):
     out = {}
     q = {E4: nv.MXTensor.empty(N, N, E4), E2: nv.MXTensor.empty(N, N, E2)}
     code_bytes = {E4: E, E2: E // 2}
+    cases, nbytes = {}, {}
     for name, lay, elem, rnd in [("mx_e4m3_row_rne", nv.NVFP4_ROW_1D, E4, nv.NVFP4_RNE),
                                  ("mx_e4m3_row_sr", nv.NVFP4_ROW_1D, E4, nv.NVFP4_SR),
                                  ("mx_e4m3_col_rne", nv.NVFP4_COL_1D, E4, nv.NVFP4_RNE),
@@ -602,17 +635,21 @@ def bench_mx_quant(nv, torch, xs, reps):
                                  ("mx_e2m1_row_rne", nv.NVFP4_ROW_1D, E2, nv.NVFP4_RNE),
                                  ("mx_e2m1_row_sr", nv.NVFP4_ROW_1D, E2, nv.NVFP4_SR),
                                  ("mx_e2m1_col_sr", nv.NVFP4_COL_1D, E2, nv.NVFP4_SR)]:
-        ms = time_events(lambda i: nv.nvfp4_mx_quantize(xs[i % NBUF], layout=lay, elem=elem, round=rnd,
-                                                        sr_seed=9 + i, out=q[elem]), reps, torch)
-        out.update(_gbs(name, E * 2 + code_bytes[elem] + E // 32, ms))
+        cases[name] = (lambda lay, elem, rnd: lambda i: nv.nvfp4_mx_quantize(
+            xs[i % NBUF], layout=lay, elem=elem, round=rnd, sr_seed=9 + i, out=q[elem]))(lay, elem, rnd)
+        nbytes[name] = E * 2 + code_bytes[elem] + E // 32
     # dequantize: one MX tensor and one output per input buffer (rotated)
     ys = [torch.empty((N, N), dtype=torch.bfloat16, device="cuda") for _ in range(NBUF)]
+    qs = {}
     for name, elem in [("mx_dequant_e4m3_bf16", E4), ("mx_dequant_e2m1_bf16", E2)]:
-        qs = [nv.nvfp4_mx_quantize(xs[b], elem=elem) for b in range(NBUF)]
-        ms = time_events(lambda i: nv.nvfp4_mx_dequantize(qs[i % NBUF], out=ys[i % NBUF]), reps, torch)
-        out.update(_gbs(name, code_bytes[elem] + E // 32 + E * 2, ms))
-        del qs
-    del ys
+        qs[elem] = [nv.nvfp4_mx_quantize(xs[b], elem=elem) for b in range(NBUF)]
+        cases[name] = (lambda elem: lambda i: nv.nvfp4_mx_dequantize(qs[elem][i % NBUF], out=ys[i % NBUF]))(elem)
+        nbytes[name] = code_bytes[elem] + E // 32 + E * 2
+    timed = time_rounds(cases, reps, torch, rounds)
+    for name in cases:
+        out.update(_gbs(name, nbytes[name], timed[name][0]))
+        out[name]["ms_rounds"] = [round(x, 5) for x in timed[name][1]]
+    del qs, ys
     return out
 
 

@@ -657,16 +657,11 @@ __device__ __forceinline__ void mx_full8_chunk_load(const MxFullSrc& src, int64_
     }
 }
 
-// (A lanes and B lanes as two loads under complementary lane masks, each a
-// scalar base plus the lane's 32-bit offset)
+// (one load: each lane's address picks A (lanes 0..31) or B (lanes 32..63))
 __device__ __forceinline__ void mx_full8_scale_load(const uint8_t* as, const uint8_t* bs, uint32_t so, int lane,
                                                     int64_t group, uint8_t* buf, int w) {
-    uint32_t o = so;
-    asm volatile("" : "+v"(o));
-    if (lane < 32)
-        __builtin_amdgcn_global_load_lds((gmem_t*)(as + group * 16 + o), (lmem_t*)(buf + 1024 * w), 16, 0, 0);
-    else
-        __builtin_amdgcn_global_load_lds((gmem_t*)(bs + group * 16 + o), (lmem_t*)(buf + 1024 * w), 16, 0, 0);
+    const uint8_t* sp = (lane < 32 ? as : bs) + group * 16 + so;
+    __builtin_amdgcn_global_load_lds((gmem_t*)sp, (lmem_t*)(buf + 1024 * w), 16, 0, 0);
 }
 
 // A lane's LDS byte offsets for the 8-wave kernel: code piece q of a fragment
