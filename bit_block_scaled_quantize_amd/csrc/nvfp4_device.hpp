@@ -373,6 +373,38 @@ __device__ __forceinline__ void encode(const float* v, BlockScale bs, float amax
     }
 }
 
+// encode<SR, 16> of t = h / 4 given h, the 16 sums of hadamard16_sums over
+// sign-flipped BF16 inputs (amax_b is the block's largest |t|).  Every such h
+// is a multiple of 2^-133, so t = h / 4 is exact (binary32 subnormals are
+// multiples of 2^-149), and whenever R / 4 is exact, fl(|t| R) = fl(|h| (R / 4)):
+// the multiply by 1/4 folds into the block multiplier.  With SR the single
+// multiply by R / 4 * 2^23 of the FOLD path then holds too (as there, with
+// nonzero |h| >= 2^-133 it needs R / 4 >= 2^-16).  A wave whose lanes do not
+// all qualify forms t and takes the general path.
+template <bool SR>
+__device__ __forceinline__ void encode_quarter16(float h[16], BlockScale bs, float amax_b, const uint32_t* w,
+                                                 uint32_t* out) {
+    const bool slow = SR ? !(amax_b * bs.R < 0x1p100f) : __builtin_isinf(bs.R);
+    if (SR) {
+        if (__all(!slow && (bs.R == 0.0f || (bs.R >= 0x1p-14f && bs.R < 0x1p100f)))) {
+            const float Rq = 0.25f * bs.R;
+            out[0] = sr_word8<true>(h, Rq, w);
+            out[1] = sr_word8<true>(h + 8, Rq, w + 4);
+            return;
+        }
+    } else {
+        if (__all(!slow && (bs.R == 0.0f || bs.R >= 0x1p-124f))) {
+            BlockScale q = bs;
+            q.R = 0.25f * bs.R;
+            encode<false, 16>(h, q, amax_b, w, out);
+            return;
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) h[j] = 0.25f * h[j];
+    encode<SR, 16, false>(h, bs, amax_b, w, out);
+}
+
 // Two E2M1 codes (byte `sel` of w; low nibble first) as exact binary32 values,
 // by the gfx950 FP4 unpack instruction with scale operand 1.0.
 __device__ __forceinline__ float2 e2m1x2_unpack(uint32_t w, int sel) {
@@ -420,6 +452,21 @@ __device__ __forceinline__ void hadamard16(float v[16], uint32_t sign_mask) {
     }
 #pragma unroll
     for (int j = 0; j < 16; ++j) v[j] = 0.25f * v[j];
+}
+
+// The butterflies of hadamard16 alone (no sign flips, no multiply by 1/4), in
+// the same order: h = H16 x.
+__device__ __forceinline__ void hadamard16_sums(float v[16]) {
+#pragma unroll
+    for (int h = 1; h < 16; h <<= 1) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            if (j & h) continue;
+            float a = v[j], b = v[j + h];
+            v[j] = a + b;
+            v[j + h] = a - b;
+        }
+    }
 }
 
 // max_i |t_i| of t = hadamard16(v): the same values as transforming and then

@@ -471,20 +471,37 @@ __device__ __forceinline__ void tile_col_blocks(const uint8_t* tile, int64_t R0,
 #pragma unroll
     for (int i = 0; i < 16; ++i)
         q[i] = *reinterpret_cast<const uint2*>(tile + (16 * rb + i) * STRIDE + 8 * (u ^ rb));
+    // BF16 with the transform: row i's sign flip rides on the unpack (adding
+    // 2^31 flips the top bit), and the multiply by 1/4 on the block multiplier
+    // (encode_quarter16)
+    constexpr bool QUARTER = RHT && sizeof(T) == 2;
+    uint32_t sflip[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sflip[i] = QUARTER ? ((sign_mask >> i) & 1u) << 31 : 0u;
 #pragma unroll
     for (int e = 0; e < UE; ++e) {
         const int64_t c = C0 + UE * u + e;
         if (c >= cols) continue;  // (not break: the loop must unroll fully)
         float col[16];
+        if constexpr (QUARTER) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) col[i] = unit_elem<T>(q[i], e);
-        if (RHT) hadamard16(col, sign_mask);
-        const float ab = absmax16(col);
+            for (int i = 0; i < 16; ++i) {
+                const uint32_t wd2 = (e >> 1) == 0 ? q[i].x : q[i].y;
+                col[i] = __uint_as_float((e & 1) ? ((wd2 & 0xFFFF0000u) ^ sflip[i]) : ((wd2 << 16) + sflip[i]));
+            }
+            hadamard16_sums(col);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) col[i] = unit_elem<T>(q[i], e);
+            if (RHT) hadamard16(col, sign_mask);
+        }
+        const float ab = QUARTER ? 0.25f * absmax16(col) : absmax16(col);
         const BlockScale bs = block_scale(ab, ts.six_st, ts.rtab);
         uint32_t wd[8];
         if (SR) philox_words16(seed, kStreamCol, (uint64_t)(c * rows + r0), wd);
         uint32_t w[2];
-        encode<SR, 16, sizeof(T) == 2 && !RHT>(col, bs, ab, wd, w);
+        if constexpr (QUARTER) encode_quarter16<SR>(col, bs, ab, wd, w);
+        else encode<SR, 16, sizeof(T) == 2 && !RHT>(col, bs, ab, wd, w);
         *reinterpret_cast<uint2*>(ccodes + c * (rows / 2) + r0 / 2) = make_uint2(w[0], w[1]);
         cscales[c * (rows / 16) + r0 / 16] = (uint8_t)bs.byte;
     }

@@ -107,6 +107,29 @@ def test_rowcol_hadamard(nv, dtype, rnd, shape):
     assert out_pair.cpu().tolist() == [3.5, 700.0]
 
 
+@pytest.mark.parametrize("rnd", [O.RNE, O.SR])
+def test_col_hadamard_bf16_multiplier_ranges(nv, rnd):
+    """BF16 columns with the Hadamard transform: the kernel folds the
+    transform's 1/4 into the block multiplier R where that is exact (and with
+    SR takes a single multiply when R >= 2^-14), and otherwise forms t = h / 4
+    first.  The inputs put whole waves on each side and mix them: columns of
+    ordinary magnitude (R near 1), columns scaled by 2^20 (R below 2^-14), the
+    two interleaved, a column block of the smallest BF16 subnormals (R = 0 or
+    large), each with the transformed amax computed, given, given 2^40 times
+    too large, and given far too small (the saturating path)."""
+    base = W.with_spikes(W.normal((208, 96), 1.0, seed=41), 1e-3, 100.0, seed=42)
+    big = base * np.float32(2.0 ** 20)
+    mixed = base.copy()
+    mixed[:, 1::2] *= np.float32(2.0 ** 20)
+    for name, xf in (("ordinary", base), ("scaled", big), ("mixed", mixed)):
+        x = W.f32_to_bf16_bits(xf)
+        x[:16, 5] = np.where(np.arange(16) % 3 == 0, 0x8001, 0x0001).astype(x.dtype)
+        true_t = O.amax(x, O.BF16, O.COL_1D, True, 91)
+        for amax_in in (None, true_t, true_t * 2.0 ** 40, 1e-30):
+            got, ref = run_both(nv, x, O.BF16, O.COL_1D, rnd, seed=43, had=True, hseed=91, amax_in=amax_in, pad=96)
+            assert_q_equal(got[0], ref[0], f"col+had {name} amax_in={amax_in}")
+
+
 @pytest.mark.parametrize("dtype", [O.BF16, O.F32])
 @pytest.mark.parametrize("layout,rnd", [(O.COL_1D, O.RNE), (O.COL_1D, O.SR), (O.ROW_COL_1D, O.RNE),
                                         (O.ROW_COL_1D, O.SR)])
