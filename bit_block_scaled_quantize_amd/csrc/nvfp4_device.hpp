@@ -288,13 +288,14 @@ __device__ __forceinline__ uint32_t sr_seed(uint32_t word, int high_half) {
 typedef float sr_f2_t __attribute__((ext_vector_type(2)));
 
 // The SR FP4 convert writing only byte SEL of acc (its op_sel bits 2 and 3
-// select the destination byte; the other three bytes keep their value).
+// select the destination byte; the other three bytes keep their value, and
+// SEL 0, written first, takes none in).
 // Written as asm with acc tied in and out: the compiler's builtin for this
 // instruction treats the whole destination register as written.
 template <int SEL>
 __device__ __forceinline__ void cvt_sr_fp4_byte(uint32_t& acc, sr_f2_t v, uint32_t seed, float scale) {
-    if constexpr (SEL == 0)
-        asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, %3" : "+v"(acc) : "v"(v), "v"(seed), "s"(scale));
+    if constexpr (SEL == 0)  // (the first of a word's four: the other bytes are written later)
+        asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, %3" : "=v"(acc) : "v"(v), "v"(seed), "s"(scale));
     else if constexpr (SEL == 1)
         asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, %2, %3 op_sel:[0,0,1,0]" : "+v"(acc) : "v"(v), "v"(seed), "s"(scale));
     else if constexpr (SEL == 2)
@@ -308,8 +309,8 @@ __device__ __forceinline__ uint32_t sr_word8(const float* p, float R, const uint
     const float R23 = R * 0x1p23f;
     // byte J of ev / od: code of element 2J / 2J + 1 in the low nibble (the
     // high nibble, from the unspecified second slot, is masked off); every
-    // byte is written, so the registers start unspecified
-    uint32_t ev = __builtin_nondeterministic_value(0u), od = __builtin_nondeterministic_value(0u);
+    // byte is written, byte 0 first
+    uint32_t ev, od;
 #pragma unroll
     for (int J = 0; J < 4; ++J) {
         const float z0 = FOLD ? __builtin_ceilf(fabsf(p[2 * J]) * R23)

@@ -419,14 +419,20 @@ __device__ __forceinline__ void tile_row_blocks(const uint4 (&raw)[8], int64_t R
             bs[i0 + k].byte = group_lane<LPB>(mine.byte, k);
         }
     }
+    // the lane's output addresses and draw index for row R0 + lr0, stepped by
+    // wave-uniform multiples of 32 rows (no per-row 64-bit products)
+    const int64_t rl0 = R0 + lr0;
+    uint8_t* const dst0 = rcodes + rl0 * (cols / 2) + gc / 2;
+    uint8_t* const sdst0 = rscales + rl0 * (cols / 16) + gc / 16;
+    const uint64_t idx0 = (uint64_t)((rl0 * cols + gc) & ~(int64_t)7);  // + 32 k cols keeps the & ~7
 #pragma unroll
     for (int k = 0; k < 8; k += 2) {
-        const int64_t r = R0 + lr0 + 32 * k;  // rows r and r + 32
+        const int64_t r = rl0 + 32 * k;  // rows r and r + 32
         if (!col_ok || r >= rows) continue;
         uint32_t wd[2][4];
         if (SR) {
-            philox_words2(seed, kStreamRow, (uint64_t)((r * cols + gc) & ~(int64_t)7),
-                          (uint64_t)(((r + 32) * cols + gc) & ~(int64_t)7), wd[0], wd[1]);
+            philox_words2(seed, kStreamRow, idx0 + (uint64_t)(32 * k) * cols, idx0 + (uint64_t)(32 * k + 32) * cols,
+                          wd[0], wd[1]);
             if (CH == 4 && (gc & 4)) {
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
@@ -446,10 +452,10 @@ __device__ __forceinline__ void tile_row_blocks(const uint4 (&raw)[8], int64_t R
             for (int e = CH; e < 8; ++e) v[e] = 0.0f;
             uint32_t w[1];
             encode<SR, 8, sizeof(T) == 2>(v, bs[k + h], a[k + h], wd[h], w);
-            uint8_t* dst = rcodes + rr * (cols / 2) + gc / 2;
+            uint8_t* dst = dst0 + (int64_t)(32 * (k + h)) * (cols / 2);
             if (CH == 8) *reinterpret_cast<uint32_t*>(dst) = w[0];
             else *reinterpret_cast<uint16_t*>(dst) = (uint16_t)w[0];
-            if (q == (k + h) % LPB) rscales[rr * (cols / 16) + gc / 16] = (uint8_t)bs[k + h].byte;
+            if (q == (k + h) % LPB) sdst0[(int64_t)(32 * (k + h)) * (cols / 16)] = (uint8_t)bs[k + h].byte;
         }
     }
 }
@@ -478,9 +484,15 @@ __device__ __forceinline__ void tile_col_blocks(const uint8_t* tile, int64_t R0,
     uint32_t sflip[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) sflip[i] = QUARTER ? ((sign_mask >> i) & 1u) << 31 : 0u;
+    // the lane's output addresses and draw index for column C0 + UE u, stepped
+    // by wave-uniform multiples of a column
+    const int64_t cl0 = C0 + UE * u;
+    uint8_t* const cdst0 = ccodes + cl0 * (rows / 2) + r0 / 2;
+    uint8_t* const csdst0 = cscales + cl0 * (rows / 16) + r0 / 16;
+    const uint64_t cidx0 = (uint64_t)(cl0 * rows + r0);
 #pragma unroll
     for (int e = 0; e < UE; ++e) {
-        const int64_t c = C0 + UE * u + e;
+        const int64_t c = cl0 + e;
         if (c >= cols) continue;  // (not break: the loop must unroll fully)
         float col[16];
         if constexpr (QUARTER) {
@@ -498,12 +510,12 @@ __device__ __forceinline__ void tile_col_blocks(const uint8_t* tile, int64_t R0,
         const float ab = QUARTER ? 0.25f * absmax16(col) : absmax16(col);
         const BlockScale bs = block_scale(ab, ts.six_st, ts.rtab);
         uint32_t wd[8];
-        if (SR) philox_words16(seed, kStreamCol, (uint64_t)(c * rows + r0), wd);
+        if (SR) philox_words16(seed, kStreamCol, cidx0 + (uint64_t)e * rows, wd);
         uint32_t w[2];
         if constexpr (QUARTER) encode_quarter16<SR>(col, bs, ab, wd, w);
         else encode<SR, 16, sizeof(T) == 2 && !RHT>(col, bs, ab, wd, w);
-        *reinterpret_cast<uint2*>(ccodes + c * (rows / 2) + r0 / 2) = make_uint2(w[0], w[1]);
-        cscales[c * (rows / 16) + r0 / 16] = (uint8_t)bs.byte;
+        *reinterpret_cast<uint2*>(cdst0 + (int64_t)e * (rows / 2)) = make_uint2(w[0], w[1]);
+        csdst0[(int64_t)e * (rows / 16)] = (uint8_t)bs.byte;
     }
 }
 
