@@ -148,6 +148,24 @@ def traffic_for(kernel_key):
     return profile_figure("traffic.json", kernel_key, "hbm_bytes_per_launch")
 
 
+# VALU issue peak: 256 CUs x 4 SIMDs, a wave64 instruction (64 lane-instructions)
+# per SIMD every 4 cycles, at 2.4 GHz
+VALU_PEAK_T_LANE_INSTR = 256 * 4 * 64 / 4 * 2.4e9 / 1e12
+
+
+def valu_view(kernel_key, launch_ms):
+    """The kernel against the VALU issue roofline: its counted VALU
+    lane-instructions per launch (profiles/valu.json) per second of its
+    launch time, against VALU_PEAK_T_LANE_INSTR; None without a matching
+    counter record."""
+    n = profile_figure("valu.json", kernel_key, "valu_lane_instr_per_launch")
+    if n is None:
+        return None
+    achieved = n / (launch_ms * 1e-3) / 1e12
+    return {"unit": "T VALU lane-instructions/s", "lane_instr_per_launch": n, "achieved": round(achieved, 2),
+            "peak": round(VALU_PEAK_T_LANE_INSTR, 2), "frac": round(achieved / VALU_PEAK_T_LANE_INSTR, 4)}
+
+
 def valu_issue_share_for(kernel_key):
     """Share of cycles the kernel's SIMDs spend issuing VALU instructions
     (SQ_INSTS_VALU x 4 / (SIMDs x cycles)): near 1, VALU issue bounds it."""
@@ -364,7 +382,8 @@ def main():
                 "timing": f"median over {args.kernel_rounds} interleaved rounds of the average of "
                           f"{args.kernel_reps} back-to-back launches (HIP events on the launch stream)",
                 "avg_launch_ms_rounds": dk["ms_rounds"],
-                "valu_issue_share": valu_issue_share_for(dom)}
+                "valu_issue_share": valu_issue_share_for(dom),
+                "valu_view": valu_view(dom, dk["ms"])}
 
     result = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,

@@ -37,11 +37,17 @@ def test_profile_figures_follow_the_kernel_sources(tmp_path, monkeypatch):
     import bench
     (tmp_path / "profiles").mkdir()
     (tmp_path / "profiles" / "valu.json").write_text(json.dumps(
-        {"kernels": {"quant_row_sr": {"valu_issue_share": 0.8, "source_hash": "abc"}}}))
+        {"kernels": {"quant_row_sr": {"valu_issue_share": 0.8, "valu_lane_instr_per_launch": 1_572_864_000,
+                                      "source_hash": "abc"}}}))
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     monkeypatch.setattr(bench, "kernel_source_hash", lambda k: "abc")
     assert bench.valu_issue_share_for("quant_row_sr") == 0.8
     assert bench.valu_issue_share_for("quant_col_sr") is None
     assert bench.traffic_for("quant_row_sr") is None  # no traffic.json here
+    # VALU view: 1.572864e9 lane-instructions in 0.05 ms = 31.46 T/s of the 39.32 T/s issue peak
+    v = bench.valu_view("quant_row_sr", 0.05)
+    assert v["achieved"] == 31.46 and v["peak"] == 39.32 and abs(v["frac"] - 0.8) < 1e-3
+    assert bench.valu_view("quant_col_sr", 0.05) is None
     monkeypatch.setattr(bench, "kernel_source_hash", lambda k: "def")
     assert bench.valu_issue_share_for("quant_row_sr") is None
+    assert bench.valu_view("quant_row_sr", 0.05) is None
