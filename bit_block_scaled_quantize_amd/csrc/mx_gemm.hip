@@ -441,6 +441,49 @@ __device__ __forceinline__ void mx_read_frags_exact(const uint8_t* slot, const M
     }
 }
 
+// Fragment o (0..3: A tile o, 4..7: B tile o - 4) of mx_read_frags_exact, on
+// its own.
+template <int ELEM>
+__device__ __forceinline__ void mx_read_frag_exact(const uint8_t* slot, const MxLaneOffsets& lo, int o, MxFrags& f) {
+    using G = MxGeo<ELEM>;
+    const bool isb = o >= 4;
+    const int i = isb ? o - 4 : o;
+    const int dc = 32 * i * G::RB, ds = 32 * i * 4;
+    const v8i_t v = mx_frag<ELEM>(slot + dc, isb ? lo.b_lo : lo.a_lo, isb ? lo.b_hi : lo.a_hi);
+    const int so = isb ? lo.sb : lo.sa;
+    int sc;
+    if constexpr (ELEM == kMxE4M3) sc = *reinterpret_cast<const uint16_t*>(slot + so - (so & 3) + ds);
+    else sc = slot[so + ds];
+    if (isb) {
+        f.b[i] = v;
+        f.sb[i] = sc;
+    } else {
+        f.a[i] = v;
+        f.sa[i] = sc;
+    }
+}
+
+// Pair pr (0..3) of substep q of fragment f as two BF16 values times sc (the
+// pairs of exact_piece, one convert each).
+template <int ELEM>
+__device__ __forceinline__ uint32_t exact_pair(const v8i_t& f, int q, int pr, float sc) {
+    v2bf_t v;
+    if constexpr (ELEM == kMxE4M3) {
+        const uint32_t d = (uint32_t)f[2 * q + (pr >> 1)];
+        v = (pr & 1) ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d, sc, true)
+                     : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d, sc, false);
+    } else {
+        const uint32_t d = (uint32_t)f[q];
+        switch (pr) {
+            case 0: v = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, sc, 0); break;
+            case 1: v = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, sc, 1); break;
+            case 2: v = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, sc, 2); break;
+            default: v = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, sc, 3); break;
+        }
+    }
+    return __builtin_bit_cast(uint32_t, v);
+}
+
 template <int ELEM, bool OUT_BF16>
 __global__ void __launch_bounds__(256, 1) k_mx_gemm_exact(MxGemmArgs p) {
     using G = MxGeo<ELEM>;
@@ -510,45 +553,82 @@ __global__ void __launch_bounds__(256, 1) k_mx_gemm_exact(MxGemmArgs p) {
             refb[i] = rref[kMxTile + brow0 + 32 * i + l32];
         }
         const MxLaneOffsets lo = mx_lane_offsets<ELEM>(arow0, brow0, l32, h);
-        MxFrags fx, fy;
-        mx_read_frags_exact<ELEM>(ring0, lo, fx);
+        // Raw fragments are held once and converted one substep ahead: the
+        // MFMAs of substep q alternate with the conversion of substep q + 1
+        // (two pairs per MFMA, into the other half of `op`); substep 3 reads
+        // the next step's raw fragments (one per MFMA, after their last use
+        // in substep 2) and then converts that step's substep 0 (four pairs
+        // per MFMA).  sched_barrier keeps the order.
+        MxFrags f;
+        uint32_t op[2][8][4];  // converted BF16 pairs: A0..A3, B0..B3
+        auto scale_of = [&](const MxFrags& fr, int o, int q) {
+            const int sh = ELEM == kMxE4M3 ? 8 * (q >> 1) : 0;
+            return o < 4 ? pow2_rel((fr.sa[o] >> sh) & 0xFF, refa[o]) : pow2_rel((fr.sb[o - 4] >> sh) & 0xFF, refb[o - 4]);
+        };
+        auto pair_of = [&](const MxFrags& fr, int o, int q, int pr, float sc) {
+            return exact_pair<ELEM>(o < 4 ? fr.a[o] : fr.b[o - 4], q, pr, sc);
+        };
+#pragma unroll
+        for (int o = 0; o < 8; ++o) mx_read_frag_exact<ELEM>(ring0, lo, o, f);
+#pragma unroll
+        for (int o = 0; o < 8; ++o) {
+            const float sc = scale_of(f, o, 0);
+#pragma unroll
+            for (int pr = 0; pr < 4; ++pr) op[0][o][pr] = pair_of(f, o, 0, pr, sc);
+        }
 
-        auto step = [&](int64_t j, uint8_t* cur, uint8_t* nxt, MxFrags& fc, MxFrags& fn) {
+        auto step = [&](int64_t j, uint8_t* cur, uint8_t* nxt) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
+                const int ob = q & 1;
                 if (q == 2) {
-                    // as in the ring kernel, half way through the step: own
-                    // loads of step j + 1 landed, the barrier, then the next
-                    // step's fragments and the loads of step j + 4 into the
-                    // slot every wave has finished reading
+                    // half way through the step: own loads of step j + 1
+                    // landed, the barrier, then the loads of step j + 4 into
+                    // the slot every wave has finished reading
                     __builtin_amdgcn_sched_barrier(0);
                     __builtin_amdgcn_s_waitcnt(mx_vmcnt_at_most(2 * G::LPS));
                     asm volatile("" ::: "memory");
                     __builtin_amdgcn_s_barrier();
                     asm volatile("" ::: "memory");
-                    mx_read_frags_exact<ELEM>(nxt, lo, fn);
                     mx_ring_load<ELEM>(src, kc_of(j + 4), cur, w);
                     __builtin_amdgcn_sched_barrier(0);
                 }
-                const int sh = ELEM == kMxE4M3 ? 8 * (q >> 1) : 0;
-                v8bf_t av[4], bv[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    av[i] = exact_piece<ELEM>(fc.a[i], q, pow2_rel((fc.sa[i] >> sh) & 0xFF, refa[i]));
-                    bv[i] = exact_piece<ELEM>(fc.b[i], q, pow2_rel((fc.sb[i] >> sh) & 0xFF, refb[i]));
-                }
+                float sc[8];
 #pragma unroll
                 for (int m = 0; m < 16; ++m) {
                     const int i = m >> 2, jj = m & 3;
-                    acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[jj], acc[i][jj], 0, 0, 0);
+                    acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        __builtin_bit_cast(v8bf_t, op[ob][i]), __builtin_bit_cast(v8bf_t, op[ob][4 + jj]), acc[i][jj],
+                        0, 0, 0);
+                    if (q < 3) {
+                        // substep q + 1 of this step: two pairs per MFMA
+#pragma unroll
+                        for (int u = 0; u < 2; ++u) {
+                            const int pc = 2 * m + u, o = pc >> 2, pr = pc & 3;
+                            if (pr == 0) sc[o] = scale_of(f, o, q + 1);
+                            op[ob ^ 1][o][pr] = pair_of(f, o, q + 1, pr, sc[o]);
+                        }
+                    } else if (m < 8) {
+                        // the next step's raw fragment m
+                        mx_read_frag_exact<ELEM>(nxt, lo, m, f);
+                    } else {
+                        // the next step's substep 0: four pairs per MFMA
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) {
+                            const int pc = 4 * (m - 8) + u, o = pc >> 2, pr = pc & 3;
+                            if (pr == 0) sc[o] = scale_of(f, o, 0);
+                            op[ob ^ 1][o][pr] = pair_of(f, o, 0, pr, sc[o]);
+                        }
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             }
         };
         for (int64_t j = 0; j < nj; j += 4) {
-            step(j, ring0, ring1, fx, fy);
-            step(j + 1, ring1, ring2, fy, fx);
-            step(j + 2, ring2, ring3, fx, fy);
-            step(j + 3, ring3, ring0, fy, fx);
+            step(j, ring0, ring1);
+            step(j + 1, ring1, ring2);
+            step(j + 2, ring2, ring3);
+            step(j + 3, ring3, ring0);
         }
         __builtin_amdgcn_s_waitcnt(mx_vmcnt_at_most(0));
     } else {
