@@ -933,6 +933,281 @@ __global__ void __launch_bounds__(512, 1) k_mx_gemm_full8(MxGemmArgs p) {
         }
 }
 
+// ============================================================ full-line exact kernel
+// Exact accumulation (as k_mx_gemm_exact) for K % 1024 == 0 with 16-byte-
+// aligned scale rows: the full-line kernel's slots (128 bytes of every tile
+// row per chunk, two slots) and scale groups (16 bytes per row, two buffers),
+// one barrier per chunk instead of one per K step, with four waves of
+// 128 x 128 tiles and the exact kernel's substep schedule: raw fragments held
+// once, substep q + 1 converted between the MFMAs of substep q, the next
+// step's raw fragments read in substep 3 (after a chunk's last step has passed
+// the barrier that hands the other slot over) and its substep 0 converted in
+// the second half of substep 3.  Each wave loads 64 rows of each operand per
+// chunk and their 16 scale bytes per group.
+template <int ELEM>
+__device__ __forceinline__ void mx_full4_chunk_load(const MxFullSrc& src, int64_t chunk, uint8_t* slot, int w) {
+    using F = MxFull<ELEM>;
+    const uint8_t* ac = src.ac + chunk * 128;
+    const uint8_t* bc = src.bc + chunk * 128;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        uint32_t o = src.a[t];
+        asm volatile("" : "+v"(o));
+        __builtin_amdgcn_global_load_lds((gmem_t*)(ac + o), (lmem_t*)(slot + (64 * w + 8 * t) * 128), 16, 0, 0);
+    }
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        uint32_t o = src.b[t];
+        asm volatile("" : "+v"(o));
+        __builtin_amdgcn_global_load_lds((gmem_t*)(bc + o), (lmem_t*)(slot + F::CODES + (64 * w + 8 * t) * 128), 16,
+                                         0, 0);
+    }
+}
+constexpr int kMxFull4ChunkLoads = 16;
+
+template <int ELEM>
+__device__ __forceinline__ void mx_full4_scale_load(const MxFullSrc& src, int64_t group, uint8_t* buf, int w) {
+    using F = MxFull<ELEM>;
+    uint32_t oa = src.sa, ob = src.sb;
+    asm volatile("" : "+v"(oa));
+    asm volatile("" : "+v"(ob));
+    __builtin_amdgcn_global_load_lds((gmem_t*)(src.as + group * 16 + oa), (lmem_t*)(buf + 64 * w * 16), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((gmem_t*)(src.bs + group * 16 + ob), (lmem_t*)(buf + F::SCB + 64 * w * 16), 16, 0,
+                                     0);
+}
+
+// A lane's LDS byte offsets for the exact full-line kernel: code piece q of
+// its A tile 0 / B tile 0 row (E4M3: q = 2 t + hi; E2M1: q = t; tile i adds
+// 4096 i) and the rows' 16 scale bytes (tile i adds 512 i), opaque to the
+// compiler so that each read is one of them plus an immediate.
+struct MxExact4Offsets {
+    uint32_t a[4], b[4];
+    uint32_t sa, sb;
+};
+
+template <int ELEM>
+__device__ __forceinline__ MxExact4Offsets mx_exact4_offsets(int wm, int wn, int l32, int h) {
+    using F = MxFull<ELEM>;
+    MxExact4Offsets o;
+    const int sw = mx_full_swz(l32);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int c = ELEM == kMxE4M3 ? (4 * (q >> 1) + 2 * (q & 1) + h) : (2 * q + h);
+        o.a[q] = (uint32_t)((128 * wm + l32) * 128 + 16 * (c ^ sw));
+        o.b[q] = (uint32_t)(F::CODES + (128 * wn + l32) * 128 + 16 * (c ^ sw));
+        asm volatile("" : "+v"(o.a[q]));
+        asm volatile("" : "+v"(o.b[q]));
+    }
+    o.sa = (uint32_t)((128 * wm + l32) * 16);
+    o.sb = (uint32_t)(F::SCB + (128 * wn + l32) * 16);
+    asm volatile("" : "+v"(o.sa));
+    asm volatile("" : "+v"(o.sb));
+    return o;
+}
+
+// Raw fragment o (0..3: A tile o, 4..7: B tile o - 4) of step t of a chunk,
+// with the scale bytes its conversion needs from step g of the group buffer
+// (E4M3: both blocks of the step, block 0 in bits 0..7; E2M1: block h).
+template <int ELEM>
+__device__ __forceinline__ void mx_exact4_read(const uint8_t* slot, const uint8_t* sbuf, int t, int g, int o, int h,
+                                               const MxExact4Offsets& off, MxFrags& f) {
+    const bool isb = o >= 4;
+    const int i = isb ? o - 4 : o;
+    v8i_t v;
+    if constexpr (ELEM == kMxE4M3) {
+        const uint32_t lo = isb ? off.b[2 * t] : off.a[2 * t], hi = isb ? off.b[2 * t + 1] : off.a[2 * t + 1];
+        const v4i_t ql = lds16(slot + lo + 4096 * i), qh = lds16(slot + hi + 4096 * i);
+        v = v8i_t{ql[0], ql[1], ql[2], ql[3], qh[0], qh[1], qh[2], qh[3]};
+    } else {
+        const v4i_t q = lds16(slot + (isb ? off.b[t] : off.a[t]) + 4096 * i);
+        v = v8i_t{q[0], q[1], q[2], q[3], 0, 0, 0, 0};
+    }
+    const uint8_t* sp = sbuf + (isb ? off.sb : off.sa) + 512 * i + 2 * g;
+    int sc;
+    if constexpr (ELEM == kMxE4M3) sc = *reinterpret_cast<const uint16_t*>(sp);
+    else sc = sp[h];
+    if (isb) {
+        f.b[i] = v;
+        f.sb[i] = sc;
+    } else {
+        f.a[i] = v;
+        f.sa[i] = sc;
+    }
+}
+
+template <int ELEM, bool OUT_BF16>
+__global__ void __launch_bounds__(256, 1) k_mx_gemm_exact_full(MxGemmArgs p) {
+    using F = MxFull<ELEM>;
+    constexpr int SPC = F::SPC;
+    __shared__ __attribute__((aligned(16))) uint8_t slot0[2 * F::CODES];
+    __shared__ __attribute__((aligned(16))) uint8_t slot1[2 * F::CODES];
+    __shared__ __attribute__((aligned(16))) uint8_t scb0[2 * F::SCB];
+    __shared__ __attribute__((aligned(16))) uint8_t scb1[2 * F::SCB];
+    __shared__ int rref[2 * kMxTile];  // largest scale byte of each tile row: A rows, then B rows
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6) & 3;
+    const int wm = w >> 1, wn = w & 1;
+    const int h = lane >> 5, l32 = lane & 31;
+    const int64_t M = p.M, N = p.N, K = p.K;
+    const int64_t m0 = (int64_t)blockIdx.y * kMxTile, n0 = (int64_t)blockIdx.x * kMxTile;
+    const int64_t kb = ELEM == kMxE4M3 ? K : K / 2, ks = K / 32;
+
+    MxFullSrc src;
+    src.ac = p.ac + m0 * kb;
+    src.bc = p.bc + n0 * kb;
+    src.as = p.as + m0 * ks;
+    src.bs = p.bs + n0 * ks;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const int r = 64 * w + 8 * t + (lane >> 3);
+        const int c = (lane & 7) ^ mx_full_swz(r);  // the swizzle is an involution
+        src.a[t] = (uint32_t)((min(m0 + r, M - 1) - m0) * kb + 16 * c);
+        src.b[t] = (uint32_t)((min(n0 + r, N - 1) - n0) * kb + 16 * c);
+    }
+    src.sa = (uint32_t)((min(m0 + 64 * w + lane, M - 1) - m0) * ks);
+    src.sb = (uint32_t)((min(n0 + 64 * w + lane, N - 1) - n0) * ks);
+
+    // each thread: the largest scale byte of one A row and one B row of the
+    // tile (rows past the end: the clamped row, never stored)
+    rref[tid] = row_max_byte(p.as + min(m0 + tid, M - 1) * ks, ks);
+    rref[kMxTile + tid] = row_max_byte(p.bs + min(n0 + tid, N - 1) * ks, ks);
+
+    v16f_t acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    const MxExact4Offsets off = mx_exact4_offsets<ELEM>(wm, wn, l32, h);
+    const int nchunks = (int)(K / (64 * SPC)), ngroups = (int)(K / 512), nsteps = (int)(K / 64);
+    auto cclamp = [&](int c) { return c < nchunks ? c : nchunks - 1; };
+    auto gclamp = [&](int g) { return g < ngroups ? g : ngroups - 1; };
+
+    // prologue: scale groups 0 and 1, chunks 0 and 1 (K >= 1024, so all exist)
+    mx_full4_scale_load<ELEM>(src, 0, scb0, w);
+    mx_full4_scale_load<ELEM>(src, 1, scb1, w);
+    mx_full4_chunk_load<ELEM>(src, 0, slot0, w);
+    mx_full4_chunk_load<ELEM>(src, 1, slot1, w);
+    __builtin_amdgcn_s_waitcnt(mx_vmcnt_at_most(kMxFull4ChunkLoads));  // all but chunk 1
+    __builtin_amdgcn_s_waitcnt(mx_lgkmcnt_zero());
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();  // (also publishes rref)
+    asm volatile("" ::: "memory");
+
+    int refa[4], refb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        refa[i] = rref[128 * wm + 32 * i + l32];
+        refb[i] = rref[kMxTile + 128 * wn + 32 * i + l32];
+    }
+    MxFrags f;
+    uint32_t op[2][8][4];  // converted BF16 pairs: A0..A3, B0..B3
+    auto scale_of = [&](int o, int q) {
+        const int sh = ELEM == kMxE4M3 ? 8 * (q >> 1) : 0;
+        return o < 4 ? pow2_rel((f.sa[o] >> sh) & 0xFF, refa[o]) : pow2_rel((f.sb[o - 4] >> sh) & 0xFF, refb[o - 4]);
+    };
+    auto pair_of = [&](int o, int q, int pr, float sc) {
+        return exact_pair<ELEM>(o < 4 ? f.a[o] : f.b[o - 4], q, pr, sc);
+    };
+#pragma unroll
+    for (int o = 0; o < 8; ++o) mx_exact4_read<ELEM>(slot0, scb0, 0, 0, o, h, off, f);
+#pragma unroll
+    for (int o = 0; o < 8; ++o) {
+        const float sc = scale_of(o, 0);
+#pragma unroll
+        for (int pr = 0; pr < 4; ++pr) op[0][o][pr] = pair_of(o, 0, pr, sc);
+    }
+
+    for (int it = 0; it < nsteps; it += 16) {
+        const int chunk0 = it / SPC, group0 = it / 8;
+#pragma unroll
+        for (int s = 0; s < 16; ++s) {
+            const int cc = s / SPC, t = s % SPC, g = s % 8;
+            uint8_t* slot = (cc & 1) ? slot1 : slot0;
+            uint8_t* other = (cc & 1) ? slot0 : slot1;
+            uint8_t* gbuf = (s / 8) ? scb1 : scb0;  // this step's scale group
+            // where the next step's fragments and scale bytes are
+            const uint8_t* nslot = (t == SPC - 1) ? other : slot;
+            const int nt = (t == SPC - 1) ? 0 : t + 1;
+            const uint8_t* nsbuf = (g == 7) ? ((s == 7) ? scb1 : scb0) : gbuf;
+            const int ng = (g == 7) ? 0 : g + 1;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int ob = q & 1;
+                float sc[8];
+#pragma unroll
+                for (int m = 0; m < 16; ++m) {
+                    if (q == 3 && m == 0 && t == SPC - 1) {
+                        // the next chunk's loads (and any scale group issued
+                        // before them) landed, this step's fragments are in
+                        // registers; after the barrier every wave has read all
+                        // of this chunk's slot, which takes the chunk after next
+                        __builtin_amdgcn_sched_barrier(0);
+                        __builtin_amdgcn_s_waitcnt(mx_vmcnt_at_most(0) & mx_lgkmcnt_zero());
+                        asm volatile("" ::: "memory");
+                        __builtin_amdgcn_s_barrier();
+                        asm volatile("" ::: "memory");
+                        if (g == 7) mx_full4_scale_load<ELEM>(src, gclamp(group0 + s / 8 + 2), gbuf, w);
+                        mx_full4_chunk_load<ELEM>(src, cclamp(chunk0 + cc + 2), slot, w);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                    const int i = m >> 2, jj = m & 3;
+                    acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        __builtin_bit_cast(v8bf_t, op[ob][i]), __builtin_bit_cast(v8bf_t, op[ob][4 + jj]), acc[i][jj],
+                        0, 0, 0);
+                    if (q < 3) {
+                        // substep q + 1 of this step: two pairs per MFMA
+#pragma unroll
+                        for (int u = 0; u < 2; ++u) {
+                            const int pc = 2 * m + u, o = pc >> 2, pr = pc & 3;
+                            if (pr == 0) sc[o] = scale_of(o, q + 1);
+                            op[ob ^ 1][o][pr] = pair_of(o, q + 1, pr, sc[o]);
+                        }
+                    } else if (m < 8) {
+                        // the next step's raw fragment m
+                        mx_exact4_read<ELEM>(nslot, nsbuf, nt, ng, m, h, off, f);
+                    } else {
+                        // the next step's substep 0: four pairs per MFMA
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) {
+                            const int pc = 4 * (m - 8) + u, o = pc >> 2, pr = pc & 3;
+                            if (pr == 0) sc[o] = scale_of(o, 0);
+                            op[ob ^ 1][o][pr] = pair_of(o, 0, pr, sc[o]);
+                        }
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+        }
+    }
+    // the last look-ahead loads (clamped re-reads) land before the LDS is released
+    __builtin_amdgcn_s_waitcnt(mx_vmcnt_at_most(0));
+
+    const int64_t nw = n0 + 128 * wn;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t c = nw + 32 * j + l32;
+            if (c >= N) continue;
+            const int rb = rref[kMxTile + 128 * wn + 32 * j + l32];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int rl = 128 * wm + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+                const int64_t m = m0 + rl;
+                if (m < M) {
+                    const float v = ldexpf(acc[i][j][r], rref[rl] + rb - 254);
+                    if (OUT_BF16)
+                        static_cast<uint16_t*>(p.C)[m * p.ldc + c] = (uint16_t)__builtin_bit_cast(uint16_t, (__bf16)v);
+                    else
+                        static_cast<float*>(p.C)[m * p.ldc + c] = v;
+                }
+            }
+        }
+}
+
 inline int64_t mx_cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 }  // namespace
@@ -943,8 +1218,16 @@ hipError_t launch_mx_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const
     if (M == 0 || N == 0) return hipSuccess;
     MxGemmArgs p{a_codes, a_scales, b_codes, b_scales, M, N, K, C, ldc};
     dim3 grid((unsigned)mx_cdiv(N, kMxTile), (unsigned)mx_cdiv(M, kMxTile));
+    const bool full = K % 1024 == 0 && K > 0 && (reinterpret_cast<uintptr_t>(a_scales) & 15) == 0 &&
+                      (reinterpret_cast<uintptr_t>(b_scales) & 15) == 0;
     if (exact) {
-#define NVFP4_MXX(E, BF) hipLaunchKernelGGL((k_mx_gemm_exact<E, BF>), grid, dim3(256), 0, s, p)
+#define NVFP4_MXX(E, BF)                                                               \
+    do {                                                                               \
+        if (full)                                                                      \
+            hipLaunchKernelGGL((k_mx_gemm_exact_full<E, BF>), grid, dim3(256), 0, s, p); \
+        else                                                                           \
+            hipLaunchKernelGGL((k_mx_gemm_exact<E, BF>), grid, dim3(256), 0, s, p);      \
+    } while (0)
         if (elem == kMxE4M3) {
             if (c_bf16) NVFP4_MXX(kMxE4M3, true); else NVFP4_MXX(kMxE4M3, false);
         } else {
@@ -953,8 +1236,6 @@ hipError_t launch_mx_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const
 #undef NVFP4_MXX
         return hipGetLastError();
     }
-    const bool full = K % 1024 == 0 && K > 0 && (reinterpret_cast<uintptr_t>(a_scales) & 15) == 0 &&
-                      (reinterpret_cast<uintptr_t>(b_scales) & 15) == 0;
 #define NVFP4_MXG(E, BF)                                                                 \
     do {                                                                                 \
         if (full)                                                                        \

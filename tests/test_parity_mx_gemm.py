@@ -139,10 +139,10 @@ def test_mx_gemm_exact_case(nv, elem, shape, accum):
                                    (264, 200, 3072)])
 def test_mx_gemm_matches_oracle(nv, elem, kind, shape, accum):
     """Ragged M and N; K below and at the 1024 multiple that selects the
-    native full-line kernel (K = 1024, 2048, and 3072: an odd number of its
-    16-step bodies) -- both native kernels are covered, and the exact kernel
-    (one kernel for every K % 64 == 0, ragged steps padded) on the same
-    inputs."""
+    full-line kernels (K = 1024, 2048, and 3072: an odd number of their
+    16-step bodies) -- both native kernels and both exact-accumulation
+    kernels (the full-line one, and the ring one that takes every K % 64 == 0
+    with ragged steps padded) are covered on the same inputs."""
     M, N, K = shape
     seed = M * 3 + N * 5 + K
     if kind == "normal":
