@@ -332,14 +332,20 @@ __global__ void __launch_bounds__(256) k_mx_dequant(const uint8_t* __restrict__ 
                 o[2 * k] = __builtin_amdgcn_ldexpf(p.x, sx[i]);
                 o[2 * k + 1] = __builtin_amdgcn_ldexpf(p.y, sx[i]);
             }
+            // non-temporal stores: the output is large and not read again here
+            // (8192^2: E2M1 to BF16 35.4 -> 30.3 us, E4M3 to FP32 91.9 -> 81.5 us,
+            // E4M3 to BF16 unchanged)
             TOut* qp = y + r * ld + b * EPL;
+            typedef uint32_t v4u_t __attribute__((ext_vector_type(4)));
             if constexpr (sizeof(TOut) == 2) {
-                *reinterpret_cast<uint4*>(qp) = make_uint4(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]),
-                                                           pack_bf16x2(o[4], o[5]), pack_bf16x2(o[6], o[7]));
+                const v4u_t v = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
+                                 pack_bf16x2(o[6], o[7])};
+                __builtin_nontemporal_store(v, reinterpret_cast<v4u_t*>(qp));
             } else {
-                float4* qq = reinterpret_cast<float4*>(qp);
-                qq[0] = make_float4(o[0], o[1], o[2], o[3]);
-                qq[1] = make_float4(o[4], o[5], o[6], o[7]);
+                const v4u_t v0 = {__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]), __float_as_uint(o[3])};
+                const v4u_t v1 = {__float_as_uint(o[4]), __float_as_uint(o[5]), __float_as_uint(o[6]), __float_as_uint(o[7])};
+                __builtin_nontemporal_store(v0, reinterpret_cast<v4u_t*>(qp));
+                __builtin_nontemporal_store(v1, reinterpret_cast<v4u_t*>(qp) + 1);
             }
         }
     }

@@ -665,8 +665,14 @@ __global__ void __launch_bounds__(256) k_dequant(const uint8_t* __restrict__ cod
             if (r >= rows) continue;  // (only the stores are predicated)
             TOut* qp = y + r * ld + b * 16 + 8 * hf;
             if constexpr (sizeof(TOut) == 2) {
-                *reinterpret_cast<uint4*>(qp) = make_uint4(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]),
-                                                           pack_bf16x2(o[4], o[5]), pack_bf16x2(o[6], o[7]));
+                // non-temporal: each wave store writes 1 KiB of one row, the
+                // output is large and not read again here (8192^2: 35.3 ->
+                // 29.3 us); the FP32 form, whose two stores per lane each
+                // cover every other 16 bytes, ran 1.7x slower that way
+                typedef uint32_t v4u_t __attribute__((ext_vector_type(4)));
+                const v4u_t v = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
+                                 pack_bf16x2(o[6], o[7])};
+                __builtin_nontemporal_store(v, reinterpret_cast<v4u_t*>(qp));
             } else {
                 float4* qq = reinterpret_cast<float4*>(qp);
                 qq[0] = make_float4(o[0], o[1], o[2], o[3]);
