@@ -73,7 +73,7 @@ namespace {
 
 // Argument checks of nvfp4_quantize other than the workspace; NVFP4_OK when
 // the request can be launched.
-nvfp4_status check_quantize(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols, int64_t ld,
+nvfp4_status check_quantize(const void* x, int32_t dt /* nvfp4_dtype */, int64_t rows, int64_t cols, int64_t ld,
                             const nvfp4_quant_opts* opts, nvfp4_tensor* out) {
     if (!opts || !out) return NVFP4_ERR_NULL;
     if (!valid_dtype(dt)) return NVFP4_ERR_ENUM;
@@ -109,7 +109,7 @@ nvfp4_status check_quantize(const void* x, nvfp4_dtype dt, int64_t rows, int64_t
     return NVFP4_OK;
 }
 
-nvfp4_status launch_checked_quantize(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols,
+nvfp4_status launch_checked_quantize(const void* x, int32_t dt /* nvfp4_dtype */, int64_t rows, int64_t cols,
                                      int64_t ld, const nvfp4_quant_opts* opts, nvfp4_tensor* out,
                                      float* ws, void* stream) {
     const int layout = opts->layout;
@@ -155,7 +155,7 @@ float* scratch_on_device_of(hipStream_t stream) {
 
 extern "C" {
 
-nvfp4_status nvfp4_quantize(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols, int64_t ld,
+nvfp4_status nvfp4_quantize(const void* x, int32_t dt /* nvfp4_dtype */, int64_t rows, int64_t cols, int64_t ld,
                             const nvfp4_quant_opts* opts, nvfp4_tensor* out, void* ws,
                             size_t ws_bytes, void* stream) {
     nvfp4_status st = check_quantize(x, dt, rows, cols, ld, opts, out);
@@ -168,7 +168,7 @@ nvfp4_status nvfp4_quantize(const void* x, nvfp4_dtype dt, int64_t rows, int64_t
     return launch_checked_quantize(x, dt, rows, cols, ld, opts, out, static_cast<float*>(ws), stream);
 }
 
-nvfp4_status nvfp4_quantize_noalloc(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols, int64_t ld,
+nvfp4_status nvfp4_quantize_noalloc(const void* x, int32_t dt /* nvfp4_dtype */, int64_t rows, int64_t cols, int64_t ld,
                                     const nvfp4_quant_opts* opts, nvfp4_tensor* out, void* stream) {
     nvfp4_status st = check_quantize(x, dt, rows, cols, ld, opts, out);
     if (st != NVFP4_OK) return st;
@@ -211,7 +211,7 @@ nvfp4_status nvfp4_requantize(const nvfp4_tensor* in, const nvfp4_quant_opts* op
     return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
 
-nvfp4_status nvfp4_dequantize(const nvfp4_tensor* q, void* y, nvfp4_dtype dt, int64_t ld,
+nvfp4_status nvfp4_dequantize(const nvfp4_tensor* q, void* y, int32_t dt /* nvfp4_dtype */, int64_t ld,
                               void* stream) {
     if (!q) return NVFP4_ERR_NULL;
     if (!valid_dtype(dt)) return NVFP4_ERR_ENUM;
@@ -227,8 +227,8 @@ nvfp4_status nvfp4_dequantize(const nvfp4_tensor* q, void* y, nvfp4_dtype dt, in
     return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
 
-nvfp4_status nvfp4_gemm(const nvfp4_tensor* A, const nvfp4_tensor* B, void* C, nvfp4_dtype c_dt,
-                        int64_t ldc, nvfp4_epilogue ep, void* stream) {
+nvfp4_status nvfp4_gemm(const nvfp4_tensor* A, const nvfp4_tensor* B, void* C, int32_t c_dt /* nvfp4_dtype */,
+                        int64_t ldc, int32_t ep /* nvfp4_epilogue */, void* stream) {
     if (!A || !B) return NVFP4_ERR_NULL;
     if (!valid_dtype(c_dt)) return NVFP4_ERR_ENUM;
     if (ep != NVFP4_EPI_NONE && ep != NVFP4_EPI_SWIGLU) return NVFP4_ERR_ENUM;
@@ -254,8 +254,8 @@ nvfp4_status nvfp4_gemm(const nvfp4_tensor* A, const nvfp4_tensor* B, void* C, n
 }
 
 nvfp4_status nvfp4_grouped_gemm(int32_t G, const nvfp4_tensor* A, const int64_t* offsets,
-                                const nvfp4_tensor* B, void* C, nvfp4_dtype c_dt, int64_t ldc,
-                                nvfp4_epilogue ep, float* amax_out, void* ws, size_t ws_bytes,
+                                const nvfp4_tensor* B, void* C, int32_t c_dt /* nvfp4_dtype */, int64_t ldc,
+                                int32_t ep /* nvfp4_epilogue */, float* amax_out, void* ws, size_t ws_bytes,
                                 void* stream) {
     (void)ws;
     (void)ws_bytes;
@@ -291,8 +291,8 @@ nvfp4_status nvfp4_grouped_gemm(int32_t G, const nvfp4_tensor* A, const int64_t*
 }
 
 // ---------------------------------------------------------------- MX formats
-nvfp4_status nvfp4_mx_quantize(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols, int64_t ld,
-                               nvfp4_layout layout, nvfp4_round round, uint64_t sr_seed,
+nvfp4_status nvfp4_mx_quantize(const void* x, int32_t dt /* nvfp4_dtype */, int64_t rows, int64_t cols, int64_t ld,
+                               int32_t layout /* nvfp4_layout */, int32_t round /* nvfp4_round */, uint64_t sr_seed,
                                nvfp4_mx_tensor* out, void* stream) {
     if (!out) return NVFP4_ERR_NULL;
     if (!valid_dtype(dt)) return NVFP4_ERR_ENUM;
@@ -316,7 +316,7 @@ nvfp4_status nvfp4_mx_quantize(const void* x, nvfp4_dtype dt, int64_t rows, int6
     return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
 
-nvfp4_status nvfp4_mx_dequantize(const nvfp4_mx_tensor* q, void* y, nvfp4_dtype dt, int64_t ld,
+nvfp4_status nvfp4_mx_dequantize(const nvfp4_mx_tensor* q, void* y, int32_t dt /* nvfp4_dtype */, int64_t ld,
                                  void* stream) {
     if (!q) return NVFP4_ERR_NULL;
     if (!valid_dtype(dt)) return NVFP4_ERR_ENUM;
@@ -333,7 +333,7 @@ nvfp4_status nvfp4_mx_dequantize(const nvfp4_mx_tensor* q, void* y, nvfp4_dtype 
     return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
 
-nvfp4_status nvfp4_mx_gemm(const nvfp4_mx_tensor* A, const nvfp4_mx_tensor* B, void* C, nvfp4_dtype c_dt,
+nvfp4_status nvfp4_mx_gemm(const nvfp4_mx_tensor* A, const nvfp4_mx_tensor* B, void* C, int32_t c_dt /* nvfp4_dtype */,
                            int64_t ldc, int32_t accum, void* stream) {
     if (!A || !B) return NVFP4_ERR_NULL;
     if (!valid_dtype(c_dt)) return NVFP4_ERR_ENUM;
@@ -364,7 +364,7 @@ nvfp4_status nvfp4_mx_gemm(const nvfp4_mx_tensor* A, const nvfp4_mx_tensor* B, v
     return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
 
-const char* nvfp4_status_string(nvfp4_status s) {
+const char* nvfp4_status_string(int32_t s /* nvfp4_status */) {
     switch (s) {
         case NVFP4_OK: return "ok";
         case NVFP4_ERR_NULL: return "a required pointer is NULL";

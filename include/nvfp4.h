@@ -53,6 +53,9 @@
  *     (it caches nothing but the device properties it queries);
  *   - every entry point validates its arguments on the host and returns an
  *     error BEFORE launching anything; outputs are then left untouched;
+ *   - enumerated arguments and fields are int32_t holding a value of the
+ *     enum named beside them, so that any value a caller passes is a defined
+ *     input; one outside the enum is refused with NVFP4_ERR_ENUM;
  *   - work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
  *     and runs asynchronously; NVFP4_ERR_HIP reports a launch failure;
  *   - inputs must be finite; NaN/Inf inputs give unspecified outputs;
@@ -150,7 +153,7 @@ size_t nvfp4_quantize_workspace_size(int64_t rows, int64_t cols, const nvfp4_qua
  * no-op that still writes tensor_scale (= 1, or from amax_in).
  * Source: asector.ru page, "NVFP4 и Blackwell"; iitak.ru page, "Детали" and
  * "Как это работает". */
-nvfp4_status nvfp4_quantize(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols, int64_t ld,
+nvfp4_status nvfp4_quantize(const void* x, int32_t dt /* nvfp4_dtype */, int64_t rows, int64_t cols, int64_t ld,
                             const nvfp4_quant_opts* opts, nvfp4_tensor* out, void* ws,
                             size_t ws_bytes, void* stream);
 
@@ -168,7 +171,7 @@ nvfp4_status nvfp4_quantize(const void* x, nvfp4_dtype dt, int64_t rows, int64_t
  * calls ordered on one stream do not.  The first call on a device looks the
  * array's address up (hipGetSymbolAddress); NVFP4_ERR_HIP if that fails.
  * Errors otherwise as for nvfp4_quantize. */
-nvfp4_status nvfp4_quantize_noalloc(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols, int64_t ld,
+nvfp4_status nvfp4_quantize_noalloc(const void* x, int32_t dt /* nvfp4_dtype */, int64_t rows, int64_t cols, int64_t ld,
                                     const nvfp4_quant_opts* opts, nvfp4_tensor* out, void* stream);
 
 /* Dequantize q into y (q->rows x q->cols in the stored orientation, element
@@ -179,7 +182,7 @@ nvfp4_status nvfp4_quantize_noalloc(const void* x, nvfp4_dtype dt, int64_t rows,
  * ld * sizeof(dtype) % 16 == 0, y and q->codes 16-byte aligned.
  * Source: iitak.ru page, "Как это работает" (converting back to a more
  * precise format). */
-nvfp4_status nvfp4_dequantize(const nvfp4_tensor* q, void* y, nvfp4_dtype dt, int64_t ld,
+nvfp4_status nvfp4_dequantize(const nvfp4_tensor* q, void* y, int32_t dt /* nvfp4_dtype */, int64_t ld,
                               void* stream);
 
 /* Re-quantize a row-blocked NVFP4 tensor `in` (rows x cols, SCALE_1D) along
@@ -213,8 +216,8 @@ nvfp4_status nvfp4_requantize(const nvfp4_tensor* in, const nvfp4_quant_opts* op
  * Source: asector.ru page, "NVFP4 и Blackwell" (scaled compute with
  * high-precision accumulation); iitak.ru page, "Детали" (the expert layers
  * whose feed-forward the SwiGLU epilogue closes). */
-nvfp4_status nvfp4_gemm(const nvfp4_tensor* A, const nvfp4_tensor* B, void* C, nvfp4_dtype c_dt,
-                        int64_t ldc, nvfp4_epilogue ep, void* stream);
+nvfp4_status nvfp4_gemm(const nvfp4_tensor* A, const nvfp4_tensor* B, void* C, int32_t c_dt /* nvfp4_dtype */,
+                        int64_t ldc, int32_t ep /* nvfp4_epilogue */, void* stream);
 
 /* Grouped (mixture-of-experts) GEMM.  A is sum_g M_g x K with one tensor
  * scale; rows offsets[g] .. offsets[g+1]-1 belong to group g (offsets: DEVICE
@@ -238,7 +241,7 @@ nvfp4_status nvfp4_gemm(const nvfp4_tensor* A, const nvfp4_tensor* B, void* C, n
  * and "Но" (experts spread over GPUs). */
 nvfp4_status nvfp4_grouped_gemm(int32_t G, const nvfp4_tensor* A, const int64_t* offsets,
                                 const nvfp4_tensor* B, void* C,
-                                nvfp4_dtype c_dt, int64_t ldc, nvfp4_epilogue ep, float* amax_out,
+                                int32_t c_dt /* nvfp4_dtype */, int64_t ldc, int32_t ep /* nvfp4_epilogue */, float* amax_out,
                                 void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
@@ -286,8 +289,8 @@ typedef struct {
  * ld * sizeof(dtype) % 16 == 0, x and out->codes 16-byte aligned; out->rows
  * and out->cols as the layout implies.  rows == 0 or cols == 0 is a no-op.
  * Errors as for nvfp4_quantize. */
-nvfp4_status nvfp4_mx_quantize(const void* x, nvfp4_dtype dt, int64_t rows, int64_t cols, int64_t ld,
-                               nvfp4_layout layout, nvfp4_round round, uint64_t sr_seed,
+nvfp4_status nvfp4_mx_quantize(const void* x, int32_t dt /* nvfp4_dtype */, int64_t rows, int64_t cols, int64_t ld,
+                               int32_t layout /* nvfp4_layout */, int32_t round /* nvfp4_round */, uint64_t sr_seed,
                                nvfp4_mx_tensor* out, void* stream);
 
 /* y = value(code) * 2^(scale byte - 127) as one binary32 rounding (exact
@@ -295,7 +298,7 @@ nvfp4_status nvfp4_mx_quantize(const void* x, nvfp4_dtype dt, int64_t rows, int6
  * nearest-even BF16 of that binary32 value.  y is q->rows x q->cols, row
  * stride ld elements.  Requirements: q->cols % 32 == 0, ld >= q->cols,
  * ld * sizeof(dtype) % 16 == 0, y and q->codes 16-byte aligned. */
-nvfp4_status nvfp4_mx_dequantize(const nvfp4_mx_tensor* q, void* y, nvfp4_dtype dt, int64_t ld,
+nvfp4_status nvfp4_mx_dequantize(const nvfp4_mx_tensor* q, void* y, int32_t dt /* nvfp4_dtype */, int64_t ld,
                                  void* stream);
 
 /* How nvfp4_mx_gemm accumulates.
@@ -329,11 +332,11 @@ typedef enum { NVFP4_MX_ACC_NATIVE = 0, NVFP4_MX_ACC_EXACT = 1 } nvfp4_mx_accum;
  * codes 16-byte aligned, scales 2-byte aligned, C aligned to its element.
  * Source: asector.ru page, "NVFP4 и Blackwell" (block-scaled tensor-core
  * compute); iitak.ru page, "Как это работает" (MXFP8 in the backward pass). */
-nvfp4_status nvfp4_mx_gemm(const nvfp4_mx_tensor* A, const nvfp4_mx_tensor* B, void* C, nvfp4_dtype c_dt,
+nvfp4_status nvfp4_mx_gemm(const nvfp4_mx_tensor* A, const nvfp4_mx_tensor* B, void* C, int32_t c_dt /* nvfp4_dtype */,
                            int64_t ldc, int32_t accum, void* stream);
 
 /* Static description of a status code. */
-const char* nvfp4_status_string(nvfp4_status s);
+const char* nvfp4_status_string(int32_t s /* nvfp4_status */);
 
 /* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
 int32_t nvfp4_version(void);
