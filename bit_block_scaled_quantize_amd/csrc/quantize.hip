@@ -62,14 +62,30 @@ __device__ __forceinline__ float tensor_amax_of(const float* __restrict__ src, i
     return a;
 }
 
+template <int NT = 256>
 __device__ __forceinline__ void store_partial(float a, float* __restrict__ partial) {
-    __shared__ float red[4];
+    __shared__ float red[NT / 64];
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) a = fmaxf(a, __shfl_xor(a, o, 64));
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = a;
     __syncthreads();
-    if (threadIdx.x == 0)
-        partial[blockIdx.y * gridDim.x + blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    if (threadIdx.x == 0) {
+        float m = red[0];
+#pragma unroll
+        for (int k = 1; k < NT / 64; ++k) m = fmaxf(m, red[k]);
+        partial[blockIdx.y * gridDim.x + blockIdx.x] = m;
+    }
+}
+
+// Element e of a raw 16-byte chunk (bf16 pairs or fp32).
+template <typename T>
+__device__ __forceinline__ float chunk_elem(const uint4& q, int e) {
+    if constexpr (sizeof(T) == 2) {
+        const uint32_t w = (e >> 1) == 0 ? q.x : (e >> 1) == 1 ? q.y : (e >> 1) == 2 ? q.z : q.w;
+        return (e & 1) ? __uint_as_float(w & 0xFFFF0000u) : __uint_as_float(w << 16);
+    } else {
+        return __uint_as_float(e == 0 ? q.x : e == 1 ? q.y : e == 2 ? q.z : q.w);
+    }
 }
 
 // 16-byte chunk j of row `row` as binary32 (8 bf16 or 4 fp32 values).
@@ -160,35 +176,39 @@ __global__ void __launch_bounds__(256) k_amax_hadamard_rows(const T* __restrict_
 }
 
 // Partial maxima with the transform down columns (16 consecutive rows;
-// rows % 16 == 0).  A thread owns a 16-row x 16-byte patch.
+// rows % 16 == 0).  A thread owns a 16-row x 16-byte patch, kept as the 16
+// loaded chunks and unpacked one column at a time (BF16: 64 registers for the
+// chunks instead of 128 for the unpacked values), in 512-thread workgroups:
+// the grid is capped at kMaxPartials workgroups, so the threads per
+// workgroup set how many loads are in flight.
+constexpr int kAmaxColsThreads = 512;
+
 template <typename T>
-__global__ void __launch_bounds__(256) k_amax_hadamard_cols(const T* __restrict__ x, int64_t rows,
+__global__ void __launch_bounds__(kAmaxColsThreads) k_amax_hadamard_cols(const T* __restrict__ x, int64_t rows,
                                                             int64_t cols, int64_t ld,
                                                             uint32_t sign_mask,
                                                             float* __restrict__ partial) {
-    constexpr int CH = 16 / sizeof(T);
+    constexpr int CH = 16 / sizeof(T), NT = kAmaxColsThreads;
     const int64_t nch = (cols + CH - 1) / CH;
     const int64_t nrb = rows / 16;
     float a = 0.0f;
     for (int64_t rb = blockIdx.y; rb < nrb; rb += gridDim.y) {
-        for (int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x; j < nch; j += (int64_t)gridDim.x * 256) {
-            float col[CH][16];
+        for (int64_t j = (int64_t)blockIdx.x * NT + threadIdx.x; j < nch; j += (int64_t)gridDim.x * NT) {
+            uint4 raw[16];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                float v[8];
-                load_chunk(x + (rb * 16 + i) * ld, j, v);
-#pragma unroll
-                for (int e = 0; e < CH; ++e) col[e][i] = v[e];
-            }
+            for (int i = 0; i < 16; ++i) raw[i] = *reinterpret_cast<const uint4*>(x + (rb * 16 + i) * ld + j * CH);
             const int64_t valid = cols - j * CH;
 #pragma unroll
             for (int e = 0; e < CH; ++e) {
-                const float t = hadamard16_absmax(col[e], sign_mask);
+                float col[16];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) col[i] = chunk_elem<T>(raw[i], e);
+                const float t = hadamard16_absmax(col, sign_mask);
                 if (e < valid) a = fmaxf(a, t);
             }
         }
     }
-    store_partial(a, partial);
+    store_partial<NT>(a, partial);
 }
 
 // tensor_scale (and amax_out) of an empty tensor: no element kernel runs.
@@ -365,17 +385,6 @@ struct ColTile {
     static constexpr int LPB = 16 / CH;          // lanes per 16-element row block
     static constexpr int STRIDE = 136;           // LDS bytes per tile row
 };
-
-// Element e of a raw 16-byte chunk (bf16 pairs or fp32).
-template <typename T>
-__device__ __forceinline__ float chunk_elem(const uint4& q, int e) {
-    if constexpr (sizeof(T) == 2) {
-        const uint32_t w = (e >> 1) == 0 ? q.x : (e >> 1) == 1 ? q.y : (e >> 1) == 2 ? q.z : q.w;
-        return (e & 1) ? __uint_as_float(w & 0xFFFF0000u) : __uint_as_float(w << 16);
-    } else {
-        return __uint_as_float(e == 0 ? q.x : e == 1 ? q.y : e == 2 ? q.z : q.w);
-    }
-}
 
 // Element e of a raw 8-byte unit.
 template <typename T>
@@ -636,9 +645,12 @@ __global__ void __launch_bounds__(256) k_quant_2d(const T* __restrict__ x, int64
 // ============================================================ dequantize
 // A lane expands half of a 16-element block (8 elements: one code word and
 // the block's multiplier) of each of 8 rows; the 64 lanes of a wave cover 32
-// blocks (512 columns) from 512 * blockIdx.x, so each wave-wide store writes
-// 1 KiB (bf16; 2 KiB as two stores for fp32) of one row contiguously and each
-// code load reads 256 contiguous bytes.  Codes are expanded two at a time by
+// blocks (512 columns), so each wave-wide store writes 1 KiB (bf16; 2 KiB as
+// two stores for fp32) of one row contiguously and each code load reads 256
+// contiguous bytes.  The four waves of a workgroup sit side by side on the
+// same 8 rows (2048 columns from 2048 * blockIdx.x), so every 128-byte line of
+// scale bytes is read by one workgroup instead of four (with waves stacked
+// over 32 rows of 512 columns, 8192^2 to BF16: 28.4 -> 26.7 us).  Codes are expanded two at a time by
 // the gfx950 FP4 unpack instruction (scale operand 1.0, so the values are
 // exact), then multiplied by the block multiplier (exact: at most 6
 // significant bits) and by s_t (one rounding).
@@ -652,12 +664,12 @@ __global__ void __launch_bounds__(256) k_dequant(const uint8_t* __restrict__ cod
     const int64_t nb = cols / 16;
     const int lane = threadIdx.x & 63;
     const int hf = lane & 1;
-    const int64_t b = (int64_t)blockIdx.x * 32 + (lane >> 1);
+    const int64_t b = (int64_t)blockIdx.x * 128 + 32 * (threadIdx.x >> 6) + (lane >> 1);
     if (b >= nb) return;
-    const int64_t nrg = (rows + 31) / 32;
+    const int64_t nrg = (rows + 7) / 8;
     const int sshift = scale_2d ? 4 : 0;
     for (int64_t rg = blockIdx.y; rg < nrg; rg += gridDim.y) {
-        const int64_t r0 = rg * 32 + 8 * (threadIdx.x >> 6);
+        const int64_t r0 = rg * 8;
         uint32_t cw[8], sb[8];
         // rows past the end read the last row (never stored), and the scale
         // row is r >> 4 for 16x16 blocks, so the loads carry no branch and
@@ -893,9 +905,9 @@ int amax_partials(const T* x, int64_t rows, int64_t cols, int64_t ld, int hadama
         hipLaunchKernelGGL(k_amax_hadamard_rows<T>, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, s, x,
                            rows, cols, ld, sign_mask, ws);
     } else if (hadamard_dim == 2) {   // down columns
-        gx = std::min<int64_t>(std::max<int64_t>(cdiv(cdiv(cols, CH), 256), 1), kMaxPartials);
+        gx = std::min<int64_t>(std::max<int64_t>(cdiv(cdiv(cols, CH), kAmaxColsThreads), 1), kMaxPartials);
         gy = std::min<int64_t>(std::max<int64_t>(rows / 16, 1), kMaxPartials / gx);
-        hipLaunchKernelGGL(k_amax_hadamard_cols<T>, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, s, x,
+        hipLaunchKernelGGL(k_amax_hadamard_cols<T>, dim3((unsigned)gx, (unsigned)gy), dim3(kAmaxColsThreads), 0, s, x,
                            rows, cols, ld, sign_mask, ws);
     } else {
         // a contiguous tensor streams as one long row
@@ -1059,7 +1071,7 @@ hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, const 
                              int64_t rows, int64_t cols, bool scale_2d, void* y, bool bf16,
                              int64_t ld, hipStream_t s) {
     if (rows == 0 || cols == 0) return hipSuccess;
-    dim3 g((unsigned)cdiv(cols / 16, 32), grid_y(cdiv(rows, 32)));
+    dim3 g((unsigned)cdiv(cols / 16, 128), grid_y(cdiv(rows, 8)));
     if (bf16)
         hipLaunchKernelGGL(k_dequant<uint16_t>, g, dim3(256), 0, s, codes, scales, ts, rows, cols,
                            (int)scale_2d, static_cast<uint16_t*>(y), ld);
