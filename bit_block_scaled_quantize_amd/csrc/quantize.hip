@@ -481,6 +481,46 @@ __device__ __forceinline__ void tile_row_blocks(const uint4 (&raw)[8], int64_t R
     }
 }
 
+// Sign-flip words of the BF16 transform path below: bit 31 of sflip[i] is
+// bit i of sign_mask.
+__device__ __forceinline__ void sign_flips16(uint32_t sign_mask, uint32_t (&sflip)[16]) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sflip[i] = ((sign_mask >> i) & 1u) << 31;
+}
+
+// Column block e of a 16-row unit q (row i's 8 bytes in q[i]: UE columns):
+// codes into w[0..1] (rows in order), the block scale returned.  idx is the
+// output index of the block's first element (its draws).  BF16 with the
+// transform: row i's sign flip rides on the unpack (adding 2^31 flips the top
+// bit; sflip from sign_flips16), and the multiply by 1/4 on the block
+// multiplier (encode_quarter16).
+template <typename T, bool SR, bool RHT>
+__device__ __forceinline__ BlockScale col_unit_block(const uint2 (&q)[16], int e, const uint32_t (&sflip)[16],
+                                                     uint32_t sign_mask, const TensorScale& ts, uint64_t seed,
+                                                     uint64_t idx, uint32_t (&w)[2]) {
+    constexpr bool QUARTER = RHT && sizeof(T) == 2;
+    float col[16];
+    if constexpr (QUARTER) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const uint32_t wd2 = (e >> 1) == 0 ? q[i].x : q[i].y;
+            col[i] = __uint_as_float((e & 1) ? ((wd2 & 0xFFFF0000u) ^ sflip[i]) : ((wd2 << 16) + sflip[i]));
+        }
+        hadamard16_sums(col);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) col[i] = unit_elem<T>(q[i], e);
+        if (RHT) hadamard16(col, sign_mask);
+    }
+    const float ab = QUARTER ? 0.25f * absmax16(col) : absmax16(col);
+    const BlockScale bs = block_scale(ab, ts.six_st, ts.rtab);
+    uint32_t wd[8];
+    if (SR) philox_words16(seed, kStreamCol, idx, wd);
+    if constexpr (QUARTER) encode_quarter16<SR>(col, bs, ab, wd, w);
+    else encode<SR, 16, sizeof(T) == 2 && !RHT>(col, bs, ab, wd, w);
+    return bs;
+}
+
 // Column blocks of a staged tile (after the barrier): thread t takes row band
 // t % 16 and 8-byte unit t / 16 (16 rows x UE columns), i.e. UE whole column
 // blocks of the transposed output.
@@ -498,13 +538,8 @@ __device__ __forceinline__ void tile_col_blocks(const uint8_t* tile, int64_t R0,
 #pragma unroll
     for (int i = 0; i < 16; ++i)
         q[i] = *reinterpret_cast<const uint2*>(tile + (16 * rb + i) * STRIDE + 8 * (u ^ rb));
-    // BF16 with the transform: row i's sign flip rides on the unpack (adding
-    // 2^31 flips the top bit), and the multiply by 1/4 on the block multiplier
-    // (encode_quarter16)
-    constexpr bool QUARTER = RHT && sizeof(T) == 2;
     uint32_t sflip[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) sflip[i] = QUARTER ? ((sign_mask >> i) & 1u) << 31 : 0u;
+    sign_flips16(sign_mask, sflip);
     // the lane's output addresses and draw index for column C0 + UE u, stepped
     // by wave-uniform multiples of a column
     const int64_t cl0 = C0 + UE * u;
@@ -515,26 +550,8 @@ __device__ __forceinline__ void tile_col_blocks(const uint8_t* tile, int64_t R0,
     for (int e = 0; e < UE; ++e) {
         const int64_t c = cl0 + e;
         if (c >= cols) continue;  // (not break: the loop must unroll fully)
-        float col[16];
-        if constexpr (QUARTER) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const uint32_t wd2 = (e >> 1) == 0 ? q[i].x : q[i].y;
-                col[i] = __uint_as_float((e & 1) ? ((wd2 & 0xFFFF0000u) ^ sflip[i]) : ((wd2 << 16) + sflip[i]));
-            }
-            hadamard16_sums(col);
-        } else {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) col[i] = unit_elem<T>(q[i], e);
-            if (RHT) hadamard16(col, sign_mask);
-        }
-        const float ab = QUARTER ? 0.25f * absmax16(col) : absmax16(col);
-        const BlockScale bs = block_scale(ab, ts.six_st, ts.rtab);
-        uint32_t wd[8];
-        if (SR) philox_words16(seed, kStreamCol, cidx0 + (uint64_t)e * rows, wd);
         uint32_t w[2];
-        if constexpr (QUARTER) encode_quarter16<SR>(col, bs, ab, wd, w);
-        else encode<SR, 16, sizeof(T) == 2 && !RHT>(col, bs, ab, wd, w);
+        const BlockScale bs = col_unit_block<T, SR, RHT>(q, e, sflip, sign_mask, ts, seed, cidx0 + (uint64_t)e * rows, w);
         // non-temporal as in the row kernel: the 16 lanes of a column write
         // one whole 128-byte line
         typedef uint32_t v2u_t __attribute__((ext_vector_type(2)));
@@ -782,11 +799,21 @@ __global__ void __launch_bounds__(256) k_amax_req(const uint8_t* __restrict__ ic
 //   per tile: thread t takes row t's chunk of that tile (32 codes) and its two
 //     multipliers, dequantizes them into binary32 in the LDS layout of the
 //     FP32 column tile, and the column phase runs exactly as for FP32 input.
-// Workgroups are grouped by XCD in runs of 8 tiles along x (xcd_tile), so the
-// 8 workgroups that share each 128-byte line of scale bytes read it through
-// one L2.
-constexpr int kReqTiles = 8;
-
+// A workgroup re-quantizes a tile of 256 rows x 256 columns.  Its codes (128
+// bytes of each row, 16-byte chunk t % 8 of rows t / 8 + 32 k, so every wave
+// load reads 8 whole 128-byte lines) go to LDS in the transpose tile's layout
+// (8-byte unit j of row r at unit j ^ (r / 16 % 16), rows 136 bytes apart),
+// and its scale bytes transposed (the bytes of column block u for rows
+// 4m .. 4m + 3 in dword 65 u + m).  After the one barrier, thread t takes row
+// band t % 16 and column block t / 16 (16 rows x 16 columns): 16 8-byte code
+// reads and 4 scale-dword reads give it the block, which it dequantizes one
+// column pair at a time (x = fl(fl(v * e4m3(sb)) * s_t), as dequant8) into the
+// column encoder of the transpose tile.  The 16 lanes of a column block share
+// it, so each wave-wide code store writes 4 whole 128-byte lines.  Workgroups
+// are grouped by XCD in runs of 8 tiles along x (xcd_tile), so the 8
+// workgroups that share each 128-byte line of scale bytes read it through one
+// L2.  (Against 8 phases of 32 columns staged as binary32 through LDS, with
+// 16 barriers and 68 KB of LDS per workgroup, on 8192^2: see the launcher.)
 template <bool SR, bool RHT>
 __global__ void __launch_bounds__(256) k_requant_col(const uint8_t* __restrict__ icodes,
                                                      const uint8_t* __restrict__ iscales,
@@ -797,90 +824,115 @@ __global__ void __launch_bounds__(256) k_requant_col(const uint8_t* __restrict__
                                                      uint8_t* __restrict__ cscales,
                                                      float* __restrict__ cts, float* amax_out,
                                                      int xcd_group) {
-    constexpr int STRIDE = ColTile<float>::STRIDE;  // 32 binary32 columns + padding
-    __shared__ __attribute__((aligned(16))) uint8_t tile[256 * STRIDE];
-    __shared__ __attribute__((aligned(16))) uint8_t raw[256 * 128];
+    constexpr int STRIDE = 136;
+    __shared__ __attribute__((aligned(16))) uint8_t ctile[256 * STRIDE];
+    __shared__ uint32_t stile[16 * 65];
     const int t = threadIdx.x;
     const TileXY tl = xcd_tile(xcd_group);
-    const int64_t R0 = tl.y * 256, Cb = tl.x * (32 * kReqTiles);
+    const int64_t R0 = tl.y * 256, C0 = tl.x * 256;
     const int64_t cb = cols / 2, sb = cols / 16;  // code and scale bytes per row
 
-    // ---- codes: chunk c = t % 8 of rows t / 8 + 32 k.  Rows past the end
-    // read a clamped in-range row (their bands are never encoded); a chunk
-    // with only 16 valid columns (cols % 32 == 16) reads its valid half twice,
-    // and chunks past the last column read the row's first chunk (neither
-    // copy is ever encoded).
-    const int c = t & 7;
-    const int64_t C0 = Cb + 32 * c;
-    const int64_t coff = C0 < cols ? C0 / 2 : 0;
-    const bool whole = C0 + 32 <= cols;
+    // ---- codes.  Rows past the end read a clamped in-range row (their bands
+    // are never encoded); a chunk with only 16 valid columns (cols % 32 == 16)
+    // fills its upper half with zeros, and chunks past the last column load
+    // nothing (neither is ever encoded).
+    const int ch = t & 7, lr0 = t >> 3;
+    const int64_t cc = C0 + 32 * ch;
     uint4 q[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-        const int64_t gr = min(R0 + (t >> 3) + 32 * k, rows - 1);
-        const uint8_t* cp = icodes + gr * cb + coff;
-        if (whole) {
+        const int64_t gr = min(R0 + lr0 + 32 * k, rows - 1);
+        const uint8_t* cp = icodes + gr * cb + cc / 2;
+        q[k] = make_uint4(0u, 0u, 0u, 0u);
+        if (cc + 32 <= cols) {
             q[k] = *reinterpret_cast<const uint4*>(cp);
-        } else {
+        } else if (cc < cols) {
             const uint2 lo = *reinterpret_cast<const uint2*>(cp);
-            q[k] = make_uint4(lo.x, lo.y, lo.x, lo.y);
+            q[k] = make_uint4(lo.x, lo.y, 0u, 0u);
         }
     }
-    // ---- scale bytes of row t for the 8 tiles (clamped like the codes)
-    const int64_t sr = min(R0 + t, rows - 1);
-    uint32_t sv[4];
-    if (sb % 16 == 0 && (reinterpret_cast<uintptr_t>(iscales) & 15) == 0 && Cb + 256 <= cols) {
-        const uint4 v = *reinterpret_cast<const uint4*>(iscales + sr * sb + Cb / 16);
-        sv[0] = v.x; sv[1] = v.y; sv[2] = v.z; sv[3] = v.w;
+    // ---- scale bytes of row t for the 16 column blocks (clamped like the codes)
+    const int64_t srow = min(R0 + t, rows - 1);
+    uint32_t sv4[4];
+    if (sb % 16 == 0 && (reinterpret_cast<uintptr_t>(iscales) & 15) == 0 && C0 + 256 <= cols) {
+        const uint4 v = *reinterpret_cast<const uint4*>(iscales + srow * sb + C0 / 16);
+        sv4[0] = v.x; sv4[1] = v.y; sv4[2] = v.z; sv4[3] = v.w;
     } else {
-        uint8_t b[16];
+        uint32_t b[16];
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-            const int64_t sc = Cb / 16 + j;
-            b[j] = iscales[sr * sb + (sc < sb ? sc : sb - 1)];
+            const int64_t sc = C0 / 16 + j;
+            b[j] = sc < sb ? iscales[srow * sb + sc] : 0u;
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            sv[j] = b[4 * j] | (b[4 * j + 1] << 8) | (b[4 * j + 2] << 16) | ((uint32_t)b[4 * j + 3] << 24);
+        for (int j = 0; j < 4; ++j) sv4[j] = b[4 * j] | (b[4 * j + 1] << 8) | (b[4 * j + 2] << 16) | (b[4 * j + 3] << 24);
     }
     const float st_in = its[0];
     const TensorScale ts = prologue(amax_src, n_part, cts, nullptr, amax_out);
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-        const int r = (t >> 3) + 32 * k;
-        *reinterpret_cast<uint4*>(raw + r * 128 + 16 * (c ^ (r & 7))) = q[k];
+        const int lr = lr0 + 32 * k;
+        const int sw = (lr >> 4) & 15;
+        uint8_t* rowp = ctile + lr * STRIDE;
+        *reinterpret_cast<uint2*>(rowp + 8 * ((2 * ch) ^ sw)) = make_uint2(q[k].x, q[k].y);
+        *reinterpret_cast<uint2*>(rowp + 8 * ((2 * ch + 1) ^ sw)) = make_uint2(q[k].z, q[k].w);
+    }
+    {
+        uint8_t* const sbytes = reinterpret_cast<uint8_t*>(stile);
+#pragma unroll
+        for (int u = 0; u < 16; ++u) sbytes[4 * (65 * u + (t >> 2)) + (t & 3)] = (uint8_t)(sv4[u >> 2] >> (8 * (u & 3)));
     }
     __syncthreads();
 
-    const int sw = (t >> 4) & 15;
-    uint8_t* rowp = tile + t * STRIDE;
-    // a rolled loop: unrolled, the eight copies of the column encoder made the
-    // kernel larger than the instruction cache
-#pragma unroll 1
-    for (int k = 0; k < kReqTiles; ++k) {
-        const int64_t T0 = Cb + 32 * k;
-        if (T0 >= cols) break;  // uniform across the workgroup
-        if (k > 0) __syncthreads();  // the previous tile's column reads are done
-        const uint4 w = *reinterpret_cast<const uint4*>(raw + t * 128 + 16 * (k ^ (t & 7)));
-        // (selects, not a dynamically indexed register array)
-        const int kp = k >> 1;
-        const uint32_t swd = kp == 0 ? sv[0] : kp == 1 ? sv[1] : kp == 2 ? sv[2] : sv[3];
-        const uint32_t sw2 = swd >> (16 * (k & 1));
-        const float m0 = e4m3_value(sw2 & 0xFFu), m1 = e4m3_value((sw2 >> 8) & 0xFFu);
-        float v[32];
-        dequant8(w.x, m0, st_in, v);
-        dequant8(w.y, m0, st_in, v + 8);
-        // a tile with 16 valid columns (the last, when cols % 32 == 16) has its
-        // valid half copied into the upper half: never encoded
-        dequant8(w.z, T0 + 32 <= cols ? m1 : m0, st_in, v + 16);
-        dequant8(w.w, T0 + 32 <= cols ? m1 : m0, st_in, v + 24);
+    // ---- column blocks: band rb, column block u (16 columns)
+    const int rb = t & 15, u = t >> 4;
+    const int64_t r0 = R0 + 16 * rb, c0 = C0 + 16 * u;
+    if (r0 >= rows || c0 >= cols) return;  // (rows, cols % 16 == 0: whole blocks; no barrier follows)
+    uint2 w16[16];
 #pragma unroll
-        for (int j = 0; j < 16; ++j)
-            *reinterpret_cast<uint2*>(rowp + 8 * (j ^ sw)) =
-                make_uint2(__float_as_uint(v[2 * j]), __float_as_uint(v[2 * j + 1]));
-        __syncthreads();
-        if (R0 + 16 * (t & 15) < rows)  // (a band past the end: no column work, but stay for the barriers)
-            tile_col_blocks<float, SR, RHT>(tile, R0, T0, rows, cols, ts, seed, sign_mask, ccodes, cscales);
+    for (int i = 0; i < 16; ++i) w16[i] = *reinterpret_cast<const uint2*>(ctile + (16 * rb + i) * STRIDE + 8 * (u ^ rb));
+    float sv[16];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const uint32_t d = stile[65 * u + 4 * rb + m];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sv[4 * m + j] = e4m3_value((d >> (8 * j)) & 0xFFu);
+    }
+    uint32_t sflip[16];
+    sign_flips16(sign_mask, sflip);
+    // the lane's output addresses and draw index for column c0, stepped by
+    // wave-uniform multiples of a column
+    uint8_t* const cdst0 = ccodes + c0 * (rows / 2) + r0 / 2;
+    uint8_t* const csdst0 = cscales + c0 * (rows / 16) + r0 / 16;
+    const uint64_t cidx0 = (uint64_t)(c0 * rows + r0);
+    // (a rolled loop over the column pairs; each row's code word is shifted a
+    // byte per pair rather than indexed, which would put w16 in scratch)
+    uint32_t wcur[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) wcur[i] = w16[i].x;
+#pragma unroll 1
+    for (int p = 0; p < 8; ++p) {
+        // columns 2p and 2p + 1: code byte p of every row, now byte 0 of wcur
+        uint2 x2[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const float2 v = e2m1x2_unpack(wcur[i], 0);
+            x2[i] = make_uint2(__float_as_uint((v.x * sv[i]) * st_in), __float_as_uint((v.y * sv[i]) * st_in));
+            wcur[i] = p == 3 ? w16[i].y : wcur[i] >> 8;
+        }
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int64_t j = 2 * p + e;
+            uint32_t cw[2];
+            const BlockScale bs =
+                col_unit_block<float, SR, RHT>(x2, e, sflip, sign_mask, ts, seed, cidx0 + (uint64_t)j * rows, cw);
+            // non-temporal as in the column kernels: the 16 lanes of a column
+            // write one whole 128-byte line
+            typedef uint32_t v2u_t __attribute__((ext_vector_type(2)));
+            const v2u_t cv = {cw[0], cw[1]};
+            __builtin_nontemporal_store(cv, reinterpret_cast<v2u_t*>(cdst0 + j * (rows / 2)));
+            csdst0[j * (rows / 16)] = (uint8_t)bs.byte;
+        }
     }
 }
 
@@ -1052,7 +1104,9 @@ hipError_t launch_requantize(const uint8_t* icodes, const uint8_t* iscales, cons
         amax = ws;
         np = (int)gx;
     }
-    dim3 g((unsigned)cdiv(cols, 32 * kReqTiles), (unsigned)cdiv(rows, 256));
+    // (8192^2, stochastic rounding: 50.5 us with 8 binary32 phases per
+    // workgroup, see the kernel)
+    dim3 g((unsigned)cdiv(cols, 256), (unsigned)cdiv(rows, 256));
     // runs of 8 tiles along x share their scale-byte lines: one XCD each
     const int xg = g.x % 8 == 0 ? 8 : 1;
 #define NVFP4_REQ(SRV, RHTV)                                                                       \
