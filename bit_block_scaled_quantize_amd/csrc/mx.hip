@@ -281,23 +281,26 @@ __global__ void __launch_bounds__(256) k_mx_col(const T* __restrict__ x, int64_t
 // even from that binary32 value.  A lane expands 8 elements (8 E4M3 code
 // bytes or 4 E2M1 ones) of each of 8 rows; the 64 lanes of a wave cover 512
 // elements of a row, so each wave-wide store writes 1 KiB (bf16) of a row
-// contiguously.  The four waves of a workgroup sit side by side on the same
-// 8 rows (2048 elements), so a 128-byte line of scale bytes (4096 elements)
-// is read by two workgroups instead of eight.  (With 16 elements per lane its two 16-byte stores each
+// contiguously.  WX of the four waves sit side by side on each of 4 / WX
+// groups of 8 rows: with WX = 4 a 128-byte line of scale bytes (4096
+// elements) is read by two workgroups instead of eight.  The launcher takes
+// the largest WX whose span (512 WX elements) divides the width.  (With 16 elements per lane its two 16-byte stores each
 // covered every other 16 bytes of 2 KiB: 8192^2 to BF16, alternating builds on
 // one box, E2M1 44.2 -> 35.3 us, E4M3 42.4 -> 40.2 us.)
-template <int ELEM, typename TOut>
+template <int ELEM, typename TOut, int WX>
 __global__ void __launch_bounds__(256) k_mx_dequant(const uint8_t* __restrict__ codes,
                                                     const uint8_t* __restrict__ scales, int64_t rows,
                                                     int64_t cols, TOut* __restrict__ y, int64_t ld) {
     constexpr int EPL = 8;                            // elements per lane
     constexpr int CB = ELEM == kMxE4M3 ? 8 : 4;       // their code bytes
     const int64_t row_bytes = ELEM == kMxE4M3 ? cols : cols / 2;
-    const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int wv = threadIdx.x >> 6;
+    const int64_t b = (int64_t)blockIdx.x * (64 * WX) + 64 * (wv % WX) + (threadIdx.x & 63);
     if (b >= cols / EPL) return;
-    const int64_t nrg = (rows + 7) / 8;
+    constexpr int RG = 8 * (4 / WX);  // rows per workgroup
+    const int64_t nrg = (rows + RG - 1) / RG;
     for (int64_t rg = blockIdx.y; rg < nrg; rg += gridDim.y) {
-        const int64_t r0 = rg * 8;
+        const int64_t r0 = rg * RG + 8 * (wv / WX);
         uint32_t cw[8][2];
         int sx[8];
 #pragma unroll
@@ -399,9 +402,20 @@ hipError_t launch_mx_quantize(const void* x, bool bf16, int64_t rows, int64_t co
 hipError_t launch_mx_dequantize(const uint8_t* codes, const uint8_t* scales, int elem, int64_t rows,
                                 int64_t cols, void* y, bool bf16, int64_t ld, hipStream_t s) {
     if (rows == 0 || cols == 0) return hipSuccess;
-    dim3 g((unsigned)mx_cdiv(cols / 8, 256), mx_grid_y(mx_cdiv(rows, 8)));
-#define NVFP4_MXDQ(E, TO) \
-    hipLaunchKernelGGL((k_mx_dequant<E, TO>), g, dim3(256), 0, s, codes, scales, rows, cols, static_cast<TO*>(y), ld)
+    const int wx = cols % 2048 == 0 ? 4 : cols % 1024 == 0 ? 2 : 1;
+    dim3 g((unsigned)mx_cdiv(cols / 8, 64 * wx), mx_grid_y(mx_cdiv(rows, 8 * (4 / wx))));
+#define NVFP4_MXDQ(E, TO)                                                                                  \
+    do {                                                                                                   \
+        if (wx == 4)                                                                                       \
+            hipLaunchKernelGGL((k_mx_dequant<E, TO, 4>), g, dim3(256), 0, s, codes, scales, rows, cols,   \
+                               static_cast<TO*>(y), ld);                                                   \
+        else if (wx == 2)                                                                                  \
+            hipLaunchKernelGGL((k_mx_dequant<E, TO, 2>), g, dim3(256), 0, s, codes, scales, rows, cols,   \
+                               static_cast<TO*>(y), ld);                                                   \
+        else                                                                                               \
+            hipLaunchKernelGGL((k_mx_dequant<E, TO, 1>), g, dim3(256), 0, s, codes, scales, rows, cols,   \
+                               static_cast<TO*>(y), ld);                                                   \
+    } while (0)
     if (elem == kMxE4M3) {
         if (bf16) NVFP4_MXDQ(kMxE4M3, uint16_t); else NVFP4_MXDQ(kMxE4M3, float);
     } else {

@@ -664,14 +664,16 @@ __global__ void __launch_bounds__(256) k_quant_2d(const T* __restrict__ x, int64
 // the block's multiplier) of each of 8 rows; the 64 lanes of a wave cover 32
 // blocks (512 columns), so each wave-wide store writes 1 KiB (bf16; 2 KiB as
 // two stores for fp32) of one row contiguously and each code load reads 256
-// contiguous bytes.  The four waves of a workgroup sit side by side on the
-// same 8 rows (2048 columns from 2048 * blockIdx.x), so every 128-byte line of
-// scale bytes is read by one workgroup instead of four (with waves stacked
-// over 32 rows of 512 columns, 8192^2 to BF16: 28.4 -> 26.7 us).  Codes are expanded two at a time by
+// contiguous bytes.  WX of the four waves sit side by side (512 WX columns
+// from 512 WX * blockIdx.x) on each of 4 / WX groups of 8 rows: with WX = 4 a
+// 128-byte line of scale bytes (2048 columns) is read by one workgroup instead
+// of four (against WX = 1, 8192^2 to BF16: 28.4 -> 26.7 us).  The launcher
+// takes the largest WX whose span divides the width, so no wave idles at the
+// right edge.  Codes are expanded two at a time by
 // the gfx950 FP4 unpack instruction (scale operand 1.0, so the values are
 // exact), then multiplied by the block multiplier (exact: at most 6
 // significant bits) and by s_t (one rounding).
-template <typename TOut>
+template <typename TOut, int WX>
 __global__ void __launch_bounds__(256) k_dequant(const uint8_t* __restrict__ codes,
                                                  const uint8_t* __restrict__ scales,
                                                  const float* __restrict__ ts, int64_t rows,
@@ -681,12 +683,14 @@ __global__ void __launch_bounds__(256) k_dequant(const uint8_t* __restrict__ cod
     const int64_t nb = cols / 16;
     const int lane = threadIdx.x & 63;
     const int hf = lane & 1;
-    const int64_t b = (int64_t)blockIdx.x * 128 + 32 * (threadIdx.x >> 6) + (lane >> 1);
+    const int wv = threadIdx.x >> 6;
+    const int64_t b = (int64_t)blockIdx.x * (32 * WX) + 32 * (wv % WX) + (lane >> 1);
     if (b >= nb) return;
-    const int64_t nrg = (rows + 7) / 8;
+    constexpr int RG = 8 * (4 / WX);  // rows per workgroup
+    const int64_t nrg = (rows + RG - 1) / RG;
     const int sshift = scale_2d ? 4 : 0;
     for (int64_t rg = blockIdx.y; rg < nrg; rg += gridDim.y) {
-        const int64_t r0 = rg * 8;
+        const int64_t r0 = rg * RG + 8 * (wv / WX);
         uint32_t cw[8], sb[8];
         // rows past the end read the last row (never stored), and the scale
         // row is r >> 4 for 16x16 blocks, so the loads carry no branch and
@@ -1125,13 +1129,17 @@ hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, const 
                              int64_t rows, int64_t cols, bool scale_2d, void* y, bool bf16,
                              int64_t ld, hipStream_t s) {
     if (rows == 0 || cols == 0) return hipSuccess;
-    dim3 g((unsigned)cdiv(cols / 16, 128), grid_y(cdiv(rows, 8)));
-    if (bf16)
-        hipLaunchKernelGGL(k_dequant<uint16_t>, g, dim3(256), 0, s, codes, scales, ts, rows, cols,
-                           (int)scale_2d, static_cast<uint16_t*>(y), ld);
-    else
-        hipLaunchKernelGGL(k_dequant<float>, g, dim3(256), 0, s, codes, scales, ts, rows, cols,
-                           (int)scale_2d, static_cast<float*>(y), ld);
+    const int wx = cols % 2048 == 0 ? 4 : cols % 1024 == 0 ? 2 : 1;
+    dim3 g((unsigned)cdiv(cols / 16, 32 * wx), grid_y(cdiv(rows, 8 * (4 / wx))));
+#define NVFP4_DQ(TO, WXV)                                                                    \
+    hipLaunchKernelGGL((k_dequant<TO, WXV>), g, dim3(256), 0, s, codes, scales, ts, rows, cols, \
+                       (int)scale_2d, static_cast<TO*>(y), ld)
+    if (bf16) {
+        if (wx == 4) NVFP4_DQ(uint16_t, 4); else if (wx == 2) NVFP4_DQ(uint16_t, 2); else NVFP4_DQ(uint16_t, 1);
+    } else {
+        if (wx == 4) NVFP4_DQ(float, 4); else if (wx == 2) NVFP4_DQ(float, 2); else NVFP4_DQ(float, 1);
+    }
+#undef NVFP4_DQ
     return hipGetLastError();
 }
 
