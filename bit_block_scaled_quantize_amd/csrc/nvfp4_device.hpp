@@ -554,4 +554,33 @@ __device__ __forceinline__ TileXY xcd_tile(int xcd_group) {
     return r;
 }
 
+// As xcd_tile, but each XCD's run of xcd_group tiles covers xcd_group / 2
+// tiles along x on each of two consecutive tile rows (when the grid width is a
+// multiple of 4 xcd_group; a last odd tile row then keeps the dispatch order,
+// and other widths take the xcd_tile order).  Column-blocked outputs write 16 scale bytes per column
+// and tile, half of a 32-byte sector whose other half belongs to the tile
+// below: pairing the two rows on one XCD lets its L2 join the halves, where
+// runs along one row left them to two L2s.
+__device__ __forceinline__ TileXY xcd_tile_pairs(int xcd_group) {
+    const int64_t gx = gridDim.x, gy = gridDim.y;
+    const int64_t L = (int64_t)blockIdx.y * gx + blockIdx.x;
+    if (xcd_group > 1 && xcd_group % 2 == 0 && gx % (4 * xcd_group) == 0 && L < (gy / 2) * 2 * gx) {
+        const int64_t H = xcd_group / 2, blk = 8 * (int64_t)xcd_group;
+        const int64_t b = L / blk, w = L % blk;
+        const int64_t k = w % 8, j = w / 8;
+        const int64_t bpr = gx / (8 * H);  // blocks per pair of tile rows
+        TileXY r;
+        r.x = (b % bpr) * 8 * H + k * H + j % H;
+        r.y = (b / bpr) * 2 + j / H;
+        return r;
+    }
+    if (xcd_group > 1 && xcd_group % 2 == 0 && gx % (4 * xcd_group) == 0) {
+        TileXY r;
+        r.x = L % gx;
+        r.y = L / gx;
+        return r;
+    }
+    return xcd_tile(xcd_group);
+}
+
 }  // namespace nvfp4

@@ -578,7 +578,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) k
     constexpr int CH = ColTile<T>::CH, TWC = ColTile<T>::TWC, STRIDE = ColTile<T>::STRIDE;
     __shared__ __attribute__((aligned(16))) uint8_t tile[256 * STRIDE];
     const int t = threadIdx.x;
-    const TileXY tl = xcd_tile(xcd_group);
+    const TileXY tl = xcd_tile_pairs(xcd_group);
     const int64_t R0 = tl.y * 256, C0 = tl.x * TWC;
 
     // ---- load 256 rows x 128 bytes; stage into LDS
@@ -832,7 +832,7 @@ __global__ void __launch_bounds__(256) k_requant_col(const uint8_t* __restrict__
     __shared__ __attribute__((aligned(16))) uint8_t ctile[256 * STRIDE];
     __shared__ uint32_t stile[16 * 65];
     const int t = threadIdx.x;
-    const TileXY tl = xcd_tile(xcd_group);
+    const TileXY tl = xcd_tile_pairs(xcd_group);
     const int64_t R0 = tl.y * 256, C0 = tl.x * 256;
     const int64_t cb = cols / 2, sb = cols / 16;  // code and scale bytes per row
 
