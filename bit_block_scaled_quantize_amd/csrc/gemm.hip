@@ -201,32 +201,13 @@ __device__ __forceinline__ int b_tile_row(int wn, int j) {
     return SWIGLU ? ((j < 2 ? 0 : 128) + 64 * wn + 32 * (j & 1)) : 128 * wn + 32 * j;
 }
 
-typedef float f2_t __attribute__((ext_vector_type(2)));
-typedef __bf16 bf2_t __attribute__((ext_vector_type(2)));
-
-// Two values rounded to BF16 (nearest-even), packed: the first in the low half.
-__device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
-    const f2_t x = {a, b};
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf2_t));
-}
-
-// Buffer resource over `bytes` bytes of output from `base`.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t out_rsrc(void* base, int64_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)(uint32_t)min(bytes, (int64_t)0xFFFFFFFF),
-                                             0x00020000);
-}
-
 // Scale by the two tensor scales and write the wave's 128 x 128 tile (or, for
 // SwiGLU, its 128 x 64 gate/up pairs) of C.  Accumulator r of MFMA tile
 // (i, j) holds row 32i + 8(r/4) + 4h + r%4, column 32j + l32 of the wave tile.
 //
-// A wave tile wholly inside C (and byte offsets within it that fit 31 bits)
-// is written through a buffer resource based at its first element: each lane
-// at a fixed byte offset (4h rows and l32 columns in), each row's offset in a
-// scalar register and each 32-column block in the instruction's offset, so an
-// element costs its scaling, half a conversion (BF16: rows in pairs) and its
-// store.  Edge tiles, and the SwiGLU epilogue (whose activation dominates
-// its cost), take the per-element bounds checks.
+// A wave tile wholly inside C goes out through store_wave_block; edge tiles,
+// and the SwiGLU epilogue (whose activation dominates its cost), take
+// per-element bounds checks.
 template <bool GROUPED, bool SWIGLU, bool OUT_BF16>
 __device__ __forceinline__ void epilogue(const GemmArgs& p, float16_t (&acc)[4][4], int64_t m0,
                                          int64_t m_end, int g, int wm, int wn, int lane) {
@@ -264,31 +245,10 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, float16_t (&acc)[4][
         return;
     }
     const int64_t nw = (int64_t)blockIdx.x * kBN + 128 * wn;
-    constexpr int ES = OUT_BF16 ? 2 : 4;
-    if (mw + 128 <= m_end && nw + 128 <= Ng && p.ldc <= (int64_t)(INT32_MAX / (128 * ES))) {
-        const __amdgpu_buffer_rsrc_t rc =
-            out_rsrc(static_cast<char*>(p.C) + (mw * p.ldc + nw) * ES, (127 * p.ldc + 128) * ES);
-        const int ldb = (int)p.ldc * ES, vo = 4 * h * ldb + ES * l32;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int r = 0; r < 16; r += 2) {
-                const int so = (32 * i + 8 * (r >> 2) + (r & 3)) * ldb;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float v0 = alpha * acc[i][j][r], v1 = alpha * acc[i][j][r + 1];
-                    if (OUT_BF16) {
-                        const uint32_t b = bf16x2_rne(v0, v1);
-                        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)b, rc, vo + 32 * ES * j, so, 0);
-                        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(b >> 16), rc, vo + 32 * ES * j, so + ldb, 0);
-                    } else {
-                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v0), rc, vo + 32 * ES * j, so, 0);
-                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v1), rc, vo + 32 * ES * j, so + ldb, 0);
-                    }
-                }
-            }
+    if (mw + 128 <= m_end && nw + 128 <= Ng &&
+        store_wave_block<4, 4, OUT_BF16>(p.C, p.ldc, mw, nw, h, l32,
+                                         [&](int i, int j, int r) { return alpha * acc[i][j][r]; }))
         return;
-    }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll

@@ -913,6 +913,10 @@ __global__ void __launch_bounds__(512, 1) k_mx_gemm_full8(MxGemmArgs p) {
     __builtin_amdgcn_s_waitcnt(mx_vmcnt_at_most(0));
 
     const int64_t mw = m0 + 128 * wm, nw = n0 + 64 * wn;
+    if (mw + 128 <= M && nw + 64 <= N &&
+        store_wave_block<4, 2, OUT_BF16>(p.C, p.ldc, mw, nw, h, l32,
+                                         [&](int i, int j, int r) { return acc[i][j][r]; }))
+        return;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -1186,6 +1190,12 @@ __global__ void __launch_bounds__(256, 1) k_mx_gemm_exact_full(MxGemmArgs p) {
     __builtin_amdgcn_s_waitcnt(mx_vmcnt_at_most(0));
 
     const int64_t nw = n0 + 128 * wn;
+    if (m0 + 128 * wm + 128 <= M && nw + 128 <= N &&
+        store_wave_block<4, 4, OUT_BF16>(p.C, p.ldc, m0 + 128 * wm, nw, h, l32, [&](int i, int j, int r) {
+            return ldexpf(acc[i][j][r], rref[128 * wm + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3)] +
+                                            rref[kMxTile + 128 * wn + 32 * j + l32] - 254);
+        }))
+        return;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll

@@ -583,4 +583,50 @@ __device__ __forceinline__ TileXY xcd_tile_pairs(int xcd_group) {
     return xcd_tile(xcd_group);
 }
 
+// ------------------------------------------------------------ GEMM tile stores
+// Store a wave's block of I x J 32x32 MFMA accumulator tiles, scaled by
+// value(i, j, r) (accumulator r of tile (i, j): row 32 i + 8 (r / 4) + 4 h +
+// r % 4, column 32 j + l32 of the block), when the whole block -- 32 I rows
+// from row0 and 32 J columns from col0 -- lies inside C (the caller checks)
+// and 32 I rows of C span under 2^31 bytes (checked here: false is returned
+// and nothing is stored otherwise).  The stores go through a buffer resource
+// based at the block's first element: each lane at a fixed byte offset, each
+// row's offset in a scalar register, each 32-column block in the
+// instruction's immediate offset, rows converted to BF16 in pairs.  Written
+// the plain way, an element costs 64-bit address arithmetic, a bounds compare
+// and a branch around its store.
+typedef float gemm_f2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 gemm_bf2_t __attribute__((ext_vector_type(2)));
+
+template <int I, int J, bool OUT_BF16, typename Value>
+__device__ __forceinline__ bool store_wave_block(void* C, int64_t ldc, int64_t row0, int64_t col0, int h, int l32,
+                                                 Value value) {
+    constexpr int ES = OUT_BF16 ? 2 : 4;
+    if (ldc > (int64_t)(INT32_MAX / (32 * I * ES))) return false;
+    const int64_t bytes = ((32 * I - 1) * ldc + 32 * J) * ES;
+    const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+        static_cast<char*>(C) + (row0 * ldc + col0) * ES, (short)0, (int)(uint32_t)bytes, 0x00020000);
+    const int ldb = (int)ldc * ES, vo = 4 * h * ldb + ES * l32;
+#pragma unroll
+    for (int i = 0; i < I; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+            const int so = (32 * i + 8 * (r >> 2) + (r & 3)) * ldb;
+#pragma unroll
+            for (int j = 0; j < J; ++j) {
+                const float v0 = value(i, j, r), v1 = value(i, j, r + 1);
+                if (OUT_BF16) {
+                    const gemm_f2_t x = {v0, v1};
+                    const uint32_t b = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, gemm_bf2_t));
+                    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)b, rc, vo + 32 * ES * j, so, 0);
+                    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(b >> 16), rc, vo + 32 * ES * j, so + ldb, 0);
+                } else {
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v0), rc, vo + 32 * ES * j, so, 0);
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v1), rc, vo + 32 * ES * j, so + ldb, 0);
+                }
+            }
+        }
+    return true;
+}
+
 }  // namespace nvfp4
