@@ -201,13 +201,29 @@ __device__ __forceinline__ int b_tile_row(int wn, int j) {
     return SWIGLU ? ((j < 2 ? 0 : 128) + 64 * wn + 32 * (j & 1)) : 128 * wn + 32 * j;
 }
 
+// The lane index computed afresh (from an opaque all-ones mask), so that
+// nothing lane-derived is held through a K loop for the epilogue.
+__device__ __forceinline__ int fresh_lane_id() {
+    uint32_t ones = ~0u;
+    asm volatile("" : "+s"(ones));
+    return (int)__builtin_amdgcn_mbcnt_hi(ones, __builtin_amdgcn_mbcnt_lo(ones, 0u));
+}
+
+// h = g sigma(g) u in binary32, with the hardware's base-2 exponential and
+// reciprocal (each within about a unit in the last place): sigma(g) =
+// 1 / (1 + 2^(-g log2 e)), 0 once the power overflows (g below about -88.7).
+__device__ __forceinline__ float swiglu_h(float gt, float up) {
+    const float e = __builtin_amdgcn_exp2f(gt * -1.44269504088896341f);
+    return gt * __builtin_amdgcn_rcpf(1.0f + e) * up;
+}
+
 // Scale by the two tensor scales and write the wave's 128 x 128 tile (or, for
 // SwiGLU, its 128 x 64 gate/up pairs) of C.  Accumulator r of MFMA tile
 // (i, j) holds row 32i + 8(r/4) + 4h + r%4, column 32j + l32 of the wave tile.
 //
-// A wave tile wholly inside C goes out through store_wave_block; edge tiles,
-// and the SwiGLU epilogue (whose activation dominates its cost), take
-// per-element bounds checks.
+// A wave tile wholly inside C goes out through store_wave_block; edge tiles
+// take per-element bounds checks.  SwiGLU's amax: rounding to BF16 is
+// monotonic, so the largest |h| rounded once is the largest rounded |h|.
 template <bool GROUPED, bool SWIGLU, bool OUT_BF16>
 __device__ __forceinline__ void epilogue(const GemmArgs& p, float16_t (&acc)[4][4], int64_t m0,
                                          int64_t m_end, int g, int wm, int wn, int lane) {
@@ -219,6 +235,14 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, float16_t (&acc)[4][
         uint16_t* C = static_cast<uint16_t*>(p.C);
         const int64_t F = Ng / 2, jw = (int64_t)blockIdx.x * (kBN / 2) + 64 * wn;
         float amax = 0.0f;
+        if (mw + 128 <= m_end && jw + 64 <= F &&
+            store_wave_block<4, 2, true>(C, p.ldc, mw, jw, h, l32, [&](int i, int jj, int r) {
+                const float hv = swiglu_h(alpha * acc[i][jj][r], alpha * acc[i][jj + 2][r]);
+                amax = fmaxf(amax, fabsf(hv));
+                return hv;
+            })) {
+            amax = __uint_as_float(f32_to_bf16_rne(amax) << 16);
+        } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -228,15 +252,14 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, float16_t (&acc)[4][
                 for (int r = 0; r < 16; ++r) {
                     const int64_t m = mw + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
                     if (m < m_end && c < F) {
-                        const float gt = alpha * acc[i][jj][r];
-                        const float up = alpha * acc[i][jj + 2][r];
-                        const float hv = gt / (1.0f + expf(-gt)) * up;
+                        const float hv = swiglu_h(alpha * acc[i][jj][r], alpha * acc[i][jj + 2][r]);
                         const uint32_t b = f32_to_bf16_rne(hv);
                         C[m * p.ldc + c] = (uint16_t)b;
                         amax = fmaxf(amax, fabsf(__uint_as_float(b << 16)));
                     }
                 }
             }
+        }
         if (p.amax_out) {
 #pragma unroll
             for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
@@ -637,7 +660,7 @@ __global__ void __launch_bounds__(256, 1) k_gemm_ring(GemmArgs p) {
         // reads again) must land before the workgroup's LDS is released
         __builtin_amdgcn_s_waitcnt(vmcnt_at_most(0));
     }
-    epilogue<GROUPED, SWIGLU, OUT_BF16>(p, acc, m0, m_end, g, wm, wn, lane);
+    epilogue<GROUPED, SWIGLU, OUT_BF16>(p, acc, m0, m_end, g, wm, wn, fresh_lane_id());
 }
 
 // ============================================================ full-line kernel
@@ -864,12 +887,7 @@ __global__ void __launch_bounds__(256, 1) k_gemm_full(GemmArgs p) {
     // the tile's rows and group found again rather than kept through the loop
     // (held there, they cost the grouped SwiGLU instance a spilled register)
     const TileRows te = tile_rows<GROUPED>(p);
-    // the lane index computed afresh (from an opaque all-ones mask), so that
-    // nothing lane-derived is held through the K loop for the epilogue
-    uint32_t ones = ~0u;
-    asm volatile("" : "+s"(ones));
-    const int le = (int)__builtin_amdgcn_mbcnt_hi(ones, __builtin_amdgcn_mbcnt_lo(ones, 0u));
-    epilogue<GROUPED, SWIGLU, OUT_BF16>(p, acc, te.m0, te.m_end, te.g, wm, wn, le);
+    epilogue<GROUPED, SWIGLU, OUT_BF16>(p, acc, te.m0, te.m_end, te.g, wm, wn, fresh_lane_id());
 }
 
 __global__ void k_zero_float(float* p) {
