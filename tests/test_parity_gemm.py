@@ -95,6 +95,41 @@ def test_gemm_256_config(nv):
     check(out_to_f64(C), Cref, Wref, False, "gemm 256")
 
 
+@pytest.mark.parametrize("M,N,K", [(512, 512, 512), (300, 224, 1024), (256, 384, 1024)])
+@pytest.mark.parametrize("out", ["f32", "bf16", "swiglu"])
+def test_gemm_strided_output(nv, M, N, K, out):
+    """C written into a column slice of a wider buffer (row pitch = width +
+    96, first column 40): whole wave tiles are written through offsets formed
+    from the row pitch.  The slice matches the oracle (SwiGLU: its h), and
+    every byte outside it keeps the buffer's fill."""
+    a = W.student_t((M, K), 3.0, seed=M + 5)
+    b = W.normal((N, K), 0.02, seed=N + 7)
+    A, B = quant_host(a, O.ROW_1D), quant_host(b, O.BLK_2D)
+    width = N // 2 if out == "swiglu" else N
+    dt = torch.float32 if out == "f32" else torch.bfloat16
+    big = torch.empty((M, width + 96), dtype=dt, device="cuda")
+    big.view(torch.uint8).fill_(0xA5)
+    C = big[:, 40:40 + width]
+    if out == "swiglu":
+        nv.nvfp4_gemm(q_to_device(A, nv), q_to_device(B, nv), out=C, epilogue=nv.NVFP4_EPI_SWIGLU)
+    else:
+        nv.nvfp4_gemm(q_to_device(A, nv), q_to_device(B, nv), out=C)
+    got = out_to_f64(C.contiguous())
+    Cref, Wref = OB.gemm(A, B)
+    if out == "swiglu":
+        F = width
+        G_, U_ = Cref[:, :F], Cref[:, F:]
+        err = np.abs(got - O.swiglu(G_, U_))
+        tol = _swiglu_tol(G_, U_, Wref[:, :F], Wref[:, F:])
+        assert (err <= tol).all(), f"strided swiglu: {np.sum(err > tol)} entries out of tolerance"
+    else:
+        check(got, Cref, Wref, out == "bf16", f"strided gemm {M}x{N}x{K}")
+    es = big.element_size()
+    raw = big.view(torch.uint8)
+    assert bool((raw[:, :40 * es] == 0xA5).all()) and bool((raw[:, (40 + width) * es:] == 0xA5).all()), \
+        "bytes outside the output slice were written"
+
+
 # -------------------------------------------------- full-size sampled checks
 # At full size the oracle quantizes only the operand rows a sampled output
 # needs, with the whole tensor's amax (rows of a row-blocked tensor and

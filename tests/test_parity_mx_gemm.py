@@ -79,10 +79,11 @@ def tolerance(elem, K, W_, smax, cref, bf16, accum=NATIVE):
     return tol
 
 
-def check(nv, qa, qb, bf16=False, entries=None, exact=False, what="", accum=NATIVE):
+def check(nv, qa, qb, bf16=False, entries=None, exact=False, what="", accum=NATIVE, out=None):
     C = nv.nvfp4_mx_gemm(up(nv, qa), up(nv, qb), out_dtype=torch.bfloat16 if bf16 else torch.float32,
-                         accum=accum)
+                         accum=accum, out=out)
     torch.cuda.synchronize()
+    C = C.contiguous()
     if bf16:
         G = W.bf16_bits_to_f32(bf16_tensor_to_bits(C)).astype(np.float64)
     else:
@@ -217,3 +218,25 @@ def test_mx_gemm_8192_sampled(nv, elem):
     ni = np.concatenate([g.integers(0, n, 1024), [0, n - 1, 0, n - 1, 256, 255]])
     for accum in ACCUMS:
         check(nv, qa, qb, entries=(mi, ni), what="8192 sampled", accum=accum)
+
+
+@pytest.mark.parametrize("accum", ACCUMS)
+@pytest.mark.parametrize("elem", ELEMS)
+@pytest.mark.parametrize("shape", [(512, 512, 1024), (300, 200, 1024)])
+@pytest.mark.parametrize("bf16", [False, True])
+def test_mx_gemm_strided_output(nv, elem, shape, accum, bf16):
+    """C written into a column slice of a wider buffer (row pitch N + 96,
+    first column 40): the output addressing of whole wave tiles comes from
+    the row pitch.  The slice matches the oracle, and every byte outside it
+    keeps the buffer's fill."""
+    M, N, K = shape
+    qa = mxq(W.student_t((M, K), 3.0, seed=M + 31), elem)
+    qb = mxq(W.student_t((N, K), 3.0, seed=N + 37), elem, seed=1)
+    dt = torch.bfloat16 if bf16 else torch.float32
+    big = torch.empty((M, N + 96), dtype=dt, device="cuda")
+    big.view(torch.uint8).fill_(0xA5)
+    check(nv, qa, qb, bf16=bf16, accum=accum, out=big[:, 40:40 + N], what=f"strided {shape}")
+    es = big.element_size()
+    raw = big.view(torch.uint8)
+    assert bool((raw[:, :40 * es] == 0xA5).all()) and bool((raw[:, (40 + N) * es:] == 0xA5).all()), \
+        "bytes outside the output slice were written"
