@@ -961,8 +961,14 @@ int amax_partials(const T* x, int64_t rows, int64_t cols, int64_t ld, int hadama
         hipLaunchKernelGGL(k_amax_hadamard_rows<T>, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, s, x,
                            rows, cols, ld, sign_mask, ws);
     } else if (hadamard_dim == 2) {   // down columns
-        gx = std::min<int64_t>(std::max<int64_t>(cdiv(cdiv(cols, CH), kAmaxColsThreads), 1), kMaxPartials);
-        gy = std::min<int64_t>(std::max<int64_t>(rows / 16, 1), kMaxPartials / gx);
+        // a workgroup takes whole 16-row bands (contiguous in memory) when
+        // there are enough of them to fill the partials; split across
+        // columns only when there are not (8192 x 20480 BF16 with the
+        // amax computed: 172 -> 168 us against bands cut in 5)
+        const int64_t nb = std::max<int64_t>(rows / 16, 1);
+        gx = std::min<int64_t>(std::max<int64_t>(cdiv(cdiv(cols, CH), kAmaxColsThreads), 1),
+                               std::max<int64_t>(kMaxPartials / nb, 1));
+        gy = std::min<int64_t>(nb, kMaxPartials / gx);
         hipLaunchKernelGGL(k_amax_hadamard_cols<T>, dim3((unsigned)gx, (unsigned)gy), dim3(kAmaxColsThreads), 0, s, x,
                            rows, cols, ld, sign_mask, ws);
     } else {
