@@ -157,10 +157,10 @@ struct TileRows {
 };
 
 template <bool GROUPED>
-__device__ __forceinline__ TileRows tile_rows(const GemmArgs& p) {
+__device__ __forceinline__ TileRows tile_rows(const GemmArgs& p, int64_t ty) {
     TileRows t{0, p.M, 0, true};
     if (GROUPED) {
-        int64_t r = blockIdx.y;
+        int64_t r = ty;
         t.ok = false;
         for (int gg = 0; gg < p.G; ++gg) {
             const int64_t lo = min(max(p.offsets[gg], (int64_t)0), p.M);
@@ -176,7 +176,7 @@ __device__ __forceinline__ TileRows tile_rows(const GemmArgs& p) {
             r -= tiles;
         }
     } else {
-        t.m0 = (int64_t)blockIdx.y * kBM;
+        t.m0 = ty * kBM;
     }
     return t;
 }
@@ -185,14 +185,14 @@ __device__ __forceinline__ TileRows tile_rows(const GemmArgs& p) {
 // rows 0..127 are gate rows j0 + r and 128..255 the matching up rows F + j0 + r
 // of the group's 2F weight rows.
 template <bool SWIGLU>
-__device__ __forceinline__ int64_t b_row(const GemmArgs& p, int64_t bbase, int r) {
+__device__ __forceinline__ int64_t b_row(const GemmArgs& p, int64_t bbase, int r, int64_t tx) {
     const int64_t Ng = p.N;
     if (SWIGLU) {
-        const int64_t F = Ng / 2, j0 = (int64_t)blockIdx.x * (kBN / 2);
+        const int64_t F = Ng / 2, j0 = tx * (kBN / 2);
         const int64_t c = min(j0 + (r & 127), F - 1);
         return bbase + (r < 128 ? c : F + c);
     }
-    return bbase + min((int64_t)blockIdx.x * kBN + r, Ng - 1);
+    return bbase + min(tx * kBN + r, Ng - 1);
 }
 
 // LDS tile row of B that MFMA column tile j of wave column wn reads.
@@ -225,15 +225,14 @@ __device__ __forceinline__ float swiglu_h(float gt, float up) {
 // take per-element bounds checks.  SwiGLU's amax: rounding to BF16 is
 // monotonic, so the largest |h| rounded once is the largest rounded |h|.
 template <bool GROUPED, bool SWIGLU, bool OUT_BF16>
-__device__ __forceinline__ void epilogue(const GemmArgs& p, float16_t (&acc)[4][4], int64_t m0,
-                                         int64_t m_end, int g, int wm, int wn, int lane) {
+__device__ __forceinline__ void epilogue(const GemmArgs& p, float16_t (&acc)[4][4], float alpha, int64_t m0,
+                                         int64_t m_end, int wm, int wn, int lane, int64_t tx) {
     const int h = lane >> 5, l32 = lane & 31;
     const int64_t Ng = p.N;
-    const float alpha = p.A.ts[0] * p.B.ts[GROUPED ? g : 0];
     const int64_t mw = m0 + 128 * wm;
     if (SWIGLU) {
         uint16_t* C = static_cast<uint16_t*>(p.C);
-        const int64_t F = Ng / 2, jw = (int64_t)blockIdx.x * (kBN / 2) + 64 * wn;
+        const int64_t F = Ng / 2, jw = tx * (kBN / 2) + 64 * wn;
         float amax = 0.0f;
         if (mw + 128 <= m_end && jw + 64 <= F &&
             store_wave_block<4, 2, true>(C, p.ldc, mw, jw, h, l32, [&](int i, int jj, int r) {
@@ -267,7 +266,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, float16_t (&acc)[4][
         }
         return;
     }
-    const int64_t nw = (int64_t)blockIdx.x * kBN + 128 * wn;
+    const int64_t nw = tx * kBN + 128 * wn;
     if (mw + 128 <= m_end && nw + 128 <= Ng &&
         store_wave_block<4, 4, OUT_BF16>(p.C, p.ldc, mw, nw, h, l32,
                                          [&](int i, int j, int r) { return alpha * acc[i][j][r]; }))
@@ -300,7 +299,7 @@ __global__ void __launch_bounds__(256, 1) k_gemm(GemmArgs p) {
     const int wm = w >> 1, wn = w & 1;
     const int h = lane >> 5, l32 = lane & 31;
 
-    const TileRows tr = tile_rows<GROUPED>(p);
+    const TileRows tr = tile_rows<GROUPED>(p, blockIdx.y);
     if (!tr.ok) return;  // uniform across the workgroup
     const int64_t m0 = tr.m0, m_end = tr.m_end;
     const int g = tr.g;
@@ -309,7 +308,7 @@ __global__ void __launch_bounds__(256, 1) k_gemm(GemmArgs p) {
 
     // ---- the A row and B row this thread stages ----
     const int64_t arow = min(m0 + tid, m_end - 1);
-    const int64_t brow = b_row<SWIGLU>(p, bbase, tid);
+    const int64_t brow = b_row<SWIGLU>(p, bbase, tid, blockIdx.x);
 
     float16_t acc[4][4];
 #pragma unroll
@@ -431,7 +430,7 @@ __global__ void __launch_bounds__(256, 1) k_gemm(GemmArgs p) {
         }
     }
 
-    epilogue<GROUPED, SWIGLU, OUT_BF16>(p, acc, m0, m_end, g, wm, wn, lane);
+    epilogue<GROUPED, SWIGLU, OUT_BF16>(p, acc, p.A.ts[0] * p.B.ts[GROUPED ? g : 0], m0, m_end, wm, wn, lane, blockIdx.x);
 }
 
 // ============================================================ ring kernel
@@ -554,7 +553,7 @@ __global__ void __launch_bounds__(256, 1) k_gemm_ring(GemmArgs p) {
     const int wm = w >> 1, wn = w & 1;
     const int h = lane >> 5, l32 = lane & 31;
 
-    const TileRows tr = tile_rows<GROUPED>(p);
+    const TileRows tr = tile_rows<GROUPED>(p, blockIdx.y);
     if (!tr.ok) return;  // uniform across the workgroup
     const int64_t m0 = tr.m0, m_end = tr.m_end;
     const int g = tr.g;
@@ -567,14 +566,14 @@ __global__ void __launch_bounds__(256, 1) k_gemm_ring(GemmArgs p) {
         const int64_t chunk = 16 * (lane & 1);
         const RowSrc a0 = row_src(p.A, min(m0 + r0, m_end - 1), K);
         const RowSrc a1 = row_src(p.A, min(m0 + r1, m_end - 1), K);
-        const RowSrc b0 = row_src(p.B, b_row<SWIGLU>(p, bbase, r0), K);
-        const RowSrc b1 = row_src(p.B, b_row<SWIGLU>(p, bbase, r1), K);
+        const RowSrc b0 = row_src(p.B, b_row<SWIGLU>(p, bbase, r0, blockIdx.x), K);
+        const RowSrc b1 = row_src(p.B, b_row<SWIGLU>(p, bbase, r1, blockIdx.x), K);
         rs.a0 = a0.codes + chunk;
         rs.a1 = a1.codes + chunk;
         rs.b0 = b0.codes + chunk;
         rs.b1 = b1.codes + chunk;
         rs.as = row_src(p.A, min(m0 + rsc, m_end - 1), K).scales;
-        rs.bs = row_src(p.B, b_row<SWIGLU>(p, bbase, rsc), K).scales;
+        rs.bs = row_src(p.B, b_row<SWIGLU>(p, bbase, rsc, blockIdx.x), K).scales;
     }
     const int arow0 = 128 * wm;
     int brow[4];
@@ -660,7 +659,7 @@ __global__ void __launch_bounds__(256, 1) k_gemm_ring(GemmArgs p) {
         // reads again) must land before the workgroup's LDS is released
         __builtin_amdgcn_s_waitcnt(vmcnt_at_most(0));
     }
-    epilogue<GROUPED, SWIGLU, OUT_BF16>(p, acc, m0, m_end, g, wm, wn, fresh_lane_id());
+    epilogue<GROUPED, SWIGLU, OUT_BF16>(p, acc, p.A.ts[0] * p.B.ts[GROUPED ? g : 0], m0, m_end, wm, wn, fresh_lane_id(), blockIdx.x);
 }
 
 // ============================================================ full-line kernel
@@ -758,8 +757,36 @@ __device__ __forceinline__ void full_read_frag(const FullSlot& slot, int t, int 
     f.zero = false;
 }
 
+// Work of workgroup L (a one-dimensional grid; tiles numbered row-major over
+// a tiles_x-wide grid of 256 x 256 tiles): tiles 0 .. t_main - 1 whole, one
+// per workgroup; the tiles after them (a last round that would leave most
+// compute units idle) each split `split` ways along K, part s taking chunk
+// pairs [s P / split, (s + 1) P / split) of the P = K / 512 pairs.  A part
+// writes its raw binary32 accumulators to `partials` (part j of the tail at
+// float4 index (64 j + e) 256 + thread, e = 0..63: coalesced across the
+// workgroup); k_gemm_tail_sum adds them up and writes the tile.
+struct FullWork {
+    int tile;
+    int part;  // -1: the whole tile
+    int64_t c0, c1;
+};
+
+__device__ __forceinline__ FullWork full_work(int t_main, int split, int64_t nchunks) {
+    FullWork wk{(int)blockIdx.x, -1, 0, nchunks};
+    if (wk.tile >= t_main) {
+        const int j = wk.tile - t_main, s = j % split;
+        const int64_t pairs = nchunks / 2;
+        wk.tile = t_main + j / split;
+        wk.part = j;
+        wk.c0 = 2 * (s * pairs / split);
+        wk.c1 = 2 * ((s + 1) * pairs / split);
+    }
+    return wk;
+}
+
 template <bool GROUPED, bool SWIGLU, bool OUT_BF16>
-__global__ void __launch_bounds__(256, 1) k_gemm_full(GemmArgs p) {
+__global__ void __launch_bounds__(256, 1) k_gemm_full(GemmArgs p, int tiles_x, int t_main, int split,
+                                                      float* __restrict__ partials) {
     __shared__ __attribute__((aligned(16))) uint8_t a0c[kFullCodes];
     __shared__ __attribute__((aligned(16))) uint8_t a1c[kFullCodes];
     __shared__ __attribute__((aligned(16))) uint8_t b0c[kFullCodes];
@@ -779,11 +806,14 @@ __global__ void __launch_bounds__(256, 1) k_gemm_full(GemmArgs p) {
     const int wm = w >> 1, wn = w & 1;
     const int h = lane >> 5, l32 = lane & 31;
 
-    const TileRows tr = tile_rows<GROUPED>(p);
+    const int64_t K = p.K, kc2 = K / 2, ks = K / 16;
+    const int64_t nchunks = K / 256;  // even: K % 512 == 0
+    const FullWork wk = full_work(t_main, split, nchunks);  // uniform across the workgroup
+    const int64_t tx = wk.tile % tiles_x, ty = wk.tile / tiles_x;
+    const TileRows tr = tile_rows<GROUPED>(p, ty);
     if (!tr.ok) return;  // uniform across the workgroup
     const int64_t m0 = tr.m0, m_end = tr.m_end;
     const int g = tr.g;
-    const int64_t K = p.K, kc2 = K / 2, ks = K / 16;
     const int64_t bbase = GROUPED ? (int64_t)g * p.N : 0;
 
     FullSrc src;
@@ -796,11 +826,11 @@ __global__ void __launch_bounds__(256, 1) k_gemm_full(GemmArgs p) {
         const int r = 64 * w + 8 * t + (lane >> 3);
         const int c = (lane & 7) ^ full_swz(r);  // the swizzle is an involution
         src.a[t] = (uint32_t)((min(m0 + r, m_end - 1) - m0) * kc2 + 16 * c);
-        src.b[t] = (uint32_t)((b_row<SWIGLU>(p, bbase, r) - bbase) * kc2 + 16 * c);
+        src.b[t] = (uint32_t)((b_row<SWIGLU>(p, bbase, r, tx) - bbase) * kc2 + 16 * c);
     }
     {
         const int r = 64 * w + lane;
-        const int64_t ga = min(m0 + r, m_end - 1), gb = b_row<SWIGLU>(p, bbase, r);
+        const int64_t ga = min(m0 + r, m_end - 1), gb = b_row<SWIGLU>(p, bbase, r, tx);
         src.sa = (uint32_t)((p.A.scale_2d ? ga / 16 : ga) * ks);
         src.sb = (uint32_t)((p.B.scale_2d ? gb / 16 : gb) * ks);
     }
@@ -817,10 +847,10 @@ __global__ void __launch_bounds__(256, 1) k_gemm_full(GemmArgs p) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    const int64_t nchunks = K / 256;  // even: K % 512 == 0
-    auto cclamp = [&](int64_t c) { return c < nchunks ? c : nchunks - 1; };
-    full_load(src, 0, slot0, w);
-    full_load(src, 1, slot1, w);
+    const int64_t c0 = wk.c0, c1 = wk.c1;
+    auto cclamp = [&](int64_t c) { return c < c1 ? c : c1 - 1; };
+    full_load(src, c0, slot0, w);
+    full_load(src, c0 + 1, slot1, w);
     __builtin_amdgcn_s_waitcnt(vmcnt_at_most(kFullLoadsPerChunk));  // chunk 0 landed
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
@@ -872,7 +902,7 @@ __global__ void __launch_bounds__(256, 1) k_gemm_full(GemmArgs p) {
             }
         }
     };
-    for (int64_t ch = 0; ch < nchunks; ch += 2) {
+    for (int64_t ch = c0; ch < c1; ch += 2) {
         step(ch, 0, slot0, slot1, fx, fy);
         step(ch, 1, slot0, slot1, fy, fx);
         step(ch, 2, slot0, slot1, fx, fy);
@@ -886,8 +916,58 @@ __global__ void __launch_bounds__(256, 1) k_gemm_full(GemmArgs p) {
     __builtin_amdgcn_s_waitcnt(vmcnt_at_most(0));
     // the tile's rows and group found again rather than kept through the loop
     // (held there, they cost the grouped SwiGLU instance a spilled register)
-    const TileRows te = tile_rows<GROUPED>(p);
-    epilogue<GROUPED, SWIGLU, OUT_BF16>(p, acc, te.m0, te.m_end, te.g, wm, wn, fresh_lane_id());
+    const TileRows te = tile_rows<GROUPED>(p, ty);
+    GemmArgs q = p;
+    float alpha = p.A.ts[0] * p.B.ts[GROUPED ? te.g : 0];
+    int64_t em0 = te.m0, em_end = te.m_end, etx = tx;
+    if constexpr (!GROUPED && !SWIGLU && !OUT_BF16) {
+        if (wk.part >= 0) {
+            // a part: its raw sums as a 256 x 256 binary32 matrix, through
+            // the same epilogue (one code path for the allocator)
+            q.C = partials + (int64_t)wk.part * kBM * kBN;
+            q.ldc = kBN;
+            q.N = kBN;
+            alpha = 1.0f;
+            em0 = 0;
+            em_end = kBM;
+            etx = 0;
+        }
+    }
+    epilogue<GROUPED, SWIGLU, OUT_BF16>(q, acc, alpha, em0, em_end, wm, wn, fresh_lane_id(), etx);
+}
+
+// The tail tiles of a split k_gemm_full launch (FP32 output): element (r, c)
+// of tile t_main + blockIdx.x is alpha times the sum of its parts' element
+// (r, c), added in part order (deterministic).
+// Workgroup (x, y) covers 16 rows from 16 y of the tile.
+__global__ void __launch_bounds__(256) k_gemm_tail_sum(GemmArgs p, int tiles_x, int t_main, int split,
+                                                       const float* __restrict__ partials) {
+    const int tile = t_main + (int)blockIdx.x;
+    const int64_t m0 = (int64_t)(tile / tiles_x) * kBM, n0 = (int64_t)(tile % tiles_x) * kBN;
+    const float alpha = p.A.ts[0] * p.B.ts[0];
+    const float* part0 = partials + (int64_t)blockIdx.x * split * kBM * kBN;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int e = 4 * (256 * k + threadIdx.x);  // first of 4 elements in 16 rows x 256
+        const int r = 16 * blockIdx.y + e / kBN, c = e % kBN;
+        float4 v = *reinterpret_cast<const float4*>(part0 + r * kBN + c);
+        for (int s = 1; s < split; ++s) {
+            const float4 u = *reinterpret_cast<const float4*>(part0 + (int64_t)s * kBM * kBN + r * kBN + c);
+            v.x += u.x;
+            v.y += u.y;
+            v.z += u.z;
+            v.w += u.w;
+        }
+        const int64_t m = m0 + r;
+        if (m >= p.M) continue;
+        const float o[4] = {alpha * v.x, alpha * v.y, alpha * v.z, alpha * v.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int64_t n = n0 + c + q;
+            if (n >= p.N) break;
+            static_cast<float*>(p.C)[m * p.ldc + n] = o[q];
+        }
+    }
 }
 
 __global__ void k_zero_float(float* p) {
@@ -903,38 +983,83 @@ inline bool fast_path(const Operand& A, const Operand& B, int64_t K) {
            (reinterpret_cast<uintptr_t>(B.scales) & 3) == 0;
 }
 
-// The full-line kernel: 512-multiple K, 16-byte-aligned scale rows, and
-// per-lane byte offsets that fit 32 bits (B's rows of one group and either
-// operand's scale rows).
-inline bool full_path(const Operand& A, const Operand& B, int64_t a_rows, int64_t b_rows, int64_t K) {
+// The full-line kernel: 512-multiple K, 16-byte-aligned scale rows, per-lane
+// byte offsets that fit 32 bits (B's rows of one group and either operand's
+// scale rows), and a tile count that fits its one-dimensional grid.
+inline bool full_path(const Operand& A, const Operand& B, int64_t a_rows, int64_t b_rows, int64_t K,
+                      int64_t tiles) {
     const uint64_t lim = (uint64_t)1 << 32;
     return K > 0 && K % 512 == 0 && (reinterpret_cast<uintptr_t>(A.scales) & 15) == 0 &&
            (reinterpret_cast<uintptr_t>(B.scales) & 15) == 0 && (uint64_t)b_rows * (uint64_t)(K / 2) < lim &&
-           (uint64_t)a_rows * (uint64_t)(K / 16) < lim && (uint64_t)b_rows * (uint64_t)(K / 16) < lim;
+           (uint64_t)a_rows * (uint64_t)(K / 16) < lim && (uint64_t)b_rows * (uint64_t)(K / 16) < lim &&
+           tiles <= INT32_MAX / 8;
 }
+
+// Bytes of one tile part's accumulators.
+constexpr int64_t kPartBytes = (int64_t)kBM * kBN * 4;
 }  // namespace
 
+GemmSplit gemm_split_plan(int64_t M, int64_t N, int64_t K, bool swiglu, int cus) {
+    GemmSplit sp{0, 1, 0};
+    if (swiglu || M <= 0 || N <= 0 || K <= 0 || K % 512 || cus <= 0) return sp;
+    const int64_t tiles = cdiv(N, kBN) * cdiv(M, kBM), tail = tiles % cus;
+    sp.t_main = tiles;
+    if (tail == 0) return sp;
+    // the last round's tiles, each split over the compute units they leave
+    // idle (at least two chunk pairs per part would be wasted on loads: one pair minimum)
+    const int64_t split = std::min<int64_t>(std::min<int64_t>(cus / tail, K / 512), kMaxTailSplit);
+    if (split < 2) return sp;
+    sp.t_main = tiles - tail;
+    sp.split = (int)split;
+    sp.bytes = tail * split * kPartBytes;
+    return sp;
+}
+
+hipError_t device_cus(int& cus) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    return e;
+}
+
 hipError_t launch_gemm(const Operand& A, const Operand& B, int64_t M, int64_t N, int64_t K,
-                       void* C, bool c_bf16, int64_t ldc, bool swiglu, hipStream_t s) {
+                       void* C, bool c_bf16, int64_t ldc, bool swiglu, void* ws, size_t ws_bytes,
+                       hipStream_t s) {
     if (M == 0 || N == 0) return hipSuccess;
     GemmArgs p{A, B, M, N, K, C, ldc, nullptr, 1, nullptr};
+    // SwiGLU: gate column j and up column F + j share a tile, 128 output columns per tile
+    const int64_t tx = swiglu ? cdiv(N / 2, kBN / 2) : cdiv(N, kBN), ty = cdiv(M, kBM);
+    if (full_path(A, B, M, N, K, tx * ty)) {
+        GemmSplit sp{tx * ty, 1, 0};
+        if (ws && !swiglu && !c_bf16) {  // parts are binary32 sums: FP32 outputs
+            int cus = 0;
+            const hipError_t e = device_cus(cus);
+            if (e != hipSuccess) return e;
+            const GemmSplit plan = gemm_split_plan(M, N, K, false, cus);
+            if (plan.split > 1 && (size_t)plan.bytes <= ws_bytes) sp = plan;
+        }
+        const int64_t tail = tx * ty - sp.t_main;
+        const dim3 grid((unsigned)(sp.t_main + tail * sp.split));
+        float* parts = static_cast<float*>(ws);
+        const int itx = (int)tx, tm = (int)sp.t_main, spl = sp.split;
+        if (swiglu)
+            hipLaunchKernelGGL((k_gemm_full<false, true, true>), grid, dim3(256), 0, s, p, itx, tm, 1, nullptr);
+        else if (c_bf16)
+            hipLaunchKernelGGL((k_gemm_full<false, false, true>), grid, dim3(256), 0, s, p, itx, tm, spl, parts);
+        else
+            hipLaunchKernelGGL((k_gemm_full<false, false, false>), grid, dim3(256), 0, s, p, itx, tm, spl, parts);
+        if (tail > 0 && sp.split > 1) {
+            hipLaunchKernelGGL(k_gemm_tail_sum, dim3((unsigned)tail, kBM / 16), dim3(256), 0, s, p, itx, tm, spl,
+                               parts);
+        }
+        return hipGetLastError();
+    }
+    const dim3 grid((unsigned)tx, (unsigned)ty);
     if (swiglu) {
-        // gate column j and up column F + j share a tile: 128 output columns per tile
-        dim3 grid((unsigned)cdiv(N / 2, kBN / 2), (unsigned)cdiv(M, kBM));
-        if (full_path(A, B, M, N, K))
-            hipLaunchKernelGGL((k_gemm_full<false, true, true>), grid, dim3(256), 0, s, p);
-        else if (fast_path(A, B, K))
+        if (fast_path(A, B, K))
             hipLaunchKernelGGL((k_gemm_ring<false, true, true>), grid, dim3(256), 0, s, p);
         else
             hipLaunchKernelGGL((k_gemm<false, true, true, false>), grid, dim3(256), 0, s, p);
-        return hipGetLastError();
-    }
-    dim3 grid((unsigned)cdiv(N, kBN), (unsigned)cdiv(M, kBM));
-    if (full_path(A, B, M, N, K)) {
-        if (c_bf16)
-            hipLaunchKernelGGL((k_gemm_full<false, false, true>), grid, dim3(256), 0, s, p);
-        else
-            hipLaunchKernelGGL((k_gemm_full<false, false, false>), grid, dim3(256), 0, s, p);
     } else if (fast_path(A, B, K)) {
         if (c_bf16)
             hipLaunchKernelGGL((k_gemm_ring<false, false, true>), grid, dim3(256), 0, s, p);
@@ -958,25 +1083,23 @@ hipError_t launch_grouped_gemm(int G, const Operand& A, const int64_t* offsets, 
     GemmArgs p{A, B, total_rows, n_per_group, K, C, ldc, offsets, G, amax_out};
     // every group wastes at most one partial tile
     const int64_t mtiles = cdiv(total_rows, kBM) + G;
+    const int64_t tx = swiglu ? cdiv(n_per_group / 2, kBN / 2) : cdiv(n_per_group, kBN);
     const bool fast = fast_path(A, B, K);
-    const bool full = full_path(A, B, total_rows, n_per_group, K);
-#define NVFP4_GROUPED(SW, BF)                                                                   \
-    do {                                                                                        \
-        if (full)                                                                               \
-            hipLaunchKernelGGL((k_gemm_full<true, SW, BF>), grid, dim3(256), 0, s, p);         \
-        else if (fast)                                                                          \
-            hipLaunchKernelGGL((k_gemm_ring<true, SW, BF>), grid, dim3(256), 0, s, p);         \
-        else                                                                                    \
-            hipLaunchKernelGGL((k_gemm<true, SW, BF, false>), grid, dim3(256), 0, s, p);       \
+    const bool full = full_path(A, B, total_rows, n_per_group, K, tx * mtiles);
+    const dim3 grid2((unsigned)tx, (unsigned)mtiles), grid1((unsigned)(tx * mtiles));
+    const int itx = (int)tx, nt = (int)(tx * mtiles);
+#define NVFP4_GROUPED(SW, BF)                                                                               \
+    do {                                                                                                    \
+        if (full)                                                                                           \
+            hipLaunchKernelGGL((k_gemm_full<true, SW, BF>), grid1, dim3(256), 0, s, p, itx, nt, 1, nullptr); \
+        else if (fast)                                                                                      \
+            hipLaunchKernelGGL((k_gemm_ring<true, SW, BF>), grid2, dim3(256), 0, s, p);                     \
+        else                                                                                                \
+            hipLaunchKernelGGL((k_gemm<true, SW, BF, false>), grid2, dim3(256), 0, s, p);                   \
     } while (0)
-    if (swiglu) {
-        dim3 grid((unsigned)cdiv(n_per_group / 2, kBN / 2), (unsigned)mtiles);
-        NVFP4_GROUPED(true, true);
-    } else {
-        dim3 grid((unsigned)cdiv(n_per_group, kBN), (unsigned)mtiles);
-        if (c_bf16) NVFP4_GROUPED(false, true);
-        else NVFP4_GROUPED(false, false);
-    }
+    if (swiglu) NVFP4_GROUPED(true, true);
+    else if (c_bf16) NVFP4_GROUPED(false, true);
+    else NVFP4_GROUPED(false, false);
 #undef NVFP4_GROUPED
     return hipGetLastError();
 }

@@ -54,7 +54,22 @@ struct Operand {
 // C (M x F, BF16) = gate * sigmoid(gate) * up with gate = columns [0, F) and
 // up = columns [F, 2F) of A * B^T.
 hipError_t launch_gemm(const Operand& A, const Operand& B, int64_t M, int64_t N, int64_t K,
-                       void* C, bool c_bf16, int64_t ldc, bool swiglu, hipStream_t s);
+                       void* C, bool c_bf16, int64_t ldc, bool swiglu, void* ws, size_t ws_bytes,
+                       hipStream_t s);
+
+// Split of a plain GEMM's last round of tiles along K (workspace for the
+// parts' accumulators: `bytes`; split 1: none).  The tiles after t_main, a
+// round that would leave compute units idle, are each computed in `split`
+// parts by otherwise idle units and summed in part order by a second kernel.
+struct GemmSplit {
+    int64_t t_main;
+    int split;
+    int64_t bytes;
+};
+constexpr int64_t kMaxTailSplit = 8;
+GemmSplit gemm_split_plan(int64_t M, int64_t N, int64_t K, bool swiglu, int cus);
+// Compute units of the current device.
+hipError_t device_cus(int& cus);
 
 // Grouped GEMM over G groups (see nvfp4_grouped_gemm).  n_per_group = rows of
 // one group's weight matrix; swiglu halves the output width.

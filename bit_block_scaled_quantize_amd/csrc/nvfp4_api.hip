@@ -227,8 +227,18 @@ nvfp4_status nvfp4_dequantize(const nvfp4_tensor* q, void* y, int32_t dt /* nvfp
     return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
 
+size_t nvfp4_gemm_workspace_size(const nvfp4_tensor* A, const nvfp4_tensor* B, int32_t c_dt /* nvfp4_dtype */,
+                                 int32_t ep /* nvfp4_epilogue */) {
+    if (!A || !B || c_dt != NVFP4_F32 || ep != NVFP4_EPI_NONE) return 0;
+    if (A->rows < 0 || B->rows < 0 || A->cols != B->cols) return 0;
+    int cus = 0;
+    if (device_cus(cus) != hipSuccess) return 0;
+    const GemmSplit sp = gemm_split_plan(A->rows, B->rows, A->cols, false, cus);
+    return sp.split > 1 ? (size_t)sp.bytes : 0;
+}
+
 nvfp4_status nvfp4_gemm(const nvfp4_tensor* A, const nvfp4_tensor* B, void* C, int32_t c_dt /* nvfp4_dtype */,
-                        int64_t ldc, int32_t ep /* nvfp4_epilogue */, void* stream) {
+                        int64_t ldc, int32_t ep /* nvfp4_epilogue */, void* ws, size_t ws_bytes, void* stream) {
     if (!A || !B) return NVFP4_ERR_NULL;
     if (!valid_dtype(c_dt)) return NVFP4_ERR_ENUM;
     if (ep != NVFP4_EPI_NONE && ep != NVFP4_EPI_SWIGLU) return NVFP4_ERR_ENUM;
@@ -248,8 +258,9 @@ nvfp4_status nvfp4_gemm(const nvfp4_tensor* A, const nvfp4_tensor* B, void* C, i
     if (M > 0 && ncols > 0 && !C) return NVFP4_ERR_NULL;
     if (!aligned(C, dtype_size(c_dt))) return NVFP4_ERR_ALIGN;
     if (cdiv(M, 128) > kMaxGridY) return NVFP4_ERR_UNSUPPORTED;
+    if (ws && !aligned(ws, 16)) return NVFP4_ERR_ALIGN;
     hipError_t e = launch_gemm(as_operand(A), as_operand(B), M, N, K, C, c_dt == NVFP4_BF16, ldc, swiglu,
-                               static_cast<hipStream_t>(stream));
+                               ws, ws ? ws_bytes : 0, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
 

@@ -28,7 +28,7 @@ NVFP4_MX_ACC_NATIVE, NVFP4_MX_ACC_EXACT = 0, 1
 
 EXPORTED = ["nvfp4_quantize_workspace_size", "nvfp4_quantize", "nvfp4_quantize_noalloc", "nvfp4_requantize",
             "nvfp4_dequantize",
-            "nvfp4_gemm", "nvfp4_grouped_gemm", "nvfp4_mx_quantize", "nvfp4_mx_dequantize", "nvfp4_mx_gemm",
+            "nvfp4_gemm", "nvfp4_gemm_workspace_size", "nvfp4_grouped_gemm", "nvfp4_mx_quantize", "nvfp4_mx_dequantize", "nvfp4_mx_gemm",
             "nvfp4_status_string", "nvfp4_version"]
 
 
@@ -68,8 +68,10 @@ def _load():
     L.nvfp4_requantize.argtypes = [ctypes.POINTER(CTensor), ctypes.POINTER(CQuantOpts),
                                    ctypes.POINTER(CTensor), vp, sz, vp]
     L.nvfp4_requantize.restype = i32
-    L.nvfp4_gemm.argtypes = [ctypes.POINTER(CTensor), ctypes.POINTER(CTensor), vp, i32, i64, i32, vp]
+    L.nvfp4_gemm.argtypes = [ctypes.POINTER(CTensor), ctypes.POINTER(CTensor), vp, i32, i64, i32, vp, sz, vp]
     L.nvfp4_gemm.restype = i32
+    L.nvfp4_gemm_workspace_size.argtypes = [ctypes.POINTER(CTensor), ctypes.POINTER(CTensor), i32, i32]
+    L.nvfp4_gemm_workspace_size.restype = sz
     L.nvfp4_grouped_gemm.argtypes = [i32, ctypes.POINTER(CTensor), vp, ctypes.POINTER(CTensor), vp,
                                      i32, i64, i32, vp, vp, sz, vp]
     L.nvfp4_grouped_gemm.restype = i32
@@ -269,18 +271,37 @@ def nvfp4_dequantize(q, dtype=torch.float32, out=None, stream=None):
     return out
 
 
+def nvfp4_gemm_workspace_size(A, B, out_dtype=torch.float32, epilogue=NVFP4_EPI_NONE):
+    """Bytes of workspace with which nvfp4_gemm splits a last partial round
+    of tiles on the current device (0: no split)."""
+    ca, cb = A.c(), B.c()
+    return int(lib.nvfp4_gemm_workspace_size(ctypes.byref(ca), ctypes.byref(cb), _dtype_code(out_dtype),
+                                             epilogue))
+
+
 @_launches_on_stream
-def nvfp4_gemm(A, B, out_dtype=torch.float32, out=None, epilogue=NVFP4_EPI_NONE, stream=None):
+def nvfp4_gemm(A, B, out_dtype=torch.float32, out=None, epilogue=NVFP4_EPI_NONE, workspace=None,
+               stream=None):
     """C = A B^T (A: M x K, B: N x K NVFP4 tensors); with NVFP4_EPI_SWIGLU
-    (N = 2F, bfloat16 output) C = gate * sigmoid(gate) * up, M x F."""
+    (N = 2F, bfloat16 output) C = gate * sigmoid(gate) * up, M x F.
+    workspace: None allocates what nvfp4_gemm_workspace_size asks for (a
+    split of a last partial round of tiles; often nothing); False passes
+    none; a device tensor is passed as is."""
     ncols = B.rows // 2 if epilogue == NVFP4_EPI_SWIGLU else B.rows
     if out is None:
         out = torch.empty((A.rows, ncols), dtype=out_dtype, device=A.codes.device)
     assert out.stride(1) == 1
     ldc = out.stride(0) if A.rows > 1 else max(ncols, out.stride(0))
     ca, cb = A.c(), B.c()
+    if workspace is None:
+        need = int(lib.nvfp4_gemm_workspace_size(ctypes.byref(ca), ctypes.byref(cb), _dtype_code(out.dtype),
+                                                 epilogue))
+        workspace = torch.empty((need + 15) // 16 * 4, dtype=torch.float32, device=out.device) if need else False
+    if workspace is False:
+        workspace = None
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.nvfp4_gemm(ctypes.byref(ca), ctypes.byref(cb), ctypes.c_void_p(out.data_ptr()),
-                        _dtype_code(out.dtype), ldc, epilogue, _stream(stream))
+                        _dtype_code(out.dtype), ldc, epilogue, _ptr(workspace), ws_bytes, _stream(stream))
     _check("nvfp4_gemm", st)
     return out
 

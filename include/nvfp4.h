@@ -213,11 +213,27 @@ nvfp4_status nvfp4_requantize(const nvfp4_tensor* in, const nvfp4_quant_opts* op
  *               sigmoid(gate) * up, and c_dt must be BF16 (else
  *               UNSUPPORTED).  The grouped GEMM offers the same epilogue
  *               with the largest |C| written to amax_out.
+ * Workspace (optional): with ws 16-byte aligned and ws_bytes >=
+ * nvfp4_gemm_workspace_size(A, B, c_dt, ep) > 0, a last round of 256 x 256
+ * output tiles that would leave compute units idle is computed in parts
+ * along K, whose binary32 sums are added in a fixed order; ws NULL or
+ * smaller: no split.  The two give the same accuracy, not always the same
+ * last bits; each is deterministic on a given device (the split depends on
+ * its compute-unit count).  ws is scratch for this call only: calls that
+ * overlap must not share it.
  * Source: asector.ru page, "NVFP4 и Blackwell" (scaled compute with
  * high-precision accumulation); iitak.ru page, "Детали" (the expert layers
  * whose feed-forward the SwiGLU epilogue closes). */
 nvfp4_status nvfp4_gemm(const nvfp4_tensor* A, const nvfp4_tensor* B, void* C, int32_t c_dt /* nvfp4_dtype */,
-                        int64_t ldc, int32_t ep /* nvfp4_epilogue */, void* stream);
+                        int64_t ldc, int32_t ep /* nvfp4_epilogue */, void* ws, size_t ws_bytes, void* stream);
+
+/* Bytes of workspace with which nvfp4_gemm splits its last round of tiles on
+ * the current device: nonzero only for FP32 output without an epilogue,
+ * K % 512 == 0 and a tile count that leaves a partial last round with enough
+ * idle compute units; 0 also for invalid arguments or when the device cannot
+ * be queried.  At most 8 parts of 256 KiB per tile of that round. */
+size_t nvfp4_gemm_workspace_size(const nvfp4_tensor* A, const nvfp4_tensor* B, int32_t c_dt /* nvfp4_dtype */,
+                                 int32_t ep /* nvfp4_epilogue */);
 
 /* Grouped (mixture-of-experts) GEMM.  A is sum_g M_g x K with one tensor
  * scale; rows offsets[g] .. offsets[g+1]-1 belong to group g (offsets: DEVICE

@@ -134,16 +134,16 @@ static void requantize_cases(void) {
 static void gemm_cases(void) {
     const nvfp4_tensor a = T(64, 64, 0, 4096), b = T(32, 64, 0, 4096), b48 = T(48, 64, 0, 4096),
                        b2 = T(32, 48, 0, 4096), a3 = T(64, 40, 0, 4096), b3 = T(32, 40, 0, 4096);
-    CHECK(nvfp4_gemm(NULL, &b, Y, NVFP4_F32, 32, NVFP4_EPI_NONE, NULL), NVFP4_ERR_NULL);
-    CHECK(nvfp4_gemm(&a, &b, Y, (nvfp4_dtype)9, 32, NVFP4_EPI_NONE, NULL), NVFP4_ERR_ENUM);
-    CHECK(nvfp4_gemm(&a, &b, Y, NVFP4_F32, 32, (nvfp4_epilogue)4, NULL), NVFP4_ERR_ENUM);
-    CHECK(nvfp4_gemm(&a, &b, Y, NVFP4_F32, 32, NVFP4_EPI_SWIGLU, NULL), NVFP4_ERR_UNSUPPORTED);
-    CHECK(nvfp4_gemm(&a, &b, Y, NVFP4_BF16, 15, NVFP4_EPI_SWIGLU, NULL), NVFP4_ERR_SHAPE);
-    CHECK(nvfp4_gemm(&a, &b48, Y, NVFP4_BF16, 24, NVFP4_EPI_SWIGLU, NULL), NVFP4_ERR_SHAPE);
-    CHECK(nvfp4_gemm(&a, &b2, Y, NVFP4_F32, 32, NVFP4_EPI_NONE, NULL), NVFP4_ERR_SHAPE);
-    CHECK(nvfp4_gemm(&a, &b, Y, NVFP4_F32, 16, NVFP4_EPI_NONE, NULL), NVFP4_ERR_SHAPE);
-    CHECK(nvfp4_gemm(&a, &b, NULL, NVFP4_F32, 32, NVFP4_EPI_NONE, NULL), NVFP4_ERR_NULL);
-    CHECK(nvfp4_gemm(&a3, &b3, Y, NVFP4_F32, 32, NVFP4_EPI_NONE, NULL), NVFP4_ERR_SHAPE);
+    CHECK(nvfp4_gemm(NULL, &b, Y, NVFP4_F32, 32, NVFP4_EPI_NONE, NULL, 0, NULL), NVFP4_ERR_NULL);
+    CHECK(nvfp4_gemm(&a, &b, Y, (nvfp4_dtype)9, 32, NVFP4_EPI_NONE, NULL, 0, NULL), NVFP4_ERR_ENUM);
+    CHECK(nvfp4_gemm(&a, &b, Y, NVFP4_F32, 32, (nvfp4_epilogue)4, NULL, 0, NULL), NVFP4_ERR_ENUM);
+    CHECK(nvfp4_gemm(&a, &b, Y, NVFP4_F32, 32, NVFP4_EPI_SWIGLU, NULL, 0, NULL), NVFP4_ERR_UNSUPPORTED);
+    CHECK(nvfp4_gemm(&a, &b, Y, NVFP4_BF16, 15, NVFP4_EPI_SWIGLU, NULL, 0, NULL), NVFP4_ERR_SHAPE);
+    CHECK(nvfp4_gemm(&a, &b48, Y, NVFP4_BF16, 24, NVFP4_EPI_SWIGLU, NULL, 0, NULL), NVFP4_ERR_SHAPE);
+    CHECK(nvfp4_gemm(&a, &b2, Y, NVFP4_F32, 32, NVFP4_EPI_NONE, NULL, 0, NULL), NVFP4_ERR_SHAPE);
+    CHECK(nvfp4_gemm(&a, &b, Y, NVFP4_F32, 16, NVFP4_EPI_NONE, NULL, 0, NULL), NVFP4_ERR_SHAPE);
+    CHECK(nvfp4_gemm(&a, &b, NULL, NVFP4_F32, 32, NVFP4_EPI_NONE, NULL, 0, NULL), NVFP4_ERR_NULL);
+    CHECK(nvfp4_gemm(&a3, &b3, Y, NVFP4_F32, 32, NVFP4_EPI_NONE, NULL, 0, NULL), NVFP4_ERR_SHAPE);
     /* grouped */
     const nvfp4_tensor ga = T(100, 64, 0, 4096), gb = T(4 * 32, 64, 1, 4096);
     const int64_t* off = (const int64_t*)(uintptr_t)65536;

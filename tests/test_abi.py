@@ -124,19 +124,24 @@ def test_requantize_rejects_bad_arguments(nv):
 def test_gemm_rejects_bad_arguments(nv):
     a, b = _t(64, 64), _t(32, 64)
     g = nv.lib.nvfp4_gemm
-    assert g(None, ctypes.byref(b), 65536, 0, 32, 0, None) == 1
-    assert g(ctypes.byref(a), ctypes.byref(b), 65536, 9, 32, 0, None) == 2
-    assert g(ctypes.byref(a), ctypes.byref(b), 65536, 0, 32, 1, None) == 5     # SwiGLU: BF16 output only
-    assert g(ctypes.byref(a), ctypes.byref(b), 65536, 1, 15, 1, None) == 3     # SwiGLU: ldc < F = 16
+    assert g(None, ctypes.byref(b), 65536, 0, 32, 0, None, 0, None) == 1
+    assert g(ctypes.byref(a), ctypes.byref(b), 65536, 9, 32, 0, None, 0, None) == 2
+    assert g(ctypes.byref(a), ctypes.byref(b), 65536, 0, 32, 1, None, 0, None) == 5     # SwiGLU: BF16 output only
+    assert g(ctypes.byref(a), ctypes.byref(b), 65536, 1, 15, 1, None, 0, None) == 3     # SwiGLU: ldc < F = 16
     b48 = _t(48, 64)
-    assert g(ctypes.byref(a), ctypes.byref(b48), 65536, 1, 24, 1, None) == 3   # SwiGLU: F = 24 not % 16
+    assert g(ctypes.byref(a), ctypes.byref(b48), 65536, 1, 24, 1, None, 0, None) == 3   # SwiGLU: F = 24 not % 16
     b2 = _t(32, 48)
-    assert g(ctypes.byref(a), ctypes.byref(b2), 65536, 0, 32, 0, None) == 3    # K mismatch
-    assert g(ctypes.byref(a), ctypes.byref(b), 65536, 0, 16, 0, None) == 3     # ldc < N
-    assert g(ctypes.byref(a), ctypes.byref(b), None, 0, 32, 0, None) == 1
+    assert g(ctypes.byref(a), ctypes.byref(b2), 65536, 0, 32, 0, None, 0, None) == 3    # K mismatch
+    assert g(ctypes.byref(a), ctypes.byref(b), 65536, 0, 16, 0, None, 0, None) == 3     # ldc < N
+    assert g(ctypes.byref(a), ctypes.byref(b), None, 0, 32, 0, None, 0, None) == 1
     a3 = _t(64, 40)
     b3 = _t(32, 40)
-    assert g(ctypes.byref(a3), ctypes.byref(b3), 65536, 0, 32, 0, None) == 3   # K % 16
+    assert g(ctypes.byref(a3), ctypes.byref(b3), 65536, 0, 32, 0, None, 0, None) == 3   # K % 16
+    assert g(ctypes.byref(a), ctypes.byref(b), 65536, 0, 32, 0, 4100, 1 << 20, None) == 4   # ws misaligned
+    s = nv.lib.nvfp4_gemm_workspace_size
+    assert s(ctypes.byref(a), ctypes.byref(b), 1, 0) == 0      # BF16 output: no split
+    assert s(ctypes.byref(a), ctypes.byref(b48), 1, 1) == 0    # SwiGLU: no split
+    assert s(None, ctypes.byref(b), 0, 0) == 0
 
 
 def test_grouped_gemm_rejects_bad_arguments(nv):
