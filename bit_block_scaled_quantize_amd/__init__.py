@@ -10,5 +10,5 @@ from .nvfp4 import (  # noqa: F401
     nvfp4_grouped_gemm,
     MXTensor, NVFP4_MX_E4M3, NVFP4_MX_E2M1, NVFP4_MX_ACC_NATIVE, NVFP4_MX_ACC_EXACT,
     nvfp4_mx_quantize, nvfp4_mx_dequantize,
-    nvfp4_mx_gemm,
+    nvfp4_mx_gemm, nvfp4_mx_gemm_workspace_size,
 )

@@ -95,6 +95,11 @@ struct MxGemmArgs {
     int64_t M, N, K;
     void* C;
     int64_t ldc;
+    // full-line native kernel only (one-dimensional grid): tiles row-major
+    // over a tiles_x-wide grid; those from t_main on split `split` ways along
+    // K, their parts' binary32 sums written as 256 x 256 matrices to `parts`
+    int tiles_x, t_main, split;
+    float* parts;
 };
 
 // Global sources of a workgroup's ring loads: wave-uniform bases (the tile's
@@ -804,6 +809,24 @@ __device__ __forceinline__ void mx_full8_read(const uint8_t* slot, const uint8_t
     }
 }
 
+// Work of full-line workgroup bx: tile bx whole (bx < t_main), or part s
+// of tile t_main + j / split (j = bx - t_main, s = j % split), which takes
+// units [s U / split, (s + 1) U / split) of the U units of 16 K steps.
+struct MxWork {
+    int tile, part, u0, u1;
+};
+__device__ __forceinline__ MxWork mx_work(const MxGemmArgs& p, int units, uint32_t bx) {
+    MxWork w{(int)bx, -1, 0, units};
+    if (w.tile >= p.t_main) {
+        const int j = w.tile - p.t_main, sp = j % p.split;
+        w.tile = p.t_main + j / p.split;
+        w.part = j;
+        w.u0 = sp * units / p.split;
+        w.u1 = (sp + 1) * units / p.split;
+    }
+    return w;
+}
+
 template <int ELEM, bool OUT_BF16>
 __global__ void __launch_bounds__(512, 1) k_mx_gemm_full8(MxGemmArgs p) {
     using F = MxFull<ELEM>;
@@ -818,7 +841,12 @@ __global__ void __launch_bounds__(512, 1) k_mx_gemm_full8(MxGemmArgs p) {
     const int wm = w >> 2, wn = w & 3;
     const int h = lane >> 5, l32 = lane & 31;
     const int64_t M = p.M, N = p.N, K = p.K;
-    const int64_t m0 = (int64_t)blockIdx.y * kMxTile, n0 = (int64_t)blockIdx.x * kMxTile;
+    // (32-bit step, chunk and group counts: K < 2^31)
+    const int units = (int)(K / 1024);  // units of 16 K steps
+    const MxWork wk = mx_work(p, units, blockIdx.x);  // uniform across the workgroup
+    const int u0 = wk.u0, u1 = wk.u1;
+    __builtin_assume(u1 > u0);  // every work item has at least one unit (split <= units)
+    const int64_t m0 = (int64_t)(wk.tile / p.tiles_x) * kMxTile, n0 = (int64_t)(wk.tile % p.tiles_x) * kMxTile;
     const int64_t kb = ELEM == kMxE4M3 ? K : K / 2, ks = K / 32;
 
     MxFullSrc src;
@@ -847,16 +875,18 @@ __global__ void __launch_bounds__(512, 1) k_mx_gemm_full8(MxGemmArgs p) {
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
     const MxFull8Offsets off = mx_full8_offsets<ELEM>(wm, wn, l32, h);
-    // (32-bit step, chunk and group counts: K < 2^31)
-    const int nchunks = (int)(K / (64 * SPC)), ngroups = (int)(K / 512), nsteps = (int)(K / 64);
-    auto cclamp = [&](int c) { return c < nchunks ? c : nchunks - 1; };
-    auto gclamp = [&](int g) { return g < ngroups ? g : ngroups - 1; };
+    // the range's chunks and scale groups (a unit is an even number of
+    // chunks and two groups, so its first chunk and group go to slot 0 and
+    // buffer 0, as the loop expects)
+    const int c_end = 16 * u1 / SPC, g_end = 2 * u1, c_first = 16 * u0 / SPC, g_first = 2 * u0;
+    auto cclamp = [&](int c) { return c < c_end ? c : c_end - 1; };
+    auto gclamp = [&](int g) { return g < g_end ? g : g_end - 1; };
 
-    // prologue: scale groups 0 and 1, chunks 0 and 1 (K >= 1024, so all exist)
-    mx_full8_scale_load(s_as, s_bs, so, lane, 0, scb0, w);
-    mx_full8_scale_load(s_as, s_bs, so, lane, 1, scb1, w);
-    mx_full8_chunk_load<ELEM>(src, 0, slot0, w);
-    mx_full8_chunk_load<ELEM>(src, 1, slot1, w);
+    // prologue: the range's first two scale groups and chunks (a unit holds both)
+    mx_full8_scale_load(s_as, s_bs, so, lane, g_first, scb0, w);
+    mx_full8_scale_load(s_as, s_bs, so, lane, g_first + 1, scb1, w);
+    mx_full8_chunk_load<ELEM>(src, c_first, slot0, w);
+    mx_full8_chunk_load<ELEM>(src, c_first + 1, slot1, w);
     __builtin_amdgcn_s_waitcnt(mx_vmcnt_at_most(8));  // all but chunk 1
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
@@ -867,7 +897,7 @@ __global__ void __launch_bounds__(512, 1) k_mx_gemm_full8(MxGemmArgs p) {
 #pragma unroll
     for (int f = 0; f < 6; ++f) mx_full8_read<ELEM>(slot0, scb0, 0, 0, f, off, fa, fb, sa, sb);
 
-    for (int it = 0; it < nsteps; it += 16) {
+    for (int it = 16 * u0; it < 16 * u1; it += 16) {
         const int chunk0 = it / SPC, group0 = it / 8;
 #pragma unroll
         for (int s = 0; s < 16; ++s) {
@@ -912,9 +942,30 @@ __global__ void __launch_bounds__(512, 1) k_mx_gemm_full8(MxGemmArgs p) {
     }
     __builtin_amdgcn_s_waitcnt(mx_vmcnt_at_most(0));
 
-    const int64_t mw = m0 + 128 * wm, nw = n0 + 64 * wn;
-    if (mw + 128 <= M && nw + 64 <= N &&
-        store_wave_block<4, 2, OUT_BF16>(p.C, p.ldc, mw, nw, h, l32,
+    // output: C, or (a part of a split tile; FP32 instances only) the part's
+    // 256 x 256 matrix, through the same code.  The work item is found again
+    // from an opaque copy of the workgroup index rather than kept through
+    // the loop (kept, the tile's origin cost registers the loop needs).
+    // (the divisors made opaque too: otherwise their reciprocals, shared
+    // with the first computation, are what is kept)
+    uint32_t bx = blockIdx.x;
+    MxGemmArgs pe = p;
+    asm volatile("" : "+s"(bx), "+s"(pe.tiles_x), "+s"(pe.split), "+s"(pe.t_main));
+    const MxWork we = mx_work(pe, units, bx);
+    void* Cp = p.C;
+    int64_t ldcp = p.ldc, Me = M, Ne = N;
+    int64_t mt = (int64_t)(we.tile / pe.tiles_x) * kMxTile, nt0 = (int64_t)(we.tile % pe.tiles_x) * kMxTile;
+    if constexpr (!OUT_BF16) {
+        if (we.part >= 0) {
+            Cp = p.parts + (int64_t)we.part * kMxTile * kMxTile;
+            ldcp = kMxTile;
+            Me = Ne = kMxTile;
+            mt = nt0 = 0;
+        }
+    }
+    const int64_t mw = mt + 128 * wm, nw = nt0 + 64 * wn;
+    if (mw + 128 <= Me && nw + 64 <= Ne &&
+        store_wave_block<4, 2, OUT_BF16>(Cp, ldcp, mw, nw, h, l32,
                                          [&](int i, int j, int r) { return acc[i][j][r]; }))
         return;
 #pragma unroll
@@ -922,19 +973,52 @@ __global__ void __launch_bounds__(512, 1) k_mx_gemm_full8(MxGemmArgs p) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int64_t c = nw + 32 * j + l32;
-            if (c >= N) continue;
+            if (c >= Ne) continue;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int64_t m = mw + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
-                if (m < M) {
+                if (m < Me) {
                     if (OUT_BF16)
-                        static_cast<uint16_t*>(p.C)[m * p.ldc + c] =
+                        static_cast<uint16_t*>(Cp)[m * ldcp + c] =
                             (uint16_t)__builtin_bit_cast(uint16_t, (__bf16)acc[i][j][r]);
                     else
-                        static_cast<float*>(p.C)[m * p.ldc + c] = acc[i][j][r];
+                        static_cast<float*>(Cp)[m * ldcp + c] = acc[i][j][r];
                 }
             }
         }
+}
+
+// The tail tiles of a split k_mx_gemm_full8 launch (FP32 output): element
+// (r, c) of tile t_main + blockIdx.x is the sum of its parts' element (r, c),
+// added in part order (deterministic).  Workgroup (x, y) covers 16 rows from
+// 16 y of the tile.
+__global__ void __launch_bounds__(256) k_mx_tail_sum(MxGemmArgs p) {
+    const int tile = p.t_main + (int)blockIdx.x;
+    const int64_t m0 = (int64_t)(tile / p.tiles_x) * kMxTile, n0 = (int64_t)(tile % p.tiles_x) * kMxTile;
+    const float* part0 = p.parts + (int64_t)blockIdx.x * p.split * kMxTile * kMxTile;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int e = 4 * (256 * k + threadIdx.x);  // first of 4 elements in 16 rows x 256
+        const int r = 16 * blockIdx.y + e / kMxTile, c = e % kMxTile;
+        float4 v = *reinterpret_cast<const float4*>(part0 + r * kMxTile + c);
+        for (int s = 1; s < p.split; ++s) {
+            const float4 u =
+                *reinterpret_cast<const float4*>(part0 + (int64_t)s * kMxTile * kMxTile + r * kMxTile + c);
+            v.x += u.x;
+            v.y += u.y;
+            v.z += u.z;
+            v.w += u.w;
+        }
+        const int64_t m = m0 + r;
+        if (m >= p.M) continue;
+        const float o[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int64_t n = n0 + c + q;
+            if (n >= p.N) break;
+            static_cast<float*>(p.C)[m * p.ldc + n] = o[q];
+        }
+    }
 }
 
 // ============================================================ full-line exact kernel
@@ -1222,11 +1306,27 @@ inline int64_t mx_cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 }  // namespace
 
+// Split of the native full-line kernel's last partial round of tiles (FP32
+// output): as gemm_split_plan, in units of 1024 K.
+GemmSplit mx_gemm_split_plan(int64_t M, int64_t N, int64_t K, bool c_bf16, bool exact, int cus) {
+    GemmSplit sp{0, 1, 0};
+    if (c_bf16 || exact || M <= 0 || N <= 0 || K <= 0 || K % 1024 || cus <= 0) return sp;
+    const int64_t tiles = mx_cdiv(N, kMxTile) * mx_cdiv(M, kMxTile), tail = tiles % cus;
+    sp.t_main = tiles;
+    if (tail == 0) return sp;
+    const int64_t split = std::min<int64_t>(std::min<int64_t>(cus / tail, K / 1024), kMaxTailSplit);
+    if (split < 2) return sp;
+    sp.t_main = tiles - tail;
+    sp.split = (int)split;
+    sp.bytes = tail * split * (int64_t)kMxTile * kMxTile * 4;
+    return sp;
+}
+
 hipError_t launch_mx_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
                           const uint8_t* b_scales, int elem, int64_t M, int64_t N, int64_t K, void* C,
-                          bool c_bf16, int64_t ldc, bool exact, hipStream_t s) {
+                          bool c_bf16, int64_t ldc, bool exact, void* ws, size_t ws_bytes, hipStream_t s) {
     if (M == 0 || N == 0) return hipSuccess;
-    MxGemmArgs p{a_codes, a_scales, b_codes, b_scales, M, N, K, C, ldc};
+    MxGemmArgs p{a_codes, a_scales, b_codes, b_scales, M, N, K, C, ldc, 0, 0, 1, nullptr};
     dim3 grid((unsigned)mx_cdiv(N, kMxTile), (unsigned)mx_cdiv(M, kMxTile));
     const bool full = K % 1024 == 0 && K > 0 && (reinterpret_cast<uintptr_t>(a_scales) & 15) == 0 &&
                       (reinterpret_cast<uintptr_t>(b_scales) & 15) == 0;
@@ -1246,10 +1346,28 @@ hipError_t launch_mx_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const
 #undef NVFP4_MXX
         return hipGetLastError();
     }
+    // the full-line kernel takes a one-dimensional grid of tiles (plus the
+    // parts of a split last round)
+    const int64_t tiles = (int64_t)grid.x * grid.y;
+    p.tiles_x = (int)grid.x;
+    p.t_main = (int)tiles;
+    if (full && ws && !c_bf16) {
+        int cus = 0;
+        const hipError_t e = device_cus(cus);
+        if (e != hipSuccess) return e;
+        const GemmSplit plan = mx_gemm_split_plan(M, N, K, false, false, cus);
+        if (plan.split > 1 && (size_t)plan.bytes <= ws_bytes) {
+            p.t_main = (int)plan.t_main;
+            p.split = plan.split;
+            p.parts = static_cast<float*>(ws);
+        }
+    }
+    const int64_t tail = tiles - p.t_main;
+    const dim3 grid1((unsigned)(p.t_main + tail * p.split));
 #define NVFP4_MXG(E, BF)                                                                 \
     do {                                                                                 \
         if (full)                                                                        \
-            hipLaunchKernelGGL((k_mx_gemm_full8<E, BF>), grid, dim3(512), 0, s, p);      \
+            hipLaunchKernelGGL((k_mx_gemm_full8<E, BF>), grid1, dim3(512), 0, s, p);     \
         else                                                                             \
             hipLaunchKernelGGL((k_mx_gemm<E, BF>), grid, dim3(256), 0, s, p);            \
     } while (0)
@@ -1259,6 +1377,8 @@ hipError_t launch_mx_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const
         if (c_bf16) NVFP4_MXG(kMxE2M1, true); else NVFP4_MXG(kMxE2M1, false);
     }
 #undef NVFP4_MXG
+    if (tail > 0)
+        hipLaunchKernelGGL(k_mx_tail_sum, dim3((unsigned)tail, kMxTile / 16), dim3(256), 0, s, p);
     return hipGetLastError();
 }
 

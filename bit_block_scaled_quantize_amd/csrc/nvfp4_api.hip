@@ -344,8 +344,18 @@ nvfp4_status nvfp4_mx_dequantize(const nvfp4_mx_tensor* q, void* y, int32_t dt /
     return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
 
+size_t nvfp4_mx_gemm_workspace_size(const nvfp4_mx_tensor* A, const nvfp4_mx_tensor* B, int32_t c_dt /* nvfp4_dtype */,
+                                    int32_t accum) {
+    if (!A || !B || c_dt != NVFP4_F32 || accum != NVFP4_MX_ACC_NATIVE) return 0;
+    if (A->rows < 0 || B->rows < 0 || A->cols != B->cols) return 0;
+    int cus = 0;
+    if (device_cus(cus) != hipSuccess) return 0;
+    const GemmSplit sp = mx_gemm_split_plan(A->rows, B->rows, A->cols, false, false, cus);
+    return sp.split > 1 ? (size_t)sp.bytes : 0;
+}
+
 nvfp4_status nvfp4_mx_gemm(const nvfp4_mx_tensor* A, const nvfp4_mx_tensor* B, void* C, int32_t c_dt /* nvfp4_dtype */,
-                           int64_t ldc, int32_t accum, void* stream) {
+                           int64_t ldc, int32_t accum, void* ws, size_t ws_bytes, void* stream) {
     if (!A || !B) return NVFP4_ERR_NULL;
     if (!valid_dtype(c_dt)) return NVFP4_ERR_ENUM;
     if (accum != NVFP4_MX_ACC_NATIVE && accum != NVFP4_MX_ACC_EXACT) return NVFP4_ERR_ENUM;
@@ -369,9 +379,11 @@ nvfp4_status nvfp4_mx_gemm(const nvfp4_mx_tensor* A, const nvfp4_mx_tensor* B, v
         !aligned(A->scales, 2) || !aligned(B->scales, 2))
         return NVFP4_ERR_ALIGN;
     if (cdiv(M, 256) > kMaxGridY) return NVFP4_ERR_UNSUPPORTED;
+    if (ws && !aligned(ws, 16)) return NVFP4_ERR_ALIGN;
     hipError_t e = launch_mx_gemm(A->codes, A->scales, B->codes, B->scales,
                                   A->elem == NVFP4_MX_E4M3 ? kMxE4M3 : kMxE2M1, M, N, K, C, c_dt == NVFP4_BF16,
-                                  ldc, accum == NVFP4_MX_ACC_EXACT, static_cast<hipStream_t>(stream));
+                                  ldc, accum == NVFP4_MX_ACC_EXACT, ws, ws ? ws_bytes : 0,
+                                  static_cast<hipStream_t>(stream));
     return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP;
 }
 

@@ -29,6 +29,7 @@ NVFP4_MX_ACC_NATIVE, NVFP4_MX_ACC_EXACT = 0, 1
 EXPORTED = ["nvfp4_quantize_workspace_size", "nvfp4_quantize", "nvfp4_quantize_noalloc", "nvfp4_requantize",
             "nvfp4_dequantize",
             "nvfp4_gemm", "nvfp4_gemm_workspace_size", "nvfp4_grouped_gemm", "nvfp4_mx_quantize", "nvfp4_mx_dequantize", "nvfp4_mx_gemm",
+            "nvfp4_mx_gemm_workspace_size",
             "nvfp4_status_string", "nvfp4_version"]
 
 
@@ -80,8 +81,10 @@ def _load():
     L.nvfp4_mx_quantize.restype = i32
     L.nvfp4_mx_dequantize.argtypes = [ctypes.POINTER(CMXTensor), vp, i32, i64, vp]
     L.nvfp4_mx_dequantize.restype = i32
-    L.nvfp4_mx_gemm.argtypes = [ctypes.POINTER(CMXTensor), ctypes.POINTER(CMXTensor), vp, i32, i64, i32, vp]
+    L.nvfp4_mx_gemm.argtypes = [ctypes.POINTER(CMXTensor), ctypes.POINTER(CMXTensor), vp, i32, i64, i32, vp, sz, vp]
     L.nvfp4_mx_gemm.restype = i32
+    L.nvfp4_mx_gemm_workspace_size.argtypes = [ctypes.POINTER(CMXTensor), ctypes.POINTER(CMXTensor), i32, i32]
+    L.nvfp4_mx_gemm_workspace_size.restype = sz
     L.nvfp4_status_string.argtypes = [i32]
     L.nvfp4_status_string.restype = ctypes.c_char_p
     L.nvfp4_version.argtypes = []
@@ -381,17 +384,33 @@ def nvfp4_mx_dequantize(q, dtype=torch.float32, out=None, stream=None):
     return out
 
 
+def nvfp4_mx_gemm_workspace_size(A, B, out_dtype=torch.float32, accum=NVFP4_MX_ACC_NATIVE):
+    """Bytes of workspace with which nvfp4_mx_gemm splits a last partial
+    round of tiles on the current device (0: no split)."""
+    ca, cb = A.c(), B.c()
+    return int(lib.nvfp4_mx_gemm_workspace_size(ctypes.byref(ca), ctypes.byref(cb), _dtype_code(out_dtype),
+                                                accum))
+
+
 @_launches_on_stream
-def nvfp4_mx_gemm(A, B, out_dtype=torch.float32, out=None, accum=NVFP4_MX_ACC_NATIVE, stream=None):
+def nvfp4_mx_gemm(A, B, out_dtype=torch.float32, out=None, accum=NVFP4_MX_ACC_NATIVE, workspace=None,
+                  stream=None):
     """C = A B^T (A: M x K, B: N x K MX tensors of one element format);
     accum NVFP4_MX_ACC_NATIVE (scaled matrix cores) or NVFP4_MX_ACC_EXACT
-    (exact products, binary32 sums)."""
+    (exact products, binary32 sums).  workspace as for nvfp4_gemm."""
     if out is None:
         out = torch.empty((A.rows, B.rows), dtype=out_dtype, device=A.codes.device)
     assert out.stride(1) == 1
     ldc = out.stride(0) if A.rows > 1 else max(B.rows, out.stride(0))
     ca, cb = A.c(), B.c()
+    if workspace is None:
+        need = int(lib.nvfp4_mx_gemm_workspace_size(ctypes.byref(ca), ctypes.byref(cb), _dtype_code(out.dtype),
+                                                    accum))
+        workspace = torch.empty((need + 15) // 16 * 4, dtype=torch.float32, device=out.device) if need else False
+    if workspace is False:
+        workspace = None
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.nvfp4_mx_gemm(ctypes.byref(ca), ctypes.byref(cb), ctypes.c_void_p(out.data_ptr()),
-                           _dtype_code(out.dtype), ldc, accum, _stream(stream))
+                           _dtype_code(out.dtype), ldc, accum, _ptr(workspace), ws_bytes, _stream(stream))
     _check("nvfp4_mx_gemm", st)
     return out

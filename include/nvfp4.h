@@ -349,7 +349,17 @@ typedef enum { NVFP4_MX_ACC_NATIVE = 0, NVFP4_MX_ACC_EXACT = 1 } nvfp4_mx_accum;
  * Source: asector.ru page, "NVFP4 и Blackwell" (block-scaled tensor-core
  * compute); iitak.ru page, "Как это работает" (MXFP8 in the backward pass). */
 nvfp4_status nvfp4_mx_gemm(const nvfp4_mx_tensor* A, const nvfp4_mx_tensor* B, void* C, int32_t c_dt /* nvfp4_dtype */,
-                           int64_t ldc, int32_t accum, void* stream);
+                           int64_t ldc, int32_t accum, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace of nvfp4_mx_gemm (optional, as for nvfp4_gemm): with ws 16-byte
+ * aligned and ws_bytes >= nvfp4_mx_gemm_workspace_size(A, B, c_dt, accum) >
+ * 0, a last round of 256 x 256 tiles that would leave compute units idle is
+ * computed in parts along K (whole 1024-element units) whose binary32 sums
+ * are added in a fixed order; nonzero only for native accumulation, FP32
+ * output, K % 1024 == 0 and such a last round on the current device; 0 also
+ * for invalid arguments or when the device cannot be queried. */
+size_t nvfp4_mx_gemm_workspace_size(const nvfp4_mx_tensor* A, const nvfp4_mx_tensor* B, int32_t c_dt /* nvfp4_dtype */,
+                                    int32_t accum);
 
 /* Static description of a status code. */
 const char* nvfp4_status_string(int32_t s /* nvfp4_status */);

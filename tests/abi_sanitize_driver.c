@@ -204,27 +204,27 @@ static void mx_cases(void) {
                     asmis = MX(64, 128, 0, 4096, 8193), aneg = MX(-1, 128, 0, 4096, 8192);
     const nvfp4_dtype f32 = NVFP4_F32;
     const nvfp4_mx_accum nat = NVFP4_MX_ACC_NATIVE;
-    CHECK(nvfp4_mx_gemm(NULL, NULL, Y, f32, 32, nat, NULL), NVFP4_ERR_NULL);
-    CHECK(nvfp4_mx_gemm(&a, &b, Y, (nvfp4_dtype)4, 32, nat, NULL), NVFP4_ERR_ENUM);
-    CHECK(nvfp4_mx_gemm(&a, &b, Y, f32, 32, (nvfp4_mx_accum)2, NULL), NVFP4_ERR_ENUM);
-    CHECK(nvfp4_mx_gemm(&a, &b, Y, f32, 32, (nvfp4_mx_accum)-1, NULL), NVFP4_ERR_ENUM);
-    CHECK(nvfp4_mx_gemm(&a3, &b, Y, f32, 32, nat, NULL), NVFP4_ERR_ENUM);
-    CHECK(nvfp4_mx_gemm(&a96, &b96, Y, f32, 32, nat, NULL), NVFP4_ERR_UNSUPPORTED);
-    CHECK(nvfp4_mx_gemm(&a80, &b80, Y, f32, 32, nat, NULL), NVFP4_ERR_SHAPE);
-    CHECK(nvfp4_mx_gemm(&a, &b192, Y, f32, 32, nat, NULL), NVFP4_ERR_SHAPE);
-    CHECK(nvfp4_mx_gemm(&a, &bfp4, Y, f32, 32, nat, NULL), NVFP4_ERR_UNSUPPORTED);
-    CHECK(nvfp4_mx_gemm(&a, &b, Y, f32, 16, nat, NULL), NVFP4_ERR_SHAPE);
-    CHECK(nvfp4_mx_gemm(&a, &b, NULL, f32, 32, nat, NULL), NVFP4_ERR_NULL);
-    CHECK(nvfp4_mx_gemm(&a, &b, (void*)(uintptr_t)65538, f32, 32, nat, NULL), NVFP4_ERR_ALIGN);
-    CHECK(nvfp4_mx_gemm(&amis, &b, Y, f32, 32, nat, NULL), NVFP4_ERR_ALIGN);
-    CHECK(nvfp4_mx_gemm(&asmis, &b, Y, f32, 32, nat, NULL), NVFP4_ERR_ALIGN);
-    CHECK(nvfp4_mx_gemm(&aneg, &b, Y, f32, 32, nat, NULL), NVFP4_ERR_SHAPE);
+    CHECK(nvfp4_mx_gemm(NULL, NULL, Y, f32, 32, nat, NULL, 0, NULL), NVFP4_ERR_NULL);
+    CHECK(nvfp4_mx_gemm(&a, &b, Y, (nvfp4_dtype)4, 32, nat, NULL, 0, NULL), NVFP4_ERR_ENUM);
+    CHECK(nvfp4_mx_gemm(&a, &b, Y, f32, 32, (nvfp4_mx_accum)2, NULL, 0, NULL), NVFP4_ERR_ENUM);
+    CHECK(nvfp4_mx_gemm(&a, &b, Y, f32, 32, (nvfp4_mx_accum)-1, NULL, 0, NULL), NVFP4_ERR_ENUM);
+    CHECK(nvfp4_mx_gemm(&a3, &b, Y, f32, 32, nat, NULL, 0, NULL), NVFP4_ERR_ENUM);
+    CHECK(nvfp4_mx_gemm(&a96, &b96, Y, f32, 32, nat, NULL, 0, NULL), NVFP4_ERR_UNSUPPORTED);
+    CHECK(nvfp4_mx_gemm(&a80, &b80, Y, f32, 32, nat, NULL, 0, NULL), NVFP4_ERR_SHAPE);
+    CHECK(nvfp4_mx_gemm(&a, &b192, Y, f32, 32, nat, NULL, 0, NULL), NVFP4_ERR_SHAPE);
+    CHECK(nvfp4_mx_gemm(&a, &bfp4, Y, f32, 32, nat, NULL, 0, NULL), NVFP4_ERR_UNSUPPORTED);
+    CHECK(nvfp4_mx_gemm(&a, &b, Y, f32, 16, nat, NULL, 0, NULL), NVFP4_ERR_SHAPE);
+    CHECK(nvfp4_mx_gemm(&a, &b, NULL, f32, 32, nat, NULL, 0, NULL), NVFP4_ERR_NULL);
+    CHECK(nvfp4_mx_gemm(&a, &b, (void*)(uintptr_t)65538, f32, 32, nat, NULL, 0, NULL), NVFP4_ERR_ALIGN);
+    CHECK(nvfp4_mx_gemm(&amis, &b, Y, f32, 32, nat, NULL, 0, NULL), NVFP4_ERR_ALIGN);
+    CHECK(nvfp4_mx_gemm(&asmis, &b, Y, f32, 32, nat, NULL, 0, NULL), NVFP4_ERR_ALIGN);
+    CHECK(nvfp4_mx_gemm(&aneg, &b, Y, f32, 32, nat, NULL, 0, NULL), NVFP4_ERR_SHAPE);
     const int64_t K4 = (int64_t)1 << 24;
     nvfp4_mx_tensor ak = MX(64, K4, 0, 4096, 8192), bk = MX(32, K4, 0, 4096, 8192), ak4 = MX(64, 2 * K4, 1, 4096, 8192),
                     bk4 = MX(32, 2 * K4, 1, 4096, 8192);
-    CHECK(nvfp4_mx_gemm(&ak, &bk, Y, f32, 32, nat, NULL), NVFP4_ERR_UNSUPPORTED);
-    CHECK(nvfp4_mx_gemm(&ak4, &bk4, Y, f32, 32, nat, NULL), NVFP4_ERR_UNSUPPORTED);
-    CHECK(nvfp4_mx_gemm(&ak, &bk, Y, f32, 32, NVFP4_MX_ACC_EXACT, NULL), NVFP4_ERR_UNSUPPORTED);
+    CHECK(nvfp4_mx_gemm(&ak, &bk, Y, f32, 32, nat, NULL, 0, NULL), NVFP4_ERR_UNSUPPORTED);
+    CHECK(nvfp4_mx_gemm(&ak4, &bk4, Y, f32, 32, nat, NULL, 0, NULL), NVFP4_ERR_UNSUPPORTED);
+    CHECK(nvfp4_mx_gemm(&ak, &bk, Y, f32, 32, NVFP4_MX_ACC_EXACT, NULL, 0, NULL), NVFP4_ERR_UNSUPPORTED);
 }
 
 static void misc_cases(void) {

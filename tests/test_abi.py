@@ -208,9 +208,9 @@ def test_mx_gemm_rejects_bad_arguments(nv):
     def g(ma=(64, 128, 0), mb=(32, 128, 0), C=65536, dt=0, ldc=32, ac=4096, asc=8192, acc=0):
         a = nv.CMXTensor(ac, asc, ma[0], ma[1], ma[2])
         b = nv.CMXTensor(4096, 8192, mb[0], mb[1], mb[2])
-        return nv.lib.nvfp4_mx_gemm(ctypes.byref(a), ctypes.byref(b), C, dt, ldc, acc, None)
+        return nv.lib.nvfp4_mx_gemm(ctypes.byref(a), ctypes.byref(b), C, dt, ldc, acc, None, 0, None)
 
-    assert nv.lib.nvfp4_mx_gemm(None, None, 65536, 0, 32, 0, None) == E["NULL"]
+    assert nv.lib.nvfp4_mx_gemm(None, None, 65536, 0, 32, 0, None, 0, None) == E["NULL"]
     assert g(dt=4) == E["ENUM"]
     assert g(acc=2) == E["ENUM"]
     assert g(acc=-1) == E["ENUM"]

@@ -79,9 +79,9 @@ def tolerance(elem, K, W_, smax, cref, bf16, accum=NATIVE):
     return tol
 
 
-def check(nv, qa, qb, bf16=False, entries=None, exact=False, what="", accum=NATIVE, out=None):
+def check(nv, qa, qb, bf16=False, entries=None, exact=False, what="", accum=NATIVE, out=None, workspace=None):
     C = nv.nvfp4_mx_gemm(up(nv, qa), up(nv, qb), out_dtype=torch.bfloat16 if bf16 else torch.float32,
-                         accum=accum, out=out)
+                         accum=accum, out=out, workspace=workspace)
     torch.cuda.synchronize()
     C = C.contiguous()
     if bf16:
@@ -240,3 +240,24 @@ def test_mx_gemm_strided_output(nv, elem, shape, accum, bf16):
     raw = big.view(torch.uint8)
     assert bool((raw[:, :40 * es] == 0xA5).all()) and bool((raw[:, (40 + N) * es:] == 0xA5).all()), \
         "bytes outside the output slice were written"
+
+
+@pytest.mark.parametrize("elem", ELEMS)
+@pytest.mark.parametrize("shape", [(768, 768, 4096), (700, 600, 2048)])
+def test_mx_gemm_tail_split(nv, elem, shape):
+    """Native accumulation, FP32 output: a last round of tiles that would
+    leave compute units idle, computed in parts along K (9 tiles: 4 parts at
+    K = 4096, 2 ragged at K = 2048) when the workspace is given.  Split and
+    unsplit (workspace=False) both against the oracle; the split result the
+    same over two calls."""
+    M, N, K = shape
+    qa = mxq(W.student_t((M, K), 3.0, seed=M + 41), elem)
+    qb = mxq(W.student_t((N, K), 3.0, seed=N + 43), elem, seed=1)
+    A, B = up(nv, qa), up(nv, qb)
+    assert nv.nvfp4_mx_gemm_workspace_size(A, B) > 0
+    C1 = nv.nvfp4_mx_gemm(A, B)
+    C2 = nv.nvfp4_mx_gemm(A, B)
+    torch.cuda.synchronize()
+    assert torch.equal(C1.view(torch.int32), C2.view(torch.int32)), "split result differs between calls"
+    check(nv, qa, qb, what=f"split {shape}")
+    check(nv, qa, qb, what=f"unsplit {shape}", workspace=False)
