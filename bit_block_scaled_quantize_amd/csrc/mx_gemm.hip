@@ -1137,7 +1137,10 @@ __global__ void __launch_bounds__(256, 1) k_mx_gemm_exact_full(MxGemmArgs p) {
     const int wm = w >> 1, wn = w & 1;
     const int h = lane >> 5, l32 = lane & 31;
     const int64_t M = p.M, N = p.N, K = p.K;
-    const int64_t m0 = (int64_t)blockIdx.y * kMxTile, n0 = (int64_t)blockIdx.x * kMxTile;
+    const int units = (int)(K / 1024);  // units of 16 K steps
+    const MxWork wk = mx_work(p, units, blockIdx.x);  // uniform across the workgroup
+    const int u0 = wk.u0, u1 = wk.u1;
+    const int64_t m0 = (int64_t)(wk.tile / p.tiles_x) * kMxTile, n0 = (int64_t)(wk.tile % p.tiles_x) * kMxTile;
     const int64_t kb = ELEM == kMxE4M3 ? K : K / 2, ks = K / 32;
 
     MxFullSrc src;
@@ -1169,15 +1172,17 @@ __global__ void __launch_bounds__(256, 1) k_mx_gemm_exact_full(MxGemmArgs p) {
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
     const MxExact4Offsets off = mx_exact4_offsets<ELEM>(wm, wn, l32, h);
-    const int nchunks = (int)(K / (64 * SPC)), ngroups = (int)(K / 512), nsteps = (int)(K / 64);
-    auto cclamp = [&](int c) { return c < nchunks ? c : nchunks - 1; };
-    auto gclamp = [&](int g) { return g < ngroups ? g : ngroups - 1; };
+    // the range's chunks and scale groups (a unit is an even number of
+    // chunks and two groups: its first chunk and group go to slot 0, buffer 0)
+    const int c_end = 16 * u1 / SPC, g_end = 2 * u1, c_first = 16 * u0 / SPC, g_first = 2 * u0;
+    auto cclamp = [&](int c) { return c < c_end ? c : c_end - 1; };
+    auto gclamp = [&](int g) { return g < g_end ? g : g_end - 1; };
 
-    // prologue: scale groups 0 and 1, chunks 0 and 1 (K >= 1024, so all exist)
-    mx_full4_scale_load<ELEM>(src, 0, scb0, w);
-    mx_full4_scale_load<ELEM>(src, 1, scb1, w);
-    mx_full4_chunk_load<ELEM>(src, 0, slot0, w);
-    mx_full4_chunk_load<ELEM>(src, 1, slot1, w);
+    // prologue: the range's first two scale groups and chunks (a unit holds both)
+    mx_full4_scale_load<ELEM>(src, g_first, scb0, w);
+    mx_full4_scale_load<ELEM>(src, g_first + 1, scb1, w);
+    mx_full4_chunk_load<ELEM>(src, c_first, slot0, w);
+    mx_full4_chunk_load<ELEM>(src, c_first + 1, slot1, w);
     __builtin_amdgcn_s_waitcnt(mx_vmcnt_at_most(kMxFull4ChunkLoads));  // all but chunk 1
     __builtin_amdgcn_s_waitcnt(mx_lgkmcnt_zero());
     asm volatile("" ::: "memory");
@@ -1208,7 +1213,7 @@ __global__ void __launch_bounds__(256, 1) k_mx_gemm_exact_full(MxGemmArgs p) {
         for (int pr = 0; pr < 4; ++pr) op[0][o][pr] = pair_of(o, 0, pr, sc);
     }
 
-    for (int it = 0; it < nsteps; it += 16) {
+    for (int it = 16 * u0; it < 16 * u1; it += 16) {
         const int chunk0 = it / SPC, group0 = it / 8;
 #pragma unroll
         for (int s = 0; s < 16; ++s) {
@@ -1273,9 +1278,27 @@ __global__ void __launch_bounds__(256, 1) k_mx_gemm_exact_full(MxGemmArgs p) {
     // the last look-ahead loads (clamped re-reads) land before the LDS is released
     __builtin_amdgcn_s_waitcnt(mx_vmcnt_at_most(0));
 
-    const int64_t nw = n0 + 128 * wn;
-    if (m0 + 128 * wm + 128 <= M && nw + 128 <= N &&
-        store_wave_block<4, 4, OUT_BF16>(p.C, p.ldc, m0 + 128 * wm, nw, h, l32, [&](int i, int j, int r) {
+    // output: C, or (a part of a split tile; FP32 instances only) the part's
+    // 256 x 256 matrix of scaled sums, through the same code; the work item
+    // found again from opaque copies (as in k_mx_gemm_full8)
+    uint32_t bx = blockIdx.x;
+    MxGemmArgs pe = p;
+    asm volatile("" : "+s"(bx), "+s"(pe.tiles_x), "+s"(pe.split), "+s"(pe.t_main));
+    const MxWork we = mx_work(pe, units, bx);
+    void* Cp = p.C;
+    int64_t ldcp = p.ldc, Me = M, Ne = N;
+    int64_t mt = (int64_t)(we.tile / pe.tiles_x) * kMxTile, nt0 = (int64_t)(we.tile % pe.tiles_x) * kMxTile;
+    if constexpr (!OUT_BF16) {
+        if (we.part >= 0) {
+            Cp = p.parts + (int64_t)we.part * kMxTile * kMxTile;
+            ldcp = kMxTile;
+            Me = Ne = kMxTile;
+            mt = nt0 = 0;
+        }
+    }
+    const int64_t nw = nt0 + 128 * wn;
+    if (mt + 128 * wm + 128 <= Me && nw + 128 <= Ne &&
+        store_wave_block<4, 4, OUT_BF16>(Cp, ldcp, mt + 128 * wm, nw, h, l32, [&](int i, int j, int r) {
             return ldexpf(acc[i][j][r], rref[128 * wm + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3)] +
                                             rref[kMxTile + 128 * wn + 32 * j + l32] - 254);
         }))
@@ -1285,18 +1308,18 @@ __global__ void __launch_bounds__(256, 1) k_mx_gemm_exact_full(MxGemmArgs p) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int64_t c = nw + 32 * j + l32;
-            if (c >= N) continue;
+            if (c >= Ne) continue;
             const int rb = rref[kMxTile + 128 * wn + 32 * j + l32];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int rl = 128 * wm + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
-                const int64_t m = m0 + rl;
-                if (m < M) {
+                const int64_t m = mt + rl;
+                if (m < Me) {
                     const float v = ldexpf(acc[i][j][r], rref[rl] + rb - 254);
                     if (OUT_BF16)
-                        static_cast<uint16_t*>(p.C)[m * p.ldc + c] = (uint16_t)__builtin_bit_cast(uint16_t, (__bf16)v);
+                        static_cast<uint16_t*>(Cp)[m * ldcp + c] = (uint16_t)__builtin_bit_cast(uint16_t, (__bf16)v);
                     else
-                        static_cast<float*>(p.C)[m * p.ldc + c] = v;
+                        static_cast<float*>(Cp)[m * ldcp + c] = v;
                 }
             }
         }
@@ -1306,11 +1329,11 @@ inline int64_t mx_cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 }  // namespace
 
-// Split of the native full-line kernel's last partial round of tiles (FP32
-// output): as gemm_split_plan, in units of 1024 K.
-GemmSplit mx_gemm_split_plan(int64_t M, int64_t N, int64_t K, bool c_bf16, bool exact, int cus) {
+// Split of the full-line kernels' last partial round of tiles (FP32 output):
+// as gemm_split_plan, in units of 1024 K.
+GemmSplit mx_gemm_split_plan(int64_t M, int64_t N, int64_t K, bool c_bf16, int cus) {
     GemmSplit sp{0, 1, 0};
-    if (c_bf16 || exact || M <= 0 || N <= 0 || K <= 0 || K % 1024 || cus <= 0) return sp;
+    if (c_bf16 || M <= 0 || N <= 0 || K <= 0 || K % 1024 || cus <= 0) return sp;
     const int64_t tiles = mx_cdiv(N, kMxTile) * mx_cdiv(M, kMxTile), tail = tiles % cus;
     sp.t_main = tiles;
     if (tail == 0) return sp;
@@ -1330,23 +1353,7 @@ hipError_t launch_mx_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const
     dim3 grid((unsigned)mx_cdiv(N, kMxTile), (unsigned)mx_cdiv(M, kMxTile));
     const bool full = K % 1024 == 0 && K > 0 && (reinterpret_cast<uintptr_t>(a_scales) & 15) == 0 &&
                       (reinterpret_cast<uintptr_t>(b_scales) & 15) == 0;
-    if (exact) {
-#define NVFP4_MXX(E, BF)                                                               \
-    do {                                                                               \
-        if (full)                                                                      \
-            hipLaunchKernelGGL((k_mx_gemm_exact_full<E, BF>), grid, dim3(256), 0, s, p); \
-        else                                                                           \
-            hipLaunchKernelGGL((k_mx_gemm_exact<E, BF>), grid, dim3(256), 0, s, p);      \
-    } while (0)
-        if (elem == kMxE4M3) {
-            if (c_bf16) NVFP4_MXX(kMxE4M3, true); else NVFP4_MXX(kMxE4M3, false);
-        } else {
-            if (c_bf16) NVFP4_MXX(kMxE2M1, true); else NVFP4_MXX(kMxE2M1, false);
-        }
-#undef NVFP4_MXX
-        return hipGetLastError();
-    }
-    // the full-line kernel takes a one-dimensional grid of tiles (plus the
+    // the full-line kernels take a one-dimensional grid of tiles (plus the
     // parts of a split last round)
     const int64_t tiles = (int64_t)grid.x * grid.y;
     p.tiles_x = (int)grid.x;
@@ -1355,7 +1362,7 @@ hipError_t launch_mx_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const
         int cus = 0;
         const hipError_t e = device_cus(cus);
         if (e != hipSuccess) return e;
-        const GemmSplit plan = mx_gemm_split_plan(M, N, K, false, false, cus);
+        const GemmSplit plan = mx_gemm_split_plan(M, N, K, false, cus);
         if (plan.split > 1 && (size_t)plan.bytes <= ws_bytes) {
             p.t_main = (int)plan.t_main;
             p.split = plan.split;
@@ -1364,12 +1371,16 @@ hipError_t launch_mx_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const
     }
     const int64_t tail = tiles - p.t_main;
     const dim3 grid1((unsigned)(p.t_main + tail * p.split));
-#define NVFP4_MXG(E, BF)                                                                 \
-    do {                                                                                 \
-        if (full)                                                                        \
-            hipLaunchKernelGGL((k_mx_gemm_full8<E, BF>), grid1, dim3(512), 0, s, p);     \
-        else                                                                             \
-            hipLaunchKernelGGL((k_mx_gemm<E, BF>), grid, dim3(256), 0, s, p);            \
+#define NVFP4_MXG(E, BF)                                                                       \
+    do {                                                                                       \
+        if (exact && full)                                                                     \
+            hipLaunchKernelGGL((k_mx_gemm_exact_full<E, BF>), grid1, dim3(256), 0, s, p);      \
+        else if (exact)                                                                        \
+            hipLaunchKernelGGL((k_mx_gemm_exact<E, BF>), grid, dim3(256), 0, s, p);            \
+        else if (full)                                                                         \
+            hipLaunchKernelGGL((k_mx_gemm_full8<E, BF>), grid1, dim3(512), 0, s, p);           \
+        else                                                                                   \
+            hipLaunchKernelGGL((k_mx_gemm<E, BF>), grid, dim3(256), 0, s, p);                  \
     } while (0)
     if (elem == kMxE4M3) {
         if (c_bf16) NVFP4_MXG(kMxE4M3, true); else NVFP4_MXG(kMxE4M3, false);
