@@ -252,7 +252,10 @@ def main():
     # priority) beside the nearest-even and dequantize calls, which overlaps
     # the two kinds of kernel; the step ends when both streams are done.
     side = torch.cuda.Stream() if args.streams == 2 else None
-    sr_calls = [(ROW, Rs), (COL, Cs), (RC, (R2s, C2s))]
+    # longest first: the stream that finishes last then ends on a short call
+    # (graph replays on one box: 0.334 ms with ROW, COL, fused; 0.328 with
+    # fused, COL, ROW)
+    sr_calls = [(RC, (R2s, C2s)), (COL, Cs), (ROW, Rs)]
 
     def step(i, streams=args.streams):
         x = xs[i % NBUF]
