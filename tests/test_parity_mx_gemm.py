@@ -222,13 +222,15 @@ def test_mx_gemm_8192_sampled(nv, elem):
 
 @pytest.mark.parametrize("accum", ACCUMS)
 @pytest.mark.parametrize("elem", ELEMS)
-@pytest.mark.parametrize("shape", [(512, 512, 1024), (300, 200, 1024)])
+@pytest.mark.parametrize("shape", [(512, 512, 1024), (300, 200, 1024), (300, 600, 2048)])
 @pytest.mark.parametrize("bf16", [False, True])
 def test_mx_gemm_strided_output(nv, elem, shape, accum, bf16):
     """C written into a column slice of a wider buffer (row pitch N + 96,
     first column 40): the output addressing of whole wave tiles comes from
-    the row pitch.  The slice matches the oracle, and every byte outside it
-    keeps the buffer's fill."""
+    the row pitch.  At K = 2048 with FP32 output the 6 tiles' last round is
+    split in two, and the parts' sum is written with that pitch too.  The
+    slice matches the oracle, and every byte outside it keeps the buffer's
+    fill."""
     M, N, K = shape
     qa = mxq(W.student_t((M, K), 3.0, seed=M + 31), elem)
     qb = mxq(W.student_t((N, K), 3.0, seed=N + 37), elem, seed=1)
