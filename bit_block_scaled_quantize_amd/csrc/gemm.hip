@@ -757,8 +757,8 @@ __device__ __forceinline__ void full_read_frag(const FullSlot& slot, int t, int 
     f.zero = false;
 }
 
-// Work of workgroup L (a one-dimensional grid; tiles numbered row-major over
-// a tiles_x-wide grid of 256 x 256 tiles): tiles 0 .. t_main - 1 whole, one
+// Work item L = first + blockIdx.x (tiles numbered row-major over a
+// tiles_x-wide grid of 256 x 256 tiles): tiles 0 .. t_main - 1 whole, one
 // per workgroup; the tiles after them (a last round that would leave most
 // compute units idle) each split `split` ways along K, part s taking chunk
 // pairs [s P / split, (s + 1) P / split) of the P = K / 512 pairs.  A part
@@ -771,8 +771,8 @@ struct FullWork {
     int64_t c0, c1;
 };
 
-__device__ __forceinline__ FullWork full_work(int t_main, int split, int64_t nchunks) {
-    FullWork wk{(int)blockIdx.x, -1, 0, nchunks};
+__device__ __forceinline__ FullWork full_work(int first, int t_main, int split, int64_t nchunks) {
+    FullWork wk{first + (int)blockIdx.x, -1, 0, nchunks};
     if (wk.tile >= t_main) {
         const int j = wk.tile - t_main, s = j % split;
         const int64_t pairs = nchunks / 2;
@@ -785,7 +785,7 @@ __device__ __forceinline__ FullWork full_work(int t_main, int split, int64_t nch
 }
 
 template <bool GROUPED, bool SWIGLU, bool OUT_BF16>
-__global__ void __launch_bounds__(256, 1) k_gemm_full(GemmArgs p, int tiles_x, int t_main, int split,
+__global__ void __launch_bounds__(256, 1) k_gemm_full(GemmArgs p, int tiles_x, int first, int t_main, int split,
                                                       float* __restrict__ partials) {
     __shared__ __attribute__((aligned(16))) uint8_t a0c[kFullCodes];
     __shared__ __attribute__((aligned(16))) uint8_t a1c[kFullCodes];
@@ -808,7 +808,7 @@ __global__ void __launch_bounds__(256, 1) k_gemm_full(GemmArgs p, int tiles_x, i
 
     const int64_t K = p.K, kc2 = K / 2, ks = K / 16;
     const int64_t nchunks = K / 256;  // even: K % 512 == 0
-    const FullWork wk = full_work(t_main, split, nchunks);  // uniform across the workgroup
+    const FullWork wk = full_work(first, t_main, split, nchunks);  // uniform across the workgroup
     const int64_t tx = wk.tile % tiles_x, ty = wk.tile / tiles_x;
     const TileRows tr = tile_rows<GROUPED>(p, ty);
     if (!tr.ok) return;  // uniform across the workgroup
@@ -936,10 +936,12 @@ __global__ void __launch_bounds__(256, 1) k_gemm_full(GemmArgs p, int tiles_x, i
     epilogue<GROUPED, SWIGLU, OUT_BF16>(q, acc, alpha, em0, em_end, wm, wn, fresh_lane_id(), etx);
 }
 
-// The tail tiles of a split k_gemm_full launch (FP32 output): element (r, c)
-// of tile t_main + blockIdx.x is alpha times the sum of its parts' element
-// (r, c), added in part order (deterministic).
+// The tail tiles of a split k_gemm_full launch: element (r, c) of tile
+// t_main + blockIdx.x is alpha times the sum of its parts' element (r, c),
+// added in part order (deterministic), rounded to BF16 as the epilogue
+// rounds for BF16 outputs.
 // Workgroup (x, y) covers 16 rows from 16 y of the tile.
+template <bool OUT_BF16>
 __global__ void __launch_bounds__(256) k_gemm_tail_sum(GemmArgs p, int tiles_x, int t_main, int split,
                                                        const float* __restrict__ partials) {
     const int tile = t_main + (int)blockIdx.x;
@@ -965,7 +967,10 @@ __global__ void __launch_bounds__(256) k_gemm_tail_sum(GemmArgs p, int tiles_x, 
         for (int q = 0; q < 4; ++q) {
             const int64_t n = n0 + c + q;
             if (n >= p.N) break;
-            static_cast<float*>(p.C)[m * p.ldc + n] = o[q];
+            if (OUT_BF16)
+                static_cast<uint16_t*>(p.C)[m * p.ldc + n] = (uint16_t)f32_to_bf16_rne(o[q]);
+            else
+                static_cast<float*>(p.C)[m * p.ldc + n] = o[q];
         }
     }
 }
@@ -1006,7 +1011,7 @@ GemmSplit gemm_split_plan(int64_t M, int64_t N, int64_t K, bool swiglu, int cus)
     sp.t_main = tiles;
     if (tail == 0) return sp;
     // the last round's tiles, each split over the compute units they leave
-    // idle (at least two chunk pairs per part would be wasted on loads: one pair minimum)
+    // idle, every part at least one pair of 256-element chunks
     const int64_t split = std::min<int64_t>(std::min<int64_t>(cus / tail, K / 512), kMaxTailSplit);
     if (split < 2) return sp;
     sp.t_main = tiles - tail;
@@ -1031,7 +1036,7 @@ hipError_t launch_gemm(const Operand& A, const Operand& B, int64_t M, int64_t N,
     const int64_t tx = swiglu ? cdiv(N / 2, kBN / 2) : cdiv(N, kBN), ty = cdiv(M, kBM);
     if (full_path(A, B, M, N, K, tx * ty)) {
         GemmSplit sp{tx * ty, 1, 0};
-        if (ws && !swiglu && !c_bf16) {  // parts are binary32 sums: FP32 outputs
+        if (ws && !swiglu) {
             int cus = 0;
             const hipError_t e = device_cus(cus);
             if (e != hipSuccess) return e;
@@ -1039,18 +1044,31 @@ hipError_t launch_gemm(const Operand& A, const Operand& B, int64_t M, int64_t N,
             if (plan.split > 1 && (size_t)plan.bytes <= ws_bytes) sp = plan;
         }
         const int64_t tail = tx * ty - sp.t_main;
-        const dim3 grid((unsigned)(sp.t_main + tail * sp.split));
         float* parts = static_cast<float*>(ws);
         const int itx = (int)tx, tm = (int)sp.t_main, spl = sp.split;
-        if (swiglu)
-            hipLaunchKernelGGL((k_gemm_full<false, true, true>), grid, dim3(256), 0, s, p, itx, tm, 1, nullptr);
-        else if (c_bf16)
-            hipLaunchKernelGGL((k_gemm_full<false, false, true>), grid, dim3(256), 0, s, p, itx, tm, spl, parts);
-        else
-            hipLaunchKernelGGL((k_gemm_full<false, false, false>), grid, dim3(256), 0, s, p, itx, tm, spl, parts);
-        if (tail > 0 && sp.split > 1) {
-            hipLaunchKernelGGL(k_gemm_tail_sum, dim3((unsigned)tail, kBM / 16), dim3(256), 0, s, p, itx, tm, spl,
-                               parts);
+        // the parts always run in the FP32 instance (their sums are binary32);
+        // with a BF16 output the whole tiles take the BF16 instance, launched
+        // first over those tiles only
+        if (swiglu) {
+            hipLaunchKernelGGL((k_gemm_full<false, true, true>), dim3((unsigned)(tx * ty)), dim3(256), 0, s, p, itx, 0,
+                               tm, 1, nullptr);
+        } else if (c_bf16) {
+            if (tm > 0)
+                hipLaunchKernelGGL((k_gemm_full<false, false, true>), dim3((unsigned)tm), dim3(256), 0, s, p, itx, 0,
+                                   tm, 1, nullptr);
+            if (tail > 0)
+                hipLaunchKernelGGL((k_gemm_full<false, false, false>), dim3((unsigned)(tail * spl)), dim3(256), 0, s,
+                                   p, itx, tm, tm, spl, parts);
+        } else {
+            hipLaunchKernelGGL((k_gemm_full<false, false, false>), dim3((unsigned)(tm + tail * spl)), dim3(256), 0, s,
+                               p, itx, 0, tm, spl, parts);
+        }
+        if (tail > 0) {
+            const dim3 g2((unsigned)tail, kBM / 16);
+            if (c_bf16)
+                hipLaunchKernelGGL((k_gemm_tail_sum<true>), g2, dim3(256), 0, s, p, itx, tm, spl, parts);
+            else
+                hipLaunchKernelGGL((k_gemm_tail_sum<false>), g2, dim3(256), 0, s, p, itx, tm, spl, parts);
         }
         return hipGetLastError();
     }
@@ -1091,7 +1109,7 @@ hipError_t launch_grouped_gemm(int G, const Operand& A, const int64_t* offsets, 
 #define NVFP4_GROUPED(SW, BF)                                                                               \
     do {                                                                                                    \
         if (full)                                                                                           \
-            hipLaunchKernelGGL((k_gemm_full<true, SW, BF>), grid1, dim3(256), 0, s, p, itx, nt, 1, nullptr); \
+            hipLaunchKernelGGL((k_gemm_full<true, SW, BF>), grid1, dim3(256), 0, s, p, itx, 0, nt, 1, nullptr); \
         else if (fast)                                                                                      \
             hipLaunchKernelGGL((k_gemm_ring<true, SW, BF>), grid2, dim3(256), 0, s, p);                     \
         else                                                                                                \

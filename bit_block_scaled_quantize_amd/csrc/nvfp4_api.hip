@@ -229,7 +229,7 @@ nvfp4_status nvfp4_dequantize(const nvfp4_tensor* q, void* y, int32_t dt /* nvfp
 
 size_t nvfp4_gemm_workspace_size(const nvfp4_tensor* A, const nvfp4_tensor* B, int32_t c_dt /* nvfp4_dtype */,
                                  int32_t ep /* nvfp4_epilogue */) {
-    if (!A || !B || c_dt != NVFP4_F32 || ep != NVFP4_EPI_NONE) return 0;
+    if (!A || !B || !valid_dtype(c_dt) || ep != NVFP4_EPI_NONE) return 0;
     if (A->rows < 0 || B->rows < 0 || A->cols != B->cols) return 0;
     int cus = 0;
     if (device_cus(cus) != hipSuccess) return 0;

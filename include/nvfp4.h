@@ -216,8 +216,8 @@ nvfp4_status nvfp4_requantize(const nvfp4_tensor* in, const nvfp4_quant_opts* op
  * Workspace (optional): with ws 16-byte aligned and ws_bytes >=
  * nvfp4_gemm_workspace_size(A, B, c_dt, ep) > 0, a last round of 256 x 256
  * output tiles that would leave compute units idle is computed in parts
- * along K, whose binary32 sums are added in a fixed order; ws NULL or
- * smaller: no split.  The two give the same accuracy, not always the same
+ * along K, whose binary32 sums are added in a fixed order (and, for BF16
+ * output, rounded once); ws NULL or smaller: no split.  The two give the same accuracy, not always the same
  * last bits; each is deterministic on a given device (the split depends on
  * its compute-unit count).  ws is scratch for this call only: calls that
  * overlap must not share it.
@@ -228,10 +228,11 @@ nvfp4_status nvfp4_gemm(const nvfp4_tensor* A, const nvfp4_tensor* B, void* C, i
                         int64_t ldc, int32_t ep /* nvfp4_epilogue */, void* ws, size_t ws_bytes, void* stream);
 
 /* Bytes of workspace with which nvfp4_gemm splits its last round of tiles on
- * the current device: nonzero only for FP32 output without an epilogue,
- * K % 512 == 0 and a tile count that leaves a partial last round with enough
- * idle compute units; 0 also for invalid arguments or when the device cannot
- * be queried.  At most 8 parts of 256 KiB per tile of that round. */
+ * the current device: nonzero only without an epilogue (FP32 or BF16
+ * output), K % 512 == 0 and a tile count that leaves a partial last round
+ * with enough idle compute units; 0 also for invalid arguments or when the
+ * device cannot be queried.  At most 8 parts of 256 KiB per tile of that
+ * round. */
 size_t nvfp4_gemm_workspace_size(const nvfp4_tensor* A, const nvfp4_tensor* B, int32_t c_dt /* nvfp4_dtype */,
                                  int32_t ep /* nvfp4_epilogue */);
 

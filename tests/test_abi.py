@@ -139,7 +139,7 @@ def test_gemm_rejects_bad_arguments(nv):
     assert g(ctypes.byref(a3), ctypes.byref(b3), 65536, 0, 32, 0, None, 0, None) == 3   # K % 16
     assert g(ctypes.byref(a), ctypes.byref(b), 65536, 0, 32, 0, 4100, 1 << 20, None) == 4   # ws misaligned
     s = nv.lib.nvfp4_gemm_workspace_size
-    assert s(ctypes.byref(a), ctypes.byref(b), 1, 0) == 0      # BF16 output: no split
+    assert s(ctypes.byref(a), ctypes.byref(b), 9, 0) == 0      # invalid dtype
     assert s(ctypes.byref(a), ctypes.byref(b48), 1, 1) == 0    # SwiGLU: no split
     assert s(None, ctypes.byref(b), 0, 0) == 0
 

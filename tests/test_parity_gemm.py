@@ -130,10 +130,11 @@ def test_gemm_strided_output(nv, M, N, K, out):
         "bytes outside the output slice were written"
 
 
+@pytest.mark.parametrize("out", ["f32", "bf16"])
 @pytest.mark.parametrize("M,N,K", [(768, 768, 4096), (700, 608, 2048), (300, 272, 1024)])
-def test_gemm_tail_split(nv, M, N, K):
+def test_gemm_tail_split(nv, M, N, K, out):
     """A last round of tiles that would leave compute units idle, computed in
-    parts along K (FP32 output, workspace given): against the oracle, the
+    parts along K (FP32 and BF16 outputs, workspace given): against the oracle, the
     same over two calls, and the unsplit call (workspace=False) against the
     oracle too.  9 tiles at K = 4096 take 8 parts each; 9 ragged tiles at
     K = 2048, 4; 4 ragged tiles at K = 1024, 2."""
@@ -141,14 +142,15 @@ def test_gemm_tail_split(nv, M, N, K):
     b = W.normal((N, K), 0.02, seed=N + 13)
     A, B = quant_host(a, O.ROW_1D), quant_host(b, O.BLK_2D)
     Ad, Bd = q_to_device(A, nv), q_to_device(B, nv)
-    assert nv.nvfp4_gemm_workspace_size(Ad, Bd) > 0
-    C1 = nv.nvfp4_gemm(Ad, Bd)
-    C2 = nv.nvfp4_gemm(Ad, Bd)
-    C0 = nv.nvfp4_gemm(Ad, Bd, workspace=False)
+    dt = torch.float32 if out == "f32" else torch.bfloat16
+    assert nv.nvfp4_gemm_workspace_size(Ad, Bd, out_dtype=dt) > 0
+    C1 = nv.nvfp4_gemm(Ad, Bd, out_dtype=dt)
+    C2 = nv.nvfp4_gemm(Ad, Bd, out_dtype=dt)
+    C0 = nv.nvfp4_gemm(Ad, Bd, out_dtype=dt, workspace=False)
     Cref, Wref = OB.gemm(A, B)
-    check(out_to_f64(C1), Cref, Wref, False, f"split gemm {M}x{N}x{K}")
-    check(out_to_f64(C0), Cref, Wref, False, f"unsplit gemm {M}x{N}x{K}")
-    assert torch.equal(C1.view(torch.int32), C2.view(torch.int32)), "split result differs between calls"
+    check(out_to_f64(C1), Cref, Wref, out == "bf16", f"split gemm {M}x{N}x{K}")
+    check(out_to_f64(C0), Cref, Wref, out == "bf16", f"unsplit gemm {M}x{N}x{K}")
+    assert torch.equal(C1.view(torch.int16), C2.view(torch.int16)), "split result differs between calls"
 
 
 # -------------------------------------------------- full-size sampled checks
