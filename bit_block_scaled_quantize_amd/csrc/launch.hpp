@@ -93,7 +93,7 @@ hipError_t launch_mx_dequantize(const uint8_t* codes, const uint8_t* scales, int
 hipError_t launch_mx_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
                           const uint8_t* b_scales, int elem, int64_t M, int64_t N, int64_t K, void* C,
                           bool c_bf16, int64_t ldc, bool exact, void* ws, size_t ws_bytes, hipStream_t s);
-// The MX GEMM's split plan (FP32 output, K % 1024 == 0).
-GemmSplit mx_gemm_split_plan(int64_t M, int64_t N, int64_t K, bool c_bf16, int cus);
+// The MX GEMM's split plan (full-line kernels: K % 1024 == 0).
+GemmSplit mx_gemm_split_plan(int64_t M, int64_t N, int64_t K, int cus);
 
 }  // namespace nvfp4

@@ -100,6 +100,7 @@ struct MxGemmArgs {
     // K, their parts' binary32 sums written as 256 x 256 matrices to `parts`
     int tiles_x, t_main, split;
     float* parts;
+    int first;  // work item of workgroup 0 (a launch of parts only starts past the whole tiles)
 };
 
 // Global sources of a workgroup's ring loads: wave-uniform bases (the tile's
@@ -809,14 +810,15 @@ __device__ __forceinline__ void mx_full8_read(const uint8_t* slot, const uint8_t
     }
 }
 
-// Work of full-line workgroup bx: tile bx whole (bx < t_main), or part s
-// of tile t_main + j / split (j = bx - t_main, s = j % split), which takes
-// units [s U / split, (s + 1) U / split) of the U units of 16 K steps.
+// Work item L = first + bx of a full-line workgroup bx: tile L whole
+// (L < t_main), or part s of tile t_main + j / split (j = L - t_main,
+// s = j % split), which takes units [s U / split, (s + 1) U / split) of the
+// U units of 16 K steps.
 struct MxWork {
     int tile, part, u0, u1;
 };
 __device__ __forceinline__ MxWork mx_work(const MxGemmArgs& p, int units, uint32_t bx) {
-    MxWork w{(int)bx, -1, 0, units};
+    MxWork w{p.first + (int)bx, -1, 0, units};
     if (w.tile >= p.t_main) {
         const int j = w.tile - p.t_main, sp = j % p.split;
         w.tile = p.t_main + j / p.split;
@@ -950,7 +952,7 @@ __global__ void __launch_bounds__(512, 1) k_mx_gemm_full8(MxGemmArgs p) {
     // with the first computation, are what is kept)
     uint32_t bx = blockIdx.x;
     MxGemmArgs pe = p;
-    asm volatile("" : "+s"(bx), "+s"(pe.tiles_x), "+s"(pe.split), "+s"(pe.t_main));
+    asm volatile("" : "+s"(bx), "+s"(pe.tiles_x), "+s"(pe.split), "+s"(pe.t_main), "+s"(pe.first));
     const MxWork we = mx_work(pe, units, bx);
     void* Cp = p.C;
     int64_t ldcp = p.ldc, Me = M, Ne = N;
@@ -988,10 +990,12 @@ __global__ void __launch_bounds__(512, 1) k_mx_gemm_full8(MxGemmArgs p) {
         }
 }
 
-// The tail tiles of a split k_mx_gemm_full8 launch (FP32 output): element
-// (r, c) of tile t_main + blockIdx.x is the sum of its parts' element (r, c),
-// added in part order (deterministic).  Workgroup (x, y) covers 16 rows from
+// The tail tiles of a split full-line launch: element (r, c) of tile
+// t_main + blockIdx.x is the sum of its parts' element (r, c), added in part
+// order (deterministic), rounded to BF16 as the epilogues round for BF16
+// outputs.  Workgroup (x, y) covers 16 rows from
 // 16 y of the tile.
+template <bool OUT_BF16>
 __global__ void __launch_bounds__(256) k_mx_tail_sum(MxGemmArgs p) {
     const int tile = p.t_main + (int)blockIdx.x;
     const int64_t m0 = (int64_t)(tile / p.tiles_x) * kMxTile, n0 = (int64_t)(tile % p.tiles_x) * kMxTile;
@@ -1016,7 +1020,10 @@ __global__ void __launch_bounds__(256) k_mx_tail_sum(MxGemmArgs p) {
         for (int q = 0; q < 4; ++q) {
             const int64_t n = n0 + c + q;
             if (n >= p.N) break;
-            static_cast<float*>(p.C)[m * p.ldc + n] = o[q];
+            if (OUT_BF16)
+                static_cast<uint16_t*>(p.C)[m * p.ldc + n] = (uint16_t)__builtin_bit_cast(uint16_t, (__bf16)o[q]);
+            else
+                static_cast<float*>(p.C)[m * p.ldc + n] = o[q];
         }
     }
 }
@@ -1283,7 +1290,7 @@ __global__ void __launch_bounds__(256, 1) k_mx_gemm_exact_full(MxGemmArgs p) {
     // found again from opaque copies (as in k_mx_gemm_full8)
     uint32_t bx = blockIdx.x;
     MxGemmArgs pe = p;
-    asm volatile("" : "+s"(bx), "+s"(pe.tiles_x), "+s"(pe.split), "+s"(pe.t_main));
+    asm volatile("" : "+s"(bx), "+s"(pe.tiles_x), "+s"(pe.split), "+s"(pe.t_main), "+s"(pe.first));
     const MxWork we = mx_work(pe, units, bx);
     void* Cp = p.C;
     int64_t ldcp = p.ldc, Me = M, Ne = N;
@@ -1329,11 +1336,11 @@ inline int64_t mx_cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 }  // namespace
 
-// Split of the full-line kernels' last partial round of tiles (FP32 output):
-// as gemm_split_plan, in units of 1024 K.
-GemmSplit mx_gemm_split_plan(int64_t M, int64_t N, int64_t K, bool c_bf16, int cus) {
+// Split of the full-line kernels' last partial round of tiles: as
+// gemm_split_plan, in units of 1024 K.
+GemmSplit mx_gemm_split_plan(int64_t M, int64_t N, int64_t K, int cus) {
     GemmSplit sp{0, 1, 0};
-    if (c_bf16 || M <= 0 || N <= 0 || K <= 0 || K % 1024 || cus <= 0) return sp;
+    if (M <= 0 || N <= 0 || K <= 0 || K % 1024 || cus <= 0) return sp;
     const int64_t tiles = mx_cdiv(N, kMxTile) * mx_cdiv(M, kMxTile), tail = tiles % cus;
     sp.t_main = tiles;
     if (tail == 0) return sp;
@@ -1349,20 +1356,20 @@ hipError_t launch_mx_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const
                           const uint8_t* b_scales, int elem, int64_t M, int64_t N, int64_t K, void* C,
                           bool c_bf16, int64_t ldc, bool exact, void* ws, size_t ws_bytes, hipStream_t s) {
     if (M == 0 || N == 0) return hipSuccess;
-    MxGemmArgs p{a_codes, a_scales, b_codes, b_scales, M, N, K, C, ldc, 0, 0, 1, nullptr};
+    MxGemmArgs p{a_codes, a_scales, b_codes, b_scales, M, N, K, C, ldc, 0, 0, 1, nullptr, 0};
     dim3 grid((unsigned)mx_cdiv(N, kMxTile), (unsigned)mx_cdiv(M, kMxTile));
     const bool full = K % 1024 == 0 && K > 0 && (reinterpret_cast<uintptr_t>(a_scales) & 15) == 0 &&
                       (reinterpret_cast<uintptr_t>(b_scales) & 15) == 0;
-    // the full-line kernels take a one-dimensional grid of tiles (plus the
-    // parts of a split last round)
+    // the full-line kernels take a one-dimensional grid of work items: the
+    // whole tiles, then the parts of a split last round
     const int64_t tiles = (int64_t)grid.x * grid.y;
     p.tiles_x = (int)grid.x;
     p.t_main = (int)tiles;
-    if (full && ws && !c_bf16) {
+    if (full && ws) {
         int cus = 0;
         const hipError_t e = device_cus(cus);
         if (e != hipSuccess) return e;
-        const GemmSplit plan = mx_gemm_split_plan(M, N, K, false, cus);
+        const GemmSplit plan = mx_gemm_split_plan(M, N, K, cus);
         if (plan.split > 1 && (size_t)plan.bytes <= ws_bytes) {
             p.t_main = (int)plan.t_main;
             p.split = plan.split;
@@ -1370,17 +1377,24 @@ hipError_t launch_mx_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const
         }
     }
     const int64_t tail = tiles - p.t_main;
-    const dim3 grid1((unsigned)(p.t_main + tail * p.split));
-#define NVFP4_MXG(E, BF)                                                                       \
-    do {                                                                                       \
-        if (exact && full)                                                                     \
-            hipLaunchKernelGGL((k_mx_gemm_exact_full<E, BF>), grid1, dim3(256), 0, s, p);      \
-        else if (exact)                                                                        \
-            hipLaunchKernelGGL((k_mx_gemm_exact<E, BF>), grid, dim3(256), 0, s, p);            \
-        else if (full)                                                                         \
-            hipLaunchKernelGGL((k_mx_gemm_full8<E, BF>), grid1, dim3(512), 0, s, p);           \
-        else                                                                                   \
-            hipLaunchKernelGGL((k_mx_gemm<E, BF>), grid, dim3(256), 0, s, p);                  \
+    // the parts run in the FP32 instance (their sums are binary32): with a
+    // BF16 output, a second launch over the parts only
+    MxGemmArgs pp = p;
+    pp.first = p.t_main;
+    const dim3 g_all((unsigned)(p.t_main + (c_bf16 ? 0 : tail * p.split))), g_parts((unsigned)(tail * p.split));
+#define NVFP4_MXG(E, BF)                                                                                  \
+    do {                                                                                                  \
+        if (exact && full) {                                                                              \
+            if (g_all.x) hipLaunchKernelGGL((k_mx_gemm_exact_full<E, BF>), g_all, dim3(256), 0, s, p);    \
+            if (BF && tail) hipLaunchKernelGGL((k_mx_gemm_exact_full<E, false>), g_parts, dim3(256), 0, s, pp); \
+        } else if (exact) {                                                                               \
+            hipLaunchKernelGGL((k_mx_gemm_exact<E, BF>), grid, dim3(256), 0, s, p);                       \
+        } else if (full) {                                                                                \
+            if (g_all.x) hipLaunchKernelGGL((k_mx_gemm_full8<E, BF>), g_all, dim3(512), 0, s, p);         \
+            if (BF && tail) hipLaunchKernelGGL((k_mx_gemm_full8<E, false>), g_parts, dim3(512), 0, s, pp); \
+        } else {                                                                                          \
+            hipLaunchKernelGGL((k_mx_gemm<E, BF>), grid, dim3(256), 0, s, p);                             \
+        }                                                                                                 \
     } while (0)
     if (elem == kMxE4M3) {
         if (c_bf16) NVFP4_MXG(kMxE4M3, true); else NVFP4_MXG(kMxE4M3, false);
@@ -1388,8 +1402,11 @@ hipError_t launch_mx_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const
         if (c_bf16) NVFP4_MXG(kMxE2M1, true); else NVFP4_MXG(kMxE2M1, false);
     }
 #undef NVFP4_MXG
-    if (tail > 0)
-        hipLaunchKernelGGL(k_mx_tail_sum, dim3((unsigned)tail, kMxTile / 16), dim3(256), 0, s, p);
+    if (tail > 0) {
+        const dim3 g2((unsigned)tail, kMxTile / 16);
+        if (c_bf16) hipLaunchKernelGGL(k_mx_tail_sum<true>, g2, dim3(256), 0, s, p);
+        else hipLaunchKernelGGL(k_mx_tail_sum<false>, g2, dim3(256), 0, s, p);
+    }
     return hipGetLastError();
 }
 

@@ -346,12 +346,12 @@ nvfp4_status nvfp4_mx_dequantize(const nvfp4_mx_tensor* q, void* y, int32_t dt /
 
 size_t nvfp4_mx_gemm_workspace_size(const nvfp4_mx_tensor* A, const nvfp4_mx_tensor* B, int32_t c_dt /* nvfp4_dtype */,
                                     int32_t accum) {
-    if (!A || !B || c_dt != NVFP4_F32) return 0;
+    if (!A || !B || !valid_dtype(c_dt)) return 0;
     if (accum != NVFP4_MX_ACC_NATIVE && accum != NVFP4_MX_ACC_EXACT) return 0;
     if (A->rows < 0 || B->rows < 0 || A->cols != B->cols) return 0;
     int cus = 0;
     if (device_cus(cus) != hipSuccess) return 0;
-    const GemmSplit sp = mx_gemm_split_plan(A->rows, B->rows, A->cols, false, cus);
+    const GemmSplit sp = mx_gemm_split_plan(A->rows, B->rows, A->cols, cus);
     return sp.split > 1 ? (size_t)sp.bytes : 0;
 }
 

@@ -244,23 +244,27 @@ def test_mx_gemm_strided_output(nv, elem, shape, accum, bf16):
         "bytes outside the output slice were written"
 
 
+@pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
 @pytest.mark.parametrize("accum", ACCUMS)
 @pytest.mark.parametrize("elem", ELEMS)
 @pytest.mark.parametrize("shape", [(768, 768, 4096), (700, 600, 2048)])
-def test_mx_gemm_tail_split(nv, elem, shape, accum):
-    """Both accumulation modes, FP32 output: a last round of tiles that would
-    leave compute units idle, computed in parts along K (9 tiles: 4 parts at
-    K = 4096, 2 ragged at K = 2048) when the workspace is given.  Split and
-    unsplit (workspace=False) both against the oracle; the split result the
-    same over two calls."""
+def test_mx_gemm_tail_split(nv, elem, shape, accum, bf16):
+    """Both accumulation modes, both output types: a last round of tiles that
+    would leave compute units idle, computed in parts along K (9 tiles: 4
+    parts at K = 4096, 2 ragged at K = 2048) when the workspace is given; a
+    BF16 output rounds the parts' binary32 sum once.  Split and unsplit
+    (workspace=False) both against the oracle; the split result the same
+    over two calls."""
     M, N, K = shape
     qa = mxq(W.student_t((M, K), 3.0, seed=M + 41), elem)
     qb = mxq(W.student_t((N, K), 3.0, seed=N + 43), elem, seed=1)
     A, B = up(nv, qa), up(nv, qb)
-    assert nv.nvfp4_mx_gemm_workspace_size(A, B, accum=accum) > 0
-    C1 = nv.nvfp4_mx_gemm(A, B, accum=accum)
-    C2 = nv.nvfp4_mx_gemm(A, B, accum=accum)
+    dt = torch.bfloat16 if bf16 else torch.float32
+    assert nv.nvfp4_mx_gemm_workspace_size(A, B, out_dtype=dt, accum=accum) > 0
+    C1 = nv.nvfp4_mx_gemm(A, B, out_dtype=dt, accum=accum)
+    C2 = nv.nvfp4_mx_gemm(A, B, out_dtype=dt, accum=accum)
     torch.cuda.synchronize()
-    assert torch.equal(C1.view(torch.int32), C2.view(torch.int32)), "split result differs between calls"
-    check(nv, qa, qb, what=f"split {shape}", accum=accum)
-    check(nv, qa, qb, what=f"unsplit {shape}", workspace=False, accum=accum)
+    assert torch.equal(C1.view(torch.int16 if bf16 else torch.int32),
+                       C2.view(torch.int16 if bf16 else torch.int32)), "split result differs between calls"
+    check(nv, qa, qb, bf16=bf16, what=f"split {shape}", accum=accum)
+    check(nv, qa, qb, bf16=bf16, what=f"unsplit {shape}", workspace=False, accum=accum)
