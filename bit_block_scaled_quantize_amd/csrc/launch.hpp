@@ -94,6 +94,8 @@ hipError_t launch_mx_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const
                           const uint8_t* b_scales, int elem, int64_t M, int64_t N, int64_t K, void* C,
                           bool c_bf16, int64_t ldc, bool exact, void* ws, size_t ws_bytes, hipStream_t s);
 // The MX GEMM's split plan (full-line kernels: K % 1024 == 0).
-GemmSplit mx_gemm_split_plan(int64_t M, int64_t N, int64_t K, int cus);
+GemmSplit mx_gemm_split_plan(int64_t M, int64_t N, int64_t K, double tile_us, int cus);
+// A lone last-round tile's time per 1024 K for this element format and accumulation mode, in µs.
+double mx_split_tile_us(int elem, bool exact);
 
 }  // namespace nvfp4

@@ -1337,14 +1337,37 @@ inline int64_t mx_cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 }  // namespace
 
 // Split of the full-line kernels' last partial round of tiles: as
-// gemm_split_plan, in units of 1024 K.
-GemmSplit mx_gemm_split_plan(int64_t M, int64_t N, int64_t K, int cus) {
+// gemm_split_plan, in whole units of 1024 K, when it pays (below).
+// Time of one tile's 1024 K when its round is the last and runs alone, in µs
+// (native E2M1 measured on a single round of 9 tiles at K = 4096; the others
+// scaled from it by their measured whole-chip rates).
+double mx_split_tile_us(int elem, bool exact) {
+    if (exact) return elem == kMxE2M1 ? 20.5 : 23.0;
+    return elem == kMxE2M1 ? 7.0 : 11.4;
+}
+
+// A split of U units of 1024 K into q parts ends when its longest part,
+// ceil(U / q) units, does, so it saves U - ceil(U / q) units of a lone
+// tile's time.  It costs about 1.5 µs + 2.6 µs per part (the second launch
+// and the sum kernel, whose reads grow with q) plus 0.3 µs per MiB of parts
+// written and re-read (fitted to timings of 9- and 64-tile last rounds at
+// K = 2048 and 4096).  The plan takes the q with the largest positive gain,
+// else no split.
+GemmSplit mx_gemm_split_plan(int64_t M, int64_t N, int64_t K, double tile_us, int cus) {
     GemmSplit sp{0, 1, 0};
     if (M <= 0 || N <= 0 || K <= 0 || K % 1024 || cus <= 0) return sp;
     const int64_t tiles = mx_cdiv(N, kMxTile) * mx_cdiv(M, kMxTile), tail = tiles % cus;
     sp.t_main = tiles;
     if (tail == 0) return sp;
-    const int64_t split = std::min<int64_t>(std::min<int64_t>(cus / tail, K / 1024), kMaxTailSplit);
+    const int64_t smax = std::min<int64_t>(std::min<int64_t>(cus / tail, K / 1024), kMaxTailSplit);
+    int64_t split = 1;
+    double best = 0.0;
+    for (int64_t q = 2; q <= smax; ++q) {
+        const int64_t units = K / 1024, longest = (units + q - 1) / q;
+        const double gain =
+            tile_us * (double)(units - longest) - 1.5 - 2.6 * (double)q - 0.3 * 0.25 * (double)(tail * q);
+        if (gain > best) best = gain, split = q;
+    }
     if (split < 2) return sp;
     sp.t_main = tiles - tail;
     sp.split = (int)split;
@@ -1369,7 +1392,7 @@ hipError_t launch_mx_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const
         int cus = 0;
         const hipError_t e = device_cus(cus);
         if (e != hipSuccess) return e;
-        const GemmSplit plan = mx_gemm_split_plan(M, N, K, cus);
+        const GemmSplit plan = mx_gemm_split_plan(M, N, K, mx_split_tile_us(elem, exact), cus);
         if (plan.split > 1 && (size_t)plan.bytes <= ws_bytes) {
             p.t_main = (int)plan.t_main;
             p.split = plan.split;

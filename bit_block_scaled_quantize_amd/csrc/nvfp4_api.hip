@@ -351,7 +351,8 @@ size_t nvfp4_mx_gemm_workspace_size(const nvfp4_mx_tensor* A, const nvfp4_mx_ten
     if (A->rows < 0 || B->rows < 0 || A->cols != B->cols) return 0;
     int cus = 0;
     if (device_cus(cus) != hipSuccess) return 0;
-    const GemmSplit sp = mx_gemm_split_plan(A->rows, B->rows, A->cols, cus);
+    const GemmSplit sp =
+        mx_gemm_split_plan(A->rows, B->rows, A->cols, mx_split_tile_us(A->elem == NVFP4_MX_E4M3 ? kMxE4M3 : kMxE2M1, accum == NVFP4_MX_ACC_EXACT), cus);
     return sp.split > 1 ? (size_t)sp.bytes : 0;
 }
 

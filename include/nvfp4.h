@@ -358,8 +358,10 @@ nvfp4_status nvfp4_mx_gemm(const nvfp4_mx_tensor* A, const nvfp4_mx_tensor* B, v
  * computed in parts along K (whole 1024-element units) whose binary32 sums
  * are added in a fixed order (both accumulation modes; exact: each part's
  * sums scaled as the whole tile's; BF16 output: rounded once); nonzero only
- * for K % 1024 == 0 and such a last round on the current device; 0 also for
- * invalid arguments or when the device cannot be queried. */
+ * for K % 1024 == 0 and such a last round on the current device, where the
+ * library's estimate of the split's saving exceeds its cost (parts written
+ * and summed); 0 also for invalid arguments or when the device cannot be
+ * queried. */
 size_t nvfp4_mx_gemm_workspace_size(const nvfp4_mx_tensor* A, const nvfp4_mx_tensor* B, int32_t c_dt /* nvfp4_dtype */,
                                     int32_t accum);
 

@@ -222,13 +222,13 @@ def test_mx_gemm_8192_sampled(nv, elem):
 
 @pytest.mark.parametrize("accum", ACCUMS)
 @pytest.mark.parametrize("elem", ELEMS)
-@pytest.mark.parametrize("shape", [(512, 512, 1024), (300, 200, 1024), (300, 600, 2048)])
+@pytest.mark.parametrize("shape", [(512, 512, 1024), (300, 200, 1024), (300, 600, 4096)])
 @pytest.mark.parametrize("bf16", [False, True])
 def test_mx_gemm_strided_output(nv, elem, shape, accum, bf16):
     """C written into a column slice of a wider buffer (row pitch N + 96,
     first column 40): the output addressing of whole wave tiles comes from
-    the row pitch.  At K = 2048 with FP32 output the 6 tiles' last round is
-    split in two, and the parts' sum is written with that pitch too.  The
+    the row pitch.  At K = 4096 the 6 tiles' last round is split in four,
+    and the parts' sum is written with that pitch too.  The
     slice matches the oracle, and every byte outside it keeps the buffer's
     fill."""
     M, N, K = shape
@@ -247,11 +247,11 @@ def test_mx_gemm_strided_output(nv, elem, shape, accum, bf16):
 @pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
 @pytest.mark.parametrize("accum", ACCUMS)
 @pytest.mark.parametrize("elem", ELEMS)
-@pytest.mark.parametrize("shape", [(768, 768, 4096), (700, 600, 2048)])
+@pytest.mark.parametrize("shape", [(768, 768, 4096), (700, 600, 5120)])
 def test_mx_gemm_tail_split(nv, elem, shape, accum, bf16):
     """Both accumulation modes, both output types: a last round of tiles that
     would leave compute units idle, computed in parts along K (9 tiles: 4
-    parts at K = 4096, 2 ragged at K = 2048) when the workspace is given; a
+    parts at K = 4096, 5 ragged at K = 5120) when the workspace is given; a
     BF16 output rounds the parts' binary32 sum once.  Split and unsplit
     (workspace=False) both against the oracle; the split result the same
     over two calls."""
@@ -268,3 +268,23 @@ def test_mx_gemm_tail_split(nv, elem, shape, accum, bf16):
                        C2.view(torch.int16 if bf16 else torch.int32)), "split result differs between calls"
     check(nv, qa, qb, bf16=bf16, what=f"split {shape}", accum=accum)
     check(nv, qa, qb, bf16=bf16, what=f"unsplit {shape}", workspace=False, accum=accum)
+
+
+@pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
+@pytest.mark.parametrize("elem", ELEMS)
+def test_mx_gemm_tail_split_uneven(nv, elem, bf16):
+    """Exact accumulation, 16 x 22 tiles at K = 5120: on 256 compute units the
+    last round is 96 tiles, split in two parts of unequal length (two and
+    three units of 1024 K).  Split and unsplit against the oracle on sampled
+    entries: 2048 anywhere and 2048 in rows 2816-4095 (the tile rows that
+    hold the last round's tiles).  Where the device has another number of
+    compute units the split differs or does not happen; the comparison
+    still holds."""
+    M, N, K = 4096, 5632, 5120
+    qa = mxq(W.student_t((M, K), 3.0, seed=51), elem)
+    qb = mxq(W.student_t((N, K), 3.0, seed=53), elem, seed=1)
+    rng = np.random.default_rng(55)
+    mi = np.concatenate([rng.integers(0, M, 2048), rng.integers(2816, M, 2048)])
+    ni = rng.integers(0, N, 4096)
+    check(nv, qa, qb, bf16=bf16, entries=(mi, ni), what="uneven split", accum=EXACT)
+    check(nv, qa, qb, bf16=bf16, entries=(mi, ni), what="uneven unsplit", workspace=False, accum=EXACT)
