@@ -89,6 +89,53 @@ def test_sequence_graph_replays_match_eager(nv):
     assert np.array_equal(ref[1].cpu().numpy(), q.codes) and np.array_equal(ref[2].cpu().numpy(), q.scales)
 
 
+def test_split_gemms_graph_replays_match_eager(nv):
+    """The GEMMs with a workspace: a last round of 9 tiles split along K runs
+    as two or three launches (whole tiles, parts, their sum), for FP32 and
+    BF16 outputs of nvfp4_gemm and nvfp4_mx_gemm (native E2M1, exact E4M3).
+    Captured once, replayed with every output and the workspaces overwritten
+    in between; each replay reproduces the eager outputs bit for bit."""
+    M = N = 768
+    K = 4096
+    dev = "cuda"
+    xa = to_device(W.f32_to_bf16_bits(W.student_t((M, K), 3.0, seed=61)))
+    xb = to_device(W.f32_to_bf16_bits(W.student_t((N, K), 3.0, seed=62)))
+    qa, qb = nv.nvfp4_quantize(xa), nv.nvfp4_quantize(xb)
+    ma, mb = nv.nvfp4_mx_quantize(xa, elem=nv.NVFP4_MX_E2M1), nv.nvfp4_mx_quantize(xb, elem=nv.NVFP4_MX_E2M1)
+    ea, eb = nv.nvfp4_mx_quantize(xa, elem=nv.NVFP4_MX_E4M3), nv.nvfp4_mx_quantize(xb, elem=nv.NVFP4_MX_E4M3)
+    calls = []
+    for dt in (torch.float32, torch.bfloat16):
+        calls.append((nv.nvfp4_gemm, qa, qb, dt, {}, nv.nvfp4_gemm_workspace_size(qa, qb, out_dtype=dt)))
+        calls.append((nv.nvfp4_mx_gemm, ma, mb, dt, {"accum": nv.NVFP4_MX_ACC_NATIVE},
+                      nv.nvfp4_mx_gemm_workspace_size(ma, mb, out_dtype=dt, accum=nv.NVFP4_MX_ACC_NATIVE)))
+        calls.append((nv.nvfp4_mx_gemm, ea, eb, dt, {"accum": nv.NVFP4_MX_ACC_EXACT},
+                      nv.nvfp4_mx_gemm_workspace_size(ea, eb, out_dtype=dt, accum=nv.NVFP4_MX_ACC_EXACT)))
+    assert all(c[5] > 0 for c in calls), [c[5] for c in calls]
+    outs = [torch.empty((M, N), dtype=c[3], device=dev) for c in calls]
+    wss = [torch.empty(c[5] // 4, dtype=torch.float32, device=dev) for c in calls]
+    torch.cuda.synchronize()
+
+    def seq():
+        for (fn, a, b, dt, kw, _), o, w in zip(calls, outs, wss):
+            fn(a, b, out_dtype=dt, out=o, workspace=w, **kw)
+
+    seq()
+    torch.cuda.synchronize()
+    ref = [o.clone() for o in outs]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        seq()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for t in outs + wss:
+            t.view(torch.uint8).fill_(0x3C + rep)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k, (o, r) in enumerate(zip(outs, ref)):
+            assert torch.equal(o.view(torch.uint8), r.view(torch.uint8)), f"replay {rep}: call {k} differs"
+
+
 def test_two_streams_match_one_stream(nv):
     """The library keeps no state between calls: the same calls split over two
     streams (default priority), overlapping, give bit-identical outputs to
