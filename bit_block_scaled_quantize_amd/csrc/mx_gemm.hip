@@ -810,6 +810,18 @@ __device__ __forceinline__ void mx_full8_read(const uint8_t* slot, const uint8_t
     }
 }
 
+// Logical tile lg -> tile (row-major index): logical tiles run down each
+// group of 4 tile rows column by column, so that consecutive logical tiles
+// (the ones an XCD runs at once) share A rows and B rows, also where the
+// grid is narrow (a 20-tile row would otherwise spread one XCD's 32 tiles
+// over 13 tile rows and 5 columns instead of 4 x 8).  A bijection on the
+// grid's tiles; the last group may hold fewer rows.
+__device__ __forceinline__ int mx_tile_of(const MxGemmArgs& p, int lg) {
+    const int rows = (int)((p.M + kMxTile - 1) / kMxTile), gsz = 4 * p.tiles_x;
+    const int grp = lg / gsz, first = 4 * grp, gm = min(rows - first, 4), r = lg - grp * gsz;
+    return (first + r % gm) * p.tiles_x + r / gm;
+}
+
 // Work item L = first + bx of a full-line workgroup bx: tile L whole
 // (L < t_main), or part s of tile t_main + j / split (j = L - t_main,
 // s = j % split), which takes units [s U / split, (s + 1) U / split) of the
@@ -825,7 +837,14 @@ __device__ __forceinline__ MxWork mx_work(const MxGemmArgs& p, int units, uint32
         w.part = j;
         w.u0 = sp * units / p.split;
         w.u1 = (sp + 1) * units / p.split;
+    } else {
+        // workgroups are dealt to the 8 XCDs in turn (L to XCD L % 8): of the
+        // first t8 (t_main rounded down to a multiple of 8), XCD x's take the
+        // x-th eighth of those logical tiles in order
+        const int t8 = p.t_main & ~7;
+        if (w.tile < t8) w.tile = (w.tile & 7) * (t8 >> 3) + (w.tile >> 3);
     }
+    w.tile = mx_tile_of(p, w.tile);
     return w;
 }
 
@@ -997,7 +1016,7 @@ __global__ void __launch_bounds__(512, 1) k_mx_gemm_full8(MxGemmArgs p) {
 // 16 y of the tile.
 template <bool OUT_BF16>
 __global__ void __launch_bounds__(256) k_mx_tail_sum(MxGemmArgs p) {
-    const int tile = p.t_main + (int)blockIdx.x;
+    const int tile = mx_tile_of(p, p.t_main + (int)blockIdx.x);
     const int64_t m0 = (int64_t)(tile / p.tiles_x) * kMxTile, n0 = (int64_t)(tile % p.tiles_x) * kMxTile;
     const float* part0 = p.parts + (int64_t)blockIdx.x * p.split * kMxTile * kMxTile;
 #pragma unroll
