@@ -288,3 +288,24 @@ def test_mx_gemm_tail_split_uneven(nv, elem, bf16):
     ni = rng.integers(0, N, 4096)
     check(nv, qa, qb, bf16=bf16, entries=(mi, ni), what="uneven split", accum=EXACT)
     check(nv, qa, qb, bf16=bf16, entries=(mi, ni), what="uneven unsplit", workspace=False, accum=EXACT)
+
+
+@pytest.mark.parametrize("elem,accum,shape,parts", [
+    (O.MX_FP4, NATIVE, (6144, 6144, 4096), 0),    # 64-tile last round, short K: not split
+    (O.MX_FP4, NATIVE, (768, 768, 4096), 9 * 4),   # 9 lone tiles: 4 parts each
+    (O.MX_FP4, NATIVE, (700, 600, 2048), 0),
+    (O.MX_FP8, NATIVE, (700, 600, 2048), 9 * 2),
+    (O.MX_FP8, EXACT, (6144, 6144, 4096), 64 * 4),
+    (O.MX_FP4, NATIVE, (20480, 5120, 8192), 64 * 2),
+])
+def test_mx_split_plan_choices(nv, elem, accum, shape, parts):
+    """The split plan's choices for the shapes its cost estimate was fitted
+    on, as workspace sizes (parts x 256 x 256 binary32), on a 256-CU device:
+    a native E2M1 last round of 64 tiles at K = 4096 or 2048 K is not split,
+    lone tiles and the slower kernels are."""
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("the plan depends on the compute unit count; these choices are for 256")
+    M, N, K = shape
+    e = nv.NVFP4_MX_E4M3 if elem == O.MX_FP8 else nv.NVFP4_MX_E2M1
+    A, B = nv.MXTensor.empty(M, K, e), nv.MXTensor.empty(N, K, e)
+    assert nv.nvfp4_mx_gemm_workspace_size(A, B, accum=accum) == parts * 256 * 256 * 4
